@@ -1,0 +1,339 @@
+// C ABI of the HiLS-Attention forward pass (declared in include/hils.h):
+// argument validation on the host, workspace layout, launch geometry and
+// HIP error mapping.  Nothing here allocates memory or synchronises.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/hils.h"
+#include "launch.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+hils_status fail(hils_status s, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return s;
+}
+
+hils_status hip_fail(hipError_t e, const char *what) {
+  return fail(HILS_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+float tau_of(const hils_config *c) {
+  return c->scale > 0.f ? c->scale : 1.0f / std::sqrt(static_cast<float>(c->head_dim));
+}
+
+size_t elem_bytes(const hils_config *c) { return c->dtype == HILS_BF16 ? 2 : 4; }
+
+int eligible(int i, int W, int S) {
+  int w0 = i - W + 1;
+  return w0 > 0 ? w0 / S : 0;
+}
+
+// Checks shared by every call.
+hils_status check_config(const hils_config *c) {
+  if (!c) return fail(HILS_ERR_INVALID_ARG, "config is NULL");
+  if (c->batch < 1 || c->seq_len < 1) return fail(HILS_ERR_INVALID_ARG, "batch and seq_len must be >= 1");
+  if (c->n_q_heads < 1 || c->n_kv_heads < 1 || c->n_q_heads % c->n_kv_heads != 0)
+    return fail(HILS_ERR_INVALID_ARG, "n_q_heads (%d) must be a positive multiple of n_kv_heads (%d)",
+                c->n_q_heads, c->n_kv_heads);
+  if (c->n_q_heads / c->n_kv_heads > 16) return fail(HILS_ERR_UNSUPPORTED, "GQA group size above 16");
+  if (c->head_dim != 64 && c->head_dim != 128) return fail(HILS_ERR_UNSUPPORTED, "head_dim must be 64 or 128");
+  if (c->chunk_size != 64) return fail(HILS_ERR_UNSUPPORTED, "chunk_size must be 64");
+  if (c->top_k < 0) return fail(HILS_ERR_INVALID_ARG, "top_k must be >= 0");
+  if (c->top_k > 32) return fail(HILS_ERR_UNSUPPORTED, "top_k above 32");
+  if (c->window < 1) return fail(HILS_ERR_INVALID_ARG, "window must be >= 1");
+  if (c->qcal_rank < 0) return fail(HILS_ERR_INVALID_ARG, "qcal_rank must be >= 0");
+  if (c->qcal_rank > 64) return fail(HILS_ERR_UNSUPPORTED, "qcal_rank above 64");
+  if (c->qcal_rank > 0 && c->hidden_dim < 1) return fail(HILS_ERR_INVALID_ARG, "hidden_dim must be >= 1 with Q-Cal");
+  if (c->dtype != HILS_BF16 && c->dtype != HILS_F32) return fail(HILS_ERR_INVALID_ARG, "unknown dtype %d", c->dtype);
+  if (!(c->scale >= 0.f) || std::isinf(c->scale)) return fail(HILS_ERR_INVALID_ARG, "scale must be finite and >= 0");
+  return HILS_OK;
+}
+
+hils_status check_ptr(const void *p, const char *name) {
+  if (!p) return fail(HILS_ERR_INVALID_ARG, "%s is NULL", name);
+  if (!aligned16(p)) return fail(HILS_ERR_INVALID_ARG, "%s is not 16-byte aligned", name);
+  return HILS_OK;
+}
+
+#define CHECK(expr)                      \
+  do {                                   \
+    hils_status s_ = (expr);             \
+    if (s_ != HILS_OK) return s_;        \
+  } while (0)
+
+hils_status check_qcal_ptrs(const hils_config *c, const void *h, const void *wd, const void *wu) {
+  if (c->qcal_rank == 0) {
+    if (h || wd || wu) return fail(HILS_ERR_INVALID_ARG, "h, w_down and w_up must be NULL when qcal_rank == 0");
+    return HILS_OK;
+  }
+  CHECK(check_ptr(h, "h"));
+  CHECK(check_ptr(wd, "w_down"));
+  CHECK(check_ptr(wu, "w_up"));
+  return HILS_OK;
+}
+
+// ------------------------------------------------------------ decode geometry
+struct DecodeGeom {
+  int P, CPB, NW, nslots, nslot_blocks;
+  size_t off_counts, off_qhat, off_cand_key, off_cand_s, off_parts, total;
+};
+
+constexpr int kMaxCand = 4096;
+
+hils_status decode_geom(const hils_config *c, DecodeGeom *g) {
+  const int G = c->n_q_heads / c->n_kv_heads, K = c->top_k, S = c->chunk_size;
+  const int nmax = eligible(c->seq_len - 1, c->window, S);
+  const int pmax = kMaxCand / (K > 0 ? K : 1);
+  int cpb = (nmax + pmax - 1) / pmax;
+  cpb = cpb < 64 ? 64 : (cpb + 63) / 64 * 64;
+  if (cpb > 1024 || cpb * G > 4096)
+    return fail(HILS_ERR_UNSUPPORTED, "decode: %d eligible chunks with top_k %d and group %d exceed the merge capacity",
+                nmax, K, G);
+  g->CPB = cpb;
+  g->P = nmax > 0 ? (nmax + cpb - 1) / cpb : 1;
+  g->NW = (c->window + S - 1 + 63) / 64;
+  g->nslots = K + g->NW;
+  g->nslot_blocks = K > 0 ? K : 1;
+  const size_t B = c->batch, Hkv = c->n_kv_heads, Hq = c->n_q_heads, D = c->head_dim;
+  size_t off = 0;
+  g->off_counts = off;
+  off = align_up(off + sizeof(unsigned) * (2 * B * Hkv + 1));
+  g->off_qhat = off;
+  if (c->qcal_rank > 0) off = align_up(off + sizeof(float) * B * Hq * D);
+  g->off_cand_key = off;
+  off = align_up(off + sizeof(unsigned long long) * B * Hkv * g->P * (K > 0 ? K : 1));
+  g->off_cand_s = off;
+  off = align_up(off + sizeof(float) * B * Hkv * g->P * (K > 0 ? K : 1) * G);
+  g->off_parts = off;
+  off = align_up(off + sizeof(float) * B * Hkv * g->nslots * G * (D + 2));
+  g->total = off;
+  return HILS_OK;
+}
+
+struct DenseGeom {
+  int P, L;
+  size_t off_counts, off_parts, total;
+};
+
+void dense_geom(const hils_config *c, DenseGeom *g) {
+  const long long T = c->seq_len;
+  const long long units = (T + 63) / 64;
+  const long long per_seq_target = 4096 / (static_cast<long long>(c->batch) * c->n_kv_heads) + 1;
+  long long upb = (units + per_seq_target - 1) / per_seq_target;  // units per block
+  if (upb < 4) upb = 4;
+  g->L = static_cast<int>(upb * 64);
+  g->P = static_cast<int>((T + g->L - 1) / g->L);
+  const size_t B = c->batch, Hkv = c->n_kv_heads, G = c->n_q_heads / c->n_kv_heads, D = c->head_dim;
+  g->off_counts = 0;
+  g->off_parts = align_up(sizeof(unsigned) * (B * Hkv + 1));
+  g->total = align_up(g->off_parts + sizeof(float) * B * Hkv * g->P * G * (D + 2));
+}
+
+size_t prefill_u_bytes(const hils_config *c) {
+  return c->qcal_rank > 0 ? align_up(sizeof(float) * c->batch * static_cast<size_t>(c->seq_len) * c->qcal_rank) : 0;
+}
+
+hils_status finish(hipError_t e, const char *what) {
+  if (e != hipSuccess) return hip_fail(e, what);
+  return HILS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *hils_status_string(hils_status s) {
+  switch (s) {
+    case HILS_OK: return "HILS_OK";
+    case HILS_ERR_INVALID_ARG: return "HILS_ERR_INVALID_ARG";
+    case HILS_ERR_UNSUPPORTED: return "HILS_ERR_UNSUPPORTED";
+    case HILS_ERR_WORKSPACE: return "HILS_ERR_WORKSPACE";
+    case HILS_ERR_HIP: return "HILS_ERR_HIP";
+  }
+  return "unknown hils_status";
+}
+
+const char *hils_last_error(void) { return g_last_error.c_str(); }
+
+hils_status hils_landmark_summary(const hils_config *cfg, const void *k, const void *q_lm, int32_t chunk_begin,
+                                  int32_t chunk_end, void *k_sum, float *b_sum, void *stream) {
+  g_last_error.clear();
+  CHECK(check_config(cfg));
+  const int C = cfg->seq_len / cfg->chunk_size;
+  if (chunk_begin < 0 || chunk_end < chunk_begin || chunk_end > C)
+    return fail(HILS_ERR_INVALID_ARG, "chunk range [%d, %d) outside [0, %d]", chunk_begin, chunk_end, C);
+  if (chunk_end == chunk_begin) return HILS_OK;
+  CHECK(check_ptr(k, "k"));
+  CHECK(check_ptr(q_lm, "q_lm"));
+  CHECK(check_ptr(k_sum, "k_sum"));
+  CHECK(check_ptr(b_sum, "b_sum"));
+  hils::SummaryArgs a{k, q_lm, k_sum, b_sum, cfg->batch, cfg->seq_len, cfg->n_q_heads, cfg->n_kv_heads, C,
+                      cfg->head_dim, chunk_begin, chunk_end, tau_of(cfg), cfg->dtype == HILS_BF16};
+  return finish(hils::launch_summary(a, static_cast<hipStream_t>(stream)), "landmark summary launch");
+}
+
+size_t hils_prefill_workspace_bytes(const hils_config *cfg) {
+  if (check_config(cfg) != HILS_OK) return 0;
+  return prefill_u_bytes(cfg) + kAlign;
+}
+
+hils_status hils_chunk_score_topk(const hils_config *cfg, const void *q, const void *h, const void *w_down,
+                                  const void *w_up, const void *k_sum, const float *b_sum, int32_t *topk_idx,
+                                  float *topk_score, void *workspace, size_t workspace_bytes, void *stream) {
+  g_last_error.clear();
+  CHECK(check_config(cfg));
+  CHECK(check_ptr(q, "q"));
+  CHECK(check_qcal_ptrs(cfg, h, w_down, w_up));
+  const int C = cfg->seq_len / cfg->chunk_size;
+  if (C > 0) {
+    CHECK(check_ptr(k_sum, "k_sum"));
+    CHECK(check_ptr(b_sum, "b_sum"));
+  }
+  if (cfg->top_k > 0) {
+    CHECK(check_ptr(topk_idx, "topk_idx"));
+    CHECK(check_ptr(topk_score, "topk_score"));
+  }
+  if (C > 8192) return fail(HILS_ERR_UNSUPPORTED, "prefill scoring supports at most 8192 chunks (got %d)", C);
+  const size_t need = hils_prefill_workspace_bytes(cfg);
+  if (!workspace || workspace_bytes < need)
+    return fail(HILS_ERR_WORKSPACE, "prefill workspace of %zu bytes given, %zu needed", workspace_bytes, need);
+  if (!aligned16(workspace)) return fail(HILS_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
+  if (cfg->top_k == 0) return HILS_OK;
+  hils::ScoreArgs a{q, h, w_down, w_up, k_sum, b_sum, topk_idx, topk_score, static_cast<float *>(workspace),
+                    static_cast<char *>(workspace) + prefill_u_bytes(cfg), cfg->batch, cfg->seq_len,
+                    cfg->n_q_heads, cfg->n_kv_heads, cfg->head_dim, cfg->chunk_size, cfg->top_k, cfg->window,
+                    cfg->qcal_rank, cfg->hidden_dim, C, tau_of(cfg), cfg->dtype == HILS_BF16};
+  return finish(hils::launch_score_valu(a, static_cast<hipStream_t>(stream)), "chunk score/top-k launch");
+}
+
+hils_status hils_sparse_attn_prefill(const hils_config *cfg, const void *q, const void *k, const void *v,
+                                     const int32_t *topk_idx, const float *topk_score, void *o, void *workspace,
+                                     size_t workspace_bytes, void *stream) {
+  g_last_error.clear();
+  CHECK(check_config(cfg));
+  CHECK(check_ptr(q, "q"));
+  CHECK(check_ptr(k, "k"));
+  CHECK(check_ptr(v, "v"));
+  CHECK(check_ptr(o, "o"));
+  if (cfg->top_k > 0) {
+    CHECK(check_ptr(topk_idx, "topk_idx"));
+    CHECK(check_ptr(topk_score, "topk_score"));
+  }
+  const size_t need = hils_prefill_workspace_bytes(cfg);
+  if (!workspace || workspace_bytes < need)
+    return fail(HILS_ERR_WORKSPACE, "prefill workspace of %zu bytes given, %zu needed", workspace_bytes, need);
+  if (!aligned16(workspace)) return fail(HILS_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
+  hils::AttnArgs a{q, k, v, topk_idx, topk_score, o, workspace, cfg->batch, cfg->seq_len, cfg->n_q_heads,
+                   cfg->n_kv_heads, cfg->head_dim, cfg->chunk_size, cfg->top_k, cfg->window, tau_of(cfg),
+                   cfg->dtype == HILS_BF16};
+  return finish(hils::launch_attn_valu(a, static_cast<hipStream_t>(stream)), "sparse attention launch");
+}
+
+size_t hils_decode_workspace_bytes(const hils_config *cfg) {
+  if (check_config(cfg) != HILS_OK) return 0;
+  DecodeGeom g;
+  if (decode_geom(cfg, &g) != HILS_OK) return 0;
+  return g.total;
+}
+
+size_t hils_decode_error_offset(const hils_config *cfg) {
+  if (check_config(cfg) != HILS_OK) return 0;
+  return sizeof(unsigned) * 2 * static_cast<size_t>(cfg->batch) * cfg->n_kv_heads;
+}
+
+hils_status hils_sparse_attn_decode(const hils_config *cfg, const void *q, const void *h, const void *w_down,
+                                    const void *w_up, const void *k_cache, const void *v_cache, const void *k_sum,
+                                    const float *b_sum, const int32_t *seq_lens, void *o, int32_t *topk_idx,
+                                    float *topk_score, void *workspace, size_t workspace_bytes, void *stream) {
+  g_last_error.clear();
+  CHECK(check_config(cfg));
+  CHECK(check_ptr(q, "q"));
+  CHECK(check_qcal_ptrs(cfg, h, w_down, w_up));
+  CHECK(check_ptr(k_cache, "k_cache"));
+  CHECK(check_ptr(v_cache, "v_cache"));
+  const int Cmax = cfg->seq_len / cfg->chunk_size;
+  if (Cmax > 0) {
+    CHECK(check_ptr(k_sum, "k_sum"));
+    CHECK(check_ptr(b_sum, "b_sum"));
+  }
+  if (!seq_lens) return fail(HILS_ERR_INVALID_ARG, "seq_lens is NULL");
+  CHECK(check_ptr(o, "o"));
+  if (cfg->top_k > 0) {
+    CHECK(check_ptr(topk_idx, "topk_idx"));
+    CHECK(check_ptr(topk_score, "topk_score"));
+  }
+  DecodeGeom g;
+  CHECK(decode_geom(cfg, &g));
+  if (!workspace || workspace_bytes < g.total)
+    return fail(HILS_ERR_WORKSPACE, "decode workspace of %zu bytes given, %zu needed", workspace_bytes, g.total);
+  if (!aligned16(workspace)) return fail(HILS_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
+  char *ws = static_cast<char *>(workspace);
+  const size_t BH = static_cast<size_t>(cfg->batch) * cfg->n_kv_heads;
+  unsigned *counts = reinterpret_cast<unsigned *>(ws + g.off_counts);
+  hils::DecodeArgs a{};
+  a.q = q; a.h = h; a.w_down = w_down; a.w_up = w_up; a.k_cache = k_cache; a.v_cache = v_cache;
+  a.k_sum = k_sum; a.b_sum = b_sum; a.seq_lens = seq_lens; a.o = o; a.topk_idx = topk_idx;
+  a.topk_score = topk_score;
+  a.qhat = reinterpret_cast<float *>(ws + g.off_qhat);
+  a.cand_key = reinterpret_cast<unsigned long long *>(ws + g.off_cand_key);
+  a.cand_s = reinterpret_cast<float *>(ws + g.off_cand_s);
+  a.parts = reinterpret_cast<float *>(ws + g.off_parts);
+  a.count1 = counts; a.count2 = counts + BH; a.err = counts + 2 * BH;
+  a.B = cfg->batch; a.Tmax = cfg->seq_len; a.Hq = cfg->n_q_heads; a.Hkv = cfg->n_kv_heads;
+  a.d = cfg->head_dim; a.S = cfg->chunk_size; a.K = cfg->top_k; a.W = cfg->window;
+  a.r = cfg->qcal_rank; a.Dh = cfg->hidden_dim; a.Cmax = Cmax;
+  a.P = g.P; a.CPB = g.CPB; a.NW = g.NW; a.nslots = g.nslots; a.nslot_blocks = g.nslot_blocks;
+  a.tau = tau_of(cfg); a.bf16 = cfg->dtype == HILS_BF16;
+  // topk buffers are also read back by the attend kernel: provide scratch when K == 0
+  return finish(hils::launch_decode(a, static_cast<hipStream_t>(stream)), "sparse decode launch");
+}
+
+size_t hils_dense_decode_workspace_bytes(const hils_config *cfg) {
+  if (check_config(cfg) != HILS_OK) return 0;
+  DenseGeom g;
+  dense_geom(cfg, &g);
+  return g.total;
+}
+
+hils_status hils_dense_attn_decode(const hils_config *cfg, const void *q, const void *k_cache, const void *v_cache,
+                                   const int32_t *seq_lens, void *o, void *workspace, size_t workspace_bytes,
+                                   void *stream) {
+  g_last_error.clear();
+  CHECK(check_config(cfg));
+  CHECK(check_ptr(q, "q"));
+  CHECK(check_ptr(k_cache, "k_cache"));
+  CHECK(check_ptr(v_cache, "v_cache"));
+  if (!seq_lens) return fail(HILS_ERR_INVALID_ARG, "seq_lens is NULL");
+  CHECK(check_ptr(o, "o"));
+  DenseGeom g;
+  dense_geom(cfg, &g);
+  if (!workspace || workspace_bytes < g.total)
+    return fail(HILS_ERR_WORKSPACE, "dense decode workspace of %zu bytes given, %zu needed", workspace_bytes, g.total);
+  if (!aligned16(workspace)) return fail(HILS_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
+  char *ws = static_cast<char *>(workspace);
+  unsigned *counts = reinterpret_cast<unsigned *>(ws + g.off_counts);
+  const size_t BH = static_cast<size_t>(cfg->batch) * cfg->n_kv_heads;
+  hils::DenseArgs a{q, k_cache, v_cache, seq_lens, o, reinterpret_cast<float *>(ws + g.off_parts), counts,
+                    counts + BH, cfg->batch, cfg->seq_len, cfg->n_q_heads, cfg->n_kv_heads, cfg->head_dim,
+                    g.P, g.L, tau_of(cfg), cfg->dtype == HILS_BF16};
+  return finish(hils::launch_dense_decode(a, static_cast<hipStream_t>(stream)), "dense decode launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,154 @@
+// Device helpers shared by the HiLS kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hils {
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- bf16
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// round to nearest, ties to even (NaN kept quiet)
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7F800000u) == 0x7F800000u) return static_cast<uint16_t>((u >> 16) | ((u & 0xFFFFu) ? 0x40u : 0u));
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// Element access for the two storage types: uint16_t = bf16 bits, float = f32.
+template <typename T> struct Elem;
+template <> struct Elem<uint16_t> {
+  __device__ __forceinline__ static float load(const uint16_t *p, size_t i) { return bf16_to_f32(p[i]); }
+  __device__ __forceinline__ static void store(uint16_t *p, size_t i, float v) { p[i] = f32_to_bf16(v); }
+  // 8 consecutive elements (16-byte aligned)
+  __device__ __forceinline__ static void load8(const uint16_t *p, float *o) {
+    uint4 w = *reinterpret_cast<const uint4 *>(p);
+    uint32_t a[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      o[2 * i] = __uint_as_float(a[i] << 16);
+      o[2 * i + 1] = __uint_as_float(a[i] & 0xFFFF0000u);
+    }
+  }
+  // 2 consecutive elements (4-byte aligned)
+  __device__ __forceinline__ static void load2(const uint16_t *p, float *o) {
+    uint32_t a = *reinterpret_cast<const uint32_t *>(p);
+    o[0] = __uint_as_float(a << 16);
+    o[1] = __uint_as_float(a & 0xFFFF0000u);
+  }
+  __device__ __forceinline__ static void store2(uint16_t *p, float a, float b) {
+    uint32_t w = static_cast<uint32_t>(f32_to_bf16(a)) | (static_cast<uint32_t>(f32_to_bf16(b)) << 16);
+    *reinterpret_cast<uint32_t *>(p) = w;
+  }
+};
+template <> struct Elem<float> {
+  __device__ __forceinline__ static float load(const float *p, size_t i) { return p[i]; }
+  __device__ __forceinline__ static void store(float *p, size_t i, float v) { p[i] = v; }
+  __device__ __forceinline__ static void load8(const float *p, float *o) {
+    float4 a = reinterpret_cast<const float4 *>(p)[0];
+    float4 b = reinterpret_cast<const float4 *>(p)[1];
+    o[0] = a.x; o[1] = a.y; o[2] = a.z; o[3] = a.w;
+    o[4] = b.x; o[5] = b.y; o[6] = b.z; o[7] = b.w;
+  }
+  __device__ __forceinline__ static void load2(const float *p, float *o) {
+    float2 a = *reinterpret_cast<const float2 *>(p);
+    o[0] = a.x; o[1] = a.y;
+  }
+  __device__ __forceinline__ static void store2(float *p, float a, float b) {
+    *reinterpret_cast<float2 *>(p) = make_float2(a, b);
+  }
+};
+
+// ---------------------------------------------------------------- reductions
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+// reduce inside aligned groups of `width` lanes (width a power of two <= 64)
+template <int width>
+__device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+  for (int o = width / 2; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+template <int width>
+__device__ __forceinline__ float group_max(float v) {
+#pragma unroll
+  for (int o = width / 2; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    unsigned long long w = __shfl_xor(v, o, kWave);
+    v = w > v ? w : v;
+  }
+  return v;
+}
+
+// ---------------------------------------------------------------- selection keys
+// A 64-bit key whose unsigned order is (score descending, chunk ascending):
+// high word = order-preserving image of the float, low word = ~chunk.
+__device__ __forceinline__ uint32_t orderable(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float from_orderable(uint32_t o) {
+  uint32_t u = (o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o;
+  return __uint_as_float(u);
+}
+__device__ __forceinline__ unsigned long long make_key(float score, int chunk) {
+  return (static_cast<unsigned long long>(orderable(score)) << 32) |
+         static_cast<uint32_t>(~static_cast<uint32_t>(chunk));
+}
+__device__ __forceinline__ int key_chunk(unsigned long long k) {
+  return static_cast<int>(~static_cast<uint32_t>(k & 0xFFFFFFFFu));
+}
+__device__ __forceinline__ float key_score(unsigned long long k) {
+  return from_orderable(static_cast<uint32_t>(k >> 32));
+}
+constexpr unsigned long long kNoKey = 0ull;  // below every real key
+
+// Loads of data another workgroup published before an atomic ticket: atomic
+// (device-coherent) loads, so a stale per-CU cache line is never used.
+__device__ __forceinline__ float load_acquired(const float *p) {
+  return __uint_as_float(__hip_atomic_load(reinterpret_cast<const uint32_t *>(p), __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT));
+}
+__device__ __forceinline__ unsigned long long load_acquired(const unsigned long long *p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// R1 partition: complete chunks before query i's window
+__device__ __forceinline__ int eligible_chunks(int i, int W, int S) {
+  int w0 = i - W + 1;
+  return w0 > 0 ? w0 / S : 0;
+}
+
+// merge two online-softmax partials (m, l) into the first; returns the scale
+// that the first partial's accumulator must be multiplied by, and sets *sb to
+// the scale for the second.
+__device__ __forceinline__ float merge_ml(float &m, float &l, float m2, float l2, float *sb) {
+  float mn = fmaxf(m, m2);
+  float sa = (m == -INFINITY) ? 0.f : __expf(m - mn);
+  float s2 = (m2 == -INFINITY) ? 0.f : __expf(m2 - mn);
+  l = l * sa + l2 * s2;
+  m = mn;
+  *sb = s2;
+  return sa;
+}
+
+}  // namespace hils

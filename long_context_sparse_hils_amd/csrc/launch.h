@@ -1,0 +1,77 @@
+// Internal interface between the C ABI (api.cpp) and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace hils {
+
+struct SummaryArgs {
+  const void *k, *q_lm;
+  void *k_sum;
+  float *b_sum;
+  int B, T, Hq, Hkv, C, d, c0, c1;
+  float tau;
+  bool bf16;
+};
+
+struct ScoreArgs {
+  const void *q, *h, *w_down, *w_up, *k_sum;
+  const float *b_sum;
+  int32_t *topk_idx;
+  float *topk_score;
+  float *u_ws;  // [B*T, r] fp32 (Q-Cal down projection)
+  void *ws;     // remaining prefill workspace
+  int B, T, Hq, Hkv, d, S, K, W, r, Dh, C;
+  float tau;
+  bool bf16;
+};
+
+struct AttnArgs {
+  const void *q, *k, *v;
+  const int32_t *topk_idx;
+  const float *topk_score;
+  void *o;
+  void *vt_ws;  // transposed value tiles for the MFMA path
+  int B, T, Hq, Hkv, d, S, K, W;
+  float tau;
+  bool bf16;
+};
+
+struct DecodeArgs {
+  const void *q, *h, *w_down, *w_up, *k_cache, *v_cache, *k_sum;
+  const float *b_sum;
+  const int32_t *seq_lens;
+  void *o;
+  int32_t *topk_idx;
+  float *topk_score;
+  float *qhat;                   // [B, Hq, d] (Q-Cal only)
+  unsigned long long *cand_key;  // [B, Hkv, P, K]
+  float *cand_s;                 // [B, Hkv, P, K, G]
+  float *parts;                  // [B, Hkv, nslots, G, d+2]
+  unsigned *count1, *count2, *err;
+  int B, Tmax, Hq, Hkv, d, S, K, W, r, Dh, Cmax;
+  int P, CPB, NW, nslots, nslot_blocks;
+  float tau;
+  bool bf16;
+};
+
+struct DenseArgs {
+  const void *q, *k_cache, *v_cache;
+  const int32_t *seq_lens;
+  void *o;
+  float *parts;  // [B, Hkv, P, G, d+2]
+  unsigned *count, *err;
+  int B, Tmax, Hq, Hkv, d, P, L;
+  float tau;
+  bool bf16;
+};
+
+hipError_t launch_summary(const SummaryArgs &a, hipStream_t st);
+hipError_t launch_score_valu(const ScoreArgs &a, hipStream_t st);
+hipError_t launch_attn_valu(const AttnArgs &a, hipStream_t st);
+hipError_t launch_decode(const DecodeArgs &a, hipStream_t st);
+hipError_t launch_dense_decode(const DenseArgs &a, hipStream_t st);
+
+}  // namespace hils

@@ -1,0 +1,93 @@
+// Landmark chunk summary (HiLS-Attention, picx.dev summary, Methodology 1,
+// Eq. 8): for one chunk of S = 64 keys and each landmark query q'_c of the
+// group, p = softmax(tau q'_c . k_j), k' = sum_j p_j k_j, b' = -sum_j p_j log p_j.
+//
+// One workgroup per (chunk, KV head, batch).  The chunk's keys are read from
+// HBM once (coalesced 16-byte loads), widened to fp32 in LDS with a padded
+// row stride so that one key per lane reads conflict-free, and shared by the
+// G query heads of the group (one wave per head).  HBM-bound: 16 KB of keys
+// per (b, g, c) against G*(d*2+4) bytes written.
+#include "hils_common.h"
+#include "launch.h"
+
+namespace hils {
+
+constexpr int kSumS = 64;      // chunk size handled here
+constexpr int kSumThreads = 256;
+
+template <typename T, int D>
+__global__ void __launch_bounds__(kSumThreads)
+landmark_summary_kernel(const T *__restrict__ k, const T *__restrict__ q_lm, T *__restrict__ k_sum,
+                        float *__restrict__ b_sum, int T_len, int Hq, int Hkv, int C, int c0,
+                        float tau) {
+  constexpr int LD = D + 1;  // padded fp32 row stride (conflict-free column reads)
+  __shared__ float keys[kSumS * LD];
+  __shared__ float qrow[4][D];
+  __shared__ float prob[4][kSumS];
+  const int c = c0 + blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int G = Hq / Hkv;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+  // stage the chunk's keys: 64 x D elements, 8 per thread per step
+  const T *kc = k + ((static_cast<size_t>(b) * Hkv + g) * T_len + static_cast<size_t>(c) * kSumS) * D;
+  for (int e8 = tid; e8 < kSumS * D / 8; e8 += kSumThreads) {
+    float v[8];
+    Elem<T>::load8(kc + e8 * 8, v);
+    int row = (e8 * 8) / D, col = (e8 * 8) % D;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) keys[row * LD + col + t] = v[t];
+  }
+  __syncthreads();
+
+  __shared__ float ent_s[4];
+  for (int h0 = 0; h0 < G; h0 += 4) {
+    const int h = g * G + h0 + wave;
+    const bool active = (h0 + wave) < G;
+    const size_t so = (static_cast<size_t>(b) * Hq + h) * C + c;
+    if (active)
+      for (int e = lane; e < D; e += 64) qrow[wave][e] = Elem<T>::load(q_lm, so * D + e);
+    __syncthreads();
+    if (active) {
+      // logit of key j = lane
+      float acc = 0.f;
+#pragma unroll 8
+      for (int e = 0; e < D; ++e) acc += qrow[wave][e] * keys[lane * LD + e];
+      const float l = tau * acc;
+      const float m = wave_max(l);
+      const float ex = expf(l - m);
+      const float z = wave_sum(ex);
+      const float p = ex / z;
+      // entropy in the shifted form: -sum p log p = log z - sum p (l - m)
+      const float ent = logf(z) - wave_sum(p * (l - m));
+      prob[wave][lane] = p;
+      if (lane == 0) ent_s[wave] = ent;
+    }
+    __syncthreads();
+    if (active) {
+      for (int e = lane; e < D; e += 64) {
+        float s = 0.f;
+#pragma unroll 8
+        for (int j = 0; j < kSumS; ++j) s += prob[wave][j] * keys[j * LD + e];
+        Elem<T>::store(k_sum, so * D + e, s);
+      }
+      if (lane == 0) b_sum[so] = fmaxf(ent_s[wave], 0.f);
+    }
+    __syncthreads();
+  }
+}
+
+template <typename T, int D>
+static hipError_t launch_summary_t(const SummaryArgs &a, hipStream_t st) {
+  dim3 grid(a.c1 - a.c0, a.Hkv, a.B);
+  landmark_summary_kernel<T, D><<<grid, kSumThreads, 0, st>>>(
+      static_cast<const T *>(a.k), static_cast<const T *>(a.q_lm), static_cast<T *>(a.k_sum),
+      a.b_sum, a.T, a.Hq, a.Hkv, a.C, a.c0, a.tau);
+  return hipGetLastError();
+}
+
+hipError_t launch_summary(const SummaryArgs &a, hipStream_t st) {
+  if (a.bf16) return a.d == 128 ? launch_summary_t<uint16_t, 128>(a, st) : launch_summary_t<uint16_t, 64>(a, st);
+  return a.d == 128 ? launch_summary_t<float, 128>(a, st) : launch_summary_t<float, 64>(a, st);
+}
+
+}  // namespace hils

@@ -1,0 +1,128 @@
+"""The C-ABI library: it loads without a GPU, exports every entry point the
+header declares, and rejects bad arguments on the host before any launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hils.h")
+
+hils = pytest.importorskip("long_context_sparse_hils_amd")
+
+
+def declared_symbols():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(hils_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    syms = declared_symbols()
+    for s in ("hils_landmark_summary", "hils_chunk_score_topk", "hils_sparse_attn_prefill",
+              "hils_sparse_attn_decode"):
+        assert s in syms
+    assert set(syms) == set(hils.ENTRY_POINTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(hils.LIB_PATH)
+    for s in declared_symbols():
+        assert hasattr(lib, s), s
+
+
+def _cfg(**kw):
+    base = dict(batch=2, seq_len=8192, n_q_heads=32, n_kv_heads=8, head_dim=128, chunk_size=64,
+                top_k=16, window=512, qcal_rank=32, hidden_dim=4096, dtype="bf16")
+    base.update(kw)
+    return hils.Config.make(**base)
+
+
+FAKE = 0x10000  # 16-byte aligned, never dereferenced: every call below fails validation
+
+
+def _status(fn, *args):
+    return fn(*args)
+
+
+def test_status_strings():
+    assert hils.status_string(0) == "HILS_OK"
+    assert hils.status_string(-3) == "HILS_ERR_WORKSPACE"
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(head_dim=96), hils.HILS_ERR_UNSUPPORTED),
+    (dict(chunk_size=32), hils.HILS_ERR_UNSUPPORTED),
+    (dict(top_k=33), hils.HILS_ERR_UNSUPPORTED),
+    (dict(top_k=-1), hils.HILS_ERR_INVALID_ARG),
+    (dict(n_q_heads=30), hils.HILS_ERR_INVALID_ARG),
+    (dict(n_q_heads=64, n_kv_heads=2), hils.HILS_ERR_UNSUPPORTED),
+    (dict(window=0), hils.HILS_ERR_INVALID_ARG),
+    (dict(dtype=7), hils.HILS_ERR_INVALID_ARG),
+    (dict(qcal_rank=65), hils.HILS_ERR_UNSUPPORTED),
+    (dict(batch=0), hils.HILS_ERR_INVALID_ARG),
+])
+def test_config_checks(over, status):
+    cfg = _cfg(**over)
+    st = hils.lib.hils_landmark_summary(ctypes.byref(cfg), FAKE, FAKE, 0, 1, FAKE, FAKE, None)
+    assert st == status
+    assert hils.last_error() != ""
+
+
+def test_null_and_misaligned_pointers():
+    cfg = _cfg()
+    assert hils.lib.hils_landmark_summary(ctypes.byref(cfg), None, FAKE, 0, 1, FAKE, FAKE, None) == \
+        hils.HILS_ERR_INVALID_ARG
+    assert "k is NULL" in hils.last_error()
+    assert hils.lib.hils_landmark_summary(ctypes.byref(cfg), FAKE + 2, FAKE, 0, 1, FAKE, FAKE, None) == \
+        hils.HILS_ERR_INVALID_ARG
+    assert "aligned" in hils.last_error()
+    assert hils.lib.hils_landmark_summary(ctypes.byref(cfg), FAKE, FAKE, 3, 2, FAKE, FAKE, None) == \
+        hils.HILS_ERR_INVALID_ARG
+    assert hils.lib.hils_landmark_summary(ctypes.byref(cfg), FAKE, FAKE, 0, 129, FAKE, FAKE, None) == \
+        hils.HILS_ERR_INVALID_ARG
+
+
+def test_qcal_pointers_must_match_rank():
+    cfg = _cfg(qcal_rank=0)
+    st = hils.lib.hils_chunk_score_topk(ctypes.byref(cfg), FAKE, FAKE, None, None, FAKE, FAKE, FAKE,
+                                        FAKE, FAKE, 1 << 30, None)
+    assert st == hils.HILS_ERR_INVALID_ARG
+    cfg = _cfg()
+    st = hils.lib.hils_chunk_score_topk(ctypes.byref(cfg), FAKE, None, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                        FAKE, FAKE, 1 << 30, None)
+    assert st == hils.HILS_ERR_INVALID_ARG
+
+
+def test_workspace_checks():
+    cfg = _cfg()
+    need = hils.hils_prefill_workspace_bytes(cfg)
+    assert need >= 2 * 8192 * 32 * 4
+    st = hils.lib.hils_chunk_score_topk(ctypes.byref(cfg), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                        FAKE, FAKE, need - 1, None)
+    assert st == hils.HILS_ERR_WORKSPACE
+    dcfg = _cfg(batch=1, seq_len=524288, qcal_rank=0, hidden_dim=0)
+    dneed = hils.hils_decode_workspace_bytes(dcfg)
+    assert dneed > 0
+    st = hils.lib.hils_sparse_attn_decode(ctypes.byref(dcfg), FAKE, None, None, None, FAKE, FAKE, FAKE,
+                                          FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, dneed - 1, None)
+    assert st == hils.HILS_ERR_WORKSPACE
+    st = hils.lib.hils_sparse_attn_decode(ctypes.byref(dcfg), FAKE, None, None, None, FAKE, FAKE, FAKE,
+                                          FAKE, None, FAKE, FAKE, FAKE, FAKE, dneed, None)
+    assert st == hils.HILS_ERR_INVALID_ARG
+    assert hils.hils_dense_decode_workspace_bytes(dcfg) > 0
+
+
+def test_workspace_sizes_scale_with_the_problem():
+    small = hils.hils_decode_workspace_bytes(_cfg(batch=1, seq_len=131072, qcal_rank=0))
+    big = hils.hils_decode_workspace_bytes(_cfg(batch=8, seq_len=131072, qcal_rank=0))
+    assert big > small > 0
+    # 4M tokens still fits the merge capacity with top-16
+    assert hils.hils_decode_workspace_bytes(_cfg(batch=1, seq_len=4194304, qcal_rank=0)) > 0
+    assert hils.hils_decode_error_offset(_cfg(batch=3, n_kv_heads=8)) == 4 * 2 * 3 * 8
+
+
+def test_invalid_config_gives_zero_workspace():
+    assert hils.hils_decode_workspace_bytes(_cfg(head_dim=100)) == 0
+    assert hils.hils_prefill_workspace_bytes(_cfg(n_q_heads=3, n_kv_heads=2)) == 0
