@@ -1,0 +1,350 @@
+#!/usr/bin/env python3
+"""Benchmark of the HiLS-Attention forward pass on one MI355X.
+
+One step = one pass of the whole hot path over one batch of seeded synthetic
+input resident in HBM:
+  * prefill at 8K (the headline line): landmark summary -> chunk scoring with
+    Q-Cal and GQA top-K -> hierarchical sparse attention, B=2 x 8192 tokens,
+    32/8 heads, d=128, S=64, K=16, W=512, r=32;
+  * decode at 512K (reported in the same JSON line under "decode_512k"): one
+    decode step for batch 1 and batch 4 over a 524288-token cache whose chunk
+    summaries were built beforehand (untimed), plus the dense causal-attention
+    decode on the same data for the speedup.
+
+Timing: HIP events on the library's stream around each call; every timed
+step starts from cold caches (a 1 GiB read-modify-write sweep outside the
+events evicts L2 and the 256 MB Infinity Cache).  The JSON line reports the
+mean over the timed steps.  Roofline: algorithmic work of the dominant
+kernel per launch over its measured duration, against MI355X peaks (bf16
+dense MFMA 2.5 PFLOP/s, HBM 8 TB/s).  The CPU baseline is the float64 oracle
+timed on a bounded sample of the same prefill workload on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "HiLS fwd query-tokens/s + % HBM peak (decode 512K) / % MFMA peak (prefill 8K)"
+PEAK_MFMA_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBS = 8000.0
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--seed", type=int, default=2)
+    p.add_argument("--no-decode", action="store_true")
+    p.add_argument("--no-dense", action="store_true")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-flush", action="store_true")
+    p.add_argument("--only", choices=["prefill", "decode"], default=None,
+                   help="profile one path (for rocprofv3 runs)")
+    p.add_argument("--decode-batches", default="1,4")
+    p.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle sample time")
+    return p.parse_args()
+
+
+# ---------------------------------------------------------------------------
+def algorithmic_prefill(wl):
+    """Flops of the prefill forward (4d per attended key per head, 2d per
+    scored chunk per head, Q-Cal down/up, summary 4d per key per head)."""
+    B, T, Hq, Hkv, d, S, K, W = (wl.batch, wl.seq_len, wl.n_q_heads, wl.n_kv_heads, wl.head_dim,
+                                 wl.chunk_size, wl.top_k, wl.window)
+    keys = 0
+    scored = 0
+    for i in range(T):
+        n = max(0, i - W + 1) // S
+        keys += min(K, n) * S + (i - n * S + 1)
+        scored += n
+    attn = 4.0 * d * keys * B * Hq
+    score = 2.0 * d * scored * B * Hq
+    qcal = (2.0 * wl.qcal_rank * wl.hidden_dim + 2.0 * Hq * d * wl.qcal_rank) * B * T if wl.qcal_rank else 0.0
+    summ = 4.0 * d * S * (T // S) * B * Hq
+    return dict(attn=attn, score=score, qcal=qcal, summary=summ, total=attn + score + qcal + summ,
+                keys_per_seq_head=keys)
+
+
+def algorithmic_decode_bytes(wl, seq_len):
+    """HBM bytes of one decode step per sequence: every eligible chunk's k'
+    (d bf16) and b' (f32) for all query heads, K selected chunks and the
+    window of K/V for every KV head, plus q/o/top-K."""
+    Hq, Hkv, d, S, K, W = wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.chunk_size, wl.top_k, wl.window
+    i = seq_len - 1
+    n = max(0, i - W + 1) // S
+    win = i - n * S + 1
+    e = 2
+    score = Hq * n * (d * e + 4)
+    gather = Hkv * min(K, n) * S * d * e * 2
+    window = Hkv * win * d * e * 2
+    small = Hq * d * e * 2 + Hkv * K * 4 + Hq * K * 4
+    return dict(score=score, gather=gather, window=window, small=small,
+                total=score + gather + window + small)
+
+
+def dense_decode_bytes(wl, seq_len):
+    return wl.n_kv_heads * seq_len * wl.head_dim * 2 * 2 + wl.n_q_heads * wl.head_dim * 2 * 2
+
+
+def traffic_record(kernel_name, src_file):
+    """HBM traffic measured with rocprofv3 counters, kept in profiles/ with
+    the sha256 of the kernel source it was measured on; null when the source
+    has changed since."""
+    path = os.path.join(ROOT, "profiles", f"{kernel_name}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    sha = hashlib.sha256(open(src_file, "rb").read()).hexdigest()
+    if rec.get("source_sha256") != sha:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+# ---------------------------------------------------------------------------
+class Timer:
+    def __init__(self, torch, stream):
+        self.torch, self.stream = torch, stream
+        self.events = []
+
+    def mark(self):
+        e = self.torch.cuda.Event(enable_timing=True)
+        e.record(self.stream)
+        self.events.append(e)
+        return e
+
+
+def bench_prefill(args, torch, hils, hs, flush):
+    wl = hs.WORKLOADS["prefill_8k"]
+    log(f"[prefill] generating inputs {wl}")
+    t0 = time.time()
+    inp = hs.prefill_inputs(wl, args.seed)
+    log(f"[prefill] inputs in {time.time() - t0:.1f}s")
+
+    def dev(a):
+        return torch.from_numpy(a.view(np.int16)).to("cuda").view(torch.bfloat16) if a.dtype == np.uint16 \
+            else torch.from_numpy(a).to("cuda")
+    d = {k: dev(v) for k, v in inp.items() if isinstance(v, np.ndarray)}
+    c = hils.Config.from_dict(wl.config_dict())
+    B, T, Hq, Hkv, D, C, K = wl.batch, wl.seq_len, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.n_chunks, wl.top_k
+    k_sum = torch.empty((B, Hq, C, D), dtype=torch.bfloat16, device="cuda")
+    b_sum = torch.empty((B, Hq, C), dtype=torch.float32, device="cuda")
+    ws = torch.empty((hils.hils_prefill_workspace_bytes(c),), dtype=torch.uint8, device="cuda")
+    idx = torch.empty((B, Hkv, T, K), dtype=torch.int32, device="cuda")
+    tsc = torch.empty((B, Hq, T, K), dtype=torch.float32, device="cuda")
+    o = torch.empty((B, Hq, T, D), dtype=torch.bfloat16, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(tm=None):
+        if tm: tm.mark()
+        hils.hils_landmark_summary(c, d["k"], d["q_lm"], 0, C, k_sum, b_sum, stream)
+        if tm: tm.mark()
+        hils.hils_chunk_score_topk(c, d["q"], d["h"], d["w_down"], d["w_up"], k_sum, b_sum, idx, tsc, ws, stream)
+        if tm: tm.mark()
+        hils.hils_sparse_attn_prefill(c, d["q"], d["k"], d["v"], idx, tsc, o, ws, stream)
+        if tm: tm.mark()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    per = []
+    wall0 = time.time()
+    for s in range(args.steps):
+        flush()
+        tm = Timer(torch, stream)
+        step(tm)
+        torch.cuda.synchronize()
+        ev = tm.events
+        per.append([ev[j].elapsed_time(ev[j + 1]) for j in range(3)])
+        log(f"[prefill] step {s}: summary {per[-1][0]:.3f} ms, score {per[-1][1]:.3f} ms, "
+            f"attention {per[-1][2]:.3f} ms")
+    wall = time.time() - wall0
+    per = np.array(per)
+    stage_ms = per.mean(axis=0)
+    ms = float(stage_ms.sum())
+    fl = algorithmic_prefill(wl)
+    res = dict(ms=ms, stage_ms=dict(summary=float(stage_ms[0]), score_topk=float(stage_ms[1]),
+                                    attention=float(stage_ms[2])),
+               wall_s_incl_flush=wall, flops=fl, wl=wl, inp=inp)
+    return res
+
+
+def bench_decode(args, torch, hils, hs, flush, batch):
+    wl = hs.WORKLOADS["decode_512k_b1" if batch == 1 else "decode_512k_b4"]
+    if wl.batch != batch:
+        wl = wl.with_(batch=batch)
+    log(f"[decode b{batch}] generating inputs")
+    t0 = time.time()
+    inp = hs.decode_inputs(wl, args.seed + 10)
+    log(f"[decode b{batch}] inputs in {time.time() - t0:.1f}s")
+
+    def dev(a):
+        return torch.from_numpy(a.view(np.int16)).to("cuda").view(torch.bfloat16) if a.dtype == np.uint16 \
+            else torch.from_numpy(a).to("cuda")
+    d = {}
+    for k_, v_ in list(inp.items()):
+        if isinstance(v_, np.ndarray):
+            d[k_] = dev(v_)
+            inp[k_] = None  # free host copies of the big caches
+    c = hils.Config.from_dict(wl.config_dict())
+    B, T, Hq, Hkv, D, C, K = wl.batch, wl.seq_len, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.n_chunks, wl.top_k
+    stream = torch.cuda.current_stream()
+    k_sum = torch.empty((B, Hq, C, D), dtype=torch.bfloat16, device="cuda")
+    b_sum = torch.empty((B, Hq, C), dtype=torch.float32, device="cuda")
+    hils.hils_landmark_summary(c, d["k_cache"], d["q_lm"], 0, C, k_sum, b_sum, stream)  # untimed, once
+    ws = torch.zeros((hils.hils_decode_workspace_bytes(c),), dtype=torch.uint8, device="cuda")
+    o = torch.empty((B, Hq, D), dtype=torch.bfloat16, device="cuda")
+    idx = torch.empty((B, Hkv, K), dtype=torch.int32, device="cuda")
+    tsc = torch.empty((B, Hq, K), dtype=torch.float32, device="cuda")
+
+    def step():
+        hils.hils_sparse_attn_decode(c, d["q"], None, None, None, d["k_cache"], d["v_cache"], k_sum, b_sum,
+                                     d["seq_lens"], o, idx, tsc, ws, stream)
+
+    def timed(fn, n, warm):
+        for _ in range(warm):
+            fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(n):
+            flush()
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        return float(np.mean(ts)), ts
+
+    ms, ts = timed(step, args.steps, args.warmup)
+    log(f"[decode b{batch}] step {ms * 1e3:.1f} us ({', '.join(f'{t * 1e3:.1f}' for t in ts)})")
+    # needle hits (information only)
+    gidx = idx.cpu().numpy()
+    hits = sum(int(n["chunk"] in gidx[n["b"], n["g"]]) for n in inp["needles"])
+    nb = algorithmic_decode_bytes(wl, T)
+    out = dict(batch=B, seq_len=T, ms_per_step=ms, value=B / (ms * 1e-3), unit="query-tokens/s",
+               bytes_per_step=nb["total"] * B,
+               roofline=dict(bound="hbm", achieved=nb["total"] * B / (ms * 1e-3) / 1e9, peak=PEAK_HBM_GBS,
+                             unit="GB/s", frac=nb["total"] * B / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                             traffic=traffic_record("decode_512k_b%d" % B,
+                                                    os.path.join(ROOT, "long_context_sparse_hils_amd", "csrc",
+                                                                 "decode.hip")),
+                             kernel="decode step (score+select kernel, attend+combine kernel)"),
+               needle_hits=f"{hits}/{len(inp['needles'])}")
+    if not args.no_dense:
+        dws = torch.zeros((hils.hils_dense_decode_workspace_bytes(c),), dtype=torch.uint8, device="cuda")
+        do = torch.empty_like(o)
+
+        def dstep():
+            hils.hils_dense_attn_decode(c, d["q"], d["k_cache"], d["v_cache"], d["seq_lens"], do, dws, stream)
+        dms, _ = timed(dstep, max(3, args.steps // 2), 1)
+        db = dense_decode_bytes(wl, T) * B
+        out["dense"] = dict(ms_per_step=dms, achieved_GBs=db / (dms * 1e-3) / 1e9,
+                            frac_hbm=db / (dms * 1e-3) / 1e9 / PEAK_HBM_GBS)
+        out["speedup_vs_dense"] = dms / ms
+        log(f"[decode b{batch}] dense {dms * 1e3:.1f} us, speedup {dms / ms:.1f}x")
+    del d, k_sum, b_sum, ws
+    torch.cuda.empty_cache()
+    return out
+
+
+def cpu_baseline(args, res):
+    """The float64 oracle, as it stands, on a bounded sample of the prefill
+    workload: all chunk summaries of batch 0, then scoring, selection and
+    fusion for an evenly strided subset of its query positions."""
+    import oracle
+    import hils_synth as hs
+    wl, inp = res["wl"], res["inp"]
+    one = wl.with_(batch=1)
+    oc = oracle.OracleConfig.from_dict(one.config_dict())
+    sub = {k: (v[:1] if isinstance(v, np.ndarray) and k not in ("w_down", "w_up") else v)
+           for k, v in inp.items()}
+    # calibrate on a small stride, then size the sample to the time target
+    t0 = time.time()
+    probe = np.arange(0, wl.seq_len, 256, dtype=np.int32)
+    oracle.prefill(oc, sub, qpos=probe)
+    t_probe = time.time() - t0
+    per_q = t_probe / probe.size
+    nq = int(min(wl.seq_len, max(probe.size, args.cpu_seconds / max(per_q, 1e-6))))
+    stride = max(1, wl.seq_len // nq)
+    qpos = np.arange(stride // 2, wl.seq_len, stride, dtype=np.int32)
+    t0 = time.time()
+    oracle.prefill(oc, sub, qpos=qpos)
+    dt = time.time() - t0
+    _ = hs
+    return dict(value=qpos.size / dt, unit="query-tokens/s", cores=oracle.threads(), kind="oracle",
+                sample=f"prefill_8k batch 0: all {wl.n_chunks} chunk summaries, then scoring/top-K/fusion for "
+                       f"{qpos.size} of {wl.seq_len} query positions (stride {stride}); {dt:.1f} s")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps(dict(error="this build runs on one GPU: the HiLS forward path here is the one-GPU "
+                                    "share; multi-GPU sharding is described, not built", n_gpus=args.gpus)))
+        sys.exit(2)
+    import torch
+    import hils_synth as hs
+    import long_context_sparse_hils_amd as hils
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    flush_buf = torch.empty((1 << 30) // 4, dtype=torch.float32, device="cuda").fill_(0)
+
+    def flush():
+        if not args.no_flush:
+            flush_buf.add_(1.0)
+
+    line = dict(metric=METRIC, unit="query-tokens/s", n_gpus=1, steps=args.steps, warmup=args.warmup,
+                higher_is_better=True, scaling="weak", vs_baseline=None, dtype="bf16", data="synthetic")
+    if args.only != "decode":
+        res = bench_prefill(args, torch, hils, hs, flush)
+        wl, fl = res["wl"], res["flops"]
+        ms = res["ms"]
+        attn_ms = res["stage_ms"]["attention"]
+        ach = fl["attn"] / (attn_ms * 1e-3) / 1e12
+        line.update(value=wl.batch * wl.seq_len / (ms * 1e-3), ms_per_step=ms,
+                    config=dict(workload="prefill_8k", batch=wl.batch, seq_len=wl.seq_len,
+                                n_q_heads=wl.n_q_heads, n_kv_heads=wl.n_kv_heads, head_dim=wl.head_dim,
+                                chunk_size=wl.chunk_size, top_k=wl.top_k, window=wl.window,
+                                qcal_rank=wl.qcal_rank, hidden_dim=wl.hidden_dim, global_batch=wl.batch,
+                                parallelism="none (1 GPU)"),
+                    stage_ms=res["stage_ms"],
+                    roofline=dict(bound="mfma", achieved=ach, peak=PEAK_MFMA_BF16_TFLOPS, unit="TFLOP/s",
+                                  frac=ach / PEAK_MFMA_BF16_TFLOPS,
+                                  traffic=traffic_record("attn_prefill_8k", os.path.join(
+                                      ROOT, "long_context_sparse_hils_amd", "csrc", "prefill_mfma.hip")),
+                                  kernel="sparse attention (hils_sparse_attn_prefill)",
+                                  flops_per_launch=fl["attn"]),
+                    whole_step_tflops=fl["total"] / (ms * 1e-3) / 1e12)
+        if not args.no_cpu_baseline:
+            log("[cpu] timing the oracle")
+            line["cpu_baseline"] = cpu_baseline(args, res)
+        del res
+    if args.only != "prefill" and not args.no_decode:
+        dec = {}
+        for b in [int(x) for x in args.decode_batches.split(",") if x]:
+            dec[f"b{b}"] = bench_decode(args, torch, hils, hs, flush, b)
+        line["decode_512k"] = dec
+        if args.only == "decode":
+            first = dec[next(iter(dec))]
+            line.update(value=first["value"], ms_per_step=first["ms_per_step"], roofline=first["roofline"],
+                        config=dict(workload="decode_512k", batch=first["batch"], seq_len=first["seq_len"]))
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

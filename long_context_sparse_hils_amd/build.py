@@ -16,7 +16,7 @@ OUT = os.path.join(HERE, "libhils.so")
 OBJ = os.path.join(HERE, "_build")
 ARCH = os.environ.get("HILS_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["summary.hip", "prefill_valu.hip", "prefill_mfma.hip", "decode.hip", "api.cpp"]
+SOURCES = ["summary.hip", "prefill_valu.hip", "prefill_mfma.hip", "score_mfma.hip", "decode.hip", "api.cpp"]
 
 FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

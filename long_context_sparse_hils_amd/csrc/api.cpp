@@ -191,7 +191,9 @@ hils_status hils_landmark_summary(const hils_config *cfg, const void *k, const v
 
 size_t hils_prefill_workspace_bytes(const hils_config *cfg) {
   if (check_config(cfg) != HILS_OK) return 0;
-  return prefill_u_bytes(cfg) + kAlign;
+  const int C = cfg->seq_len / cfg->chunk_size;
+  return prefill_u_bytes(cfg) +
+         align_up(hils::score_mfma_ws_bytes(cfg->batch, cfg->seq_len, cfg->n_q_heads, C, cfg->qcal_rank)) + kAlign;
 }
 
 hils_status hils_chunk_score_topk(const hils_config *cfg, const void *q, const void *h, const void *w_down,
@@ -220,7 +222,9 @@ hils_status hils_chunk_score_topk(const hils_config *cfg, const void *q, const v
                     static_cast<char *>(workspace) + prefill_u_bytes(cfg), cfg->batch, cfg->seq_len,
                     cfg->n_q_heads, cfg->n_kv_heads, cfg->head_dim, cfg->chunk_size, cfg->top_k, cfg->window,
                     cfg->qcal_rank, cfg->hidden_dim, C, tau_of(cfg), cfg->dtype == HILS_BF16};
-  return finish(hils::launch_score_valu(a, static_cast<hipStream_t>(stream)), "chunk score/top-k launch");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (hils::score_mfma_supported(a)) return finish(hils::launch_score_mfma(a, st), "chunk score/top-k launch");
+  return finish(hils::launch_score_valu(a, st), "chunk score/top-k launch");
 }
 
 hils_status hils_sparse_attn_prefill(const hils_config *cfg, const void *q, const void *k, const void *v,
@@ -243,7 +247,9 @@ hils_status hils_sparse_attn_prefill(const hils_config *cfg, const void *q, cons
   hils::AttnArgs a{q, k, v, topk_idx, topk_score, o, workspace, cfg->batch, cfg->seq_len, cfg->n_q_heads,
                    cfg->n_kv_heads, cfg->head_dim, cfg->chunk_size, cfg->top_k, cfg->window, tau_of(cfg),
                    cfg->dtype == HILS_BF16};
-  return finish(hils::launch_attn_valu(a, static_cast<hipStream_t>(stream)), "sparse attention launch");
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (hils::attn_mfma_supported(a)) return finish(hils::launch_attn_mfma(a, st), "sparse attention launch");
+  return finish(hils::launch_attn_valu(a, st), "sparse attention launch");
 }
 
 size_t hils_decode_workspace_bytes(const hils_config *cfg) {

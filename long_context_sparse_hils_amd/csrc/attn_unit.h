@@ -30,6 +30,7 @@ struct UnitSmem {
   float q[kMaxG][D];          // query rows of the group (fp32)
   float p[kMaxG][kUnitKeys];  // logits, then probabilities
   float m[kMaxG], l[kMaxG];
+  uint4 v[kUnitKeys * D * 4 / 16];  // the unit's value rows, raw (<= fp32 size)
 };
 
 // Number of (head, dim-pair) outputs each thread owns.
@@ -51,7 +52,16 @@ __device__ __forceinline__ void attend_unit(UnitSmem<D> &sm, const T *__restrict
                                             const T *__restrict__ vrow, int nk, int G, float tau,
                                             float2 (&o)[pairs_per_thread<D>()]) {
   constexpr int QD = D / 4;  // elements per quarter
+  constexpr int VPT = kUnitKeys * D * static_cast<int>(sizeof(T)) / 16 / kUnitThreads;  // 16-B pieces per thread
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  // value rows: issue the loads first, park them in LDS after the logits
+  const int vpieces = nk * D * static_cast<int>(sizeof(T)) / 16;
+  uint4 vreg[VPT];
+#pragma unroll
+  for (int r = 0; r < VPT; ++r) {
+    const int pc = t + r * kUnitThreads;
+    vreg[r] = pc < vpieces ? reinterpret_cast<const uint4 *>(vrow)[pc] : make_uint4(0, 0, 0, 0);
+  }
   {
     const int j = t >> 2, qq = t & 3;
     float kv[QD];
@@ -70,6 +80,8 @@ __device__ __forceinline__ void attend_unit(UnitSmem<D> &sm, const T *__restrict
       if (qq == 0) sm.p[h][j] = (j < nk) ? tau * acc : -INFINITY;
     }
   }
+#pragma unroll
+  for (int r = 0; r < VPT; ++r) sm.v[t + r * kUnitThreads] = vreg[r];
   __syncthreads();
   for (int h = wave; h < G; h += kUnitThreads / 64) {
     const float lam = sm.p[h][lane];
@@ -86,9 +98,10 @@ __device__ __forceinline__ void attend_unit(UnitSmem<D> &sm, const T *__restrict
     const int h = pr / (D / 2), e2 = pr % (D / 2);
     float2 acc = make_float2(0.f, 0.f);
     if (h < G) {
+      const T *vs = reinterpret_cast<const T *>(sm.v);
       for (int j = 0; j < nk; ++j) {
         float v2[2];
-        Elem<T>::load2(vrow + static_cast<size_t>(j) * D + 2 * e2, v2);
+        Elem<T>::load2(vs + j * D + 2 * e2, v2);
         const float pj = sm.p[h][j];
         acc.x += pj * v2[0];
         acc.y += pj * v2[1];

@@ -73,11 +73,19 @@ struct D1Smem {
   int is_last;
 };
 
+// a score-slice block and a window-unit block never need both layouts
+template <int D>
+union D1Shared {
+  D1Smem sc;
+  UnitSmem<D> us;
+};
+
 template <typename T, int D, bool QCAL>
 __global__ void __launch_bounds__(kDecThreads)
 decode_score_kernel(DecodeArgs a) {
-  __shared__ D1Smem sm;
-  __shared__ UnitSmem<D> us;
+  __shared__ D1Shared<D> shm;
+  D1Smem &sm = shm.sc;
+  UnitSmem<D> &us = shm.us;
   const int g = blockIdx.y, b = blockIdx.z, blk = blockIdx.x, t = threadIdx.x;
   const int lane = t & 63, wave = t >> 6;
   const int G = a.Hq / a.Hkv, K = a.K;
@@ -92,7 +100,7 @@ decode_score_kernel(DecodeArgs a) {
     const int j0 = n * a.S + u * kUnitKeys;
     float *rec = a.parts + ((static_cast<size_t>(b) * a.Hkv + g) * a.nslots + K + u) * G * (D + 2);
     if (j0 > i) {
-      for (int hh = t; hh < G; hh += kDecThreads) { rec[hh * (D + 2)] = -INFINITY; rec[hh * (D + 2) + 1] = 0.f; }
+      for (int hh = t; hh < G; hh += kDecThreads) { publish(rec + hh * (D + 2), -INFINITY); publish(rec + hh * (D + 2) + 1, 0.f); }
       return;
     }
     const int nk = min(kUnitKeys, i - j0 + 1);
@@ -106,9 +114,9 @@ decode_score_kernel(DecodeArgs a) {
       const int pr = t + r * kUnitThreads, hh = pr / (D / 2), e2 = pr % (D / 2);
       if (hh < G) {
         float *rh = rec + hh * (D + 2);
-        rh[2 + 2 * e2] = ou[r].x;
-        rh[3 + 2 * e2] = ou[r].y;
-        if (e2 == 0) { rh[0] = us.m[hh]; rh[1] = us.l[hh]; }
+        publish(rh + 2 + 2 * e2, ou[r].x);
+        publish(rh + 3 + 2 * e2, ou[r].y);
+        if (e2 == 0) { publish(rh, us.m[hh]); publish(rh + 1, us.l[hh]); }
       }
     }
     return;
@@ -130,11 +138,12 @@ decode_score_kernel(DecodeArgs a) {
     const int seg = lane % LPH;
     const T *ks = static_cast<const T *>(a.k_sum);
     const size_t hbase = static_cast<size_t>(b) * a.Hq + g * G;
-    for (int row0 = wave * R; row0 < nrows; row0 += 4 * R * 2) {
-      float part[2];
-      int rows[2];
+    constexpr int UN = 4;  // wave loads in flight per iteration
+    for (int row0 = wave * R; row0 < nrows; row0 += 4 * R * UN) {
+      float part[UN];
+      int rows[UN];
 #pragma unroll
-      for (int uu = 0; uu < 2; ++uu) {
+      for (int uu = 0; uu < UN; ++uu) {
         const int row = row0 + uu * 4 * R + lane / LPH;
         rows[uu] = row;
         part[uu] = 0.f;
@@ -148,7 +157,7 @@ decode_score_kernel(DecodeArgs a) {
         }
       }
 #pragma unroll
-      for (int uu = 0; uu < 2; ++uu) {
+      for (int uu = 0; uu < UN; ++uu) {
         const float dot = group_sum<LPH>(part[uu]);
         const int row = rows[uu];
         if (seg == 0 && row < nrows) {
@@ -179,23 +188,20 @@ decode_score_kernel(DecodeArgs a) {
         best = wave_max_u64(best);
         prev = best;
       }
-      if (lane == 0) a.cand_key[cbase + k] = best;
+      if (lane == 0) publish(a.cand_key + cbase + k, best);
       if (best != kNoKey) {
         const int cl = key_chunk(best) - c0;
-        for (int hh = lane; hh < G; hh += 64) a.cand_s[(cbase + k) * G + hh] = sm.sc.s[cl * G + hh];
+        for (int hh = lane; hh < G; hh += 64) publish(a.cand_s + (cbase + k) * G + hh, sm.sc.s[cl * G + hh]);
       }
     }
   }
   // ---------------- ticket: the last slice block of (b, g) merges
-  __threadfence();
-  __syncthreads();
-  if (t == 0) {
-    const unsigned prevcnt = atomicAdd(a.count1 + b * a.Hkv + g, 1u);
-    sm.is_last = (prevcnt == static_cast<unsigned>(a.P - 1));
+  {
+    const unsigned before = arrive(a.count1 + b * a.Hkv + g);
+    if (t == 0) sm.is_last = (before == static_cast<unsigned>(a.P - 1));
   }
   __syncthreads();
   if (!sm.is_last) return;
-  __threadfence();
   const int total = a.P * K;
   const size_t cb0 = (static_cast<size_t>(b) * a.Hkv + g) * a.P * K;
   for (int x = t; x < total; x += kDecThreads) sm.cand[x] = load_acquired(a.cand_key + cb0 + x);
@@ -233,7 +239,7 @@ decode_score_kernel(DecodeArgs a) {
         a.topk_score[(static_cast<size_t>(b) * a.Hq + g * G + hh) * K + k] = -INFINITY;
     }
   }
-  if (t == 0) atomicExch(a.count1 + b * a.Hkv + g, 0u);
+  if (t == 0) reset_counter(a.count1 + b * a.Hkv + g);
 }
 
 // ------------------------------------------------------------------ D2
@@ -252,7 +258,7 @@ decode_attend_kernel(DecodeArgs a) {
     float *rec = recs + static_cast<size_t>(slot) * G * (D + 2);
     const int c = a.topk_idx[(static_cast<size_t>(b) * a.Hkv + g) * K + slot];
     if (c < 0) {
-      for (int hh = t; hh < G; hh += kDecThreads) { rec[hh * (D + 2)] = -INFINITY; rec[hh * (D + 2) + 1] = 0.f; }
+      for (int hh = t; hh < G; hh += kDecThreads) { publish(rec + hh * (D + 2), -INFINITY); publish(rec + hh * (D + 2) + 1, 0.f); }
     } else {
       load_q_rows<T, D>(us, static_cast<const T *>(a.q) + (static_cast<size_t>(b) * a.Hq + g * G) * D, D, G);
       __syncthreads();
@@ -267,22 +273,19 @@ decode_attend_kernel(DecodeArgs a) {
         if (hh < G) {
           float *rh = rec + hh * (D + 2);
           const float inv = 1.f / us.l[hh];
-          rh[2 + 2 * e2] = ou[r].x * inv;
-          rh[3 + 2 * e2] = ou[r].y * inv;
-          if (e2 == 0) { rh[0] = a.topk_score[(static_cast<size_t>(b) * a.Hq + g * G + hh) * K + slot]; rh[1] = 1.f; }
+          publish(rh + 2 + 2 * e2, ou[r].x * inv);
+          publish(rh + 3 + 2 * e2, ou[r].y * inv);
+          if (e2 == 0) { publish(rh, a.topk_score[(static_cast<size_t>(b) * a.Hq + g * G + hh) * K + slot]); publish(rh + 1, 1.f); }
         }
       }
     }
   }
-  __threadfence();
-  __syncthreads();
-  if (t == 0) {
-    const unsigned prevcnt = atomicAdd(a.count2 + b * a.Hkv + g, 1u);
-    is_last = (prevcnt == static_cast<unsigned>(a.nslot_blocks - 1));
+  {
+    const unsigned before = arrive(a.count2 + b * a.Hkv + g);
+    if (t == 0) is_last = (before == static_cast<unsigned>(a.nslot_blocks - 1));
   }
   __syncthreads();
   if (!is_last) return;
-  __threadfence();
   // combine every slot (chunks 0..K-1, window units K..) in slot order
   for (int x = t; x < G * D; x += kDecThreads) {
     const int hh = x / D, e = x % D;
@@ -301,7 +304,7 @@ decode_attend_kernel(DecodeArgs a) {
     }
     Elem<T>::store(static_cast<T *>(a.o), (static_cast<size_t>(b) * a.Hq + g * G + hh) * D + e, o / l);
   }
-  if (t == 0) atomicExch(a.count2 + b * a.Hkv + g, 0u);
+  if (t == 0) reset_counter(a.count2 + b * a.Hkv + g);
 }
 
 // ------------------------------------------------------------------ dense comparator
@@ -319,7 +322,7 @@ dense_decode_kernel(DenseArgs a) {
   const int j_lo = p * a.L, j_hi = min(i + 1, (p + 1) * a.L);
   constexpr int NP = pairs_per_thread<D>();
   if (j_lo >= j_hi) {
-    for (int hh = t; hh < G; hh += kDecThreads) { rec[hh * (D + 2)] = -INFINITY; rec[hh * (D + 2) + 1] = 0.f; }
+    for (int hh = t; hh < G; hh += kDecThreads) { publish(rec + hh * (D + 2), -INFINITY); publish(rec + hh * (D + 2) + 1, 0.f); }
   } else {
     load_q_rows<T, D>(us, static_cast<const T *>(a.q) + (static_cast<size_t>(b) * a.Hq + g * G) * D, D, G);
     __syncthreads();
@@ -342,21 +345,18 @@ dense_decode_kernel(DenseArgs a) {
       const int pr = t + r * kUnitThreads, hh = pr / (D / 2), e2 = pr % (D / 2);
       if (hh < G) {
         float *rh = rec + hh * (D + 2);
-        rh[2 + 2 * e2] = acc.o[r].x;
-        rh[3 + 2 * e2] = acc.o[r].y;
-        if (e2 == 0) { rh[0] = acc.m[r]; rh[1] = acc.l[r]; }
+        publish(rh + 2 + 2 * e2, acc.o[r].x);
+        publish(rh + 3 + 2 * e2, acc.o[r].y);
+        if (e2 == 0) { publish(rh, acc.m[r]); publish(rh + 1, acc.l[r]); }
       }
     }
   }
-  __threadfence();
-  __syncthreads();
-  if (t == 0) {
-    const unsigned prevcnt = atomicAdd(a.count + b * a.Hkv + g, 1u);
-    is_last = (prevcnt == static_cast<unsigned>(a.P - 1));
+  {
+    const unsigned before = arrive(a.count + b * a.Hkv + g);
+    if (t == 0) is_last = (before == static_cast<unsigned>(a.P - 1));
   }
   __syncthreads();
   if (!is_last) return;
-  __threadfence();
   for (int x = t; x < G * D; x += kDecThreads) {
     const int hh = x / D, e = x % D;
     float m = -INFINITY, l = 0.f, o = 0.f;
@@ -374,7 +374,7 @@ dense_decode_kernel(DenseArgs a) {
     }
     Elem<T>::store(static_cast<T *>(a.o), (static_cast<size_t>(b) * a.Hq + g * G + hh) * D + e, o / l);
   }
-  if (t == 0) atomicExch(a.count + b * a.Hkv + g, 0u);
+  if (t == 0) reset_counter(a.count + b * a.Hkv + g);
 }
 
 // ------------------------------------------------------------------ launchers

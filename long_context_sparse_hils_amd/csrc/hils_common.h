@@ -122,8 +122,34 @@ __device__ __forceinline__ float key_score(unsigned long long k) {
 }
 constexpr unsigned long long kNoKey = 0ull;  // below every real key
 
-// Loads of data another workgroup published before an atomic ticket: atomic
-// (device-coherent) loads, so a stale per-CU cache line is never used.
+// Cross-workgroup hand-off without whole-cache maintenance.  The L2 of one
+// XCD is not coherent with the others', and a device-scope fence writes back
+// and invalidates the whole L2 of the XCD.  Instead, data handed to another
+// workgroup is written with device-scope atomic stores (written through to
+// the coherent memory side), each thread waits for its stores before the
+// workgroup barrier that precedes the ticket, and the workgroup that takes the
+// last ticket reads the data with device-scope atomic loads.
+__device__ __forceinline__ void publish(float *p, float v) {
+  __hip_atomic_store(reinterpret_cast<uint32_t *>(p), __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void publish(unsigned long long *p, unsigned long long v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Call from every thread after its publish() stores: returns, in thread 0 of
+// the workgroup, the number of workgroups that arrived before this one.
+__device__ __forceinline__ unsigned arrive(unsigned *counter) {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  unsigned before = 0;
+  if (threadIdx.x == 0) before = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return before;
+}
+__device__ __forceinline__ void reset_counter(unsigned *counter) {
+  __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Loads of data another workgroup published before an atomic ticket.
 __device__ __forceinline__ float load_acquired(const float *p) {
   return __uint_as_float(__hip_atomic_load(reinterpret_cast<const uint32_t *>(p), __ATOMIC_RELAXED,
                                            __HIP_MEMORY_SCOPE_AGENT));

@@ -70,7 +70,12 @@ struct DenseArgs {
 
 hipError_t launch_summary(const SummaryArgs &a, hipStream_t st);
 hipError_t launch_score_valu(const ScoreArgs &a, hipStream_t st);
+bool score_mfma_supported(const ScoreArgs &a);
+size_t score_mfma_ws_bytes(int B, int T, int Hq, int C, int r);
+hipError_t launch_score_mfma(const ScoreArgs &a, hipStream_t st);
 hipError_t launch_attn_valu(const AttnArgs &a, hipStream_t st);
+bool attn_mfma_supported(const AttnArgs &a);
+hipError_t launch_attn_mfma(const AttnArgs &a, hipStream_t st);
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t st);
 hipError_t launch_dense_decode(const DenseArgs &a, hipStream_t st);
 
