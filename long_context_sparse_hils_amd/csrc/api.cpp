@@ -96,20 +96,26 @@ struct DecodeGeom {
 };
 
 constexpr int kMaxCand = 4096;
+constexpr int kMaxSlotRows = 2040;  // partial records one combine step holds in LDS
 
 hils_status decode_geom(const hils_config *c, DecodeGeom *g) {
   const int G = c->n_q_heads / c->n_kv_heads, K = c->top_k, S = c->chunk_size;
   const int nmax = eligible(c->seq_len - 1, c->window, S);
-  const int pmax = kMaxCand / (K > 0 ? K : 1);
-  int cpb = (nmax + pmax - 1) / pmax;
-  cpb = cpb < 64 ? 64 : (cpb + 63) / 64 * 64;
-  if (cpb > 1024 || cpb * G > 4096)
+  // chunks per score slice: 64, 256 or 1024, the smallest that keeps the
+  // P * K candidates within what one workgroup merges
+  const int kk = K > 0 ? K : 1;
+  int cpb = 64;
+  while (cpb < 1024 && static_cast<long long>((nmax + cpb - 1) / cpb) * kk > kMaxCand) cpb *= 4;
+  if (static_cast<long long>((nmax + cpb - 1) / cpb) * kk > kMaxCand || cpb * G > 4096)
     return fail(HILS_ERR_UNSUPPORTED, "decode: %d eligible chunks with top_k %d and group %d exceed the merge capacity",
                 nmax, K, G);
   g->CPB = cpb;
   g->P = nmax > 0 ? (nmax + cpb - 1) / cpb : 1;
   g->NW = (c->window + S - 1 + 63) / 64;
   g->nslots = K + g->NW;
+  if (g->nslots * G > kMaxSlotRows)
+    return fail(HILS_ERR_UNSUPPORTED, "decode: (top_k + window units) x group = %d exceeds %d", g->nslots * G,
+                kMaxSlotRows);
   g->nslot_blocks = K > 0 ? K : 1;
   const size_t B = c->batch, Hkv = c->n_kv_heads, Hq = c->n_q_heads, D = c->head_dim;
   size_t off = 0;
@@ -135,12 +141,14 @@ struct DenseGeom {
 void dense_geom(const hils_config *c, DenseGeom *g) {
   const long long T = c->seq_len;
   const long long units = (T + 63) / 64;
-  const long long per_seq_target = 4096 / (static_cast<long long>(c->batch) * c->n_kv_heads) + 1;
+  const long long G = c->n_q_heads / c->n_kv_heads;
+  long long per_seq_target = 4096 / (static_cast<long long>(c->batch) * c->n_kv_heads) + 1;
+  if (per_seq_target > kMaxSlotRows / G) per_seq_target = kMaxSlotRows / G;
   long long upb = (units + per_seq_target - 1) / per_seq_target;  // units per block
   if (upb < 4) upb = 4;
   g->L = static_cast<int>(upb * 64);
   g->P = static_cast<int>((T + g->L - 1) / g->L);
-  const size_t B = c->batch, Hkv = c->n_kv_heads, G = c->n_q_heads / c->n_kv_heads, D = c->head_dim;
+  const size_t B = c->batch, Hkv = c->n_kv_heads, D = c->head_dim;
   g->off_counts = 0;
   g->off_parts = align_up(sizeof(unsigned) * (B * Hkv + 1));
   g->total = align_up(g->off_parts + sizeof(float) * B * Hkv * g->P * G * (D + 2));

@@ -25,12 +25,12 @@ constexpr int kUnitThreads = 256;
 constexpr int kMaxG = 16;
 constexpr int kUnitKeys = 64;
 
-template <int D>
+template <typename T, int D>
 struct UnitSmem {
   float q[kMaxG][D];          // query rows of the group (fp32)
   float p[kMaxG][kUnitKeys];  // logits, then probabilities
   float m[kMaxG], l[kMaxG];
-  uint4 v[kUnitKeys * D * 4 / 16];  // the unit's value rows, raw (<= fp32 size)
+  uint4 v[kUnitKeys * D * sizeof(T) / 16];  // the unit's value rows, raw
 };
 
 // Number of (head, dim-pair) outputs each thread owns.
@@ -38,7 +38,7 @@ template <int D>
 constexpr int pairs_per_thread() { return (kMaxG * D / 2 + kUnitThreads - 1) / kUnitThreads; }
 
 template <typename T, int D>
-__device__ __forceinline__ void load_q_rows(UnitSmem<D> &sm, const T *q, size_t head_stride, int G) {
+__device__ __forceinline__ void load_q_rows(UnitSmem<T, D> &sm, const T *q, size_t head_stride, int G) {
   for (int x = threadIdx.x; x < G * D; x += kUnitThreads)
     sm.q[x / D][x % D] = Elem<T>::load(q, static_cast<size_t>(x / D) * head_stride + (x % D));
 }
@@ -48,7 +48,7 @@ __device__ __forceinline__ void load_q_rows(UnitSmem<D> &sm, const T *q, size_t 
 // unnormalised output pairs (see pairs_per_thread).  Must be called by all
 // threads of the block.
 template <typename T, int D>
-__device__ __forceinline__ void attend_unit(UnitSmem<D> &sm, const T *__restrict__ krow,
+__device__ __forceinline__ void attend_unit(UnitSmem<T, D> &sm, const T *__restrict__ krow,
                                             const T *__restrict__ vrow, int nk, int G, float tau,
                                             float2 (&o)[pairs_per_thread<D>()]) {
   constexpr int QD = D / 4;  // elements per quarter

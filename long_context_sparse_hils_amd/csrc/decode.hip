@@ -59,35 +59,134 @@ decode_qcal_kernel(const T *__restrict__ q, const T *__restrict__ h, const T *__
 }
 
 // ------------------------------------------------------------------ D1
+constexpr int kRowsMax = 4096;  // CPB * G rows of one score slice
 struct D1Smem {
   union {
     struct {
       float qh[kMaxG * 128];
-      float s[1024 * 4];  // per (chunk, head) scores of the slice; CPB*G <= 4096
+      float s[kRowsMax];  // per (chunk, head) score of the slice
       float sig[1024];
     } sc;
-    unsigned long long cand[kMaxCand];
   };
-  unsigned long long red[4];
-  int redx[4];
+  uint32_t w_ord[4][64];
+  int w_idx[4][64];
+  int w_pos[4][64];
   int is_last;
 };
 
 // a score-slice block and a window-unit block never need both layouts
-template <int D>
+template <typename T, int D>
 union D1Shared {
   D1Smem sc;
-  UnitSmem<D> us;
+  UnitSmem<T, D> us;
 };
 
-template <typename T, int D, bool QCAL>
+// Per-slice top-K: wave 0 selects among the slice's chunks (NJ per lane).
+template <int NJ>
+__device__ __forceinline__ void slice_select(const DecodeArgs &a, D1Smem &sm, int nch, int c0, int G, size_t cbase) {
+  const int lane = threadIdx.x & 63, K = a.K;
+  uint32_t ord[NJ];
+  int idx[NJ], rank[NJ];
+  bool win[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int cl = lane + 64 * j;
+    ord[j] = cl < nch ? orderable(sm.sc.sig[cl]) : 0u;
+    idx[j] = c0 + cl;
+  }
+  wave_select<NJ>(ord, idx, K, win, rank);
+  int nwin = 0;
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) nwin += __popcll(__ballot(win[j]));
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    if (win[j]) {
+      const int cl = lane + 64 * j;
+      publish(a.cand_key + cbase + rank[j], make_key(sm.sc.sig[cl], idx[j]));
+      for (int hh = 0; hh < G; ++hh) publish(a.cand_s + (cbase + rank[j]) * G + hh, sm.sc.s[cl * G + hh]);
+    }
+  }
+  for (int k = nwin + lane; k < K; k += 64) publish(a.cand_key + cbase + k, kNoKey);
+}
+
+// Merge of the P*K candidates of (b, g): each wave keeps its top-K, wave 0
+// picks the final top-K from the waves' winners.
+template <int NJ>
+__device__ __forceinline__ void merge_select(const DecodeArgs &a, D1Smem &sm, int b, int g, int n) {
+  // NJ candidates per lane: P * K <= 4 waves * 64 lanes * NJ
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, t = threadIdx.x;
+  const int K = a.K, G = a.Hq / a.Hkv;
+  const int total = a.P * K;
+  const size_t cb0 = (static_cast<size_t>(b) * a.Hkv + g) * a.P * K;
+  uint32_t ord[NJ];
+  int idx[NJ], rank[NJ];
+  bool win[NJ];
+  unsigned long long key[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int x = wave * 64 * NJ + j * 64 + lane;
+    key[j] = x < total ? load_acquired(a.cand_key + cb0 + x) : kNoKey;
+  }
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    ord[j] = static_cast<uint32_t>(key[j] >> 32);
+    idx[j] = key[j] == kNoKey ? 0x7FFFFFFF : key_chunk(key[j]);
+  }
+  wave_select<NJ>(ord, idx, K, win, rank);
+#pragma unroll
+  for (int j = 0; j < NJ; ++j)
+    if (win[j]) {
+      sm.w_ord[wave][rank[j]] = ord[j];
+      sm.w_idx[wave][rank[j]] = idx[j];
+      sm.w_pos[wave][rank[j]] = wave * 64 * NJ + j * 64 + lane;
+    }
+  int nw = 0;
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) nw += __popcll(__ballot(win[j]));
+  for (int k = nw + lane; k < 64; k += 64) sm.w_ord[wave][k] = 0u;
+  __syncthreads();
+  if (wave == 0) {
+    uint32_t o2[2];
+    int i2[2], p2[2], r2[2];
+    bool w2[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int x = j * 64 + lane;  // x = wave * K + k
+      const int ww = x / max(K, 1), kk = x % max(K, 1);
+      const bool ok = K > 0 && ww < 4;
+      o2[j] = ok ? sm.w_ord[ww][kk] : 0u;
+      i2[j] = ok ? sm.w_idx[ww][kk] : 0x7FFFFFFF;
+      p2[j] = ok ? sm.w_pos[ww][kk] : 0;
+    }
+    wave_select<2>(o2, i2, K, w2, r2);
+    int nwin = 0;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) nwin += __popcll(__ballot(w2[j]));
+    const int keep = min(K, n);
+    (void)keep;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      if (w2[j]) {
+        a.topk_idx[(static_cast<size_t>(b) * a.Hkv + g) * K + r2[j]] = i2[j];
+        for (int hh = 0; hh < G; ++hh)
+          a.topk_score[(static_cast<size_t>(b) * a.Hq + g * G + hh) * K + r2[j]] =
+              load_acquired(a.cand_s + (cb0 + p2[j]) * G + hh);
+      }
+    for (int k = nwin + lane; k < K; k += 64) {
+      a.topk_idx[(static_cast<size_t>(b) * a.Hkv + g) * K + k] = -1;
+      for (int hh = 0; hh < G; ++hh) a.topk_score[(static_cast<size_t>(b) * a.Hq + g * G + hh) * K + k] = -INFINITY;
+    }
+  }
+  (void)t;
+}
+
+template <typename T, int D, bool QCAL, int SNJ, int MNJ>
 __global__ void __launch_bounds__(kDecThreads)
 decode_score_kernel(DecodeArgs a) {
-  __shared__ D1Shared<D> shm;
+  __shared__ D1Shared<T, D> shm;
   D1Smem &sm = shm.sc;
-  UnitSmem<D> &us = shm.us;
+  UnitSmem<T, D> &us = shm.us;
   const int g = blockIdx.y, b = blockIdx.z, blk = blockIdx.x, t = threadIdx.x;
-  const int lane = t & 63, wave = t >> 6;
   const int G = a.Hq / a.Hkv, K = a.K;
   const int seq = clamp_seq(a.seq_lens, b, a.Tmax, a.err, blk == 0 && g == 0 && t == 0);
   const int i = seq - 1;
@@ -122,49 +221,52 @@ decode_score_kernel(DecodeArgs a) {
     return;
   }
 
-  // ---------------- score slice
+  // ---------------- score slice: chunks [c0, c0 + nch) of the G heads
   const int c0 = blk * a.CPB;
-  const int c1 = min(c0 + a.CPB, n);
-  const int nch = max(0, c1 - c0);
+  const int nch = max(0, min(c0 + a.CPB, n) - c0);
+  constexpr int LPH = D / 8;                         // lanes per (chunk, head) row, 8 elements each
+  constexpr int RPP = static_cast<int>(sizeof(T)) / 2;  // 16-byte loads per 8-element piece
+  constexpr int U = 8 / RPP;                         // pieces in flight per thread
+  constexpr int RS = U * kDecThreads / LPH;          // rows per batch
+  const int nrows = nch * G;
+  const T *ks = static_cast<const T *>(a.k_sum);
+  const size_t hbase = static_cast<size_t>(b) * a.Hq + g * G;
   for (int x = t; x < G * D; x += kDecThreads) {
-    const size_t qo = (static_cast<size_t>(b) * a.Hq + g * G) * D + x;
+    const size_t qo = hbase * D + x;
     sm.sc.qh[x] = QCAL ? a.qhat[qo] : Elem<T>::load(static_cast<const T *>(a.q), qo);
   }
-  __syncthreads();
-  {
-    constexpr int LPH = D / 8;      // lanes per (chunk, head) row
-    constexpr int R = 64 / LPH;     // rows per wave load
-    const int nrows = nch * G;
-    const int seg = lane % LPH;
-    const T *ks = static_cast<const T *>(a.k_sum);
-    const size_t hbase = static_cast<size_t>(b) * a.Hq + g * G;
-    constexpr int UN = 4;  // wave loads in flight per iteration
-    for (int row0 = wave * R; row0 < nrows; row0 += 4 * R * UN) {
-      float part[UN];
-      int rows[UN];
+  for (int rb = 0; rb < nrows; rb += RS) {
+    uint4 kv[U * RPP];
+    float bs[U];
 #pragma unroll
-      for (int uu = 0; uu < UN; ++uu) {
-        const int row = row0 + uu * 4 * R + lane / LPH;
-        rows[uu] = row;
-        part[uu] = 0.f;
-        if (row < nrows) {
-          const int cl = row / G, hh = row % G;
-          float kv[8];
-          Elem<T>::load8(ks + ((hbase + hh) * a.Cmax + c0 + cl) * D + seg * 8, kv);
-          const float *qv = sm.sc.qh + hh * D + seg * 8;
+    for (int u = 0; u < U; ++u) {
+      const int p = u * kDecThreads + t;
+      const int row = rb + p / LPH, seg = p % LPH;
 #pragma unroll
-          for (int x = 0; x < 8; ++x) part[uu] += qv[x] * kv[x];
-        }
+      for (int r = 0; r < RPP; ++r) kv[u * RPP + r] = make_uint4(0, 0, 0, 0);
+      bs[u] = 0.f;
+      if (row < nrows) {
+        const int cl = row / G, hh = row % G;
+        const size_t ro = (hbase + hh) * a.Cmax + c0 + cl;
+#pragma unroll
+        for (int r = 0; r < RPP; ++r) kv[u * RPP + r] = reinterpret_cast<const uint4 *>(ks + ro * D + seg * 8)[r];
+        if (seg == 0) bs[u] = a.b_sum[ro];
       }
+    }
+    __syncthreads();  // q-hat in LDS (first batch); loads stay in flight
 #pragma unroll
-      for (int uu = 0; uu < UN; ++uu) {
-        const float dot = group_sum<LPH>(part[uu]);
-        const int row = rows[uu];
-        if (seg == 0 && row < nrows) {
-          const int cl = row / G, hh = row % G;
-          sm.sc.s[row] = a.tau * dot + a.b_sum[(hbase + hh) * a.Cmax + c0 + cl];
-        }
-      }
+    for (int u = 0; u < U; ++u) {
+      const int p = u * kDecThreads + t;
+      const int row = rb + p / LPH, seg = p % LPH;
+      const int hh = (row < nrows) ? row % G : 0;
+      float kf[8];
+      Elem<T>::load8(reinterpret_cast<const T *>(&kv[u * RPP]), kf);
+      const float *qv = sm.sc.qh + hh * D + seg * 8;
+      float part = 0.f;
+#pragma unroll
+      for (int x = 0; x < 8; ++x) part += qv[x] * kf[x];
+      const float dot = dpp_group_sum<LPH>(part);
+      if (seg == 0 && row < nrows) sm.sc.s[row] = a.tau * dot + bs[u];
     }
   }
   __syncthreads();
@@ -175,26 +277,7 @@ decode_score_kernel(DecodeArgs a) {
   }
   __syncthreads();
   const size_t cbase = ((static_cast<size_t>(b) * a.Hkv + g) * a.P + blk) * K;
-  if (wave == 0) {
-    const int keep = min(K, nch);
-    unsigned long long prev = ~0ull;
-    for (int k = 0; k < K; ++k) {
-      unsigned long long best = kNoKey;
-      if (k < keep) {
-        for (int cl = lane; cl < nch; cl += 64) {
-          const unsigned long long key = make_key(sm.sc.sig[cl], c0 + cl);
-          if (key < prev && key > best) best = key;
-        }
-        best = wave_max_u64(best);
-        prev = best;
-      }
-      if (lane == 0) publish(a.cand_key + cbase + k, best);
-      if (best != kNoKey) {
-        const int cl = key_chunk(best) - c0;
-        for (int hh = lane; hh < G; hh += 64) publish(a.cand_s + (cbase + k) * G + hh, sm.sc.s[cl * G + hh]);
-      }
-    }
-  }
+  if ((t >> 6) == 0 && K > 0) slice_select<SNJ>(a, sm, nch, c0, G, cbase);
   // ---------------- ticket: the last slice block of (b, g) merges
   {
     const unsigned before = arrive(a.count1 + b * a.Hkv + g);
@@ -202,51 +285,60 @@ decode_score_kernel(DecodeArgs a) {
   }
   __syncthreads();
   if (!sm.is_last) return;
-  const int total = a.P * K;
-  const size_t cb0 = (static_cast<size_t>(b) * a.Hkv + g) * a.P * K;
-  for (int x = t; x < total; x += kDecThreads) sm.cand[x] = load_acquired(a.cand_key + cb0 + x);
-  __syncthreads();
-  const int keep = min(K, n);
-  unsigned long long prev = ~0ull;
-  for (int k = 0; k < K; ++k) {
-    if (k < keep) {
-      unsigned long long best = kNoKey;
-      int bx = -1;
-      for (int x = t; x < total; x += kDecThreads) {
-        const unsigned long long key = sm.cand[x];
-        if (key < prev && key > best) { best = key; bx = x; }
-      }
-      unsigned long long wb = wave_max_u64(best);
-      const unsigned long long ball = __ballot(best == wb && bx >= 0);
-      const int src = ball ? __ffsll(static_cast<long long>(ball)) - 1 : 0;
-      const int wx = __shfl(bx, src, 64);
-      if (lane == 0) { sm.red[wave] = wb; sm.redx[wave] = wx; }
-      __syncthreads();
-      unsigned long long bb = sm.red[0];
-      int bbx = sm.redx[0];
-      for (int w = 1; w < kDecThreads / 64; ++w)
-        if (sm.red[w] > bb) { bb = sm.red[w]; bbx = sm.redx[w]; }
-      prev = bb;
-      const int c = key_chunk(bb);
-      if (t == 0) a.topk_idx[(static_cast<size_t>(b) * a.Hkv + g) * K + k] = c;
-      for (int hh = t; hh < G; hh += kDecThreads)
-        a.topk_score[(static_cast<size_t>(b) * a.Hq + g * G + hh) * K + k] =
-            load_acquired(a.cand_s + (cb0 + bbx) * G + hh);
-      __syncthreads();
-    } else {
-      if (t == 0) a.topk_idx[(static_cast<size_t>(b) * a.Hkv + g) * K + k] = -1;
-      for (int hh = t; hh < G; hh += kDecThreads)
-        a.topk_score[(static_cast<size_t>(b) * a.Hq + g * G + hh) * K + k] = -INFINITY;
-    }
-  }
+  if (K > 0) merge_select<MNJ>(a, sm, b, g, n);
   if (t == 0) reset_counter(a.count1 + b * a.Hkv + g);
+}
+
+// ------------------------------------------------------------------ combine
+// Log-sum-exp combine of nslots partial records (m, l, o[D]) per head, in
+// slot order, into o = sum_s e^{m_s - M} o_s / sum_s e^{m_s - M} l_s.
+// The records were published by other workgroups; all loads are issued
+// before they are used.  scratch: >= 2 * nslots * G + G floats of LDS.
+template <typename T, int D>
+__device__ __forceinline__ void combine_slots(const float *recs, int nslots, int G, float *scratch, T *out) {
+  const int t = threadIdx.x;
+  float *w = scratch;                  // [nslots * G]: e^{m - M}
+  float *lt = scratch + nslots * G;    // [G]: sum w * l
+  for (int x = t; x < nslots * G; x += kDecThreads) {
+    const float *rh = recs + static_cast<size_t>(x) * (D + 2);
+    w[x] = load_acquired(rh);
+    scratch[nslots * G + G + x] = load_acquired(rh + 1);
+  }
+  __syncthreads();
+  for (int hh = t; hh < G; hh += kDecThreads) {
+    float M = -INFINITY;
+    for (int s = 0; s < nslots; ++s) M = fmaxf(M, w[s * G + hh]);
+    float L = 0.f;
+    for (int s = 0; s < nslots; ++s) {
+      const float m = w[s * G + hh];
+      const float e = (m == -INFINITY) ? 0.f : __expf(m - M);
+      w[s * G + hh] = e;
+      L += e * scratch[nslots * G + G + s * G + hh];
+    }
+    lt[hh] = L;
+  }
+  __syncthreads();
+  for (int x = t; x < G * D; x += kDecThreads) {
+    const int hh = x / D, e = x % D;
+    float acc = 0.f;
+    int s = 0;
+    for (; s + 8 <= nslots; s += 8) {
+      float o8[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) o8[q] = load_acquired(recs + (static_cast<size_t>(s + q) * G + hh) * (D + 2) + 2 + e);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) acc += w[(s + q) * G + hh] * o8[q];
+    }
+    for (; s < nslots; ++s) acc += w[s * G + hh] * load_acquired(recs + (static_cast<size_t>(s) * G + hh) * (D + 2) + 2 + e);
+    Elem<T>::store(out, static_cast<size_t>(hh) * D + e, acc / lt[hh]);
+  }
 }
 
 // ------------------------------------------------------------------ D2
 template <typename T, int D>
 __global__ void __launch_bounds__(kDecThreads)
 decode_attend_kernel(DecodeArgs a) {
-  __shared__ UnitSmem<D> us;
+  __shared__ UnitSmem<T, D> us;
   __shared__ int is_last;
   const int g = blockIdx.y, b = blockIdx.z, slot = blockIdx.x, t = threadIdx.x;
   const int G = a.Hq / a.Hkv, K = a.K;
@@ -287,23 +379,8 @@ decode_attend_kernel(DecodeArgs a) {
   __syncthreads();
   if (!is_last) return;
   // combine every slot (chunks 0..K-1, window units K..) in slot order
-  for (int x = t; x < G * D; x += kDecThreads) {
-    const int hh = x / D, e = x % D;
-    float m = -INFINITY, l = 0.f, o = 0.f;
-    for (int s = 0; s < a.nslots; ++s) {
-      const float *rh = recs + (static_cast<size_t>(s) * G + hh) * (D + 2);
-      const float m2 = load_acquired(rh);
-      if (m2 == -INFINITY) continue;
-      const float l2 = load_acquired(rh + 1);
-      const float o2 = load_acquired(rh + 2 + e);
-      const float mn = fmaxf(m, m2);
-      const float sa = (m == -INFINITY) ? 0.f : __expf(m - mn), sb = __expf(m2 - mn);
-      o = o * sa + o2 * sb;
-      l = l * sa + l2 * sb;
-      m = mn;
-    }
-    Elem<T>::store(static_cast<T *>(a.o), (static_cast<size_t>(b) * a.Hq + g * G + hh) * D + e, o / l);
-  }
+  combine_slots<T, D>(recs, a.nslots, G, reinterpret_cast<float *>(us.v),
+                      static_cast<T *>(a.o) + (static_cast<size_t>(b) * a.Hq + g * G) * D);
   if (t == 0) reset_counter(a.count2 + b * a.Hkv + g);
 }
 
@@ -311,7 +388,7 @@ decode_attend_kernel(DecodeArgs a) {
 template <typename T, int D>
 __global__ void __launch_bounds__(kDecThreads)
 dense_decode_kernel(DenseArgs a) {
-  __shared__ UnitSmem<D> us;
+  __shared__ UnitSmem<T, D> us;
   __shared__ int is_last;
   const int g = blockIdx.y, b = blockIdx.z, p = blockIdx.x, t = threadIdx.x;
   const int G = a.Hq / a.Hkv;
@@ -357,27 +434,29 @@ dense_decode_kernel(DenseArgs a) {
   }
   __syncthreads();
   if (!is_last) return;
-  for (int x = t; x < G * D; x += kDecThreads) {
-    const int hh = x / D, e = x % D;
-    float m = -INFINITY, l = 0.f, o = 0.f;
-    for (int s = 0; s < a.P; ++s) {
-      const float *rh = recs + (static_cast<size_t>(s) * G + hh) * (D + 2);
-      const float m2 = load_acquired(rh);
-      if (m2 == -INFINITY) continue;
-      const float l2 = load_acquired(rh + 1);
-      const float o2 = load_acquired(rh + 2 + e);
-      const float mn = fmaxf(m, m2);
-      const float sa = (m == -INFINITY) ? 0.f : __expf(m - mn), sb = __expf(m2 - mn);
-      o = o * sa + o2 * sb;
-      l = l * sa + l2 * sb;
-      m = mn;
-    }
-    Elem<T>::store(static_cast<T *>(a.o), (static_cast<size_t>(b) * a.Hq + g * G + hh) * D + e, o / l);
-  }
+  combine_slots<T, D>(recs, a.P, G, reinterpret_cast<float *>(us.v),
+                      static_cast<T *>(a.o) + (static_cast<size_t>(b) * a.Hq + g * G) * D);
   if (t == 0) reset_counter(a.count + b * a.Hkv + g);
 }
 
 // ------------------------------------------------------------------ launchers
+template <typename T, int D, bool QCAL, int SNJ, int MNJ>
+static void launch_d1(const DecodeArgs &a, hipStream_t st) {
+  decode_score_kernel<T, D, QCAL, SNJ, MNJ><<<dim3(a.P + a.NW, a.Hkv, a.B), kDecThreads, 0, st>>>(a);
+}
+
+// slice width SNJ = CPB / 64 in {1, 4, 16}; merge width MNJ = P*K / 256 rounded up to {4, 8, 16}
+template <typename T, int D, bool QCAL>
+static void dispatch_d1(const DecodeArgs &a, hipStream_t st) {
+  const int snj = a.CPB / 64, mnj_need = (a.P * a.K + kDecThreads - 1) / kDecThreads;
+  const int mnj = mnj_need <= 4 ? 4 : (mnj_need <= 8 ? 8 : 16);
+#define HILS_D1(S_, M_) \
+  if (snj == S_ && mnj == M_) return launch_d1<T, D, QCAL, S_, M_>(a, st);
+  HILS_D1(1, 4) HILS_D1(1, 8) HILS_D1(1, 16) HILS_D1(4, 4) HILS_D1(4, 8) HILS_D1(4, 16)
+  HILS_D1(16, 4) HILS_D1(16, 8) HILS_D1(16, 16)
+#undef HILS_D1
+}
+
 template <typename T, int D>
 static hipError_t decode_t(const DecodeArgs &a, hipStream_t st) {
   if (a.r > 0) {
@@ -386,9 +465,9 @@ static hipError_t decode_t(const DecodeArgs &a, hipStream_t st) {
         static_cast<const T *>(a.w_up), a.qhat, a.Hq, a.r, a.Dh);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    decode_score_kernel<T, D, true><<<dim3(a.P + a.NW, a.Hkv, a.B), kDecThreads, 0, st>>>(a);
+    dispatch_d1<T, D, true>(a, st);
   } else {
-    decode_score_kernel<T, D, false><<<dim3(a.P + a.NW, a.Hkv, a.B), kDecThreads, 0, st>>>(a);
+    dispatch_d1<T, D, false>(a, st);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

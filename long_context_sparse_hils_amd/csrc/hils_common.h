@@ -13,12 +13,15 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }
 
-// round to nearest, ties to even (NaN kept quiet)
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// fp32 -> bf16, round to nearest even (one v_cvt_pk_bf16_f32 per pair)
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
+}
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7F800000u) == 0x7F800000u) return static_cast<uint16_t>((u >> 16) | ((u & 0xFFFFu) ? 0x40u : 0u));
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return static_cast<uint16_t>(u >> 16);
+  return static_cast<uint16_t>(pack_bf16x2(f, 0.f) & 0xFFFFu);
 }
 
 // Element access for the two storage types: uint16_t = bf16 bits, float = f32.
@@ -43,8 +46,7 @@ template <> struct Elem<uint16_t> {
     o[1] = __uint_as_float(a & 0xFFFF0000u);
   }
   __device__ __forceinline__ static void store2(uint16_t *p, float a, float b) {
-    uint32_t w = static_cast<uint32_t>(f32_to_bf16(a)) | (static_cast<uint32_t>(f32_to_bf16(b)) << 16);
-    *reinterpret_cast<uint32_t *>(p) = w;
+    *reinterpret_cast<uint32_t *>(p) = pack_bf16x2(a, b);
   }
 };
 template <> struct Elem<float> {
@@ -87,6 +89,19 @@ template <int width>
 __device__ __forceinline__ float group_max(float v) {
 #pragma unroll
   for (int o = width / 2; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+// Sums inside aligned groups of 8 or 16 lanes with DPP lane moves (no LDS
+// traffic): xor-1 and xor-2 inside quads, then mirror inside 8 and 16 lanes.
+template <int width>
+__device__ __forceinline__ float dpp_group_sum(float v) {
+  static_assert(width == 8 || width == 16, "width");
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false));
+  if (width == 16)
+    v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x140, 0xF, 0xF, false));
   return v;
 }
 
@@ -156,6 +171,66 @@ __device__ __forceinline__ float load_acquired(const float *p) {
 }
 __device__ __forceinline__ unsigned long long load_acquired(const unsigned long long *p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Wave-wide top-k selection by (score desc, index asc) without sorting.
+// Each lane holds NJ candidates: ord[j] = orderable(score) (0 = no
+// candidate) and a unique index idx[j].  A bitwise binary search over the
+// 32-bit keys, counting with ballots, finds the k-th largest key theta; the
+// winners are every key above theta plus the lowest-index keys equal to it.
+// On return win[j] marks winners and rank[j] is the winner's position.
+template <int NJ>
+__device__ __forceinline__ void wave_select(const uint32_t (&ord)[NJ], const int (&idx)[NJ], int k,
+                                            bool (&win)[NJ], int (&rank)[NJ]) {
+  const int lane = threadIdx.x & 63;
+  int avail = 0;
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) avail += __popcll(__ballot(ord[j] != 0u));
+  const int keep = min(k, avail);
+  uint32_t theta = 0u;
+  if (keep > 0) {
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t cand = theta | (1u << bit);
+      int cnt = 0;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) cnt += __popcll(__ballot(ord[j] >= cand));
+      if (cnt >= keep) theta = cand;
+    }
+  }
+  int cnt_gt = 0;
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    win[j] = keep > 0 && ord[j] > theta;
+    cnt_gt += __popcll(__ballot(win[j]));
+  }
+  // ties at theta: take the lowest indices first
+  for (int need = keep - cnt_gt; need > 0; --need) {
+    int best = 0x7FFFFFFF;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+      if (!win[j] && ord[j] == theta && ord[j] != 0u) best = min(best, idx[j]);
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) best = min(best, __shfl_xor(best, o, 64));
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+      if (!win[j] && ord[j] == theta && idx[j] == best) win[j] = true;
+  }
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) rank[j] = 0;
+#pragma unroll
+  for (int jj = 0; jj < NJ; ++jj) {
+    unsigned long long wm = __ballot(win[jj]);
+    while (wm) {
+      const int src = __ffsll(static_cast<long long>(wm)) - 1;
+      wm &= wm - 1ull;
+      const uint32_t o2 = __shfl(ord[jj], src, 64);
+      const int i2 = __shfl(idx[jj], src, 64);
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+        if (win[j] && (o2 > ord[j] || (o2 == ord[j] && i2 < idx[j]))) ++rank[j];
+    }
+  }
+  (void)lane;
 }
 
 // R1 partition: complete chunks before query i's window

@@ -38,33 +38,35 @@ __device__ __forceinline__ f32x4 mfma16(const bf16x8 &a, const bf16x8 &b, const 
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const uint4 &u) { return __builtin_bit_cast(bf16x8, u); }
 
-__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  return static_cast<uint32_t>(f32_to_bf16(a)) | (static_cast<uint32_t>(f32_to_bf16(b)) << 16);
-}
 
 constexpr int kItemKeys = 64;
 
-template <int D, int G, int WAVES>
+template <int D, int G, int WAVES, int TPW>
 struct AttnCfg {
   static constexpr int kThreads = WAVES * 64;
   static constexpr int kQPT = 16 / G;         // queries per 16-row tile
-  static constexpr int kQPW = 2 * kQPT;       // queries per wave (two tiles)
+  static constexpr int kQPW = TPW * kQPT;     // queries per wave (TPW tiles)
   static constexpr int kQT = WAVES * kQPW;    // queries per workgroup
   static constexpr int kKS = D / 32;          // k-steps of S^T
   static constexpr int kDT = D / 16;          // d tiles of O^T
-  static constexpr int kKLD = D + 8;          // padded K row (bf16)
+  // K rows: D=128 unpadded with pieces XOR-swizzled (conflict-free operand
+  // reads); D=64 padded rows
+  static constexpr bool kSwz = (D == 128);
+  static constexpr int kKLD = kSwz ? D : D + 8;
   static constexpr int kVLD = kItemKeys + 8;  // padded V^T row (bf16)
   static constexpr int kPieces = kItemKeys * D / 8;  // 16-byte pieces per tensor per item
   static constexpr int kPPT = (kPieces + kThreads - 1) / kThreads;
 };
 
-template <int D, int G, int WAVES>
+template <int D, int G, int WAVES, int TPW>
 struct AttnSmem {
-  using C = AttnCfg<D, G, WAVES>;
+  using C = AttnCfg<D, G, WAVES, TPW>;
   uint16_t ks[2][kItemKeys * C::kKLD];
   uint16_t vt[2][D * C::kVLD];
   int16_t sel[C::kQT * 32];
   int16_t ulist[C::kQT * 32];
+  float alpha[C::kQT * 32 * G];  // fusion score of (query, slot, head)
+  int8_t slot_tab[2][C::kQT];    // per staged item: the slot of that chunk in each query's selection, or -1
   uint32_t umask[256];
   int nunion;
 };
@@ -74,12 +76,22 @@ __device__ __forceinline__ int perm_key(int kt, int m) {
   return 32 * (kt >> 1) + 8 * (m >> 2) + 4 * (kt & 1) + (m & 3);
 }
 
-template <int D, int G, int WAVES>
+// 16-byte piece pc of K row r is stored at piece pc ^ swz(r): the 16 rows
+// one MFMA operand read touches ({0..3, 8..11, 16..19, 24..27} + const) then
+// fall in 16 different bank groups.
+__device__ __forceinline__ int k_swz(int r) { return (r & 3) | ((r >> 1) & 12); }
+
+template <bool SWZ, int KLD>
+__device__ __forceinline__ int k_off(int r, int pc) {
+  return SWZ ? r * KLD + ((pc ^ k_swz(r)) << 3) : r * KLD + (pc << 3);
+}
+
+template <int D, int G, int WAVES, int TPW>
 __global__ void __launch_bounds__(WAVES * 64)
 attn_prefill_mfma_kernel(AttnArgs a, int ntiles, int xcd_map) {
-  using C = AttnCfg<D, G, WAVES>;
+  using C = AttnCfg<D, G, WAVES, TPW>;
   extern __shared__ __align__(16) unsigned char smem_raw[];
-  AttnSmem<D, G, WAVES> &sm = *reinterpret_cast<AttnSmem<D, G, WAVES> *>(smem_raw);
+  AttnSmem<D, G, WAVES, TPW> &sm = *reinterpret_cast<AttnSmem<D, G, WAVES, TPW> *>(smem_raw);
 
   const int T = a.T, K = a.K, S = a.S, W = a.W, Hq = a.Hq, Hkv = a.Hkv;
   const int C_chunks = T / S;
@@ -121,6 +133,9 @@ attn_prefill_mfma_kernel(AttnArgs a, int ntiles, int xcd_map) {
     if (i < T) c = a.topk_idx[((static_cast<size_t>(b) * Hkv + g) * T + i) * K + k];
     sm.sel[q * 32 + k] = static_cast<int16_t>(c);
     if (c >= 0) atomicOr(&sm.umask[c >> 5], 1u << (c & 31));
+    for (int hh = 0; hh < G; ++hh)
+      sm.alpha[(q * 32 + k) * G + hh] =
+          c >= 0 ? a.topk_score[((static_cast<size_t>(b) * Hq + g * G + hh) * T + i) * K + k] : -INFINITY;
   }
   __syncthreads();
   if (wave == 0) {
@@ -157,10 +172,10 @@ attn_prefill_mfma_kernel(AttnArgs a, int ntiles, int xcd_map) {
   const int nitems = nunion + nwin;
 
   // ---- per-lane row identity for the two tiles
-  int row_q[2], row_h[2];
-  bool row_ok[2];
+  int row_q[TPW], row_h[TPW];
+  bool row_ok[TPW];
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
+  for (int t = 0; t < TPW; ++t) {
     const int q = wave * C::kQPW + t * C::kQPT + ln / G;
     row_q[t] = q;
     row_h[t] = g * G + (ln % G);
@@ -168,9 +183,9 @@ attn_prefill_mfma_kernel(AttnArgs a, int ntiles, int xcd_map) {
   }
 
   // ---- Q operands (B of S^T = K Q^T): lane holds row ln, d = 32 ks + 8 lg .. +8
-  bf16x8 qop[2][C::kKS];
+  bf16x8 qop[TPW][C::kKS];
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
+  for (int t = 0; t < TPW; ++t) {
     const int i = q0 + row_q[t];
     const size_t qo = ((static_cast<size_t>(b) * Hq + row_h[t]) * T + (row_ok[t] ? i : 0)) * D;
 #pragma unroll
@@ -181,19 +196,19 @@ attn_prefill_mfma_kernel(AttnArgs a, int ntiles, int xcd_map) {
   }
 
   // ---- row statistics from the selected chunk scores
-  float m_row[2], l_row[2];
-  f32x4 acc[2][C::kDT];
+  float m_row[TPW], l_row[TPW];
+  f32x4 acc[TPW][C::kDT];
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
+  for (int t = 0; t < TPW; ++t) {
     float mx = -INFINITY;
-    const size_t so = ((static_cast<size_t>(b) * Hq + row_h[t]) * T + (q0 + row_q[t])) * K;
+    const int hh = ln % G;
     if (row_ok[t])
       for (int k = 0; k < K; ++k)
-        if (sm.sel[row_q[t] * 32 + k] >= 0) mx = fmaxf(mx, a.topk_score[so + k]);
+        if (sm.sel[row_q[t] * 32 + k] >= 0) mx = fmaxf(mx, sm.alpha[(row_q[t] * 32 + k) * G + hh]);
     float l = 0.f;
     if (row_ok[t] && mx != -INFINITY)
       for (int k = 0; k < K; ++k)
-        if (sm.sel[row_q[t] * 32 + k] >= 0) l += __expf(a.topk_score[so + k] - mx);
+        if (sm.sel[row_q[t] * 32 + k] >= 0) l += __expf(sm.alpha[(row_q[t] * 32 + k) * G + hh] - mx);
     m_row[t] = mx;
     l_row[t] = l;
 #pragma unroll
@@ -204,7 +219,12 @@ attn_prefill_mfma_kernel(AttnArgs a, int ntiles, int xcd_map) {
   auto item_key0 = [&](int x) -> int {
     return x < nunion ? static_cast<int>(sm.ulist[x]) * S : jw0 + (x - nunion) * kItemKeys;
   };
-  uint4 pk[C::kPPT], pv[C::kPPT];
+  // K: thread -> 16-byte pieces (key, piece) row-major; V: thread -> a pair
+  // of keys x one 8-element piece, so the transposed [d][key] tile is written
+  // with conflict-free 32-bit stores (one per d).
+  constexpr int kVPairs = kItemKeys / 2 * (D / 8);          // (key pair, piece) units
+  constexpr int kVPT = (kVPairs + C::kThreads - 1) / C::kThreads;
+  uint4 pk[C::kPPT], pv[kVPT][2];
   auto fetch = [&](int x) {
     const int j0 = item_key0(x);
 #pragma unroll
@@ -212,9 +232,32 @@ attn_prefill_mfma_kernel(AttnArgs a, int ntiles, int xcd_map) {
       const int p = tid + r * C::kThreads;
       const int key = p / (D / 8), seg = p % (D / 8);
       const bool ok = p < C::kPieces && (j0 + key) < T;
-      const size_t off = static_cast<size_t>(j0 + key) * D + seg * 8;
-      pk[r] = ok ? *reinterpret_cast<const uint4 *>(kb + off) : make_uint4(0, 0, 0, 0);
-      pv[r] = ok ? *reinterpret_cast<const uint4 *>(vb + off) : make_uint4(0, 0, 0, 0);
+      pk[r] = ok ? *reinterpret_cast<const uint4 *>(kb + static_cast<size_t>(j0 + key) * D + seg * 8)
+                 : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int r = 0; r < kVPT; ++r) {
+      const int p = tid + r * C::kThreads;
+      const int kp = p % (kItemKeys / 2), seg = p / (kItemKeys / 2);
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const int key = 2 * kp + h2;
+        const bool ok = p < kVPairs && (j0 + key) < T;
+        pv[r][h2] = ok ? *reinterpret_cast<const uint4 *>(vb + static_cast<size_t>(j0 + key) * D + seg * 8)
+                       : make_uint4(0, 0, 0, 0);
+      }
+    }
+  };
+  // slot of item x's chunk in each query's selection (chunk items only)
+  auto build_slots = [&](int x, int buf) {
+    if (x < nunion) {
+      const int c = sm.ulist[x];
+      for (int q = tid; q < C::kQT; q += C::kThreads) {
+        int sl = -1;
+        for (int k = 0; k < K; ++k)
+          if (sm.sel[q * 32 + k] == c) sl = k;
+        sm.slot_tab[buf][q] = static_cast<int8_t>(sl);
+      }
     }
   };
   auto stage = [&](int buf) {
@@ -223,12 +266,22 @@ attn_prefill_mfma_kernel(AttnArgs a, int ntiles, int xcd_map) {
       const int p = tid + r * C::kThreads;
       if (p < C::kPieces) {
         const int key = p / (D / 8), seg = p % (D / 8);
-        *reinterpret_cast<uint4 *>(&sm.ks[buf][key * C::kKLD + seg * 8]) = pk[r];
-        const uint32_t w4[4] = {pv[r].x, pv[r].y, pv[r].z, pv[r].w};
+        *reinterpret_cast<uint4 *>(&sm.ks[buf][k_off<C::kSwz, C::kKLD>(key, seg)]) = pk[r];
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < kVPT; ++r) {
+      const int p = tid + r * C::kThreads;
+      if (p < kVPairs) {
+        const int kp = p % (kItemKeys / 2), seg = p / (kItemKeys / 2);
+        const uint32_t a0[4] = {pv[r][0].x, pv[r][0].y, pv[r][0].z, pv[r][0].w};
+        const uint32_t a1[4] = {pv[r][1].x, pv[r][1].y, pv[r][1].z, pv[r][1].w};
+        uint32_t *vt32 = reinterpret_cast<uint32_t *>(sm.vt[buf]) + ((seg * 8 * C::kVLD + 2 * kp) >> 1);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          sm.vt[buf][(seg * 8 + 2 * e) * C::kVLD + key] = static_cast<uint16_t>(w4[e] & 0xFFFFu);
-          sm.vt[buf][(seg * 8 + 2 * e + 1) * C::kVLD + key] = static_cast<uint16_t>(w4[e] >> 16);
+          // d = seg*8 + 2e: low halves of the two keys; d + 1: high halves
+          vt32[(2 * e * C::kVLD) >> 1] = __builtin_amdgcn_perm(a1[e], a0[e], 0x05040100u);
+          vt32[((2 * e + 1) * C::kVLD) >> 1] = __builtin_amdgcn_perm(a1[e], a0[e], 0x07060302u);
         }
       }
     }
@@ -237,27 +290,36 @@ attn_prefill_mfma_kernel(AttnArgs a, int ntiles, int xcd_map) {
   if (nitems > 0) {
     fetch(0);
     stage(0);
+    build_slots(0, 0);
   }
   __syncthreads();
 
+  // per-lane LDS offsets of the S^T A operand (K rows).  For the permuted
+  // key rows the XOR swizzle of row perm_key(kt, ln) is ln itself, so only
+  // the key-tile term depends on kt (a compile-time constant).
+  int koffb[C::kKS];
+#pragma unroll
+  for (int s = 0; s < C::kKS; ++s) {
+    const int r0 = 8 * (ln >> 2) + (ln & 3);
+    koffb[s] = C::kSwz ? r0 * C::kKLD + (((4 * s + lg) ^ ln) << 3) : r0 * C::kKLD + ((4 * s + lg) << 3);
+  }
+
   const float tau = a.tau;
+  const float tl2e = tau * 1.4426950408889634f;  // tau * log2(e)
   for (int x = 0; x < nitems; ++x) {
     const int buf = x & 1;
     if (x + 1 < nitems) fetch(x + 1);
     const bool is_chunk = x < nunion;
     const int j0 = item_key0(x);
-    const int chunk = j0 / S;
     const uint16_t *ksb = sm.ks[buf];
     const uint16_t *vtb = sm.vt[buf];
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+    for (int t = 0; t < TPW; ++t) {
       // which rows take part
       int slot = -1;
       int lo = 0, hi = -1;  // valid key range of this row (window items)
       if (is_chunk) {
-        if (row_ok[t])
-          for (int k = 0; k < K; ++k)
-            if (sm.sel[row_q[t] * 32 + k] == chunk) slot = k;
+        if (row_ok[t]) slot = sm.slot_tab[buf][row_q[t]];
       } else if (row_ok[t]) {
         const int i = q0 + row_q[t];
         lo = max(j0, eligible_chunks(i, W, S) * S);
@@ -266,36 +328,41 @@ attn_prefill_mfma_kernel(AttnArgs a, int ntiles, int xcd_map) {
       const bool mine = is_chunk ? (slot >= 0) : (lo <= hi);
       if (__ballot(mine) == 0ull) continue;  // wave-uniform skip
       float alpha = -INFINITY;  // this row's fusion score for the chunk
-      if (slot >= 0)
-        alpha = a.topk_score[((static_cast<size_t>(b) * Hq + row_h[t]) * T + (q0 + row_q[t])) * K + slot];
+      if (slot >= 0) alpha = sm.alpha[(row_q[t] * 32 + slot) * G + (ln % G)];
 
       // S^T = K Q^T over the item's 64 keys (4 tiles of 16 keys)
       f32x4 st[4];
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt) {
-        st[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const uint16_t *krow = ksb + perm_key(kt, ln) * C::kKLD + 8 * lg;
+      for (int kt = 0; kt < 4; ++kt) st[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      // k-step outer, key tile inner; the scheduling barriers keep the
+      // compiler from hoisting every operand load (register pressure)
 #pragma unroll
-        for (int s = 0; s < C::kKS; ++s) {
-          const uint4 u = *reinterpret_cast<const uint4 *>(krow + 32 * s);
-          st[kt] = mfma16(as_bf16x8(u), qop[t][s], st[kt]);
-        }
+      for (int s = 0; s < C::kKS; ++s) {
+        uint4 u[4];
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+          u[kt] = *reinterpret_cast<const uint4 *>(ksb + koffb[s] + (32 * (kt >> 1) + 4 * (kt & 1)) * C::kKLD);
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt) st[kt] = mfma16(as_bf16x8(u[kt]), qop[t][s], st[kt]);
+        __builtin_amdgcn_sched_barrier(0);
       }
       // softmax pieces: this lane holds keys perm_key(kt, 4 lg + i) of row ln
       float p[4][4];
       if (is_chunk) {
+        // exact softmax over the chunk's 64 keys: e = 2^{(s - max) tau log2 e}
         float mc = -INFINITY;
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) { p[kt][i] = tau * st[kt][i]; mc = fmaxf(mc, p[kt][i]); }
+          for (int i = 0; i < 4; ++i) mc = fmaxf(mc, st[kt][i]);
         mc = fmaxf(mc, __shfl_xor(mc, 16, 64));
         mc = fmaxf(mc, __shfl_xor(mc, 32, 64));
+        const float off = -mc * tl2e;
         float lc = 0.f;
 #pragma unroll
         for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) { p[kt][i] = __expf(p[kt][i] - mc); lc += p[kt][i]; }
+          for (int i = 0; i < 4; ++i) { p[kt][i] = __builtin_amdgcn_exp2f(fmaf(st[kt][i], tl2e, off)); lc += p[kt][i]; }
         lc += __shfl_xor(lc, 16, 64);
         lc += __shfl_xor(lc, 32, 64);
         const float w = (slot >= 0) ? __expf(alpha - m_row[t]) / lc : 0.f;
@@ -325,11 +392,12 @@ attn_prefill_mfma_kernel(AttnArgs a, int ntiles, int xcd_map) {
             for (int i = 0; i < 4; ++i) p[kt][i] = 0.f;
         } else {
           const float sc = (m_row[t] == -INFINITY) ? 0.f : __expf(m_row[t] - mn);
+          const float off = -mn * 1.4426950408889634f;
 #pragma unroll
           for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              p[kt][i] = (p[kt][i] == -INFINITY) ? 0.f : __expf(p[kt][i] - mn);
+              p[kt][i] = (p[kt][i] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(fmaf(p[kt][i], 1.4426950408889634f, off));
               ls += p[kt][i];
             }
           ls += __shfl_xor(ls, 16, 64);
@@ -355,25 +423,33 @@ attn_prefill_mfma_kernel(AttnArgs a, int ntiles, int xcd_map) {
       }
       // O^T += V^T P^T
 #pragma unroll
-      for (int dt = 0; dt < C::kDT; ++dt) {
-        const uint16_t *vrow = vtb + (16 * dt + ln) * C::kVLD + 8 * lg;
+      for (int dt = 0; dt < C::kDT; dt += 2) {
+        uint4 u[2][2];
 #pragma unroll
-        for (int sl = 0; sl < 2; ++sl) {
-          const uint4 u = *reinterpret_cast<const uint4 *>(vrow + 32 * sl);
-          acc[t][dt] = mfma16(as_bf16x8(u), pb[sl], acc[t][dt]);
-        }
+        for (int d2 = 0; d2 < 2; ++d2)
+#pragma unroll
+          for (int sl = 0; sl < 2; ++sl)
+            u[d2][sl] = *reinterpret_cast<const uint4 *>(vtb + (16 * (dt + d2) + ln) * C::kVLD + 8 * lg + 32 * sl);
+#pragma unroll
+        for (int d2 = 0; d2 < 2; ++d2)
+#pragma unroll
+          for (int sl = 0; sl < 2; ++sl) acc[t][dt + d2] = mfma16(as_bf16x8(u[d2][sl]), pb[sl], acc[t][dt + d2]);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     // buffer buf ^ 1 was last read while computing item x-1, which every
     // thread finished before the barrier that ended that iteration
-    if (x + 1 < nitems) stage(buf ^ 1);
+    if (x + 1 < nitems) {
+      stage(buf ^ 1);
+      build_slots(x + 1, buf ^ 1);
+    }
     __syncthreads();
   }
 
   // ---- epilogue: o = acc / l, lane holds d = 16 dt + 4 lg + (0..3) of row ln
   uint16_t *ob = static_cast<uint16_t *>(a.o);
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
+  for (int t = 0; t < TPW; ++t) {
     if (!row_ok[t]) continue;
     const float inv = 1.f / l_row[t];
     const size_t oo = ((static_cast<size_t>(b) * Hq + row_h[t]) * T + (q0 + row_q[t])) * D;
@@ -389,13 +465,13 @@ attn_prefill_mfma_kernel(AttnArgs a, int ntiles, int xcd_map) {
 
 template <int D, int G>
 static hipError_t attn_mfma_t(const AttnArgs &a, hipStream_t st) {
-  constexpr int WAVES = 8;
-  using C = AttnCfg<D, G, WAVES>;
+  constexpr int WAVES = 8, TPW = 2;
+  using C = AttnCfg<D, G, WAVES, TPW>;
   const int ntiles = (a.T + C::kQT - 1) / C::kQT;
   const int npairs = a.Hkv * a.B;
   const int xcd_map = (npairs % 8 == 0) ? 1 : 0;
-  const size_t smem = sizeof(AttnSmem<D, G, WAVES>);
-  auto kern = attn_prefill_mfma_kernel<D, G, WAVES>;
+  const size_t smem = sizeof(AttnSmem<D, G, WAVES, TPW>);
+  auto kern = attn_prefill_mfma_kernel<D, G, WAVES, TPW>;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem));
   if (e != hipSuccess) return e;

@@ -138,7 +138,7 @@ __global__ void __launch_bounds__(kUnitThreads)
 attn_valu_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__restrict__ v,
                  const int32_t *__restrict__ topk_idx, const float *__restrict__ topk_score,
                  T *__restrict__ o, int T_len, int Hq, int Hkv, int S, int K, int W, float tau) {
-  __shared__ UnitSmem<D> sm;
+  __shared__ UnitSmem<T, D> sm;
   const int i = blockIdx.x, g = blockIdx.y, b = blockIdx.z, t = threadIdx.x;
   const int G = Hq / Hkv;
   const size_t qstride = static_cast<size_t>(T_len) * D;  // between heads
