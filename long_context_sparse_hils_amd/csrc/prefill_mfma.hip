@@ -63,10 +63,11 @@ struct AttnSmem {
   using C = AttnCfg<D, G, WAVES, TPW>;
   uint16_t ks[2][kItemKeys * C::kKLD];
   uint16_t vt[2][D * C::kVLD];
-  int16_t sel[C::kQT * 32];
+  int16_t sel[32 * C::kQT];       // [slot][query]: selected chunk, -1 if none
   int16_t ulist[C::kQT * 32];
-  float alpha[C::kQT * 32 * G];  // fusion score of (query, slot, head)
-  int8_t slot_tab[2][C::kQT];    // per staged item: the slot of that chunk in each query's selection, or -1
+  float alpha[C::kQT * 32 * G];    // fusion score of (query, slot, head)
+  int8_t slot_tab[2][C::kQT];      // per staged item: slot of its chunk in each query's selection, or -1
+  float alpha_tab[2][C::kQT * G];  // per staged item: each (query, head)'s fusion score for it
   uint32_t umask[256];
   int nunion;
 };
@@ -131,7 +132,7 @@ attn_prefill_mfma_kernel(AttnArgs a, int ntiles, int xcd_map) {
     const int q = x / K, k = x % K, i = q0 + q;
     int c = -1;
     if (i < T) c = a.topk_idx[((static_cast<size_t>(b) * Hkv + g) * T + i) * K + k];
-    sm.sel[q * 32 + k] = static_cast<int16_t>(c);
+    sm.sel[k * C::kQT + q] = static_cast<int16_t>(c);
     if (c >= 0) atomicOr(&sm.umask[c >> 5], 1u << (c & 31));
     for (int hh = 0; hh < G; ++hh)
       sm.alpha[(q * 32 + k) * G + hh] =
@@ -204,11 +205,11 @@ attn_prefill_mfma_kernel(AttnArgs a, int ntiles, int xcd_map) {
     const int hh = ln % G;
     if (row_ok[t])
       for (int k = 0; k < K; ++k)
-        if (sm.sel[row_q[t] * 32 + k] >= 0) mx = fmaxf(mx, sm.alpha[(row_q[t] * 32 + k) * G + hh]);
+        if (sm.sel[k * C::kQT + row_q[t]] >= 0) mx = fmaxf(mx, sm.alpha[(row_q[t] * 32 + k) * G + hh]);
     float l = 0.f;
     if (row_ok[t] && mx != -INFINITY)
       for (int k = 0; k < K; ++k)
-        if (sm.sel[row_q[t] * 32 + k] >= 0) l += __expf(sm.alpha[(row_q[t] * 32 + k) * G + hh] - mx);
+        if (sm.sel[k * C::kQT + row_q[t]] >= 0) l += __expf(sm.alpha[(row_q[t] * 32 + k) * G + hh] - mx);
     m_row[t] = mx;
     l_row[t] = l;
 #pragma unroll
@@ -255,8 +256,10 @@ attn_prefill_mfma_kernel(AttnArgs a, int ntiles, int xcd_map) {
       for (int q = tid; q < C::kQT; q += C::kThreads) {
         int sl = -1;
         for (int k = 0; k < K; ++k)
-          if (sm.sel[q * 32 + k] == c) sl = k;
+          if (sm.sel[k * C::kQT + q] == c) sl = k;
         sm.slot_tab[buf][q] = static_cast<int8_t>(sl);
+        for (int hh = 0; hh < G; ++hh)
+          sm.alpha_tab[buf][q * G + hh] = sl >= 0 ? sm.alpha[(q * 32 + sl) * G + hh] : -INFINITY;
       }
     }
   };
@@ -328,7 +331,7 @@ attn_prefill_mfma_kernel(AttnArgs a, int ntiles, int xcd_map) {
       const bool mine = is_chunk ? (slot >= 0) : (lo <= hi);
       if (__ballot(mine) == 0ull) continue;  // wave-uniform skip
       float alpha = -INFINITY;  // this row's fusion score for the chunk
-      if (slot >= 0) alpha = sm.alpha[(row_q[t] * 32 + slot) * G + (ln % G)];
+      if (slot >= 0) alpha = sm.alpha_tab[buf][row_q[t] * G + (ln % G)];
 
       // S^T = K Q^T over the item's 64 keys (4 tiles of 16 keys)
       f32x4 st[4];

@@ -53,7 +53,39 @@ qcal_u_mfma_kernel(const uint16_t *__restrict__ h, const uint16_t *__restrict__ 
   f32x4s acc[4];
 #pragma unroll
   for (int nt = 0; nt < 4; ++nt) acc[nt] = f32x4s{0.f, 0.f, 0.f, 0.f};
-  for (int e0 = 0; e0 < Dh; e0 += 32) {
+  constexpr int UK = 8;  // k-steps whose loads are issued together
+  int e0 = 0;
+  for (; e0 + 32 * UK <= Dh; e0 += 32 * UK) {
+    uint4 av[UK], bv[UK][2];
+#pragma unroll
+    for (int u = 0; u < UK; ++u) {
+      av[u] = tok_ok ? *reinterpret_cast<const uint4 *>(hrow + e0 + 32 * u) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        const int aa = 16 * nt + ln;
+        bv[u][nt] = (nt < NT && aa < r)
+                        ? *reinterpret_cast<const uint4 *>(w_down + static_cast<size_t>(aa) * Dh + e0 + 32 * u + 8 * lg)
+                        : make_uint4(0, 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < UK; ++u)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) acc[nt] = mfma_s(av[u], bv[u][nt], acc[nt]);
+    if (NT > 2) {
+#pragma unroll
+      for (int u = 0; u < UK; ++u)
+#pragma unroll
+        for (int nt = 2; nt < 4; ++nt) {
+          const int aa = 16 * nt + ln;
+          const uint4 b2 = (nt < NT && aa < r)
+                               ? *reinterpret_cast<const uint4 *>(w_down + static_cast<size_t>(aa) * Dh + e0 + 32 * u + 8 * lg)
+                               : make_uint4(0, 0, 0, 0);
+          acc[nt] = mfma_s(av[u], b2, acc[nt]);
+        }
+    }
+  }
+  for (; e0 < Dh; e0 += 32) {
     const uint4 av = tok_ok ? *reinterpret_cast<const uint4 *>(hrow + e0) : make_uint4(0, 0, 0, 0);
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt) {
@@ -115,9 +147,10 @@ qcal_m_kernel(const uint16_t *__restrict__ k_sum, const uint16_t *__restrict__ w
 // ------------------------------------------------------------------ scores + top-K
 constexpr int kScoreMaxC = 256;
 
+template <int NJ>
 struct ScoreWaveSmem {
-  float sig[16][kScoreMaxC];
-  int8_t rank[16][kScoreMaxC];
+  float sig[16][64 * NJ];
+  int8_t rank[16][64 * NJ];
 };
 
 // s for head h, chunk tile ct (16 chunks) and the wave's 16 queries.
@@ -156,19 +189,19 @@ __device__ __forceinline__ f32x4s score_tile(const ScoreArgs &a, const uint16_t 
   return sv;
 }
 
-template <int D>
+template <int D, int NJ>
 __global__ void __launch_bounds__(256)
 score_topk_mfma_kernel(ScoreArgs a, const uint16_t *__restrict__ u_hi, const uint16_t *__restrict__ u_lo,
                        const uint16_t *__restrict__ m_hi, const uint16_t *__restrict__ m_lo, int RP) {
   constexpr int KS = D / 32;
-  __shared__ ScoreWaveSmem wsm[4];
+  __shared__ ScoreWaveSmem<NJ> wsm[4];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int ln = lane & 15, lg = lane >> 4;
   const int T = a.T, C = a.C, K = a.K, Hq = a.Hq, Hkv = a.Hkv, G = Hq / Hkv;
   const int g = blockIdx.y, b = blockIdx.z;
   const int qw0 = blockIdx.x * 64 + wave * 16;  // the wave's first query
   if (qw0 >= T) return;                         // whole wave idle (no barriers below)
-  ScoreWaveSmem &sm = wsm[wave];
+  ScoreWaveSmem<NJ> &sm = wsm[wave];
   const bool qcal = a.r > 0;
   const int i_me = qw0 + ln;                     // this lane's query (B column)
   const bool q_ok = i_me < T;
@@ -191,7 +224,7 @@ score_topk_mfma_kernel(ScoreArgs a, const uint16_t *__restrict__ u_hi, const uin
   const uint16_t *ksb = static_cast<const uint16_t *>(a.k_sum);
 
   // ---- pass 1: group score sigma into LDS
-  for (int x = lane; x < 16 * kScoreMaxC; x += 64) (&sm.sig[0][0])[x] = -INFINITY;
+  for (int x = lane; x < 16 * 64 * NJ; x += 64) (&sm.sig[0][0])[x] = -INFINITY;
   for (int hh = 0; hh < G; ++hh) {
     const int h = g * G + hh;
     uint4 qv[KS];
@@ -202,12 +235,15 @@ score_topk_mfma_kernel(ScoreArgs a, const uint16_t *__restrict__ u_hi, const uin
     const float *bs_h = a.b_sum + (static_cast<size_t>(b) * Hq + h) * C;
     const uint16_t *mh_h = qcal ? m_hi + (static_cast<size_t>(b) * Hq + h) * C * RP : nullptr;
     const uint16_t *ml_h = qcal ? m_lo + (static_cast<size_t>(b) * Hq + h) * C * RP : nullptr;
-    for (int ct = 0; ct < nct; ++ct) {
-      const f32x4s sv = score_tile<D>(a, ks_h, bs_h, qv, mh_h, ml_h, uh, ul, ct, ln, lg, RP, qcal);
+    for (int ct = 0; ct < nct; ct += 2) {
+      // two chunk tiles per step so their operand loads overlap
+      const f32x4s sv0 = score_tile<D>(a, ks_h, bs_h, qv, mh_h, ml_h, uh, ul, ct, ln, lg, RP, qcal);
+      const f32x4s sv1 = score_tile<D>(a, ks_h, bs_h, qv, mh_h, ml_h, uh, ul, ct + 1, ln, lg, RP, qcal);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int c = 16 * ct + 4 * lg + i;
-        if (c < n_me) sm.sig[ln][c] = fmaxf(sm.sig[ln][c], sv[i]);
+        const int c0 = 16 * ct + 4 * lg + i, c1 = c0 + 16;
+        if (c0 < n_me) sm.sig[ln][c0] = fmaxf(sm.sig[ln][c0], sv0[i]);
+        if (c1 < n_me) sm.sig[ln][c1] = fmaxf(sm.sig[ln][c1], sv1[i]);
       }
     }
   }
@@ -220,9 +256,9 @@ score_topk_mfma_kernel(ScoreArgs a, const uint16_t *__restrict__ u_hi, const uin
     if (i >= T) break;
     const int n = min(eligible_chunks(i, a.W, a.S), C);
     const int keep = min(K, n);
-    uint32_t ord[kScoreMaxC / 64];
+    uint32_t ord[NJ];
 #pragma unroll
-    for (int j = 0; j < kScoreMaxC / 64; ++j) {
+    for (int j = 0; j < NJ; ++j) {
       const int c = lane + 64 * j;
       ord[j] = c < n ? orderable(sm.sig[q][c]) : 0u;  // 0 = below every real score
       sm.rank[q][c] = -1;
@@ -234,18 +270,18 @@ score_topk_mfma_kernel(ScoreArgs a, const uint16_t *__restrict__ u_hi, const uin
         const uint32_t cand = theta | (1u << bit);
         int cnt = 0;
 #pragma unroll
-        for (int j = 0; j < kScoreMaxC / 64; ++j) cnt += __popcll(__ballot(ord[j] >= cand));
+        for (int j = 0; j < NJ; ++j) cnt += __popcll(__ballot(ord[j] >= cand));
         if (cnt >= keep) theta = cand;
       }
     }
     // winners: ord > theta, then the lowest-index ord == theta to fill
     int cnt_gt = 0;
 #pragma unroll
-    for (int j = 0; j < kScoreMaxC / 64; ++j) cnt_gt += __popcll(__ballot(keep > 0 && ord[j] > theta));
+    for (int j = 0; j < NJ; ++j) cnt_gt += __popcll(__ballot(keep > 0 && ord[j] > theta));
     int need_eq = keep - cnt_gt;
-    bool win[kScoreMaxC / 64];
+    bool win[NJ];
 #pragma unroll
-    for (int j = 0; j < kScoreMaxC / 64; ++j) {
+    for (int j = 0; j < NJ; ++j) {
       const bool gt = keep > 0 && ord[j] > theta;
       const bool eq = keep > 0 && ord[j] == theta && (lane + 64 * j) < n;
       const unsigned long long eqm = __ballot(eq);
@@ -254,11 +290,11 @@ score_topk_mfma_kernel(ScoreArgs a, const uint16_t *__restrict__ u_hi, const uin
       need_eq -= min(need_eq, __popcll(eqm));
     }
     // rank of each winner among the winners by (score desc, chunk asc)
-    int rk[kScoreMaxC / 64];
+    int rk[NJ];
 #pragma unroll
-    for (int j = 0; j < kScoreMaxC / 64; ++j) rk[j] = 0;
+    for (int j = 0; j < NJ; ++j) rk[j] = 0;
 #pragma unroll
-    for (int jj = 0; jj < kScoreMaxC / 64; ++jj) {
+    for (int jj = 0; jj < NJ; ++jj) {
       unsigned long long wm = __ballot(win[jj]);
       while (wm) {
         const int src = __ffsll(static_cast<long long>(wm)) - 1;
@@ -266,7 +302,7 @@ score_topk_mfma_kernel(ScoreArgs a, const uint16_t *__restrict__ u_hi, const uin
         const uint32_t o2 = __shfl(ord[jj], src, 64);
         const int c2 = src + 64 * jj;
 #pragma unroll
-        for (int j = 0; j < kScoreMaxC / 64; ++j) {
+        for (int j = 0; j < NJ; ++j) {
           const int c = lane + 64 * j;
           if (win[j] && (o2 > ord[j] || (o2 == ord[j] && c2 < c))) ++rk[j];
         }
@@ -274,7 +310,7 @@ score_topk_mfma_kernel(ScoreArgs a, const uint16_t *__restrict__ u_hi, const uin
     }
     const size_t ibase = ((static_cast<size_t>(b) * Hkv + g) * T + i) * K;
 #pragma unroll
-    for (int j = 0; j < kScoreMaxC / 64; ++j) {
+    for (int j = 0; j < NJ; ++j) {
       const int c = lane + 64 * j;
       if (win[j]) {
         sm.rank[q][c] = static_cast<int8_t>(rk[j]);
@@ -301,14 +337,18 @@ score_topk_mfma_kernel(ScoreArgs a, const uint16_t *__restrict__ u_hi, const uin
     const float *bs_h = a.b_sum + (static_cast<size_t>(b) * Hq + h) * C;
     const uint16_t *mh_h = qcal ? m_hi + (static_cast<size_t>(b) * Hq + h) * C * RP : nullptr;
     const uint16_t *ml_h = qcal ? m_lo + (static_cast<size_t>(b) * Hq + h) * C * RP : nullptr;
-    for (int ct = 0; ct < nct; ++ct) {
-      const f32x4s sv = score_tile<D>(a, ks_h, bs_h, qv, mh_h, ml_h, uh, ul, ct, ln, lg, RP, qcal);
+    for (int ct = 0; ct < nct; ct += 2) {
+      const f32x4s sv0 = score_tile<D>(a, ks_h, bs_h, qv, mh_h, ml_h, uh, ul, ct, ln, lg, RP, qcal);
+      const f32x4s sv1 = score_tile<D>(a, ks_h, bs_h, qv, mh_h, ml_h, uh, ul, ct + 1, ln, lg, RP, qcal);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int c = 16 * ct + 4 * lg + i;
-        if (c < n_me) {
-          const int rk = sm.rank[ln][c];
-          if (rk >= 0) a.topk_score[((static_cast<size_t>(b) * Hq + h) * T + i_me) * K + rk] = sv[i];
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          const int c = 16 * (ct + hf) + 4 * lg + i;
+          if (c < n_me) {
+            const int rk = sm.rank[ln][c];
+            if (rk >= 0) a.topk_score[((static_cast<size_t>(b) * Hq + h) * T + i_me) * K + rk] = hf ? sv1[i] : sv0[i];
+          }
         }
       }
     }
@@ -352,10 +392,12 @@ hipError_t launch_score_mfma(const ScoreArgs &a, hipStream_t st) {
     if (e != hipSuccess) return e;
   }
   dim3 grid((a.T + 63) / 64, a.Hkv, a.B);
-  if (a.d == 128)
-    score_topk_mfma_kernel<128><<<grid, 256, 0, st>>>(a, u_hi, u_lo, m_hi, m_lo, RP);
-  else
-    score_topk_mfma_kernel<64><<<grid, 256, 0, st>>>(a, u_hi, u_lo, m_hi, m_lo, RP);
+  // candidates per lane in the selection: ceil(C / 64) rounded to 1, 2 or 4
+  const int nj = a.C <= 64 ? 1 : (a.C <= 128 ? 2 : 4);
+#define HILS_SCORE(DD, NN) \
+  if (a.d == DD && nj == NN) score_topk_mfma_kernel<DD, NN><<<grid, 256, 0, st>>>(a, u_hi, u_lo, m_hi, m_lo, RP);
+  HILS_SCORE(128, 1) HILS_SCORE(128, 2) HILS_SCORE(128, 4) HILS_SCORE(64, 1) HILS_SCORE(64, 2) HILS_SCORE(64, 4)
+#undef HILS_SCORE
   return hipGetLastError();
 }
 
