@@ -100,16 +100,28 @@ def dense_decode_bytes(wl, seq_len):
     return wl.n_kv_heads * seq_len * wl.head_dim * 2 * 2 + wl.n_q_heads * wl.head_dim * 2 * 2
 
 
-def traffic_record(kernel_name, src_file):
-    """HBM traffic measured with rocprofv3 counters, kept in profiles/ with
-    the sha256 of the kernel source it was measured on; null when the source
-    has changed since."""
-    path = os.path.join(ROOT, "profiles", f"{kernel_name}_traffic.json")
+def source_digest(files):
+    """sha256 over the concatenated kernel sources a measurement depends on."""
+    h = hashlib.sha256()
+    for f in files:
+        h.update(open(os.path.join(ROOT, "long_context_sparse_hils_amd", "csrc", f), "rb").read())
+    return h.hexdigest()
+
+
+ATTN_SOURCES = ["prefill_mfma.hip", "hils_common.h"]
+DECODE_SOURCES = ["decode.hip", "attn_unit.h", "hils_common.h", "api.cpp"]
+
+
+def traffic_record(name, sources):
+    """HBM bytes per launch measured with rocprofv3 counters (FETCH_SIZE and
+    WRITE_SIZE, scaled by a plain-copy calibration), kept in profiles/ with
+    the sha256 of the kernel sources it was measured on; null once those
+    sources have changed."""
+    path = os.path.join(ROOT, "profiles", f"{name}_traffic.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    sha = hashlib.sha256(open(src_file, "rb").read()).hexdigest()
-    if rec.get("source_sha256") != sha:
+    if rec.get("source_sha256") != source_digest(sources):
         return None
     return rec.get("bytes_per_launch")
 
@@ -240,9 +252,7 @@ def bench_decode(args, torch, hils, hs, flush, batch):
                bytes_per_step=nb["total"] * B,
                roofline=dict(bound="hbm", achieved=nb["total"] * B / (ms * 1e-3) / 1e9, peak=PEAK_HBM_GBS,
                              unit="GB/s", frac=nb["total"] * B / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
-                             traffic=traffic_record("decode_512k_b%d" % B,
-                                                    os.path.join(ROOT, "long_context_sparse_hils_amd", "csrc",
-                                                                 "decode.hip")),
+                             traffic=traffic_record("decode_512k_b%d" % B, DECODE_SOURCES),
                              kernel="decode step (score+select kernel, attend+combine kernel)"),
                needle_hits=f"{hits}/{len(inp['needles'])}")
     if not args.no_dense:
@@ -325,8 +335,7 @@ def main():
                     stage_ms=res["stage_ms"],
                     roofline=dict(bound="mfma", achieved=ach, peak=PEAK_MFMA_BF16_TFLOPS, unit="TFLOP/s",
                                   frac=ach / PEAK_MFMA_BF16_TFLOPS,
-                                  traffic=traffic_record("attn_prefill_8k", os.path.join(
-                                      ROOT, "long_context_sparse_hils_amd", "csrc", "prefill_mfma.hip")),
+                                  traffic=traffic_record("attn_prefill_8k", ATTN_SOURCES),
                                   kernel="sparse attention (hils_sparse_attn_prefill)",
                                   flops_per_launch=fl["attn"]),
                     whole_step_tflops=fl["total"] / (ms * 1e-3) / 1e12)

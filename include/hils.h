@@ -162,8 +162,8 @@ size_t hils_decode_workspace_bytes(const hils_config *cfg);
  *   b_sum      [B, H_q, C_max]    f32    must hold summaries
  *   seq_lens   [B]                int32, device; 1 <= seq_lens[b] <= T_max.
  *              Out-of-range values are clamped to that range on the device
- *              (no out-of-bounds access) and counted in the workspace word
- *              returned by hils_decode_error_count().
+ *              (no out-of-bounds access) and counted in the workspace
+ *              word at byte offset hils_decode_error_offset(cfg).
  *   o          [B, H_q, d]        dtype out
  *   topk_idx   [B, H_kv, K]       int32 out (-1 pad)
  *   topk_score [B, H_q, K]        f32 out (-inf pad)
