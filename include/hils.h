@@ -135,7 +135,9 @@ hils_status hils_chunk_score_topk(const hils_config *cfg, const void *q, const v
  *   topk_idx   [B, H_kv, T, K]  int32 (as written by hils_chunk_score_topk;
  *                               entries must be -1 or eligible chunks < n_i)
  *   topk_score [B, H_q, T, K]   f32
- *   workspace  >= hils_prefill_workspace_bytes(cfg) bytes, device memory.
+ *   workspace  >= hils_prefill_workspace_bytes(cfg) bytes, device memory
+ *              (may be the one given to hils_chunk_score_topk: this call
+ *              overwrites it with transposed value tiles, in stream order).
  */
 hils_status hils_sparse_attn_prefill(const hils_config *cfg, const void *q, const void *k,
                                      const void *v, const int32_t *topk_idx,

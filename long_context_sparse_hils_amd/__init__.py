@@ -69,6 +69,11 @@ def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built; run `python -m long_context_sparse_hils_amd.build` "
                           "(or __graft_entry__.build())")
+    # torch ships its own copy of the HIP runtime.  Loading torch first makes
+    # libhils bind to that same runtime (one runtime per process), so the
+    # device pointers and streams torch hands over are valid in libhils; a
+    # second runtime loaded from /opt/rocm would not see torch's allocations.
+    import torch  # noqa: F401
     lib = ctypes.CDLL(LIB_PATH)
     P, C, I32, SZ = ctypes.c_void_p, ctypes.POINTER(Config), ctypes.c_int32, ctypes.c_size_t
     sig = {

@@ -200,8 +200,15 @@ hils_status hils_landmark_summary(const hils_config *cfg, const void *k, const v
 size_t hils_prefill_workspace_bytes(const hils_config *cfg) {
   if (check_config(cfg) != HILS_OK) return 0;
   const int C = cfg->seq_len / cfg->chunk_size;
-  return prefill_u_bytes(cfg) +
-         align_up(hils::score_mfma_ws_bytes(cfg->batch, cfg->seq_len, cfg->n_q_heads, C, cfg->qcal_rank)) + kAlign;
+  // scoring uses the workspace first; the attention call then reuses it for
+  // the transposed value tiles of its MFMA path (bf16)
+  const size_t score = prefill_u_bytes(cfg) +
+                       align_up(hils::score_mfma_ws_bytes(cfg->batch, cfg->seq_len, cfg->n_q_heads, C, cfg->qcal_rank)) +
+                       kAlign;
+  const size_t attn = cfg->dtype == HILS_BF16
+                          ? align_up(hils::attn_mfma_ws_bytes(cfg->batch, cfg->n_kv_heads, cfg->seq_len, cfg->head_dim))
+                          : 0;
+  return score > attn ? score : attn;
 }
 
 hils_status hils_chunk_score_topk(const hils_config *cfg, const void *q, const void *h, const void *w_down,

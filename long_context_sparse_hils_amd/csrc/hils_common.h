@@ -105,6 +105,27 @@ __device__ __forceinline__ float dpp_group_sum(float v) {
   return v;
 }
 
+// Reductions over the four lanes l, l^16, l^32, l^48 with the gfx950 row
+// swaps (v_permlane16_swap / v_permlane32_swap: plain VALU moves, no LDS).
+// Called with the same register as both operands, a swap returns the value
+// and its partner's in every lane.
+__device__ __forceinline__ float max_rows4(float v) {
+  const uint32_t b = __float_as_uint(v);
+  auto r = __builtin_amdgcn_permlane16_swap(b, b, false, false);
+  v = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  const uint32_t c = __float_as_uint(v);
+  auto s = __builtin_amdgcn_permlane32_swap(c, c, false, false);
+  return fmaxf(__uint_as_float(s[0]), __uint_as_float(s[1]));
+}
+__device__ __forceinline__ float sum_rows4(float v) {
+  const uint32_t b = __float_as_uint(v);
+  auto r = __builtin_amdgcn_permlane16_swap(b, b, false, false);
+  v = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  const uint32_t c = __float_as_uint(v);
+  auto s = __builtin_amdgcn_permlane32_swap(c, c, false, false);
+  return __uint_as_float(s[0]) + __uint_as_float(s[1]);
+}
+
 __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) {

@@ -33,7 +33,7 @@ struct AttnArgs {
   const int32_t *topk_idx;
   const float *topk_score;
   void *o;
-  void *vt_ws;  // transposed value tiles for the MFMA path
+  void *vt_ws;  // prefill workspace: transposed value tiles of the MFMA path
   int B, T, Hq, Hkv, d, S, K, W;
   float tau;
   bool bf16;
@@ -75,6 +75,7 @@ size_t score_mfma_ws_bytes(int B, int T, int Hq, int C, int r);
 hipError_t launch_score_mfma(const ScoreArgs &a, hipStream_t st);
 hipError_t launch_attn_valu(const AttnArgs &a, hipStream_t st);
 bool attn_mfma_supported(const AttnArgs &a);
+size_t attn_mfma_ws_bytes(int B, int Hkv, int T, int d);
 hipError_t launch_attn_mfma(const AttnArgs &a, hipStream_t st);
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t st);
 hipError_t launch_dense_decode(const DenseArgs &a, hipStream_t st);

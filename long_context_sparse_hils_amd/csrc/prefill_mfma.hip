@@ -3,27 +3,34 @@
 // (Eq. 10) and 3 (query packing: M adjacent queries x G heads share the
 // union of their selected chunks so that matrix tiles stay full).
 //
-// Workgroup = (tile of QT adjacent queries, KV head g, batch b), WAVES waves.
+// Workgroup = (tile of QT adjacent queries, KV head g, batch b), 4 waves (one
+// per SIMD) in under 80 KB of LDS, so that two workgroups share a CU and
+// fill each other's barrier waits and softmax phases with MFMA work.
 // Each wave owns 32 (query, head) rows = two 16-row MFMA tiles of
 // 16/G queries x G heads, with fp32 output accumulators in registers.
 //
 // The workgroup walks a list of 64-key "items": first every chunk in the
 // union of its queries' selections, then the 64-key blocks of the window
-// band.  Each item's K (row-major, padded rows) and V (transposed to
-// [d][key] while staging, padded rows) are staged once in LDS, double
-// buffered, and shared by all waves.  Per item and row tile:
+// band.  Each item's K (row-major, XOR-swizzled 16-byte pieces) and V^T
+// ([d][key], padded rows; read from value tiles transposed once per call by
+// a small kernel) are staged once in LDS, double buffered, and shared by all
+// waves.  Per item, each wave runs only the row tiles that take part (one of
+// their rows selected the chunk / overlaps the window block), and the tiles
+// it runs share every K and V^T operand read:
 //   S^T = K Q^T           16x16x32 bf16 MFMA, keys in M, rows in N
 //   chunk item:  p = softmax over the chunk's 64 keys (exact), scaled by the
 //                fusion weight e^{s_hat - M_row}; rows that did not select
 //                the chunk get weight 0
-//   window item: online softmax (running max/sum per row) over the band,
-//                masked to [n_i * S, i]
+//   window item: softmax against the row's reference maximum, masked to
+//                [n_i * S, i] only on blocks that cross a row's window edge
 //   O^T += V^T P^T        16x16x32 bf16 MFMA, d in M, rows in N
 // The key order inside S^T is permuted so that its accumulator layout is
 // exactly the B-operand layout of the P^T product (no cross-lane moves).
 // Row statistics start from M_row = max of the row's selected chunk scores
 // and l_row = sum e^{s_hat - M_row}; one joint normaliser over chunks and
-// window (Eq. 10's Z-hat_i).
+// window (Eq. 10's Z-hat_i).  A window block moves M_row only when its own
+// maximum exceeds M_row by more than kLazyRescale; numerator and denominator
+// always share the reference, so the result does not depend on when it moves.
 #include "hils_common.h"
 #include "launch.h"
 
@@ -38,8 +45,9 @@ __device__ __forceinline__ f32x4 mfma16(const bf16x8 &a, const bf16x8 &b, const 
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const uint4 &u) { return __builtin_bit_cast(bf16x8, u); }
 
-
 constexpr int kItemKeys = 64;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLazyRescale = 8.f;  // natural-log units: probabilities stay below e^8
 
 template <int D, int G, int WAVES, int TPW>
 struct AttnCfg {
@@ -49,66 +57,251 @@ struct AttnCfg {
   static constexpr int kQT = WAVES * kQPW;    // queries per workgroup
   static constexpr int kKS = D / 32;          // k-steps of S^T
   static constexpr int kDT = D / 16;          // d tiles of O^T
-  // K rows: D=128 unpadded with pieces XOR-swizzled (conflict-free operand
-  // reads); D=64 padded rows
-  static constexpr bool kSwz = (D == 128);
-  static constexpr int kKLD = kSwz ? D : D + 8;
-  static constexpr int kVLD = kItemKeys + 8;  // padded V^T row (bf16)
-  static constexpr int kPieces = kItemKeys * D / 8;  // 16-byte pieces per tensor per item
-  static constexpr int kPPT = (kPieces + kThreads - 1) / kThreads;
+  static constexpr int kKMax = 32;            // largest top-K
+  static constexpr int kRowPieces = D / 8;    // 16-byte pieces per K row
+  // one staged item = 64 K rows + D V^T rows of 128 bytes, loaded straight
+  // into LDS in 1 KB wave-wide pieces
+  static constexpr int kLoadsK = kItemKeys * D * 2 / 1024 / WAVES;
+  static constexpr int kLoadsV = D * kItemKeys * 2 / 1024 / WAVES;
+  static_assert(kLoadsK * WAVES * 1024 == kItemKeys * D * 2, "K item must split evenly over the waves");
 };
 
 template <int D, int G, int WAVES, int TPW>
 struct AttnSmem {
   using C = AttnCfg<D, G, WAVES, TPW>;
-  uint16_t ks[2][kItemKeys * C::kKLD];
-  uint16_t vt[2][D * C::kVLD];
-  int16_t sel[32 * C::kQT];       // [slot][query]: selected chunk, -1 if none
-  int16_t ulist[C::kQT * 32];
-  float alpha[C::kQT * 32 * G];    // fusion score of (query, slot, head)
-  int8_t slot_tab[2][C::kQT];      // per staged item: slot of its chunk in each query's selection, or -1
-  float alpha_tab[2][C::kQT * G];  // per staged item: each (query, head)'s fusion score for it
+  uint16_t ks[2][kItemKeys * D];   // K rows, 16-byte pieces XOR-swizzled per row
+  uint16_t vt[2][D * kItemKeys];   // V^T rows, 16-byte pieces XOR-swizzled per row
+  int16_t spos[C::kQT * C::kKMax];   // per query: union positions of its chunks, ascending
+  int8_t sk[C::kQT * C::kKMax];      // their slots in the query's top-K list
+  int16_t ulist[C::kQT * C::kKMax];  // union of selected chunks, ascending
   uint32_t umask[256];
+  int wbase[256];                    // union positions before each 32-chunk word
   int nunion;
 };
+
+constexpr int16_t kNoPos = 0x7FFF;  // cursor sentinel: no further selected chunk
 
 // key held by S^T tile kt, row m (the permutation described above)
 __device__ __forceinline__ int perm_key(int kt, int m) {
   return 32 * (kt >> 1) + 8 * (m >> 2) + 4 * (kt & 1) + (m & 3);
 }
 
-// 16-byte piece pc of K row r is stored at piece pc ^ swz(r): the 16 rows
-// one MFMA operand read touches ({0..3, 8..11, 16..19, 24..27} + const) then
-// fall in 16 different bank groups.
-__device__ __forceinline__ int k_swz(int r) { return (r & 3) | ((r >> 1) & 12); }
+// XOR swizzle of the 16-byte pieces of K row r.  The 16 rows that one MFMA
+// operand read touches (perm_key(kt, 0..15)) then fall in 16 different bank
+// groups; for those rows the swizzle equals ln (D = 128) or ln >> 1 (D = 64).
+template <int D>
+__device__ __forceinline__ int k_swz(int r) {
+  return D == 128 ? ((r & 3) | ((r >> 1) & 12)) : (((r >> 1) & 1) | ((r >> 2) & 6));
+}
+// XOR swizzle of the 8 pieces of V^T row d: rows d and d ^ 1 share a 256-byte
+// bank line, so the swizzle runs over d >> 1.
+__device__ __forceinline__ int v_swz(int d) { return (d >> 1) & 7; }
 
-template <bool SWZ, int KLD>
-__device__ __forceinline__ int k_off(int r, int pc) {
-  return SWZ ? r * KLD + ((pc ^ k_swz(r)) << 3) : r * KLD + (pc << 3);
+// ------------------------------------------------------------------ V^T tiles
+// v [B, Hkv, T, D] -> vt [B, Hkv, nblk, D, 64]: block blk holds keys
+// 64 blk .. 64 blk + 63 transposed (keys at or past T are zero).
+template <int D>
+__global__ void __launch_bounds__(256)
+vt_transpose_kernel(const uint16_t *__restrict__ v, uint16_t *__restrict__ vt, int T, int nblk) {
+  constexpr int LD = D + 2;  // padded row (4-byte aligned, spreads column reads over banks)
+  __shared__ uint16_t tile[kItemKeys * LD];
+  const int blk = blockIdx.x, pair = blockIdx.y;
+  const uint16_t *src = v + static_cast<size_t>(pair) * T * D;
+  const int j0 = blk * kItemKeys;
+  for (int p = threadIdx.x; p < kItemKeys * D / 8; p += 256) {
+    const int key = p / (D / 8), seg = p % (D / 8);
+    const uint4 u = (j0 + key < T) ? *reinterpret_cast<const uint4 *>(src + static_cast<size_t>(j0 + key) * D + seg * 8)
+                                   : make_uint4(0u, 0u, 0u, 0u);
+    uint32_t *row = reinterpret_cast<uint32_t *>(tile + key * LD + seg * 8);
+    row[0] = u.x; row[1] = u.y; row[2] = u.z; row[3] = u.w;
+  }
+  __syncthreads();
+  uint16_t *dst = vt + (static_cast<size_t>(pair) * nblk + blk) * D * kItemKeys;
+  for (int p = threadIdx.x; p < D * kItemKeys / 8; p += 256) {
+    const int d = p / 8, kp = p % 8;
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      w[e] = static_cast<uint32_t>(tile[(8 * kp + 2 * e) * LD + d]) |
+             (static_cast<uint32_t>(tile[(8 * kp + 2 * e + 1) * LD + d]) << 16);
+    *reinterpret_cast<uint4 *>(dst + d * kItemKeys + kp * 8) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
 }
 
+// ------------------------------------------------------------------ one item
+// Per-lane state of a wave's row tiles.
+template <int D, int TPW>
+struct RowState {
+  bf16x8 qop[TPW][D / 32];   // Q as the B operand of S^T: row ln, d = 32 s + 8 lg .. +8
+  f32x4 acc[TPW][D / 16];    // O^T: lane holds d = 16 dt + 4 lg + (0..3) of row ln
+  float m_row[TPW], l_row[TPW];
+};
+
+// Attend one staged item with one 16-row tile.  CHUNK: exact chunk softmax
+// weighted by wgt; otherwise a window block, masked to [lo, hi] per row when
+// MASKED.  The tile's S^T, softmax and O^T update are one straight-line block;
+// tiles of a wave run one after the other (each a wave-uniform branch).
+template <int D, bool CHUNK, bool MASKED>
+__device__ __forceinline__ void attend_tile(const bf16x8 (&qop)[D / 32], f32x4 (&acc)[D / 16], float &m_row,
+                                            float &l_row, const uint16_t *ksb, const uint16_t *vtb, int koff,
+                                            int voff, float wgt, int lo, int hi, int j0, float tau, float tl2e,
+                                            int lg) {
+  constexpr int KS = D / 32, DT = D / 16;
+  // S^T = K Q^T; the operands of k-step s + 1 are read while the MFMAs of
+  // step s run, and the scheduling barrier keeps later reads from being
+  // hoisted further (registers)
+  f32x4 st[4];
+  {
+    uint4 u[2][4];
+    auto load_k = [&](uint4 (&dst)[4], int s) {
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+        dst[kt] = *reinterpret_cast<const uint4 *>(ksb + (koff ^ (32 * s)) + (32 * (kt >> 1) + 4 * (kt & 1)) * D);
+    };
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) st[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    load_k(u[0], 0);
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      if (s + 1 < KS) load_k(u[(s + 1) & 1], s + 1);
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) st[kt] = mfma16(as_bf16x8(u[s & 1][kt]), qop[s], st[kt]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+  // V^T operands of the first d-tile pair, read while the softmax runs
+  uint4 v[2][2][2];
+  auto load_v = [&](uint4 (&dst)[2][2], int dt) {
+#pragma unroll
+    for (int d2 = 0; d2 < 2; ++d2)
+#pragma unroll
+      for (int sl = 0; sl < 2; ++sl)
+        dst[d2][sl] = *reinterpret_cast<const uint4 *>(vtb + (voff ^ (32 * sl)) + 16 * (dt + d2) * kItemKeys);
+  };
+  load_v(v[0], 0);
+  // softmax pieces: this lane holds keys perm_key(kt, 4 lg + i) of row ln
+  float p[4][4];
+  if (CHUNK) {
+    float mc = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mc = fmaxf(mc, st[kt][i]);
+    mc = max_rows4(mc);
+    const float off = -mc * tl2e;
+    float lc = 0.f;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        p[kt][i] = __builtin_amdgcn_exp2f(fmaf(st[kt][i], tl2e, off));
+        lc += p[kt][i];
+      }
+    lc = sum_rows4(lc);
+    const float w = wgt / lc;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) p[kt][i] *= w;
+  } else {
+    float mb = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float x = st[kt][i];
+        if (MASKED) {
+          const int j = j0 + perm_key(kt, 4 * lg + i);
+          x = (j >= lo && j <= hi) ? x : -INFINITY;
+        }
+        p[kt][i] = x;
+        mb = fmaxf(mb, x);
+      }
+    mb = max_rows4(mb);
+    const float cand = mb * tau;  // the block's largest logit of this row
+    float ref = m_row;
+    float sc = 1.f;
+    if (cand > ref + kLazyRescale) {
+      sc = (ref == -INFINITY) ? 0.f : __expf(ref - cand);
+      ref = cand;
+    }
+    const float off = -ref * kLog2e;
+    float ls = 0.f;
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float e = __builtin_amdgcn_exp2f(fmaf(p[kt][i], tl2e, off));
+        if (MASKED) e = (p[kt][i] == -INFINITY) ? 0.f : e;
+        p[kt][i] = e;
+        ls += e;
+      }
+    ls = sum_rows4(ls);
+    l_row = l_row * sc + ls;
+    m_row = ref;
+    if (__ballot(sc != 1.f)) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) acc[dt] *= sc;
+    }
+  }
+  bf16x8 pb[2];
+#pragma unroll
+  for (int sl = 0; sl < 2; ++sl) {
+    uint4 u;
+    u.x = pack_bf16x2(p[2 * sl][0], p[2 * sl][1]);
+    u.y = pack_bf16x2(p[2 * sl][2], p[2 * sl][3]);
+    u.z = pack_bf16x2(p[2 * sl + 1][0], p[2 * sl + 1][1]);
+    u.w = pack_bf16x2(p[2 * sl + 1][2], p[2 * sl + 1][3]);
+    pb[sl] = as_bf16x8(u);
+  }
+  // O^T += V^T P^T; the next d-tile pair's operands are read while this
+  // pair's MFMAs run
+#pragma unroll
+  for (int st2 = 0; st2 < DT / 2; ++st2) {
+    const int dt = 2 * st2;
+    if (st2 + 1 < DT / 2) load_v(v[(st2 + 1) & 1], dt + 2);
+#pragma unroll
+    for (int d2 = 0; d2 < 2; ++d2)
+#pragma unroll
+      for (int sl = 0; sl < 2; ++sl) acc[dt + d2] = mfma16(as_bf16x8(v[st2 & 1][d2][sl]), pb[sl], acc[dt + d2]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// Run the item for the wave's tiles that take part (bit t of `mask`).
+template <int D, int TPW, bool CHUNK, bool MASKED>
+__device__ __forceinline__ void run_item(int mask, RowState<D, TPW> &R, const uint16_t *ksb, const uint16_t *vtb,
+                                         int koff, int voff, const float (&wgt)[TPW], const int (&lo)[TPW],
+                                         const int (&hi)[TPW], int j0, float tau, float tl2e, int lg) {
+#pragma unroll
+  for (int t = 0; t < TPW; ++t)
+    if ((mask >> t) & 1)
+      attend_tile<D, CHUNK, MASKED>(R.qop[t], R.acc[t], R.m_row[t], R.l_row[t], ksb, vtb, koff, voff, wgt[t], lo[t],
+                                    hi[t], j0, tau, tl2e, lg);
+}
+
+// ------------------------------------------------------------------ kernel
+// One tile per wave: four waves per SIMD (two workgroups per CU), at most 128
+// registers; two tiles per wave: two waves per SIMD, at most 256.
 template <int D, int G, int WAVES, int TPW>
-__global__ void __launch_bounds__(WAVES * 64)
-attn_prefill_mfma_kernel(AttnArgs a, int ntiles, int xcd_map) {
+__global__ void __launch_bounds__(WAVES * 64, TPW == 1 ? 4 : 2)
+attn_prefill_mfma_kernel(AttnArgs a, int ntiles, int xcd_map, int nblk) {
   using C = AttnCfg<D, G, WAVES, TPW>;
   extern __shared__ __align__(16) unsigned char smem_raw[];
   AttnSmem<D, G, WAVES, TPW> &sm = *reinterpret_cast<AttnSmem<D, G, WAVES, TPW> *>(smem_raw);
 
-  const int T = a.T, K = a.K, S = a.S, W = a.W, Hq = a.Hq, Hkv = a.Hkv;
-  const int C_chunks = T / S;
+  const int T = a.T, K = a.K, W = a.W, Hq = a.Hq, Hkv = a.Hkv;
+  const int C_chunks = T / kItemKeys;  // chunk size S = 64 on this path
   // ---- workgroup -> (tile, g, b); heaviest (latest) tiles first, and the
   // tiles of one (b, g) on one XCD so its K/V stay in that XCD's L2
   int tile, g, b;
   {
     const int L = blockIdx.x;
-    const int npairs = Hkv * a.B;
     int pair, slot;
     if (xcd_map) {
       const int xcd = L & 7, s = L >> 3;
-      const int per = npairs / 8;           // pairs per XCD
       pair = xcd + 8 * (s / ntiles);
       slot = s % ntiles;
-      (void)per;
     } else {
       pair = L / ntiles;
       slot = L % ntiles;
@@ -123,20 +316,22 @@ attn_prefill_mfma_kernel(AttnArgs a, int ntiles, int xcd_map) {
 
   const uint16_t *qb = static_cast<const uint16_t *>(a.q);
   const uint16_t *kb = static_cast<const uint16_t *>(a.k) + (static_cast<size_t>(b) * Hkv + g) * T * D;
-  const uint16_t *vb = static_cast<const uint16_t *>(a.v) + (static_cast<size_t>(b) * Hkv + g) * T * D;
+  const uint16_t *vtg = static_cast<const uint16_t *>(a.vt_ws) + (static_cast<size_t>(b) * Hkv + g) * nblk * D * kItemKeys;
 
-  // ---- selection table and the union of selected chunks
+  // ---- the union of the tile's selected chunks (bit mask -> ascending list)
   for (int x = tid; x < 256; x += C::kThreads) sm.umask[x] = 0u;
   __syncthreads();
-  for (int x = tid; x < C::kQT * K; x += C::kThreads) {
-    const int q = x / K, k = x % K, i = q0 + q;
+  // selections in a register per (query, slot)
+  constexpr int kPairs = (C::kQT * C::kKMax + C::kThreads - 1) / C::kThreads;
+  int my_c[kPairs];
+#pragma unroll
+  for (int r = 0; r < kPairs; ++r) {
+    const int x = tid + r * C::kThreads, q = x / C::kKMax, k = x % C::kKMax, i = q0 + q;
     int c = -1;
-    if (i < T) c = a.topk_idx[((static_cast<size_t>(b) * Hkv + g) * T + i) * K + k];
-    sm.sel[k * C::kQT + q] = static_cast<int16_t>(c);
+    if (q < C::kQT && k < K && i < T) c = a.topk_idx[((static_cast<size_t>(b) * Hkv + g) * T + i) * K + k];
+    my_c[r] = c;
+    if (q < C::kQT) sm.ulist[x] = static_cast<int16_t>(c);  // scratch copy of the raw lists
     if (c >= 0) atomicOr(&sm.umask[c >> 5], 1u << (c & 31));
-    for (int hh = 0; hh < G; ++hh)
-      sm.alpha[(q * 32 + k) * G + hh] =
-          c >= 0 ? a.topk_score[((static_cast<size_t>(b) * Hq + g * G + hh) * T + i) * K + k] : -INFINITY;
   }
   __syncthreads();
   if (wave == 0) {
@@ -152,300 +347,229 @@ attn_prefill_mfma_kernel(AttnArgs a, int ntiles, int xcd_map) {
         const int y = __shfl_up(incl, o, 64);
         if (lane >= o) incl += y;
       }
-      int pos = base + incl - cnt;
-      uint32_t bb = bits;
+      if (w < nwords) sm.wbase[w] = base + incl - cnt;
+      base += __shfl(incl, 63, 64);
+    }
+    if (lane == 0) sm.nunion = base;
+  }
+  // ---- per query: its chunks' union positions in ascending order (= chunk
+  // order), with their fusion scores.  Entry (q, k) takes rank
+  //   #{valid c2 < c} + #{earlier valid c2 == c}        for a valid c,
+  //   n_valid + #{earlier invalid entries}              otherwise,
+  // a bijection onto 0 .. kKMax-1 (invalid ranks hold the sentinel).
+#pragma unroll
+  for (int r = 0; r < kPairs; ++r) {
+    const int x = tid + r * C::kThreads, q = x / C::kKMax, k = x % C::kKMax;
+    if (q >= C::kQT) continue;
+    const int c = my_c[r];
+    int below = 0, nvalid = 0, inv_before = 0;
+    for (int k2 = 0; k2 < K; ++k2) {
+      const int c2 = sm.ulist[q * C::kKMax + k2];
+      nvalid += c2 >= 0;
+      below += (c2 >= 0) & ((c2 < c) | ((c2 == c) & (k2 < k)));
+      inv_before += (c2 < 0) & (k2 < k);
+    }
+    inv_before += max(0, k - K);  // entries k2 >= K are invalid too
+    my_c[r] = c >= 0 ? below : -1 - (nvalid + inv_before);
+  }
+  __syncthreads();  // wbase, nunion ready; the raw lists are read no more
+#pragma unroll
+  for (int r = 0; r < kPairs; ++r) {
+    const int x = tid + r * C::kThreads, q = x / C::kKMax, k = x % C::kKMax, i = q0 + q;
+    if (q >= C::kQT) continue;
+    (void)i;
+    if (my_c[r] >= 0) {
+      const int rank = my_c[r];
+      const int c = sm.ulist[q * C::kKMax + k];
+      const int upos = sm.wbase[c >> 5] + __popc(sm.umask[c >> 5] & ((1u << (c & 31)) - 1u));
+      sm.spos[q * C::kKMax + rank] = static_cast<int16_t>(upos);
+      sm.sk[q * C::kKMax + rank] = static_cast<int8_t>(k);
+    } else {
+      sm.spos[q * C::kKMax + (-1 - my_c[r])] = kNoPos;
+    }
+  }
+  __syncthreads();
+  // the ascending union list (overwrites the scratch copy)
+  if (wave == 0) {
+    const int nwords = (C_chunks + 31) >> 5;
+    for (int w = lane; w < nwords; w += 64) {
+      int pos = sm.wbase[w];
+      uint32_t bb = sm.umask[w];
       while (bb) {
         const int bit = __ffs(bb) - 1;
         bb &= bb - 1;
         sm.ulist[pos++] = static_cast<int16_t>(w * 32 + bit);
       }
-      base += __shfl(incl, 63, 64);
     }
-    if (lane == 0) sm.nunion = base;
   }
   __syncthreads();
   const int nunion = sm.nunion;
 
   // window band of the tile: 64-key blocks from n_{first} * S to the last query
   const int i_first = q0, i_last = min(q0 + C::kQT - 1, T - 1);
-  const int jw0 = eligible_chunks(i_first, W, S) * S;
+  const int jw0 = eligible_chunks(i_first, W, kItemKeys) * kItemKeys;
   const int nwin = (i_last - jw0) / kItemKeys + 1;
   const int nitems = nunion + nwin;
 
-  // ---- per-lane row identity for the two tiles
-  int row_q[TPW], row_h[TPW];
+  // ---- per-lane row identity for the tiles
+  int row_q[TPW];
+  const int row_h = g * G + (ln % G);  // the same head in every tile
   bool row_ok[TPW];
 #pragma unroll
   for (int t = 0; t < TPW; ++t) {
     const int q = wave * C::kQPW + t * C::kQPT + ln / G;
     row_q[t] = q;
-    row_h[t] = g * G + (ln % G);
     row_ok[t] = (q0 + q) < T;
   }
 
+  RowState<D, TPW> R;
   // ---- Q operands (B of S^T = K Q^T): lane holds row ln, d = 32 ks + 8 lg .. +8
-  bf16x8 qop[TPW][C::kKS];
 #pragma unroll
   for (int t = 0; t < TPW; ++t) {
     const int i = q0 + row_q[t];
-    const size_t qo = ((static_cast<size_t>(b) * Hq + row_h[t]) * T + (row_ok[t] ? i : 0)) * D;
+    const size_t qo = ((static_cast<size_t>(b) * Hq + row_h) * T + (row_ok[t] ? i : 0)) * D;
 #pragma unroll
     for (int s = 0; s < C::kKS; ++s) {
       uint4 u = row_ok[t] ? *reinterpret_cast<const uint4 *>(qb + qo + 32 * s + 8 * lg) : make_uint4(0, 0, 0, 0);
-      qop[t][s] = as_bf16x8(u);
+      R.qop[t][s] = as_bf16x8(u);
     }
   }
 
-  // ---- row statistics from the selected chunk scores
-  float m_row[TPW], l_row[TPW];
-  f32x4 acc[TPW][C::kDT];
+  // ---- row statistics from the selected chunk scores, and each row's
+  // cursor into its ascending selection list
+  int cur[TPW], nxt_pos[TPW];
+  float nxt_alpha[TPW];
+  // this row's fusion scores, indexed by top-K slot: a.topk_score + tsc_off[t]
+  const float *tsc_b = a.topk_score + static_cast<size_t>(b) * Hq * T * K;
+  int tsc_off[TPW];
 #pragma unroll
   for (int t = 0; t < TPW; ++t) {
+    const int qk = row_q[t] * C::kKMax;
+    tsc_off[t] = (row_h * T + (row_ok[t] ? q0 + row_q[t] : 0)) * K;
     float mx = -INFINITY;
-    const int hh = ln % G;
     if (row_ok[t])
-      for (int k = 0; k < K; ++k)
-        if (sm.sel[k * C::kQT + row_q[t]] >= 0) mx = fmaxf(mx, sm.alpha[(row_q[t] * 32 + k) * G + hh]);
+      for (int k = 0; k < K && sm.spos[qk + k] != kNoPos; ++k) mx = fmaxf(mx, tsc_b[tsc_off[t] + sm.sk[qk + k]]);
     float l = 0.f;
     if (row_ok[t] && mx != -INFINITY)
-      for (int k = 0; k < K; ++k)
-        if (sm.sel[k * C::kQT + row_q[t]] >= 0) l += __expf(sm.alpha[(row_q[t] * 32 + k) * G + hh] - mx);
-    m_row[t] = mx;
-    l_row[t] = l;
+      for (int k = 0; k < K && sm.spos[qk + k] != kNoPos; ++k) l += __expf(tsc_b[tsc_off[t] + sm.sk[qk + k]] - mx);
+    R.m_row[t] = mx;
+    R.l_row[t] = l;
 #pragma unroll
-    for (int dt = 0; dt < C::kDT; ++dt) acc[t][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int dt = 0; dt < C::kDT; ++dt) R.acc[t][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    cur[t] = 0;
+    nxt_pos[t] = (row_ok[t] && K > 0) ? sm.spos[qk] : kNoPos;
+    nxt_alpha[t] = nxt_pos[t] != kNoPos ? tsc_b[tsc_off[t] + sm.sk[qk]] : 0.f;
   }
 
-  // ---- staging: item x -> LDS buffer
+  // ---- staging: item x -> LDS buffer, straight from global memory.  Wave w
+  // fills 1 KB slices w, w + WAVES, ... of each tensor; lane l's 16 bytes land
+  // at byte 16 l of the slice, i.e. at one (row, physical piece) pair, and the
+  // lane fetches the logical piece the swizzle puts there.
   auto item_key0 = [&](int x) -> int {
-    return x < nunion ? static_cast<int>(sm.ulist[x]) * S : jw0 + (x - nunion) * kItemKeys;
+    return x < nunion ? static_cast<int>(sm.ulist[x]) * kItemKeys : jw0 + (x - nunion) * kItemKeys;
   };
-  // K: thread -> 16-byte pieces (key, piece) row-major; V: thread -> a pair
-  // of keys x one 8-element piece, so the transposed [d][key] tile is written
-  // with conflict-free 32-bit stores (one per d).
-  constexpr int kVPairs = kItemKeys / 2 * (D / 8);          // (key pair, piece) units
-  constexpr int kVPT = (kVPairs + C::kThreads - 1) / C::kThreads;
-  uint4 pk[C::kPPT], pv[kVPT][2];
-  auto fetch = [&](int x) {
-    const int j0 = item_key0(x);
+  auto issue_loads = [&](int j0, int buf) {
+    const uint16_t *vsrc = vtg + static_cast<size_t>(j0 / kItemKeys) * D * kItemKeys;
 #pragma unroll
-    for (int r = 0; r < C::kPPT; ++r) {
-      const int p = tid + r * C::kThreads;
-      const int key = p / (D / 8), seg = p % (D / 8);
-      const bool ok = p < C::kPieces && (j0 + key) < T;
-      pk[r] = ok ? *reinterpret_cast<const uint4 *>(kb + static_cast<size_t>(j0 + key) * D + seg * 8)
-                 : make_uint4(0, 0, 0, 0);
+    for (int i = 0; i < C::kLoadsK; ++i) {
+      const int slice = i * WAVES + wave;
+      const int sl = slice * 64 + lane;  // 16-byte slot
+      const int r = sl / C::kRowPieces, pp = sl % C::kRowPieces;
+      const int pc = pp ^ k_swz<D>(r);
+      const int key = min(j0 + r, T - 1);  // rows past T are never used unmasked
+      __builtin_amdgcn_global_load_lds(kb + static_cast<uint32_t>(key * D + pc * 8),
+                                       (__attribute__((address_space(3))) void *)(sm.ks[buf] + slice * 512), 16, 0, 0);
     }
 #pragma unroll
-    for (int r = 0; r < kVPT; ++r) {
-      const int p = tid + r * C::kThreads;
-      const int kp = p % (kItemKeys / 2), seg = p / (kItemKeys / 2);
-#pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
-        const int key = 2 * kp + h2;
-        const bool ok = p < kVPairs && (j0 + key) < T;
-        pv[r][h2] = ok ? *reinterpret_cast<const uint4 *>(vb + static_cast<size_t>(j0 + key) * D + seg * 8)
-                       : make_uint4(0, 0, 0, 0);
-      }
-    }
-  };
-  // slot of item x's chunk in each query's selection (chunk items only)
-  auto build_slots = [&](int x, int buf) {
-    if (x < nunion) {
-      const int c = sm.ulist[x];
-      for (int q = tid; q < C::kQT; q += C::kThreads) {
-        int sl = -1;
-        for (int k = 0; k < K; ++k)
-          if (sm.sel[k * C::kQT + q] == c) sl = k;
-        sm.slot_tab[buf][q] = static_cast<int8_t>(sl);
-        for (int hh = 0; hh < G; ++hh)
-          sm.alpha_tab[buf][q * G + hh] = sl >= 0 ? sm.alpha[(q * 32 + sl) * G + hh] : -INFINITY;
-      }
-    }
-  };
-  auto stage = [&](int buf) {
-#pragma unroll
-    for (int r = 0; r < C::kPPT; ++r) {
-      const int p = tid + r * C::kThreads;
-      if (p < C::kPieces) {
-        const int key = p / (D / 8), seg = p % (D / 8);
-        *reinterpret_cast<uint4 *>(&sm.ks[buf][k_off<C::kSwz, C::kKLD>(key, seg)]) = pk[r];
-      }
-    }
-#pragma unroll
-    for (int r = 0; r < kVPT; ++r) {
-      const int p = tid + r * C::kThreads;
-      if (p < kVPairs) {
-        const int kp = p % (kItemKeys / 2), seg = p / (kItemKeys / 2);
-        const uint32_t a0[4] = {pv[r][0].x, pv[r][0].y, pv[r][0].z, pv[r][0].w};
-        const uint32_t a1[4] = {pv[r][1].x, pv[r][1].y, pv[r][1].z, pv[r][1].w};
-        uint32_t *vt32 = reinterpret_cast<uint32_t *>(sm.vt[buf]) + ((seg * 8 * C::kVLD + 2 * kp) >> 1);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          // d = seg*8 + 2e: low halves of the two keys; d + 1: high halves
-          vt32[(2 * e * C::kVLD) >> 1] = __builtin_amdgcn_perm(a1[e], a0[e], 0x05040100u);
-          vt32[((2 * e + 1) * C::kVLD) >> 1] = __builtin_amdgcn_perm(a1[e], a0[e], 0x07060302u);
-        }
-      }
+    for (int i = 0; i < C::kLoadsV; ++i) {
+      const int slice = i * WAVES + wave;
+      const int sl = slice * 64 + lane;
+      const int d = sl / 8, pp = sl % 8;
+      const int pc = pp ^ v_swz(d);
+      __builtin_amdgcn_global_load_lds(vsrc + static_cast<uint32_t>(d * kItemKeys + pc * 8),
+                                       (__attribute__((address_space(3))) void *)(sm.vt[buf] + slice * 512), 16, 0, 0);
     }
   };
 
+  int j0_cur = 0, j0_nxt = 0;
   if (nitems > 0) {
-    fetch(0);
-    stage(0);
-    build_slots(0, 0);
+    j0_cur = item_key0(0);
+    issue_loads(j0_cur, 0);
   }
+  if (nitems > 1) j0_nxt = item_key0(1);
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  // per-lane LDS offsets of the S^T A operand (K rows).  For the permuted
-  // key rows the XOR swizzle of row perm_key(kt, ln) is ln itself, so only
-  // the key-tile term depends on kt (a compile-time constant).
-  int koffb[C::kKS];
-#pragma unroll
-  for (int s = 0; s < C::kKS; ++s) {
-    const int r0 = 8 * (ln >> 2) + (ln & 3);
-    koffb[s] = C::kSwz ? r0 * C::kKLD + (((4 * s + lg) ^ ln) << 3) : r0 * C::kKLD + ((4 * s + lg) << 3);
-  }
+  // per-lane LDS offsets of the S^T A operand (K rows perm_key(kt, ln); their
+  // swizzle does not depend on kt) and of the O^T A operand (V^T rows 16 dt + ln)
+  // k-step s reads piece (4 s + lg) ^ swizzle = piece(0) ^ 4 s: offset koff ^ 32 s;
+  // key slot sl reads piece (lg + 4 sl) ^ swizzle: offset voff ^ 32 sl
+  const int r0 = 8 * (ln >> 2) + (ln & 3);
+  const int koff = r0 * D + ((lg ^ k_swz<D>(r0)) << 3);
+  const int voff = ln * kItemKeys + ((lg ^ v_swz(ln)) << 3);
 
   const float tau = a.tau;
-  const float tl2e = tau * 1.4426950408889634f;  // tau * log2(e)
+  const float tl2e = tau * kLog2e;
   for (int x = 0; x < nitems; ++x) {
     const int buf = x & 1;
-    if (x + 1 < nitems) fetch(x + 1);
-    const bool is_chunk = x < nunion;
-    const int j0 = item_key0(x);
+    // buffer buf ^ 1 was last read in iteration x - 1, before the barrier
+    // that ended it
+    if (x + 1 < nitems) issue_loads(j0_nxt, buf ^ 1);
+    const int j0_nn = (x + 2 < nitems) ? item_key0(x + 2) : 0;
     const uint16_t *ksb = sm.ks[buf];
     const uint16_t *vtb = sm.vt[buf];
+    const int j0 = j0_cur;
+    float wgt[TPW];
+    int lo[TPW], hi[TPW];
+    int mask = 0;
+    if (x < nunion) {
 #pragma unroll
-    for (int t = 0; t < TPW; ++t) {
-      // which rows take part
-      int slot = -1;
-      int lo = 0, hi = -1;  // valid key range of this row (window items)
-      if (is_chunk) {
-        if (row_ok[t]) slot = sm.slot_tab[buf][row_q[t]];
-      } else if (row_ok[t]) {
-        const int i = q0 + row_q[t];
-        lo = max(j0, eligible_chunks(i, W, S) * S);
-        hi = min(j0 + kItemKeys - 1, i);
-      }
-      const bool mine = is_chunk ? (slot >= 0) : (lo <= hi);
-      if (__ballot(mine) == 0ull) continue;  // wave-uniform skip
-      float alpha = -INFINITY;  // this row's fusion score for the chunk
-      if (slot >= 0) alpha = sm.alpha_tab[buf][row_q[t] * G + (ln % G)];
-
-      // S^T = K Q^T over the item's 64 keys (4 tiles of 16 keys)
-      f32x4 st[4];
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt) st[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-      // k-step outer, key tile inner; the scheduling barriers keep the
-      // compiler from hoisting every operand load (register pressure)
-#pragma unroll
-      for (int s = 0; s < C::kKS; ++s) {
-        uint4 u[4];
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
-          u[kt] = *reinterpret_cast<const uint4 *>(ksb + koffb[s] + (32 * (kt >> 1) + 4 * (kt & 1)) * C::kKLD);
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt) st[kt] = mfma16(as_bf16x8(u[kt]), qop[t][s], st[kt]);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      // softmax pieces: this lane holds keys perm_key(kt, 4 lg + i) of row ln
-      float p[4][4];
-      if (is_chunk) {
-        // exact softmax over the chunk's 64 keys: e = 2^{(s - max) tau log2 e}
-        float mc = -INFINITY;
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) mc = fmaxf(mc, st[kt][i]);
-        mc = fmaxf(mc, __shfl_xor(mc, 16, 64));
-        mc = fmaxf(mc, __shfl_xor(mc, 32, 64));
-        const float off = -mc * tl2e;
-        float lc = 0.f;
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) { p[kt][i] = __builtin_amdgcn_exp2f(fmaf(st[kt][i], tl2e, off)); lc += p[kt][i]; }
-        lc += __shfl_xor(lc, 16, 64);
-        lc += __shfl_xor(lc, 32, 64);
-        const float w = (slot >= 0) ? __expf(alpha - m_row[t]) / lc : 0.f;
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) p[kt][i] *= w;
-      } else {
-        float mb = -INFINITY;
-#pragma unroll
-        for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int j = j0 + perm_key(kt, 4 * lg + i);
-            const float s = (j >= lo && j <= hi) ? tau * st[kt][i] : -INFINITY;
-            p[kt][i] = s;
-            mb = fmaxf(mb, s);
-          }
-        mb = fmaxf(mb, __shfl_xor(mb, 16, 64));
-        mb = fmaxf(mb, __shfl_xor(mb, 32, 64));
-        const float mn = fmaxf(m_row[t], mb);
-        float ls = 0.f;
-        if (mn == -INFINITY) {
-#pragma unroll
-          for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) p[kt][i] = 0.f;
-        } else {
-          const float sc = (m_row[t] == -INFINITY) ? 0.f : __expf(m_row[t] - mn);
-          const float off = -mn * 1.4426950408889634f;
-#pragma unroll
-          for (int kt = 0; kt < 4; ++kt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              p[kt][i] = (p[kt][i] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(fmaf(p[kt][i], 1.4426950408889634f, off));
-              ls += p[kt][i];
-            }
-          ls += __shfl_xor(ls, 16, 64);
-          ls += __shfl_xor(ls, 32, 64);
-          if (sc != 1.f) {
-#pragma unroll
-            for (int dt = 0; dt < C::kDT; ++dt) acc[t][dt] *= sc;
-          }
-          l_row[t] = l_row[t] * sc + ls;
-          m_row[t] = mn;
+      for (int t = 0; t < TPW; ++t) {
+        if (nxt_pos[t] < x) {  // only after a repeated entry: skip it
+          const int qk = row_q[t] * C::kKMax;
+          ++cur[t];
+          nxt_pos[t] = cur[t] < K ? sm.spos[qk + cur[t]] : kNoPos;
+          nxt_alpha[t] = nxt_pos[t] != kNoPos ? tsc_b[tsc_off[t] + sm.sk[qk + cur[t]]] : 0.f;
+        }
+        const bool act = nxt_pos[t] == x;
+        wgt[t] = act ? __expf(nxt_alpha[t] - R.m_row[t]) : 0.f;
+        lo[t] = 0;
+        hi[t] = -1;
+        if (__ballot(act)) mask |= 1 << t;
+        if (act) {
+          const int qk = row_q[t] * C::kKMax;
+          ++cur[t];
+          nxt_pos[t] = cur[t] < K ? sm.spos[qk + cur[t]] : kNoPos;
+          nxt_alpha[t] = nxt_pos[t] != kNoPos ? tsc_b[tsc_off[t] + sm.sk[qk + cur[t]]] : 0.f;
         }
       }
-      // P^T as the B operand: k-slot sl holds keys 32 sl + 8 lg .. +8
-      bf16x8 pb[2];
+      run_item<D, TPW, true, false>(mask, R, ksb, vtb, koff, voff, wgt, lo, hi, j0, tau, tl2e, lg);
+    } else {
+      bool edge = false;
 #pragma unroll
-      for (int sl = 0; sl < 2; ++sl) {
-        uint4 u;
-        u.x = pack_bf16x2(p[2 * sl][0], p[2 * sl][1]);
-        u.y = pack_bf16x2(p[2 * sl][2], p[2 * sl][3]);
-        u.z = pack_bf16x2(p[2 * sl + 1][0], p[2 * sl + 1][1]);
-        u.w = pack_bf16x2(p[2 * sl + 1][2], p[2 * sl + 1][3]);
-        pb[sl] = as_bf16x8(u);
+      for (int t = 0; t < TPW; ++t) {
+        wgt[t] = 0.f;
+        lo[t] = 0;
+        hi[t] = -1;
+        if (row_ok[t]) {
+          const int i = q0 + row_q[t];
+          lo[t] = max(j0, (max(0, i - W + 1) >> 6) << 6);  // n_i * S with S = 64
+          hi[t] = min(j0 + kItemKeys - 1, i);
+        }
+        const bool mine = lo[t] <= hi[t];
+        if (__ballot(mine)) mask |= 1 << t;
+        // a row whose window does not cover the whole block needs the mask
+        edge = edge || (row_ok[t] && (lo[t] != j0 || hi[t] != j0 + kItemKeys - 1));
       }
-      // O^T += V^T P^T
-#pragma unroll
-      for (int dt = 0; dt < C::kDT; dt += 2) {
-        uint4 u[2][2];
-#pragma unroll
-        for (int d2 = 0; d2 < 2; ++d2)
-#pragma unroll
-          for (int sl = 0; sl < 2; ++sl)
-            u[d2][sl] = *reinterpret_cast<const uint4 *>(vtb + (16 * (dt + d2) + ln) * C::kVLD + 8 * lg + 32 * sl);
-#pragma unroll
-        for (int d2 = 0; d2 < 2; ++d2)
-#pragma unroll
-          for (int sl = 0; sl < 2; ++sl) acc[t][dt + d2] = mfma16(as_bf16x8(u[d2][sl]), pb[sl], acc[t][dt + d2]);
-        __builtin_amdgcn_sched_barrier(0);
-      }
+      if (__ballot(edge))
+        run_item<D, TPW, false, true>(mask, R, ksb, vtb, koff, voff, wgt, lo, hi, j0, tau, tl2e, lg);
+      else
+        run_item<D, TPW, false, false>(mask, R, ksb, vtb, koff, voff, wgt, lo, hi, j0, tau, tl2e, lg);
     }
-    // buffer buf ^ 1 was last read while computing item x-1, which every
-    // thread finished before the barrier that ended that iteration
-    if (x + 1 < nitems) {
-      stage(buf ^ 1);
-      build_slots(x + 1, buf ^ 1);
-    }
+    j0_cur = j0_nxt;
+    j0_nxt = j0_nn;
+    // this wave's loads of item x + 1 have landed; after the barrier, all have
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
 
@@ -454,13 +578,13 @@ attn_prefill_mfma_kernel(AttnArgs a, int ntiles, int xcd_map) {
 #pragma unroll
   for (int t = 0; t < TPW; ++t) {
     if (!row_ok[t]) continue;
-    const float inv = 1.f / l_row[t];
-    const size_t oo = ((static_cast<size_t>(b) * Hq + row_h[t]) * T + (q0 + row_q[t])) * D;
+    const float inv = 1.f / R.l_row[t];
+    const size_t oo = ((static_cast<size_t>(b) * Hq + row_h) * T + (q0 + row_q[t])) * D;
 #pragma unroll
     for (int dt = 0; dt < C::kDT; ++dt) {
       uint2 w;
-      w.x = pack_bf16x2(acc[t][dt][0] * inv, acc[t][dt][1] * inv);
-      w.y = pack_bf16x2(acc[t][dt][2] * inv, acc[t][dt][3] * inv);
+      w.x = pack_bf16x2(R.acc[t][dt][0] * inv, R.acc[t][dt][1] * inv);
+      w.y = pack_bf16x2(R.acc[t][dt][2] * inv, R.acc[t][dt][3] * inv);
       *reinterpret_cast<uint2 *>(ob + oo + 16 * dt + 4 * lg) = w;
     }
   }
@@ -468,17 +592,22 @@ attn_prefill_mfma_kernel(AttnArgs a, int ntiles, int xcd_map) {
 
 template <int D, int G>
 static hipError_t attn_mfma_t(const AttnArgs &a, hipStream_t st) {
-  constexpr int WAVES = 8, TPW = 2;
+  constexpr int WAVES = 4, TPW = 2;
   using C = AttnCfg<D, G, WAVES, TPW>;
   const int ntiles = (a.T + C::kQT - 1) / C::kQT;
   const int npairs = a.Hkv * a.B;
+  const int nblk = (a.T + kItemKeys - 1) / kItemKeys;
+  vt_transpose_kernel<D><<<dim3(nblk, npairs), 256, 0, st>>>(static_cast<const uint16_t *>(a.v),
+                                                             static_cast<uint16_t *>(a.vt_ws), a.T, nblk);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   const int xcd_map = (npairs % 8 == 0) ? 1 : 0;
   const size_t smem = sizeof(AttnSmem<D, G, WAVES, TPW>);
   auto kern = attn_prefill_mfma_kernel<D, G, WAVES, TPW>;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem));
+  e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                          static_cast<int>(smem));
   if (e != hipSuccess) return e;
-  kern<<<dim3(ntiles * npairs), C::kThreads, smem, st>>>(a, ntiles, xcd_map);
+  kern<<<dim3(ntiles * npairs), C::kThreads, smem, st>>>(a, ntiles, xcd_map, nblk);
   return hipGetLastError();
 }
 
@@ -486,6 +615,11 @@ bool attn_mfma_supported(const AttnArgs &a) {
   const int G = a.Hq / a.Hkv;
   return a.bf16 && (a.d == 64 || a.d == 128) && (G == 1 || G == 2 || G == 4 || G == 8 || G == 16) &&
          a.S == kItemKeys && a.K <= 32 && a.T / a.S <= 8192;
+}
+
+size_t attn_mfma_ws_bytes(int B, int Hkv, int T, int d) {
+  const size_t nblk = (static_cast<size_t>(T) + kItemKeys - 1) / kItemKeys;
+  return static_cast<size_t>(B) * Hkv * nblk * kItemKeys * d * 2;
 }
 
 hipError_t launch_attn_mfma(const AttnArgs &a, hipStream_t st) {
