@@ -126,6 +126,29 @@ __device__ __forceinline__ float sum_rows4(float v) {
   return __uint_as_float(s[0]) + __uint_as_float(s[1]);
 }
 
+__device__ __forceinline__ uint32_t usum_rows4(uint32_t v) {
+  auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = r[0] + r[1];
+  auto s = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return s[0] + s[1];
+}
+__device__ __forceinline__ uint32_t umin_rows4(uint32_t v) {
+  auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = min(static_cast<uint32_t>(r[0]), static_cast<uint32_t>(r[1]));
+  auto s = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return min(static_cast<uint32_t>(s[0]), static_cast<uint32_t>(s[1]));
+}
+// Exclusive prefix sum over the rows4 group in row order (row = lane >> 4).
+// After a 16-swap every lane holds its pair's (even row, odd row) values;
+// after a 32-swap of the pair sums, (rows 0+1, rows 2+3).
+__device__ __forceinline__ uint32_t uprefix_rows4(uint32_t v) {
+  const int row = (threadIdx.x & 63) >> 4;
+  auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  const uint32_t pair = r[0] + r[1];
+  auto s = __builtin_amdgcn_permlane32_swap(pair, pair, false, false);
+  return ((row & 1) ? static_cast<uint32_t>(r[0]) : 0u) + ((row & 2) ? static_cast<uint32_t>(s[0]) : 0u);
+}
+
 __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) {

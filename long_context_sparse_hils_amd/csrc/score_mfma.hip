@@ -13,13 +13,17 @@
 // Kernels:
 //   qcal_u_mfma      u[token, a]   MFMA GEMM over D_h  -> u_hi/u_lo [B*T, RP]
 //   qcal_m           m[b, h, c, a] VALU (tiny)          -> m_hi/m_lo [B, Hq, C, RP]
-//   score_topk_mfma  per (64 queries, KV head, batch): S^T tiles of 16
-//                    chunks x 16 queries per head, max over the group's heads
-//                    into LDS, then per query a ballot-driven radix select of
-//                    the K-th largest group score and a rank pass that orders
-//                    the winners by (score desc, chunk asc); a second MFMA
-//                    pass (same arithmetic, bit-identical) writes each head's
-//                    own score for the winners.
+//   score_topk_mfma  per (128 queries, KV head, batch), 8 waves of 16 queries:
+//                    tiles of 16 chunks x (up to 4 heads) of k', m and b' are
+//                    staged once in LDS for all waves (double buffered, loaded
+//                    straight from global memory); each wave forms S^T tiles
+//                    of 16 chunks x 16 queries per head, keeps the max over
+//                    the group's heads in LDS, then per query runs a
+//                    ballot-driven radix select of the K-th largest group
+//                    score and a rank pass that orders the winners by (score
+//                    desc, chunk asc); a second pass over the tiles (same
+//                    arithmetic, bit-identical) writes each head's own score
+//                    for the winners.
 #include "hils_common.h"
 #include "launch.h"
 
@@ -147,70 +151,78 @@ qcal_m_kernel(const uint16_t *__restrict__ k_sum, const uint16_t *__restrict__ w
 // ------------------------------------------------------------------ scores + top-K
 constexpr int kScoreMaxC = 256;
 
-template <int NJ>
-struct ScoreWaveSmem {
-  float sig[16][64 * NJ];
-  int8_t rank[16][64 * NJ];
+// Shared memory of the score kernel: two staged items, then per wave the
+// selection scratch.  An item holds one head's summaries k' (IC rows of D),
+// Q-Cal projections m hi/lo (IC rows of RP) and entropies b' (IC floats) for
+// IC consecutive chunks.  Rows of P 16-byte pieces are XOR-swizzled so that
+// the 16 rows one MFMA operand read touches fall in 16 different bank groups.
+template <int D, int NJ, int WAVES>
+struct ScoreSelect {
+  uint2 win[WAVES][16][32];        // per query: its winners (ordered score, chunk), compacted
+  int8_t rtab[WAVES][16][64 * NJ]; // winner chunk -> its position in the query's list
 };
-
-// s for head h, chunk tile ct (16 chunks) and the wave's 16 queries.
-// Lane holds chunks 16 ct + 4 lg + i (i < 4) for query ln.
-template <int D>
-__device__ __forceinline__ f32x4s score_tile(const ScoreArgs &a, const uint16_t *ks_h, const float *bs_h,
-                                             const uint4 *qv, const uint16_t *mh_h, const uint16_t *ml_h,
-                                             const uint4 *uh, const uint4 *ul, int ct, int ln, int lg, int RP,
-                                             bool qcal) {
-  constexpr int KS = D / 32;
-  const int c_row = 16 * ct + ln;  // A-operand row (chunk)
-  const bool c_ok = c_row < a.C;
-  f32x4s acc = f32x4s{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int s = 0; s < KS; ++s) {
-    const uint4 av = c_ok ? *reinterpret_cast<const uint4 *>(ks_h + static_cast<size_t>(c_row) * D + 32 * s + 8 * lg)
-                          : make_uint4(0, 0, 0, 0);
-    acc = mfma_s(av, qv[s], acc);
+struct ScoreItemLayout {
+  int ks, mh, ml, bs, bytes;  // byte offsets inside one item, and its size
+  __host__ __device__ ScoreItemLayout(int D, int IC, int RP) {
+    ks = 0;
+    mh = IC * D * 2;
+    ml = mh + IC * RP * 2;
+    bs = ml + IC * RP * 2;
+    bytes = bs + IC * 4;
   }
-  if (qcal) {
-    for (int s = 0; s < RP / 32; ++s) {
-      const size_t mo = static_cast<size_t>(c_row) * RP + 32 * s + 8 * lg;
-      const uint4 mh = c_ok ? *reinterpret_cast<const uint4 *>(mh_h + mo) : make_uint4(0, 0, 0, 0);
-      const uint4 ml = c_ok ? *reinterpret_cast<const uint4 *>(ml_h + mo) : make_uint4(0, 0, 0, 0);
-      acc = mfma_s(mh, uh[s], acc);
-      acc = mfma_s(mh, ul[s], acc);
-      acc = mfma_s(ml, uh[s], acc);
-    }
-  }
-  f32x4s sv;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int c = 16 * ct + 4 * lg + i;
-    sv[i] = a.tau * acc[i] + (c < a.C ? bs_h[c] : 0.f);
-  }
-  return sv;
+};
+template <int D, int NJ, int WAVES>
+size_t score_smem_bytes(int IC, int RP) {
+  return 2 * static_cast<size_t>(ScoreItemLayout(D, IC, RP).bytes) + sizeof(ScoreSelect<D, NJ, WAVES>);
 }
 
-template <int D, int NJ>
-__global__ void __launch_bounds__(256)
+// swizzled piece of logical piece pc in row r of a row of P pieces (P = 4, 8, 16)
+__device__ __forceinline__ int score_swz(int r, int P) { return (r >> (P == 16 ? 0 : (P == 8 ? 1 : 2))) & (P - 1); }
+
+// Workgroup = (WAVES x 16 queries, KV head g, batch b).  Lane (ln, lg) of a
+// wave works on query ln; in an S^T tile of 16 chunks it holds chunks
+// 16 ct + 4 lg + i (i < 4), so the group scores of one query live in the
+// four lanes ln, ln + 16, ln + 32, ln + 48 (16 NJ values each), and the
+// selection runs for the wave's 16 queries at once.
+// HR = 4: the group has at most 4 heads and every head's scores stay in
+// registers through the selection (one pass over the summaries); HR = 0:
+// a second pass recomputes the winners' per-head scores.  QR = RP / 32 when
+// known at compile time (0: no Q-Cal), else -1.
+template <int D, int NJ, int WAVES, int IC, int HR, int QR>
+__global__ void __launch_bounds__(WAVES * 64)
 score_topk_mfma_kernel(ScoreArgs a, const uint16_t *__restrict__ u_hi, const uint16_t *__restrict__ u_lo,
-                       const uint16_t *__restrict__ m_hi, const uint16_t *__restrict__ m_lo, int RP) {
+                       const uint16_t *__restrict__ m_hi, const uint16_t *__restrict__ m_lo, int RP_arg) {
+  const int RP = QR >= 0 ? 32 * QR : RP_arg;
   constexpr int KS = D / 32;
-  __shared__ ScoreWaveSmem<NJ> wsm[4];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  constexpr int QW = WAVES * 16;      // queries per workgroup
+  constexpr int NT = 4 * NJ;          // chunk tiles of 16 (64 NJ chunks)
+  constexpr int NV = 16 * NJ;         // candidate values per lane
+  constexpr int TPI = IC / 16;        // chunk tiles per item
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  const ScoreItemLayout lay(D, IC, RP);
+  ScoreSelect<D, NJ, WAVES> &sm = *reinterpret_cast<ScoreSelect<D, NJ, WAVES> *>(smem_raw + 2 * lay.bytes);
+  auto item_ks = [&](int buf) { return reinterpret_cast<uint16_t *>(smem_raw + buf * lay.bytes + lay.ks); };
+  auto item_mh = [&](int buf) { return reinterpret_cast<uint16_t *>(smem_raw + buf * lay.bytes + lay.mh); };
+  auto item_ml = [&](int buf) { return reinterpret_cast<uint16_t *>(smem_raw + buf * lay.bytes + lay.ml); };
+  auto item_bs = [&](int buf) { return reinterpret_cast<float *>(smem_raw + buf * lay.bytes + lay.bs); };
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int ln = lane & 15, lg = lane >> 4;
   const int T = a.T, C = a.C, K = a.K, Hq = a.Hq, Hkv = a.Hkv, G = Hq / Hkv;
   const int g = blockIdx.y, b = blockIdx.z;
-  const int qw0 = blockIdx.x * 64 + wave * 16;  // the wave's first query
-  if (qw0 >= T) return;                         // whole wave idle (no barriers below)
-  ScoreWaveSmem<NJ> &sm = wsm[wave];
-  const bool qcal = a.r > 0;
-  const int i_me = qw0 + ln;                     // this lane's query (B column)
+  const int q_wg = blockIdx.x * QW;
+  const int qw0 = q_wg + wave * 16;  // the wave's first query
+  const bool qcal = QR >= 0 ? QR > 0 : a.r > 0;
+  const int i_me = qw0 + ln;         // this lane's query (B column)
   const bool q_ok = i_me < T;
   const int n_me = q_ok ? min(eligible_chunks(i_me, a.W, a.S), C) : 0;
-  const int i_last = min(qw0 + 15, T - 1);
-  const int n_wave = min(eligible_chunks(i_last, a.W, a.S), C);
-  const int nct = (n_wave + 15) / 16;
+  const int n_wave = qw0 < T ? min(eligible_chunks(min(qw0 + 15, T - 1), a.W, a.S), C) : 0;
+  const int n_wg = min(eligible_chunks(min(q_wg + QW - 1, T - 1), a.W, a.S), C);
+  const int nblk = (n_wg + IC - 1) / IC;          // chunk blocks of one head
+  const int nitems = G * nblk;                    // head outer, chunk block inner
 
-  uint4 uh[2], ul[2];
+  uint4 uh[2], ul[2];  // this lane's query's u = W_down h as the B operand
+#pragma unroll
+  for (int s = 0; s < 2; ++s) { uh[s] = make_uint4(0, 0, 0, 0); ul[s] = make_uint4(0, 0, 0, 0); }
   if (qcal) {
     const size_t uo = (static_cast<size_t>(b) * T + (q_ok ? i_me : 0)) * RP + 8 * lg;
 #pragma unroll
@@ -223,135 +235,292 @@ score_topk_mfma_kernel(ScoreArgs a, const uint16_t *__restrict__ u_hi, const uin
   const uint16_t *qb = static_cast<const uint16_t *>(a.q);
   const uint16_t *ksb = static_cast<const uint16_t *>(a.k_sum);
 
-  // ---- pass 1: group score sigma into LDS
-  for (int x = lane; x < 16 * 64 * NJ; x += 64) (&sm.sig[0][0])[x] = -INFINITY;
-  for (int hh = 0; hh < G; ++hh) {
+  // ---- staging of item x = (head hh, chunk block cb) straight into LDS in
+  // 1 KB wave-wide slices (lane l's 16 bytes land at byte 16 l of a slice);
+  // the entropies go through a register of the last two waves
+  constexpr int kPk = D / 8;              // pieces per k' row
+  constexpr int kSlK = IC * D * 2 / 1024;  // k' slices
+  const int Pm = RP / 8;                  // pieces per m row
+  const int slm = qcal ? IC * RP * 2 / 1024 : 0;  // m slices (hi or lo)
+  float bs_reg = 0.f;
+  auto issue_item = [&](int x, int buf) {
+    const int hh = x / nblk, cb = x % nblk;
+    const int h = g * G + hh, c0 = cb * IC;
+    const int nsl = kSlK + 2 * slm;
+    for (int sl = wave; sl < nsl; sl += WAVES) {
+      const uint16_t *src;
+      uint16_t *dst;
+      if (sl < kSlK) {
+        const int slot = sl * 64 + lane, r = slot / kPk, pp = slot % kPk;
+        const int c = min(c0 + r, C - 1);  // rows past C are never used
+        src = ksb + ((static_cast<size_t>(b) * Hq + h) * C + c) * D + ((pp ^ score_swz(r, kPk)) << 3);
+        dst = item_ks(buf) + sl * 512;
+      } else {
+        const int y = sl - kSlK, lohi = y / slm, part = y % slm;
+        const int slot = part * 64 + lane, r = slot / Pm, pp = slot % Pm;
+        const int c = min(c0 + r, C - 1);
+        src = (lohi ? m_lo : m_hi) + ((static_cast<size_t>(b) * Hq + h) * C + c) * RP + ((pp ^ score_swz(r, Pm)) << 3);
+        dst = (lohi ? item_ml(buf) : item_mh(buf)) + part * 512;
+      }
+      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)dst, 16, 0, 0);
+    }
+    const int wb = wave - (WAVES - 2);  // 0 or 1 for the last two waves
+    if (wb >= 0) {
+      const int c = c0 + 64 * wb + lane;
+      bs_reg = (64 * wb + lane < IC && c < C) ? a.b_sum[(static_cast<size_t>(b) * Hq + h) * C + c] : 0.f;
+    }
+  };
+  auto finish_item = [&](int buf) {
+    const int wb = wave - (WAVES - 2);
+    if (wb >= 0 && 64 * wb + lane < IC) item_bs(buf)[64 * wb + lane] = bs_reg;
+  };
+
+  // Q operands of head hh: lane holds query ln, d = 32 s + 8 lg .. +8
+  uint4 qv[KS];
+  auto load_q = [&](uint4 (&dst)[KS], int hh) {
     const int h = g * G + hh;
-    uint4 qv[KS];
     const size_t qo = ((static_cast<size_t>(b) * Hq + h) * T + (q_ok ? i_me : 0)) * D + 8 * lg;
 #pragma unroll
-    for (int s = 0; s < KS; ++s) qv[s] = q_ok ? *reinterpret_cast<const uint4 *>(qb + qo + 32 * s) : make_uint4(0, 0, 0, 0);
-    const uint16_t *ks_h = ksb + (static_cast<size_t>(b) * Hq + h) * C * D;
-    const float *bs_h = a.b_sum + (static_cast<size_t>(b) * Hq + h) * C;
-    const uint16_t *mh_h = qcal ? m_hi + (static_cast<size_t>(b) * Hq + h) * C * RP : nullptr;
-    const uint16_t *ml_h = qcal ? m_lo + (static_cast<size_t>(b) * Hq + h) * C * RP : nullptr;
-    for (int ct = 0; ct < nct; ct += 2) {
-      // two chunk tiles per step so their operand loads overlap
-      const f32x4s sv0 = score_tile<D>(a, ks_h, bs_h, qv, mh_h, ml_h, uh, ul, ct, ln, lg, RP, qcal);
-      const f32x4s sv1 = score_tile<D>(a, ks_h, bs_h, qv, mh_h, ml_h, uh, ul, ct + 1, ln, lg, RP, qcal);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int c0 = 16 * ct + 4 * lg + i, c1 = c0 + 16;
-        if (c0 < n_me) sm.sig[ln][c0] = fmaxf(sm.sig[ln][c0], sv0[i]);
-        if (c1 < n_me) sm.sig[ln][c1] = fmaxf(sm.sig[ln][c1], sv1[i]);
-      }
-    }
-  }
-  __builtin_amdgcn_s_waitcnt(0);
-  __builtin_amdgcn_wave_barrier();
+    for (int s = 0; s < KS; ++s) dst[s] = q_ok ? *reinterpret_cast<const uint4 *>(qb + qo + 32 * s) : make_uint4(0, 0, 0, 0);
+  };
 
-  // ---- selection per query: radix select of the K-th largest key
-  for (int q = 0; q < 16; ++q) {
-    const int i = qw0 + q;
-    if (i >= T) break;
-    const int n = min(eligible_chunks(i, a.W, a.S), C);
-    const int keep = min(K, n);
-    uint32_t ord[NJ];
+  // s of chunk tile ctl of the staged item: lane holds chunks 16 ctl + 4 lg + i
+  auto score_tile = [&](int buf, int ctl) -> f32x4s {
+    const uint16_t *iks = item_ks(buf), *imh = item_mh(buf), *iml = item_ml(buf);
+    const float *ibs = item_bs(buf);
+    const int r = 16 * ctl + ln;  // A-operand row
+    f32x4s acc = f32x4s{0.f, 0.f, 0.f, 0.f};
+    uint4 av[KS];
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const int c = lane + 64 * j;
-      ord[j] = c < n ? orderable(sm.sig[q][c]) : 0u;  // 0 = below every real score
-      sm.rank[q][c] = -1;
-    }
-    // theta = the largest value with #{ord >= theta} >= keep
-    uint32_t theta = 0u;
-    if (keep > 0) {
-      for (int bit = 31; bit >= 0; --bit) {
-        const uint32_t cand = theta | (1u << bit);
-        int cnt = 0;
+    for (int s = 0; s < KS; ++s)
+      av[s] = *reinterpret_cast<const uint4 *>(iks + r * D + (((4 * s + lg) ^ score_swz(r, kPk)) << 3));
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) cnt += __popcll(__ballot(ord[j] >= cand));
-        if (cnt >= keep) theta = cand;
+    for (int s = 0; s < KS; ++s) acc = mfma_s(av[s], qv[s], acc);
+    if (qcal) {
+      for (int s = 0; s < RP / 32; ++s) {
+        const int off = r * RP + (((4 * s + lg) ^ score_swz(r, Pm)) << 3);
+        const uint4 mh = *reinterpret_cast<const uint4 *>(imh + off);
+        const uint4 ml = *reinterpret_cast<const uint4 *>(iml + off);
+        acc = mfma_s(mh, uh[s], acc);
+        acc = mfma_s(mh, ul[s], acc);
+        acc = mfma_s(ml, uh[s], acc);
       }
     }
-    // winners: ord > theta, then the lowest-index ord == theta to fill
-    int cnt_gt = 0;
+    f32x4s sv;
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) cnt_gt += __popcll(__ballot(keep > 0 && ord[j] > theta));
-    int need_eq = keep - cnt_gt;
-    bool win[NJ];
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const bool gt = keep > 0 && ord[j] > theta;
-      const bool eq = keep > 0 && ord[j] == theta && (lane + 64 * j) < n;
-      const unsigned long long eqm = __ballot(eq);
-      const int before = __popcll(eqm & ((1ull << lane) - 1ull));
-      win[j] = gt || (eq && before < need_eq);
-      need_eq -= min(need_eq, __popcll(eqm));
-    }
-    // rank of each winner among the winners by (score desc, chunk asc)
-    int rk[NJ];
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) rk[j] = 0;
-#pragma unroll
-    for (int jj = 0; jj < NJ; ++jj) {
-      unsigned long long wm = __ballot(win[jj]);
-      while (wm) {
-        const int src = __ffsll(static_cast<long long>(wm)) - 1;
-        wm &= wm - 1ull;
-        const uint32_t o2 = __shfl(ord[jj], src, 64);
-        const int c2 = src + 64 * jj;
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-          const int c = lane + 64 * j;
-          if (win[j] && (o2 > ord[j] || (o2 == ord[j] && c2 < c))) ++rk[j];
-        }
-      }
-    }
-    const size_t ibase = ((static_cast<size_t>(b) * Hkv + g) * T + i) * K;
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const int c = lane + 64 * j;
-      if (win[j]) {
-        sm.rank[q][c] = static_cast<int8_t>(rk[j]);
-        a.topk_idx[ibase + rk[j]] = c;
-      }
-    }
-    for (int k = keep + lane; k < K; k += 64) a.topk_idx[ibase + k] = -1;
-    for (int x = lane; x < G * (K - keep); x += 64) {
-      const int hh = x / (K - keep), k = keep + x % (K - keep);
-      a.topk_score[((static_cast<size_t>(b) * Hq + g * G + hh) * T + i) * K + k] = -INFINITY;
-    }
-  }
-  __builtin_amdgcn_s_waitcnt(0);
-  __builtin_amdgcn_wave_barrier();
+    for (int i = 0; i < 4; ++i) sv[i] = a.tau * acc[i] + ibs[16 * ctl + 4 * lg + i];
+    return sv;
+  };
 
-  // ---- pass 2: each head's own score of the winners (same arithmetic as pass 1)
-  for (int hh = 0; hh < G; ++hh) {
-    const int h = g * G + hh;
-    uint4 qv[KS];
-    const size_t qo = ((static_cast<size_t>(b) * Hq + h) * T + (q_ok ? i_me : 0)) * D + 8 * lg;
+  // candidate v = 4 ct + i holds chunk 16 ct + 4 lg + i
+  float sig[HR > 0 ? 1 : NV];                  // group maxima (HR = 0)
+  float sc[HR > 0 ? HR : 1][HR > 0 ? NV : 1];  // per-head scores (HR = 4); the group max comes after
+  int rank[HR > 0 ? 1 : NV];                   // winner positions for the second pass (HR = 0)
+  if constexpr (HR == 0) {
 #pragma unroll
-    for (int s = 0; s < KS; ++s) qv[s] = q_ok ? *reinterpret_cast<const uint4 *>(qb + qo + 32 * s) : make_uint4(0, 0, 0, 0);
-    const uint16_t *ks_h = ksb + (static_cast<size_t>(b) * Hq + h) * C * D;
-    const float *bs_h = a.b_sum + (static_cast<size_t>(b) * Hq + h) * C;
-    const uint16_t *mh_h = qcal ? m_hi + (static_cast<size_t>(b) * Hq + h) * C * RP : nullptr;
-    const uint16_t *ml_h = qcal ? m_lo + (static_cast<size_t>(b) * Hq + h) * C * RP : nullptr;
-    for (int ct = 0; ct < nct; ct += 2) {
-      const f32x4s sv0 = score_tile<D>(a, ks_h, bs_h, qv, mh_h, ml_h, uh, ul, ct, ln, lg, RP, qcal);
-      const f32x4s sv1 = score_tile<D>(a, ks_h, bs_h, qv, mh_h, ml_h, uh, ul, ct + 1, ln, lg, RP, qcal);
+    for (int v = 0; v < NV; ++v) { sig[v] = -INFINITY; rank[v] = -1; }
+  }
+  // (HR > 0: every sc[h2][v] with h2 < G and an eligible chunk is written by
+  // pass 1 before it is read; the others are never read)
+
+  // One pass over the items.  PASS 1: group maximum into sig (and, with HR,
+  // each head's score into sc).  PASS 2 (HR = 0): each head's own score of
+  // the winners into topk_score (the same arithmetic as pass 1, so the
+  // values are bit-identical).
+  auto run_pass = [&](bool pass2) {
+    if (nitems > 0) {
+      issue_item(0, 0);
+      __builtin_amdgcn_s_waitcnt(0);
+      finish_item(0);
+    }
+    __syncthreads();
+    for (int x = 0; x < nitems; ++x) {
+      const int buf = x & 1;
+      const int hh = x / nblk, cb = x % nblk;
+      if (cb == 0) load_q(qv, hh);
+      // buffer buf ^ 1 was last read in iteration x - 1, before its barrier
+      if (x + 1 < nitems) issue_item(x + 1, buf ^ 1);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int cbb = 0; cbb < NT / TPI + (NT % TPI ? 1 : 0); ++cbb) {
+        if (cbb != cb) continue;
 #pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          const int c = 16 * (ct + hf) + 4 * lg + i;
-          if (c < n_me) {
-            const int rk = sm.rank[ln][c];
-            if (rk >= 0) a.topk_score[((static_cast<size_t>(b) * Hq + h) * T + i_me) * K + rk] = hf ? sv1[i] : sv0[i];
+        for (int ctl = 0; ctl < TPI; ++ctl) {
+          const int ct = cbb * TPI + ctl;
+          if (ct >= NT) break;
+          if (HR == 0 && 16 * ct >= n_wave) break;  // wave-uniform: no chunk of the tile is eligible
+          const f32x4s sv = score_tile(buf, ctl);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            if (!pass2) {
+              if constexpr (HR > 0) {
+#pragma unroll
+                for (int h2 = 0; h2 < HR; ++h2)
+                  if (h2 == hh) sc[h2][4 * ct + i] = sv[i];
+              } else {
+                sig[4 * ct + i] = fmaxf(sig[4 * ct + i], sv[i]);
+              }
+            } else if constexpr (HR == 0) {
+              if (rank[4 * ct + i] >= 0)
+                a.topk_score[((static_cast<size_t>(b) * Hq + g * G + hh) * T + i_me) * K + rank[4 * ct + i]] = sv[i];
+            }
           }
+          // one tile's operand reads in flight at a time (registers)
+          if (HR > 0) __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(0);
+      if (x + 1 < nitems) finish_item(buf ^ 1);
+      __syncthreads();
+    }
+  };
+
+  // ---- pass 1: group scores
+  run_pass(false);
+
+  // ---- selection for the wave's 16 queries at once (4 lanes per query)
+  const int keep = min(K, n_me);
+  uint32_t ord[NV];
+#pragma unroll
+  for (int v = 0; v < NV; ++v) {
+    const int c = 16 * (v >> 2) + 4 * lg + (v & 3);
+    float gv;
+    if constexpr (HR > 0) {
+      gv = sc[0][v];
+#pragma unroll
+      for (int h2 = 1; h2 < HR; ++h2)
+        if (h2 < G) gv = fmaxf(gv, sc[h2][v]);
+    } else {
+      gv = sig[v];
+    }
+    ord[v] = c < n_me ? orderable(gv) : 0u;  // 0 = below every real score
+  }
+  // Bitwise search, from the top bit, for the largest theta with
+  // #{ord >= theta} >= keep.  A query stops as soon as exactly `keep`
+  // candidates are at or above the trial value (its winners, no ties);
+  // otherwise theta ends as the keep-th largest value, with ties at it.
+  uint32_t theta = 0u;
+  bool done = keep == 0;
+  for (int bit = 31; bit >= 0; --bit) {
+    if (!__ballot(!done)) break;  // every query of the wave has its threshold
+    const uint32_t cand = theta | (1u << bit);
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int v = 0; v < NV; ++v) cnt += ord[v] >= cand ? 1u : 0u;
+    cnt = usum_rows4(cnt);
+    if (!done && static_cast<int>(cnt) >= keep) {
+      theta = cand;
+      done = static_cast<int>(cnt) == keep;
+    }
+  }
+  // winners as a bit mask over the lane's candidates
+  uint32_t winm = 0u;
+  uint32_t ngt = 0;
+#pragma unroll
+  for (int v = 0; v < NV; ++v) {
+    const bool w = keep > 0 && (done ? ord[v] >= theta : ord[v] > theta);
+    winm |= w ? (1u << v) : 0u;
+    ngt += w ? 1u : 0u;
+  }
+  // ties at theta (queries not done): the lowest chunks first, one per round
+  int need_eq = keep - static_cast<int>(usum_rows4(ngt));
+  while (__ballot(need_eq > 0)) {
+    uint32_t mloc = 0xFFFFu;
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      const uint32_t c = 16 * (v >> 2) + 4 * lg + (v & 3);
+      if (need_eq > 0 && !((winm >> v) & 1u) && ord[v] == theta && ord[v] != 0u) mloc = min(mloc, c);
+    }
+    const uint32_t m = umin_rows4(mloc);
+    if (need_eq > 0) {
+#pragma unroll
+      for (int v = 0; v < NV; ++v) {
+        const uint32_t c = 16 * (v >> 2) + 4 * lg + (v & 3);
+        if (c == m) winm |= 1u << v;
+      }
+      need_eq = m == 0xFFFFu ? 0 : need_eq - 1;
+    }
+  }
+  // compact each query's winners (in lane-row order) into LDS
+  {
+    uint32_t pos = uprefix_rows4(static_cast<uint32_t>(__popc(winm)));
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      if ((winm >> v) & 1u) {
+        sm.win[wave][ln][pos] = make_uint2(ord[v], static_cast<uint32_t>(16 * (v >> 2) + 4 * lg + (v & 3)));
+        ++pos;
+      }
+    }
+  }
+  // (LDS operations of one wave complete in order: no wait needed)
+  __builtin_amdgcn_wave_barrier();
+  // position of winner p among the query's winners by (score desc, chunk
+  // asc); lane (ln, lg) ranks winners p = lg, lg + 4, ...
+  {
+    constexpr int PPL = 8;  // winners per lane (K <= 32)
+    uint32_t pk[PPL];
+    int pc[PPL], pr[PPL];
+#pragma unroll
+    for (int j = 0; j < PPL; ++j) {
+      const int p = lg + 4 * j;
+      const uint2 e = p < keep ? sm.win[wave][ln][p] : make_uint2(0u, 0u);
+      pk[j] = e.x;
+      pc[j] = static_cast<int>(e.y);
+      pr[j] = 0;
+    }
+    const uint4 *row = reinterpret_cast<const uint4 *>(&sm.win[wave][ln][0]);
+    for (int e2 = 0; e2 < (K + 1) / 2; ++e2) {
+      const uint4 w2 = row[e2];  // entries 2 e2 and 2 e2 + 1
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int p2 = 2 * e2 + half;
+        const uint32_t k2 = half ? w2.z : w2.x;
+        const int c2 = static_cast<int>(half ? w2.w : w2.y);
+        if (p2 < keep) {
+#pragma unroll
+          for (int j = 0; j < PPL; ++j) pr[j] += (k2 > pk[j] || (k2 == pk[j] && c2 < pc[j])) ? 1 : 0;
         }
       }
     }
+    const size_t ibase = ((static_cast<size_t>(b) * Hkv + g) * T + i_me) * K;
+#pragma unroll
+    for (int j = 0; j < PPL; ++j) {
+      const int p = lg + 4 * j;
+      if (q_ok && p < keep) {
+        a.topk_idx[ibase + pr[j]] = pc[j];
+        sm.rtab[wave][ln][pc[j]] = static_cast<int8_t>(pr[j]);
+      }
+    }
+    // padding of the lists past keep
+    if (q_ok) {
+      for (int k = keep + lg; k < K; k += 4) a.topk_idx[ibase + k] = -1;
+      for (int x = lg; x < G * (K - keep); x += 4) {
+        const int hh = x / (K - keep), k = keep + x % (K - keep);
+        a.topk_score[((static_cast<size_t>(b) * Hq + g * G + hh) * T + i_me) * K + k] = -INFINITY;
+      }
+    }
+  }
+  __builtin_amdgcn_wave_barrier();
+
+  if constexpr (HR > 0) {
+    // ---- each head's own score of the winners, from registers
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      if ((winm >> v) & 1u) {
+        const int c = 16 * (v >> 2) + 4 * lg + (v & 3);
+        const int rk = sm.rtab[wave][ln][c];
+#pragma unroll
+        for (int h2 = 0; h2 < HR; ++h2)
+          if (h2 < G) a.topk_score[((static_cast<size_t>(b) * Hq + g * G + h2) * T + i_me) * K + rk] = sc[h2][v];
+      }
+    }
+  } else {
+#pragma unroll
+    for (int v = 0; v < NV; ++v) {
+      const int c = 16 * (v >> 2) + 4 * lg + (v & 3);
+      rank[v] = ((winm >> v) & 1u) ? static_cast<int>(sm.rtab[wave][ln][c]) : -1;
+    }
+    // ---- pass 2: each head's own score of the winners
+    run_pass(true);
   }
 }
 
@@ -391,14 +560,31 @@ hipError_t launch_score_mfma(const ScoreArgs &a, hipStream_t st) {
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  dim3 grid((a.T + 63) / 64, a.Hkv, a.B);
   // candidates per lane in the selection: ceil(C / 64) rounded to 1, 2 or 4
   const int nj = a.C <= 64 ? 1 : (a.C <= 128 ? 2 : 4);
-#define HILS_SCORE(DD, NN) \
-  if (a.d == DD && nj == NN) score_topk_mfma_kernel<DD, NN><<<grid, 256, 0, st>>>(a, u_hi, u_lo, m_hi, m_lo, RP);
-  HILS_SCORE(128, 1) HILS_SCORE(128, 2) HILS_SCORE(128, 4) HILS_SCORE(64, 1) HILS_SCORE(64, 2) HILS_SCORE(64, 4)
+  // groups of at most 4 heads keep every head's scores in registers (one
+  // pass); items of 64 chunks
+  const int hr = (a.Hq / a.Hkv <= 4 && nj <= 2) ? 4 : 0;
+  const int RPa = a.r > 0 ? RP : 0;
+  const int qr = RPa / 32;
+#define HILS_SCORE(DD, NN, WW, HRR, QRR)                                                                    \
+  if (a.d == DD && nj == NN && hr == HRR && (QRR < 0 || qr == QRR)) {                                     \
+    auto kern = score_topk_mfma_kernel<DD, NN, WW, 64, HRR, QRR>;                                         \
+    const size_t smem = score_smem_bytes<DD, NN, WW>(64, RPa);                                           \
+    hipError_t e2 = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),                              \
+                                        hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem)); \
+    if (e2 != hipSuccess) return e2;                                                                      \
+    kern<<<dim3((a.T + WW * 16 - 1) / (WW * 16), a.Hkv, a.B), WW * 64, smem, st>>>(a, u_hi, u_lo, m_hi, m_lo, RPa); \
+    return hipGetLastError();                                                                             \
+  }
+  HILS_SCORE(128, 1, 8, 4, 0) HILS_SCORE(128, 1, 8, 4, 1) HILS_SCORE(128, 1, 8, 4, 2)
+  HILS_SCORE(128, 2, 8, 4, 0) HILS_SCORE(128, 2, 8, 4, 1) HILS_SCORE(128, 2, 8, 4, 2)
+  HILS_SCORE(64, 1, 8, 4, 0) HILS_SCORE(64, 1, 8, 4, 1) HILS_SCORE(64, 1, 8, 4, 2)
+  HILS_SCORE(64, 2, 8, 4, 0) HILS_SCORE(64, 2, 8, 4, 1) HILS_SCORE(64, 2, 8, 4, 2)
+  HILS_SCORE(128, 1, 8, 0, -1) HILS_SCORE(128, 2, 8, 0, -1) HILS_SCORE(128, 4, 4, 0, -1)
+  HILS_SCORE(64, 1, 8, 0, -1) HILS_SCORE(64, 2, 8, 0, -1) HILS_SCORE(64, 4, 4, 0, -1)
 #undef HILS_SCORE
-  return hipGetLastError();
+  return hipErrorInvalidValue;  // no instantiation for this shape (score_mfma_supported excludes it)
 }
 
 }  // namespace hils
