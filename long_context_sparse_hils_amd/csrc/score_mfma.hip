@@ -158,7 +158,7 @@ constexpr int kScoreMaxC = 256;
 // the 16 rows one MFMA operand read touches fall in 16 different bank groups.
 template <int D, int NJ, int WAVES>
 struct ScoreSelect {
-  uint2 win[WAVES][16][32];        // per query: its winners (ordered score, chunk), compacted
+  unsigned long long win[WAVES][16][32];  // per query: its winners' sort keys, compacted
   int8_t rtab[WAVES][16][64 * NJ]; // winner chunk -> its position in the query's list
 };
 struct ScoreItemLayout {
@@ -394,22 +394,42 @@ score_topk_mfma_kernel(ScoreArgs a, const uint16_t *__restrict__ u_hi, const uin
     }
     ord[v] = c < n_me ? orderable(gv) : 0u;  // 0 = below every real score
   }
-  // Bitwise search, from the top bit, for the largest theta with
-  // #{ord >= theta} >= keep.  A query stops as soon as exactly `keep`
-  // candidates are at or above the trial value (its winners, no ties);
-  // otherwise theta ends as the keep-th largest value, with ties at it.
-  uint32_t theta = 0u;
+  // Bitwise search for the largest theta with #{ord >= theta} >= keep.
+  // theta lies between the smallest and the largest eligible value, so it
+  // shares their common leading bits: the search starts below them (scores
+  // of one query often agree in sign, exponent and the top mantissa bits).
+  // A query stops as soon as exactly `keep` candidates are at or above the
+  // trial value (its winners, no ties); otherwise theta ends as the keep-th
+  // largest value, with ties at it.
+  uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+#pragma unroll
+  for (int v = 0; v < NV; ++v) {
+    hi = max(hi, ord[v]);
+    lo = min(lo, ord[v] != 0u ? ord[v] : 0xFFFFFFFFu);
+  }
+  lo = umin_rows4(lo);
+  hi = ~umin_rows4(~hi);
+  const uint32_t spread = keep > 0 ? lo ^ hi : 0u;
+  const int top = spread ? 31 - __clz(spread) : -1;  // highest bit where lo and hi differ
+  uint32_t theta = keep > 0 ? (top == 31 ? 0u : lo & ~((2u << top) - 1u)) : 0u;
   bool done = keep == 0;
+  if (!done && top < 0) {  // every eligible value of the query is equal
+    theta = lo;
+    done = n_me == keep;
+  }
+  bool open = !done && top >= 0;  // still searching
   for (int bit = 31; bit >= 0; --bit) {
-    if (!__ballot(!done)) break;  // every query of the wave has its threshold
+    if (!__ballot(open)) break;                  // every query of the wave has its threshold
+    if (!__ballot(open && bit <= top)) continue;  // inside every open query's common prefix
     const uint32_t cand = theta | (1u << bit);
     uint32_t cnt = 0;
 #pragma unroll
     for (int v = 0; v < NV; ++v) cnt += ord[v] >= cand ? 1u : 0u;
     cnt = usum_rows4(cnt);
-    if (!done && static_cast<int>(cnt) >= keep) {
+    if (open && bit <= top && static_cast<int>(cnt) >= keep) {
       theta = cand;
       done = static_cast<int>(cnt) == keep;
+      open = !done;
     }
   }
   // winners as a bit mask over the lane's candidates
@@ -446,7 +466,10 @@ score_topk_mfma_kernel(ScoreArgs a, const uint16_t *__restrict__ u_hi, const uin
 #pragma unroll
     for (int v = 0; v < NV; ++v) {
       if ((winm >> v) & 1u) {
-        sm.win[wave][ln][pos] = make_uint2(ord[v], static_cast<uint32_t>(16 * (v >> 2) + 4 * lg + (v & 3)));
+        // key: ordered score above, 0xFFFF - chunk below (a larger key is
+        // the higher score, then the lower chunk)
+        sm.win[wave][ln][pos] = (static_cast<unsigned long long>(ord[v]) << 32) |
+                                (0xFFFFu - static_cast<uint32_t>(16 * (v >> 2) + 4 * lg + (v & 3)));
         ++pos;
       }
     }
@@ -456,38 +479,35 @@ score_topk_mfma_kernel(ScoreArgs a, const uint16_t *__restrict__ u_hi, const uin
   // position of winner p among the query's winners by (score desc, chunk
   // asc); lane (ln, lg) ranks winners p = lg, lg + 4, ...
   {
-    constexpr int PPL = 8;  // winners per lane (K <= 32)
-    uint32_t pk[PPL];
-    int pc[PPL], pr[PPL];
+    constexpr int PPL = 8;  // winners per lane (K <= 32); j < ceil(K / 4) used
+    unsigned long long pk[PPL];
+    int pr[PPL];
 #pragma unroll
     for (int j = 0; j < PPL; ++j) {
       const int p = lg + 4 * j;
-      const uint2 e = p < keep ? sm.win[wave][ln][p] : make_uint2(0u, 0u);
-      pk[j] = e.x;
-      pc[j] = static_cast<int>(e.y);
+      pk[j] = (4 * j < K && p < keep) ? sm.win[wave][ln][p] : 0ull;
       pr[j] = 0;
     }
-    const uint4 *row = reinterpret_cast<const uint4 *>(&sm.win[wave][ln][0]);
+    const ulonglong2 *row = reinterpret_cast<const ulonglong2 *>(&sm.win[wave][ln][0]);
     for (int e2 = 0; e2 < (K + 1) / 2; ++e2) {
-      const uint4 w2 = row[e2];  // entries 2 e2 and 2 e2 + 1
+      const ulonglong2 w2 = row[e2];  // entries 2 e2 and 2 e2 + 1
+      const unsigned long long k0 = 2 * e2 < keep ? w2.x : 0ull;
+      const unsigned long long k1 = 2 * e2 + 1 < keep ? w2.y : 0ull;
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const int p2 = 2 * e2 + half;
-        const uint32_t k2 = half ? w2.z : w2.x;
-        const int c2 = static_cast<int>(half ? w2.w : w2.y);
-        if (p2 < keep) {
-#pragma unroll
-          for (int j = 0; j < PPL; ++j) pr[j] += (k2 > pk[j] || (k2 == pk[j] && c2 < pc[j])) ? 1 : 0;
-        }
+      for (int j = 0; j < PPL; ++j) {
+        if (4 * j >= K) break;  // uniform
+        pr[j] += (k0 > pk[j] ? 1 : 0) + (k1 > pk[j] ? 1 : 0);
       }
     }
     const size_t ibase = ((static_cast<size_t>(b) * Hkv + g) * T + i_me) * K;
 #pragma unroll
     for (int j = 0; j < PPL; ++j) {
       const int p = lg + 4 * j;
+      if (4 * j >= K) break;
       if (q_ok && p < keep) {
-        a.topk_idx[ibase + pr[j]] = pc[j];
-        sm.rtab[wave][ln][pc[j]] = static_cast<int8_t>(pr[j]);
+        const int c = 0xFFFF - static_cast<int>(pk[j] & 0xFFFFu);
+        a.topk_idx[ibase + pr[j]] = c;
+        sm.rtab[wave][ln][c] = static_cast<int8_t>(pr[j]);
       }
     }
     // padding of the lists past keep
