@@ -315,8 +315,10 @@ def main():
     flush_buf = torch.empty((1 << 30) // 4, dtype=torch.float32, device="cuda").fill_(0)
 
     def flush():
+        # Read 1 GiB: evicts L2 and the memory-side cache without leaving
+        # dirty lines whose write-back would land in the measured kernels.
         if not args.no_flush:
-            flush_buf.add_(1.0)
+            flush_buf.sum()
 
     line = dict(metric=METRIC, unit="query-tokens/s", n_gpus=1, steps=args.steps, warmup=args.warmup,
                 higher_is_better=True, scaling="weak", vs_baseline=None, dtype="bf16", data="synthetic")

@@ -43,108 +43,175 @@ __device__ __forceinline__ void split_bf16(float x, uint16_t &hi, uint16_t &lo) 
 }
 
 // ------------------------------------------------------------------ u = W_down h
-// 64 tokens per workgroup (16 per wave), RP/16 output tiles; K-loop over D_h.
-__global__ void __launch_bounds__(256)
+// A streaming GEMM over D_h: h (B*T x D_h) is read once and is the whole HBM
+// traffic; W_down (r x D_h) is re-read from L2 by every workgroup.  One
+// workgroup per 16 TT tokens; its 4 waves take quarters of D_h and add their
+// partial (16 TT) x RP tiles through LDS.  Each wave holds TT token tiles,
+// so one W_down operand serves TT MFMAs: the vector-memory requests, not
+// HBM, bound this kernel, and W_down's share of them falls as 1 / TT.
+template <int NT, int TT>  // output tiles of 16 (RP / 16); token tiles per wave
+__global__ void __launch_bounds__(256, 4)
 qcal_u_mfma_kernel(const uint16_t *__restrict__ h, const uint16_t *__restrict__ w_down, uint16_t *__restrict__ u_hi,
-                   uint16_t *__restrict__ u_lo, int Ntok, int r, int RP, int Dh) {
+                   uint16_t *__restrict__ u_lo, int Ntok, int r, int Dh) {
+  constexpr int RP = 16 * NT;
+  __shared__ float part[4][16 * TT][RP + 1];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int ln = lane & 15, lg = lane >> 4;
-  const int tok0 = blockIdx.x * 64 + wave * 16;
-  const int NT = RP / 16;
-  const int tok = tok0 + ln;
-  const bool tok_ok = tok < Ntok;
-  const uint16_t *hrow = h + static_cast<size_t>(tok_ok ? tok : 0) * Dh + 8 * lg;
-  f32x4s acc[4];
+  const int tok0 = blockIdx.x * 16 * TT;
+  const uint16_t *hrow[TT];
+  bool tok_ok[TT];
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) acc[nt] = f32x4s{0.f, 0.f, 0.f, 0.f};
-  constexpr int UK = 8;  // k-steps whose loads are issued together
-  int e0 = 0;
-  for (; e0 + 32 * UK <= Dh; e0 += 32 * UK) {
-    uint4 av[UK], bv[UK][2];
+  for (int t = 0; t < TT; ++t) {
+    tok_ok[t] = tok0 + 16 * t + ln < Ntok;
+    hrow[t] = h + static_cast<size_t>(tok_ok[t] ? tok0 + 16 * t + ln : 0) * Dh + 8 * lg;
+  }
+  const uint16_t *wrow[NT];
 #pragma unroll
-    for (int u = 0; u < UK; ++u) {
-      av[u] = tok_ok ? *reinterpret_cast<const uint4 *>(hrow + e0 + 32 * u) : make_uint4(0, 0, 0, 0);
+  for (int nt = 0; nt < NT; ++nt)
+    wrow[nt] = 16 * nt + ln < r ? w_down + static_cast<size_t>(16 * nt + ln) * Dh + 8 * lg : nullptr;
+  f32x4s acc[TT][NT];
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        const int aa = 16 * nt + ln;
-        bv[u][nt] = (nt < NT && aa < r)
-                        ? *reinterpret_cast<const uint4 *>(w_down + static_cast<size_t>(aa) * Dh + e0 + 32 * u + 8 * lg)
-                        : make_uint4(0, 0, 0, 0);
-      }
+  for (int t = 0; t < TT; ++t)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) acc[t][nt] = f32x4s{0.f, 0.f, 0.f, 0.f};
+  // the wave's quarter of the 32-wide k-steps: a lane reads 16 bytes, the 4
+  // lanes of a row 64 contiguous bytes per load
+  const int nst = Dh / 32;
+  const int s0 = nst * wave / 4, s1 = nst * (wave + 1) / 4;
+  int s = s0;
+  for (; s + 4 <= s1; s += 4) {
+    uint4 av[4][TT], bv[4][NT];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = 32 * (s + j);
+#pragma unroll
+      for (int t = 0; t < TT; ++t)
+        av[j][t] = tok_ok[t] ? *reinterpret_cast<const uint4 *>(hrow[t] + e) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        bv[j][nt] = wrow[nt] ? *reinterpret_cast<const uint4 *>(wrow[nt] + e) : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
-    for (int u = 0; u < UK; ++u)
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) acc[nt] = mfma_s(av[u], bv[u][nt], acc[nt]);
-    if (NT > 2) {
+      for (int t = 0; t < TT; ++t)
 #pragma unroll
-      for (int u = 0; u < UK; ++u)
+        for (int nt = 0; nt < NT; ++nt) acc[t][nt] = mfma_s(av[j][t], bv[j][nt], acc[t][nt]);
+  }
+  for (; s < s1; ++s) {
+    const int e = 32 * s;
 #pragma unroll
-        for (int nt = 2; nt < 4; ++nt) {
-          const int aa = 16 * nt + ln;
-          const uint4 b2 = (nt < NT && aa < r)
-                               ? *reinterpret_cast<const uint4 *>(w_down + static_cast<size_t>(aa) * Dh + e0 + 32 * u + 8 * lg)
-                               : make_uint4(0, 0, 0, 0);
-          acc[nt] = mfma_s(av[u], b2, acc[nt]);
-        }
+    for (int t = 0; t < TT; ++t) {
+      const uint4 av = tok_ok[t] ? *reinterpret_cast<const uint4 *>(hrow[t] + e) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        acc[t][nt] = mfma_s(av, wrow[nt] ? *reinterpret_cast<const uint4 *>(wrow[nt] + e) : make_uint4(0, 0, 0, 0),
+                            acc[t][nt]);
     }
   }
-  for (; e0 < Dh; e0 += 32) {
-    const uint4 av = tok_ok ? *reinterpret_cast<const uint4 *>(hrow + e0) : make_uint4(0, 0, 0, 0);
+  // D[m = token 16 t + 4 lg + q][n = a = 16 nt + ln]
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      if (nt < NT) {
-        const int aa = 16 * nt + ln;
-        const uint4 bv = aa < r ? *reinterpret_cast<const uint4 *>(w_down + static_cast<size_t>(aa) * Dh + e0 + 8 * lg)
-                                : make_uint4(0, 0, 0, 0);
-        acc[nt] = mfma_s(av, bv, acc[nt]);
-      }
-    }
-  }
-  // D[m = token 4 lg + i][n = a]
+  for (int t = 0; t < TT; ++t)
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
-    if (nt < NT) {
+    for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int tk = tok0 + 4 * lg + i, aa = 16 * nt + ln;
-        if (tk < Ntok) {
-          uint16_t hi, lo;
-          split_bf16(acc[nt][i], hi, lo);
-          u_hi[static_cast<size_t>(tk) * RP + aa] = hi;
-          u_lo[static_cast<size_t>(tk) * RP + aa] = lo;
-        }
-      }
+      for (int q = 0; q < 4; ++q) part[wave][16 * t + 4 * lg + q][16 * nt + ln] = acc[t][nt][q];
+  __syncthreads();
+  for (int x = threadIdx.x; x < 16 * TT * RP; x += 256) {
+    const int tk = x / RP, aa = x % RP;
+    if (tok0 + tk < Ntok) {
+      const float v = (part[0][tk][aa] + part[1][tk][aa]) + (part[2][tk][aa] + part[3][tk][aa]);
+      uint16_t hi, lo;
+      split_bf16(v, hi, lo);
+      const size_t o = static_cast<size_t>(tok0 + tk) * RP + aa;
+      u_hi[o] = hi;
+      u_lo[o] = lo;
     }
   }
 }
 
 // ------------------------------------------------------------------ m = W_up_h^T k'
-// One workgroup per (32 chunks, query head, batch); W_up's head slice in LDS.
+// One workgroup per (32 chunks, query head, batch); W_up's head slice and
+// the 32 summaries in LDS.  Thread (chunk t / 8, a4 = t % 8) forms the
+// outputs a = 32 j + 4 a4 .. + 4 of its chunk.
 template <int D>
 __global__ void __launch_bounds__(256)
 qcal_m_kernel(const uint16_t *__restrict__ k_sum, const uint16_t *__restrict__ w_up, uint16_t *__restrict__ m_hi,
               uint16_t *__restrict__ m_lo, int Hq, int C, int r, int RP) {
-  __shared__ float wu[D][65];
+  __shared__ float4 wu[D][16];  // [e][a / 4], zero for a >= r
   __shared__ float kc[32][D + 1];
   const int c0 = blockIdx.x * 32, h = blockIdx.y, b = blockIdx.z, t = threadIdx.x;
-  for (int x = t; x < D * r; x += 256) wu[x / r][x % r] = bf16_to_f32(w_up[(static_cast<size_t>(h) * D + x / r) * r + x % r]);
-  for (int x = t; x < 32 * D; x += 256) {
-    const int cc = x / D, e = x % D;
-    kc[cc][e] = (c0 + cc < C) ? bf16_to_f32(k_sum[((static_cast<size_t>(b) * Hq + h) * C + c0 + cc) * D + e]) : 0.f;
+  // The head's W_up slice (D x r, contiguous) and the 32 summaries
+  // (32 x D, contiguous) are read with 16-byte loads, all issued before any
+  // is used.
+  constexpr int KV = 32 * D / 8 / 256;  // 16-byte pieces of k' per thread
+  const int nw = D * r / 8;             // 16-byte pieces of the W_up slice (D is a multiple of 8)
+  const uint16_t *wsl = w_up + static_cast<size_t>(h) * D * r;
+  const uint16_t *ksl = k_sum + ((static_cast<size_t>(b) * Hq + h) * C + c0) * D;
+  uint4 wv[4], kv[KV];  // nw <= D * 64 / 8 = 4 * 256 pieces for D = 128
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int x = t + 256 * j;
+    wv[j] = x < nw ? *reinterpret_cast<const uint4 *>(wsl + 8 * x) : make_uint4(0, 0, 0, 0);
+  }
+#pragma unroll
+  for (int j = 0; j < KV; ++j) {
+    const int x = t + 256 * j;
+    kv[j] = c0 + (8 * x) / D < C ? *reinterpret_cast<const uint4 *>(ksl + 8 * x) : make_uint4(0, 0, 0, 0);
+  }
+  float *wuf = reinterpret_cast<float *>(&wu[0][0]);
+  for (int x = t; x < D * 16; x += 256) wu[x / 16][x % 16] = make_float4(0.f, 0.f, 0.f, 0.f);
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int x = t + 256 * j;
+    if (x < nw) {
+      const uint32_t w4[4] = {wv[j].x, wv[j].y, wv[j].z, wv[j].w};
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int flat = 8 * x + q, e = flat / r, aa = flat - e * r;
+        wuf[e * 64 + aa] = bf16_to_f32(static_cast<uint16_t>(w4[q >> 1] >> (16 * (q & 1))));
+      }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < KV; ++j) {
+    const int x = t + 256 * j, cc = (8 * x) / D, e = (8 * x) % D;
+    const uint32_t k4[4] = {kv[j].x, kv[j].y, kv[j].z, kv[j].w};
+#pragma unroll
+    for (int q = 0; q < 8; ++q) kc[cc][e + q] = bf16_to_f32(static_cast<uint16_t>(k4[q >> 1] >> (16 * (q & 1))));
   }
   __syncthreads();
-  for (int x = t; x < 32 * RP; x += 256) {
-    const int cc = x / RP, aa = x % RP;
-    if (c0 + cc >= C) continue;
-    float acc = 0.f;
-    if (aa < r)
-      for (int e = 0; e < D; ++e) acc += wu[e][aa] * kc[cc][e];
-    uint16_t hi, lo;
-    split_bf16(acc, hi, lo);
-    const size_t o = ((static_cast<size_t>(b) * Hq + h) * C + c0 + cc) * RP + aa;
-    m_hi[o] = hi;
-    m_lo[o] = lo;
+  const int cc = t >> 3, a4 = t & 7;
+  if (c0 + cc >= C) return;
+  const int NJ = RP / 32;
+  float acc[2][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll 4
+  for (int e = 0; e < D; ++e) {
+    const float kv = kc[cc][e];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      if (j < NJ) {
+        const float4 w = wu[e][8 * j + a4];
+        acc[j][0] += w.x * kv;
+        acc[j][1] += w.y * kv;
+        acc[j][2] += w.z * kv;
+        acc[j][3] += w.w * kv;
+      }
+    }
+  }
+  const size_t o = ((static_cast<size_t>(b) * Hq + h) * C + c0 + cc) * RP;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    if (j < NJ) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        uint16_t hi, lo;
+        split_bf16(acc[j][q], hi, lo);
+        m_hi[o + 32 * j + 4 * a4 + q] = hi;
+        m_lo[o + 32 * j + 4 * a4 + q] = lo;
+      }
+    }
   }
 }
 
@@ -563,9 +630,11 @@ hipError_t launch_score_mfma(const ScoreArgs &a, hipStream_t st) {
   uint16_t *m_lo = m_hi + static_cast<size_t>(a.B) * a.Hq * a.C * RP;
   if (a.r > 0) {
     const int ntok = a.B * a.T;
-    qcal_u_mfma_kernel<<<(ntok + 63) / 64, 256, 0, st>>>(static_cast<const uint16_t *>(a.h),
-                                                      static_cast<const uint16_t *>(a.w_down), u_hi, u_lo, ntok,
-                                                      a.r, RP, a.Dh);
+    const uint16_t *hp = static_cast<const uint16_t *>(a.h), *wd = static_cast<const uint16_t *>(a.w_down);
+    if (RP == 32)
+      qcal_u_mfma_kernel<2, 2><<<(ntok + 31) / 32, 256, 0, st>>>(hp, wd, u_hi, u_lo, ntok, a.r, a.Dh);
+    else
+      qcal_u_mfma_kernel<4, 1><<<(ntok + 15) / 16, 256, 0, st>>>(hp, wd, u_hi, u_lo, ntok, a.r, a.Dh);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     dim3 gm((a.C + 31) / 32, a.Hq, a.B);
