@@ -101,11 +101,15 @@ constexpr int kMaxSlotRows = 2040;  // partial records one combine step holds in
 hils_status decode_geom(const hils_config *c, DecodeGeom *g) {
   const int G = c->n_q_heads / c->n_kv_heads, K = c->top_k, S = c->chunk_size;
   const int nmax = eligible(c->seq_len - 1, c->window, S);
-  // chunks per score slice: 64, 256 or 1024, the smallest that keeps the
-  // P * K candidates within what one workgroup merges
+  // chunks per score slice: 64, 256 or 1024, the smallest that leaves at
+  // most 32 slices per (sequence, KV head) (a short candidate merge; each
+  // slice streams enough summaries to keep its loads in flight), within
+  // what one workgroup merges (P * K candidates)
   const int kk = K > 0 ? K : 1;
   int cpb = 64;
-  while (cpb < 1024 && static_cast<long long>((nmax + cpb - 1) / cpb) * kk > kMaxCand) cpb *= 4;
+  while (cpb < 1024 && ((nmax + cpb - 1) / cpb > 32 ||
+                        static_cast<long long>((nmax + cpb - 1) / cpb) * kk > kMaxCand))
+    cpb *= 4;
   if (static_cast<long long>((nmax + cpb - 1) / cpb) * kk > kMaxCand || cpb * G > 4096)
     return fail(HILS_ERR_UNSUPPORTED, "decode: %d eligible chunks with top_k %d and group %d exceed the merge capacity",
                 nmax, K, G);

@@ -68,6 +68,7 @@ struct D1Smem {
       float sig[1024];
     } sc;
   };
+  unsigned long long wkey[4][64];  // per-wave ranking scratch of wave_select
   uint32_t w_ord[4][64];
   int w_idx[4][64];
   int w_pos[4][64];
@@ -94,7 +95,7 @@ __device__ __forceinline__ void slice_select(const DecodeArgs &a, D1Smem &sm, in
     ord[j] = cl < nch ? orderable(sm.sc.sig[cl]) : 0u;
     idx[j] = c0 + cl;
   }
-  wave_select<NJ>(ord, idx, K, win, rank);
+  wave_select<NJ>(ord, idx, K, win, rank, sm.wkey[0]);
   int nwin = 0;
 #pragma unroll
   for (int j = 0; j < NJ; ++j) nwin += __popcll(__ballot(win[j]));
@@ -132,7 +133,7 @@ __device__ __forceinline__ void merge_select(const DecodeArgs &a, D1Smem &sm, in
     ord[j] = static_cast<uint32_t>(key[j] >> 32);
     idx[j] = key[j] == kNoKey ? 0x7FFFFFFF : key_chunk(key[j]);
   }
-  wave_select<NJ>(ord, idx, K, win, rank);
+  wave_select<NJ>(ord, idx, K, win, rank, sm.wkey[wave]);
 #pragma unroll
   for (int j = 0; j < NJ; ++j)
     if (win[j]) {
@@ -158,7 +159,7 @@ __device__ __forceinline__ void merge_select(const DecodeArgs &a, D1Smem &sm, in
       i2[j] = ok ? sm.w_idx[ww][kk] : 0x7FFFFFFF;
       p2[j] = ok ? sm.w_pos[ww][kk] : 0;
     }
-    wave_select<2>(o2, i2, K, w2, r2);
+    wave_select<2>(o2, i2, K, w2, r2, sm.wkey[0]);
     int nwin = 0;
 #pragma unroll
     for (int j = 0; j < 2; ++j) nwin += __popcll(__ballot(w2[j]));
@@ -167,10 +168,15 @@ __device__ __forceinline__ void merge_select(const DecodeArgs &a, D1Smem &sm, in
 #pragma unroll
     for (int j = 0; j < 2; ++j)
       if (w2[j]) {
+        // the winner's per-head scores: every load issued before any store
+        float hs[kMaxG];
+#pragma unroll
+        for (int hh = 0; hh < kMaxG; ++hh)
+          if (hh < G) hs[hh] = load_acquired(a.cand_s + (cb0 + p2[j]) * G + hh);
         a.topk_idx[(static_cast<size_t>(b) * a.Hkv + g) * K + r2[j]] = i2[j];
-        for (int hh = 0; hh < G; ++hh)
-          a.topk_score[(static_cast<size_t>(b) * a.Hq + g * G + hh) * K + r2[j]] =
-              load_acquired(a.cand_s + (cb0 + p2[j]) * G + hh);
+#pragma unroll
+        for (int hh = 0; hh < kMaxG; ++hh)
+          if (hh < G) a.topk_score[(static_cast<size_t>(b) * a.Hq + g * G + hh) * K + r2[j]] = hs[hh];
       }
     for (int k = nwin + lane; k < K; k += 64) {
       a.topk_idx[(static_cast<size_t>(b) * a.Hkv + g) * K + k] = -1;
@@ -235,25 +241,27 @@ decode_score_kernel(DecodeArgs a) {
     const size_t qo = hbase * D + x;
     sm.sc.qh[x] = QCAL ? a.qhat[qo] : Elem<T>::load(static_cast<const T *>(a.q), qo);
   }
-  for (int rb = 0; rb < nrows; rb += RS) {
-    uint4 kv[U * RPP];
-    float bs[U];
+  // Batches of RS rows, double buffered in registers: the loads of batch
+  // n + 1 are in flight while batch n is reduced.
+  // Branch-free: rows past the slice read its row 0 again (their dots are
+  // never stored; chunk c0 exists even when the slice is empty), and every
+  // lane of a row reads the row's b'.  A load under a
+  // lane-dependent branch would make the compiler wait for every load in
+  // flight at the branch's end.
+  auto load_batch = [&](int rb, uint4 (&kv)[U * RPP], float (&bs)[U]) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int p = u * kDecThreads + t;
       const int row = rb + p / LPH, seg = p % LPH;
+      const int rr = row < nrows ? row : 0;
+      const int cl = rr / G, hh = rr % G;
+      const size_t ro = (hbase + hh) * a.Cmax + c0 + cl;
 #pragma unroll
-      for (int r = 0; r < RPP; ++r) kv[u * RPP + r] = make_uint4(0, 0, 0, 0);
-      bs[u] = 0.f;
-      if (row < nrows) {
-        const int cl = row / G, hh = row % G;
-        const size_t ro = (hbase + hh) * a.Cmax + c0 + cl;
-#pragma unroll
-        for (int r = 0; r < RPP; ++r) kv[u * RPP + r] = reinterpret_cast<const uint4 *>(ks + ro * D + seg * 8)[r];
-        if (seg == 0) bs[u] = a.b_sum[ro];
-      }
+      for (int r = 0; r < RPP; ++r) kv[u * RPP + r] = reinterpret_cast<const uint4 *>(ks + ro * D + seg * 8)[r];
+      bs[u] = a.b_sum[ro];
     }
-    __syncthreads();  // q-hat in LDS (first batch); loads stay in flight
+  };
+  auto reduce_batch = [&](int rb, const uint4 (&kv)[U * RPP], const float (&bs)[U]) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int p = u * kDecThreads + t;
@@ -267,6 +275,22 @@ decode_score_kernel(DecodeArgs a) {
       for (int x = 0; x < 8; ++x) part += qv[x] * kf[x];
       const float dot = dpp_group_sum<LPH>(part);
       if (seg == 0 && row < nrows) sm.sc.s[row] = a.tau * dot + bs[u];
+    }
+  };
+  {
+    // Every batch load is issued unconditionally (past the slice it re-reads
+    // the slice's first rows, cached): the number of loads in flight is then
+    // the same on every path, and each reduction waits only for its own batch.
+    uint4 kvA[U * RPP], kvB[U * RPP];
+    float bsA[U], bsB[U];
+    load_batch(0, kvA, bsA);
+    __syncthreads();  // q-hat in LDS; the first batch's loads stay in flight
+    for (int rb = 0; rb < nrows; rb += 2 * RS) {
+      load_batch(rb + RS, kvB, bsB);
+      reduce_batch(rb, kvA, bsA);
+      if (rb + RS >= nrows) break;
+      load_batch(rb + 2 * RS, kvA, bsA);
+      reduce_batch(rb + RS, kvB, bsB);
     }
   }
   __syncthreads();

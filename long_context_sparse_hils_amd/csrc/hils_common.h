@@ -222,29 +222,56 @@ __device__ __forceinline__ unsigned long long load_acquired(const unsigned long 
 // candidate) and a unique index idx[j].  A bitwise binary search over the
 // 32-bit keys, counting with ballots, finds the k-th largest key theta; the
 // winners are every key above theta plus the lowest-index keys equal to it.
-// On return win[j] marks winners and rank[j] is the winner's position.
+// theta lies between the smallest and the largest candidate, so the search
+// starts below their common leading bits, and it stops early once exactly k
+// keys are at or above the trial value.
+// On return win[j] marks winners and rank[j] is the winner's position:
+// the winners' 64-bit keys (ord, ~idx) are compacted into `scratch` (LDS
+// private to the wave, >= min(k, 64 NJ) entries) and every lane counts the
+// larger keys there (broadcast reads, no cross-lane shuffles).
 template <int NJ>
 __device__ __forceinline__ void wave_select(const uint32_t (&ord)[NJ], const int (&idx)[NJ], int k,
-                                            bool (&win)[NJ], int (&rank)[NJ]) {
+                                            bool (&win)[NJ], int (&rank)[NJ], unsigned long long *scratch) {
   const int lane = threadIdx.x & 63;
   int avail = 0;
+  uint32_t lo = 0xFFFFFFFFu, hi = 0u;
 #pragma unroll
-  for (int j = 0; j < NJ; ++j) avail += __popcll(__ballot(ord[j] != 0u));
+  for (int j = 0; j < NJ; ++j) {
+    avail += __popcll(__ballot(ord[j] != 0u));
+    hi = max(hi, ord[j]);
+    lo = min(lo, ord[j] != 0u ? ord[j] : 0xFFFFFFFFu);
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    lo = min(lo, static_cast<uint32_t>(__shfl_xor(static_cast<int>(lo), o, kWave)));
+    hi = max(hi, static_cast<uint32_t>(__shfl_xor(static_cast<int>(hi), o, kWave)));
+  }
   const int keep = min(k, avail);
   uint32_t theta = 0u;
+  bool exact = false;  // exactly `keep` keys are >= theta
   if (keep > 0) {
-    for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t spread = lo ^ hi;
+    const int top = spread ? 31 - __clz(spread) : -1;  // highest bit where lo and hi differ
+    theta = top < 0 ? lo : (top == 31 ? 0u : lo & ~((2u << top) - 1u));
+    for (int bit = top; bit >= 0; --bit) {
       const uint32_t cand = theta | (1u << bit);
       int cnt = 0;
 #pragma unroll
       for (int j = 0; j < NJ; ++j) cnt += __popcll(__ballot(ord[j] >= cand));
-      if (cnt >= keep) theta = cand;
+      if (cnt >= keep) {
+        theta = cand;
+        if (cnt == keep) {
+          exact = true;
+          break;
+        }
+      }
     }
+    if (top < 0) exact = avail == keep;
   }
   int cnt_gt = 0;
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
-    win[j] = keep > 0 && ord[j] > theta;
+    win[j] = keep > 0 && (exact ? ord[j] >= theta : ord[j] > theta);
     cnt_gt += __popcll(__ballot(win[j]));
   }
   // ties at theta: take the lowest indices first
@@ -259,21 +286,25 @@ __device__ __forceinline__ void wave_select(const uint32_t (&ord)[NJ], const int
     for (int j = 0; j < NJ; ++j)
       if (!win[j] && ord[j] == theta && idx[j] == best) win[j] = true;
   }
+  unsigned long long key[NJ];
+  int nwin = 0;
 #pragma unroll
-  for (int j = 0; j < NJ; ++j) rank[j] = 0;
-#pragma unroll
-  for (int jj = 0; jj < NJ; ++jj) {
-    unsigned long long wm = __ballot(win[jj]);
-    while (wm) {
-      const int src = __ffsll(static_cast<long long>(wm)) - 1;
-      wm &= wm - 1ull;
-      const uint32_t o2 = __shfl(ord[jj], src, 64);
-      const int i2 = __shfl(idx[jj], src, 64);
-#pragma unroll
-      for (int j = 0; j < NJ; ++j)
-        if (win[j] && (o2 > ord[j] || (o2 == ord[j] && i2 < idx[j]))) ++rank[j];
-    }
+  for (int j = 0; j < NJ; ++j) {
+    key[j] = (static_cast<unsigned long long>(ord[j]) << 32) | static_cast<uint32_t>(~static_cast<uint32_t>(idx[j]));
+    const unsigned long long m = __ballot(win[j]);
+    const int below = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
+                                                __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
+    if (win[j]) scratch[nwin + below] = key[j];
+    nwin += __popcll(m);
+    rank[j] = 0;
   }
+  __builtin_amdgcn_wave_barrier();  // (LDS operations of one wave complete in order)
+  for (int e = 0; e < nwin; ++e) {
+    const unsigned long long ke = scratch[e];
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) rank[j] += ke > key[j] ? 1 : 0;
+  }
+  __builtin_amdgcn_wave_barrier();  // scratch may be reused after this
   (void)lane;
 }
 
