@@ -91,30 +91,17 @@ hils_status check_qcal_ptrs(const hils_config *c, const void *h, const void *wd,
 
 // ------------------------------------------------------------ decode geometry
 struct DecodeGeom {
-  int P, CPB, NW, nslots, nslot_blocks;
-  size_t off_counts, off_qhat, off_cand_key, off_cand_s, off_parts, total;
+  int P, NW, nslots, nslot_blocks;
+  size_t off_counts, off_qhat, off_sig, off_hsc, off_parts, total;
 };
 
-constexpr int kMaxCand = 4096;
+constexpr int kDecodeCPB = 64;      // chunks per score slice
 constexpr int kMaxSlotRows = 2040;  // partial records one combine step holds in LDS
 
 hils_status decode_geom(const hils_config *c, DecodeGeom *g) {
   const int G = c->n_q_heads / c->n_kv_heads, K = c->top_k, S = c->chunk_size;
   const int nmax = eligible(c->seq_len - 1, c->window, S);
-  // chunks per score slice: 64, 256 or 1024, the smallest that leaves at
-  // most 32 slices per (sequence, KV head) (a short candidate merge; each
-  // slice streams enough summaries to keep its loads in flight), within
-  // what one workgroup merges (P * K candidates)
-  const int kk = K > 0 ? K : 1;
-  int cpb = 64;
-  while (cpb < 1024 && ((nmax + cpb - 1) / cpb > 32 ||
-                        static_cast<long long>((nmax + cpb - 1) / cpb) * kk > kMaxCand))
-    cpb *= 4;
-  if (static_cast<long long>((nmax + cpb - 1) / cpb) * kk > kMaxCand || cpb * G > 4096)
-    return fail(HILS_ERR_UNSUPPORTED, "decode: %d eligible chunks with top_k %d and group %d exceed the merge capacity",
-                nmax, K, G);
-  g->CPB = cpb;
-  g->P = nmax > 0 ? (nmax + cpb - 1) / cpb : 1;
+  g->P = nmax > 0 ? (nmax + kDecodeCPB - 1) / kDecodeCPB : 1;
   g->NW = (c->window + S - 1 + 63) / 64;
   g->nslots = K + g->NW;
   if (g->nslots * G > kMaxSlotRows)
@@ -123,14 +110,15 @@ hils_status decode_geom(const hils_config *c, DecodeGeom *g) {
   g->nslot_blocks = K > 0 ? K : 1;
   const size_t B = c->batch, Hkv = c->n_kv_heads, Hq = c->n_q_heads, D = c->head_dim;
   size_t off = 0;
+  const size_t Cmax = static_cast<size_t>(c->seq_len / S);
   g->off_counts = off;
-  off = align_up(off + sizeof(unsigned) * (2 * B * Hkv + 1));
+  off = align_up(off + sizeof(unsigned) * (B * Hkv + 1));
   g->off_qhat = off;
   if (c->qcal_rank > 0) off = align_up(off + sizeof(float) * B * Hq * D);
-  g->off_cand_key = off;
-  off = align_up(off + sizeof(unsigned long long) * B * Hkv * g->P * (K > 0 ? K : 1));
-  g->off_cand_s = off;
-  off = align_up(off + sizeof(float) * B * Hkv * g->P * (K > 0 ? K : 1) * G);
+  g->off_sig = off;
+  off = align_up(off + sizeof(float) * B * Hkv * Cmax);
+  g->off_hsc = off;
+  off = align_up(off + sizeof(float) * B * Hkv * Cmax * G);
   g->off_parts = off;
   off = align_up(off + sizeof(float) * B * Hkv * g->nslots * G * (D + 2));
   g->total = off;
@@ -280,7 +268,7 @@ size_t hils_decode_workspace_bytes(const hils_config *cfg) {
 
 size_t hils_decode_error_offset(const hils_config *cfg) {
   if (check_config(cfg) != HILS_OK) return 0;
-  return sizeof(unsigned) * 2 * static_cast<size_t>(cfg->batch) * cfg->n_kv_heads;
+  return sizeof(unsigned) * static_cast<size_t>(cfg->batch) * cfg->n_kv_heads;
 }
 
 hils_status hils_sparse_attn_decode(const hils_config *cfg, const void *q, const void *h, const void *w_down,
@@ -317,14 +305,14 @@ hils_status hils_sparse_attn_decode(const hils_config *cfg, const void *q, const
   a.k_sum = k_sum; a.b_sum = b_sum; a.seq_lens = seq_lens; a.o = o; a.topk_idx = topk_idx;
   a.topk_score = topk_score;
   a.qhat = reinterpret_cast<float *>(ws + g.off_qhat);
-  a.cand_key = reinterpret_cast<unsigned long long *>(ws + g.off_cand_key);
-  a.cand_s = reinterpret_cast<float *>(ws + g.off_cand_s);
+  a.sig = reinterpret_cast<float *>(ws + g.off_sig);
+  a.hsc = reinterpret_cast<float *>(ws + g.off_hsc);
   a.parts = reinterpret_cast<float *>(ws + g.off_parts);
-  a.count1 = counts; a.count2 = counts + BH; a.err = counts + 2 * BH;
+  a.count = counts; a.err = counts + BH;
   a.B = cfg->batch; a.Tmax = cfg->seq_len; a.Hq = cfg->n_q_heads; a.Hkv = cfg->n_kv_heads;
   a.d = cfg->head_dim; a.S = cfg->chunk_size; a.K = cfg->top_k; a.W = cfg->window;
   a.r = cfg->qcal_rank; a.Dh = cfg->hidden_dim; a.Cmax = Cmax;
-  a.P = g.P; a.CPB = g.CPB; a.NW = g.NW; a.nslots = g.nslots; a.nslot_blocks = g.nslot_blocks;
+  a.P = g.P; a.NW = g.NW; a.nslots = g.nslots; a.nslot_blocks = g.nslot_blocks;
   a.tau = tau_of(cfg); a.bf16 = cfg->dtype == HILS_BF16;
   // topk buffers are also read back by the attend kernel: provide scratch when K == 0
   return finish(hils::launch_decode(a, static_cast<hipStream_t>(stream)), "sparse decode launch");

@@ -10,14 +10,15 @@
 // Launch structure (all on the caller's stream, no host round trip):
 //   [qcal]  q-hat = q + W_up W_down h                      (only when r > 0)
 //   D1      grid (P score slices + NW window units, H_kv, B)
-//           score slice: stream CPB chunks' k'/b' of the G heads (the
-//           dominant HBM stream), local top-K -> candidates in the
-//           workspace; the last slice block of (b, g) to finish (atomic
-//           ticket) merges all candidates into the final top-K.
+//           score slice: stream 64 chunks' k'/b' of the G heads (the
+//           dominant HBM stream) -> each chunk's group score sigma and
+//           per-head scores in the workspace.
 //           window unit: 64 window keys -> online-softmax partial.
-//   D2      grid (K chunk slots, H_kv, B): attend one selected chunk -> its
-//           (s_hat, 1, o_c) partial; the last block of (b, g) combines the
-//           chunk and window partials in a fixed order (deterministic).
+//   D2      grid (K chunk slots, H_kv, B): every slot workgroup selects the
+//           top-K from sigma (identically), attends the chunk of its rank
+//           -> its (s_hat, 1, o_c) partial; the last block of (b, g)
+//           combines the chunk and window partials in a fixed order
+//           (deterministic).
 #include "attn_unit.h"
 #include "hils_common.h"
 #include "launch.h"
@@ -25,7 +26,6 @@
 namespace hils {
 
 constexpr int kDecThreads = 256;
-constexpr int kMaxCand = 4096;  // P * K candidates merged by one block
 
 __device__ __forceinline__ int clamp_seq(const int32_t *seq_lens, int b, int Tmax, unsigned *err, bool count) {
   int s = seq_lens[b];
@@ -59,20 +59,11 @@ decode_qcal_kernel(const T *__restrict__ q, const T *__restrict__ h, const T *__
 }
 
 // ------------------------------------------------------------------ D1
-constexpr int kRowsMax = 4096;  // CPB * G rows of one score slice
+constexpr int kCPB = 64;                    // chunks per score slice
+constexpr int kRowsMax = kCPB * kMaxG;      // (chunk, head) rows of one slice
 struct D1Smem {
-  union {
-    struct {
-      float qh[kMaxG * 128];
-      float s[kRowsMax];  // per (chunk, head) score of the slice
-      float sig[1024];
-    } sc;
-  };
-  unsigned long long wkey[4][64];  // per-wave ranking scratch of wave_select
-  uint32_t w_ord[4][64];
-  int w_idx[4][64];
-  int w_pos[4][64];
-  int is_last;
+  float qh[kMaxG * 128];
+  float s[kRowsMax];  // per (chunk, head) score of the slice
 };
 
 // a score-slice block and a window-unit block never need both layouts
@@ -82,111 +73,10 @@ union D1Shared {
   UnitSmem<T, D> us;
 };
 
-// Per-slice top-K: wave 0 selects among the slice's chunks (NJ per lane).
-template <int NJ>
-__device__ __forceinline__ void slice_select(const DecodeArgs &a, D1Smem &sm, int nch, int c0, int G, size_t cbase) {
-  const int lane = threadIdx.x & 63, K = a.K;
-  uint32_t ord[NJ];
-  int idx[NJ], rank[NJ];
-  bool win[NJ];
-#pragma unroll
-  for (int j = 0; j < NJ; ++j) {
-    const int cl = lane + 64 * j;
-    ord[j] = cl < nch ? orderable(sm.sc.sig[cl]) : 0u;
-    idx[j] = c0 + cl;
-  }
-  wave_select<NJ>(ord, idx, K, win, rank, sm.wkey[0]);
-  int nwin = 0;
-#pragma unroll
-  for (int j = 0; j < NJ; ++j) nwin += __popcll(__ballot(win[j]));
-#pragma unroll
-  for (int j = 0; j < NJ; ++j) {
-    if (win[j]) {
-      const int cl = lane + 64 * j;
-      publish(a.cand_key + cbase + rank[j], make_key(sm.sc.sig[cl], idx[j]));
-      for (int hh = 0; hh < G; ++hh) publish(a.cand_s + (cbase + rank[j]) * G + hh, sm.sc.s[cl * G + hh]);
-    }
-  }
-  for (int k = nwin + lane; k < K; k += 64) publish(a.cand_key + cbase + k, kNoKey);
-}
-
-// Merge of the P*K candidates of (b, g): each wave keeps its top-K, wave 0
-// picks the final top-K from the waves' winners.
-template <int NJ>
-__device__ __forceinline__ void merge_select(const DecodeArgs &a, D1Smem &sm, int b, int g, int n) {
-  // NJ candidates per lane: P * K <= 4 waves * 64 lanes * NJ
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, t = threadIdx.x;
-  const int K = a.K, G = a.Hq / a.Hkv;
-  const int total = a.P * K;
-  const size_t cb0 = (static_cast<size_t>(b) * a.Hkv + g) * a.P * K;
-  uint32_t ord[NJ];
-  int idx[NJ], rank[NJ];
-  bool win[NJ];
-  unsigned long long key[NJ];
-#pragma unroll
-  for (int j = 0; j < NJ; ++j) {
-    const int x = wave * 64 * NJ + j * 64 + lane;
-    key[j] = x < total ? load_acquired(a.cand_key + cb0 + x) : kNoKey;
-  }
-#pragma unroll
-  for (int j = 0; j < NJ; ++j) {
-    ord[j] = static_cast<uint32_t>(key[j] >> 32);
-    idx[j] = key[j] == kNoKey ? 0x7FFFFFFF : key_chunk(key[j]);
-  }
-  wave_select<NJ>(ord, idx, K, win, rank, sm.wkey[wave]);
-#pragma unroll
-  for (int j = 0; j < NJ; ++j)
-    if (win[j]) {
-      sm.w_ord[wave][rank[j]] = ord[j];
-      sm.w_idx[wave][rank[j]] = idx[j];
-      sm.w_pos[wave][rank[j]] = wave * 64 * NJ + j * 64 + lane;
-    }
-  int nw = 0;
-#pragma unroll
-  for (int j = 0; j < NJ; ++j) nw += __popcll(__ballot(win[j]));
-  for (int k = nw + lane; k < 64; k += 64) sm.w_ord[wave][k] = 0u;
-  __syncthreads();
-  if (wave == 0) {
-    uint32_t o2[2];
-    int i2[2], p2[2], r2[2];
-    bool w2[2];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int x = j * 64 + lane;  // x = wave * K + k
-      const int ww = x / max(K, 1), kk = x % max(K, 1);
-      const bool ok = K > 0 && ww < 4;
-      o2[j] = ok ? sm.w_ord[ww][kk] : 0u;
-      i2[j] = ok ? sm.w_idx[ww][kk] : 0x7FFFFFFF;
-      p2[j] = ok ? sm.w_pos[ww][kk] : 0;
-    }
-    wave_select<2>(o2, i2, K, w2, r2, sm.wkey[0]);
-    int nwin = 0;
-#pragma unroll
-    for (int j = 0; j < 2; ++j) nwin += __popcll(__ballot(w2[j]));
-    const int keep = min(K, n);
-    (void)keep;
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-      if (w2[j]) {
-        // the winner's per-head scores: every load issued before any store
-        float hs[kMaxG];
-#pragma unroll
-        for (int hh = 0; hh < kMaxG; ++hh)
-          if (hh < G) hs[hh] = load_acquired(a.cand_s + (cb0 + p2[j]) * G + hh);
-        a.topk_idx[(static_cast<size_t>(b) * a.Hkv + g) * K + r2[j]] = i2[j];
-#pragma unroll
-        for (int hh = 0; hh < kMaxG; ++hh)
-          if (hh < G) a.topk_score[(static_cast<size_t>(b) * a.Hq + g * G + hh) * K + r2[j]] = hs[hh];
-      }
-    for (int k = nwin + lane; k < K; k += 64) {
-      a.topk_idx[(static_cast<size_t>(b) * a.Hkv + g) * K + k] = -1;
-      for (int hh = 0; hh < G; ++hh) a.topk_score[(static_cast<size_t>(b) * a.Hq + g * G + hh) * K + k] = -INFINITY;
-    }
-  }
-  (void)t;
-}
-
-template <typename T, int D, bool QCAL, int SNJ, int MNJ>
+// D1: score slices stream k'/b' of the group's heads and store every
+// eligible chunk's group score sigma = max over the heads (and each head's
+// own score); the selection runs in D2, after the kernel boundary.
+template <typename T, int D, bool QCAL>
 __global__ void __launch_bounds__(kDecThreads)
 decode_score_kernel(DecodeArgs a) {
   __shared__ D1Shared<T, D> shm;
@@ -228,8 +118,8 @@ decode_score_kernel(DecodeArgs a) {
   }
 
   // ---------------- score slice: chunks [c0, c0 + nch) of the G heads
-  const int c0 = blk * a.CPB;
-  const int nch = max(0, min(c0 + a.CPB, n) - c0);
+  const int c0 = blk * kCPB;
+  const int nch = max(0, min(c0 + kCPB, n) - c0);
   constexpr int LPH = D / 8;                         // lanes per (chunk, head) row, 8 elements each
   constexpr int RPP = static_cast<int>(sizeof(T)) / 2;  // 16-byte loads per 8-element piece
   constexpr int U = 8 / RPP;                         // pieces in flight per thread
@@ -237,10 +127,6 @@ decode_score_kernel(DecodeArgs a) {
   const int nrows = nch * G;
   const T *ks = static_cast<const T *>(a.k_sum);
   const size_t hbase = static_cast<size_t>(b) * a.Hq + g * G;
-  for (int x = t; x < G * D; x += kDecThreads) {
-    const size_t qo = hbase * D + x;
-    sm.sc.qh[x] = QCAL ? a.qhat[qo] : Elem<T>::load(static_cast<const T *>(a.q), qo);
-  }
   // Batches of RS rows, double buffered in registers: the loads of batch
   // n + 1 are in flight while batch n is reduced.
   // Branch-free: rows past the slice read its row 0 again (their dots are
@@ -269,12 +155,12 @@ decode_score_kernel(DecodeArgs a) {
       const int hh = (row < nrows) ? row % G : 0;
       float kf[8];
       Elem<T>::load8(reinterpret_cast<const T *>(&kv[u * RPP]), kf);
-      const float *qv = sm.sc.qh + hh * D + seg * 8;
+      const float *qv = sm.qh + hh * D + seg * 8;
       float part = 0.f;
 #pragma unroll
       for (int x = 0; x < 8; ++x) part += qv[x] * kf[x];
       const float dot = dpp_group_sum<LPH>(part);
-      if (seg == 0 && row < nrows) sm.sc.s[row] = a.tau * dot + bs[u];
+      if (seg == 0 && row < nrows) sm.s[row] = a.tau * dot + bs[u];
     }
   };
   {
@@ -284,7 +170,12 @@ decode_score_kernel(DecodeArgs a) {
     uint4 kvA[U * RPP], kvB[U * RPP];
     float bsA[U], bsB[U];
     load_batch(0, kvA, bsA);
-    __syncthreads();  // q-hat in LDS; the first batch's loads stay in flight
+    // the query rows go to LDS while the first batch is in flight
+    for (int x = t; x < G * D; x += kDecThreads) {
+      const size_t qo = hbase * D + x;
+      sm.qh[x] = QCAL ? a.qhat[qo] : Elem<T>::load(static_cast<const T *>(a.q), qo);
+    }
+    __syncthreads();
     for (int rb = 0; rb < nrows; rb += 2 * RS) {
       load_batch(rb + RS, kvB, bsB);
       reduce_batch(rb, kvA, bsA);
@@ -294,23 +185,15 @@ decode_score_kernel(DecodeArgs a) {
     }
   }
   __syncthreads();
+  // sigma and the per-head scores of the slice's chunks: rows are (chunk,
+  // head) in chunk-major order, as hsc stores them
+  const size_t bg = static_cast<size_t>(b) * a.Hkv + g;
   for (int cl = t; cl < nch; cl += kDecThreads) {
     float m = -INFINITY;
-    for (int hh = 0; hh < G; ++hh) m = fmaxf(m, sm.sc.s[cl * G + hh]);
-    sm.sc.sig[cl] = m;
+    for (int hh = 0; hh < G; ++hh) m = fmaxf(m, sm.s[cl * G + hh]);
+    a.sig[bg * a.Cmax + c0 + cl] = m;
   }
-  __syncthreads();
-  const size_t cbase = ((static_cast<size_t>(b) * a.Hkv + g) * a.P + blk) * K;
-  if ((t >> 6) == 0 && K > 0) slice_select<SNJ>(a, sm, nch, c0, G, cbase);
-  // ---------------- ticket: the last slice block of (b, g) merges
-  {
-    const unsigned before = arrive(a.count1 + b * a.Hkv + g);
-    if (t == 0) sm.is_last = (before == static_cast<unsigned>(a.P - 1));
-  }
-  __syncthreads();
-  if (!sm.is_last) return;
-  if (K > 0) merge_select<MNJ>(a, sm, b, g, n);
-  if (t == 0) reset_counter(a.count1 + b * a.Hkv + g);
+  for (int x = t; x < nrows; x += kDecThreads) a.hsc[(bg * a.Cmax + c0) * G + x] = sm.s[x];
 }
 
 // ------------------------------------------------------------------ combine
@@ -342,44 +225,316 @@ __device__ __forceinline__ void combine_slots(const float *recs, int nslots, int
     lt[hh] = L;
   }
   __syncthreads();
+  // every slot's o value of the thread's output: loads issued together
+  constexpr int kPre = 32;
   for (int x = t; x < G * D; x += kDecThreads) {
     const int hh = x / D, e = x % D;
     float acc = 0.f;
-    int s = 0;
-    for (; s + 8 <= nslots; s += 8) {
-      float o8[8];
+    for (int s0 = 0; s0 < nslots; s0 += kPre) {
+      float ov[kPre];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) o8[q] = load_acquired(recs + (static_cast<size_t>(s + q) * G + hh) * (D + 2) + 2 + e);
+      for (int q = 0; q < kPre; ++q)
+        if (s0 + q < nslots) ov[q] = load_acquired(recs + (static_cast<size_t>(s0 + q) * G + hh) * (D + 2) + 2 + e);
 #pragma unroll
-      for (int q = 0; q < 8; ++q) acc += w[(s + q) * G + hh] * o8[q];
+      for (int q = 0; q < kPre; ++q)
+        if (s0 + q < nslots) acc += w[(s0 + q) * G + hh] * ov[q];
     }
-    for (; s < nslots; ++s) acc += w[s * G + hh] * load_acquired(recs + (static_cast<size_t>(s) * G + hh) * (D + 2) + 2 + e);
     Elem<T>::store(out, static_cast<size_t>(hh) * D + e, acc / lt[hh]);
   }
 }
 
 // ------------------------------------------------------------------ D2
+constexpr int kSelVPT = 32;
+constexpr int kSelWaves = kDecThreads / 64;
+constexpr int kSurvMax = 256;  // survivors the one-wave exact select takes (plus the kept winners)
+constexpr int kSurvNJ = (kSurvMax + 32 + 63) / 64;
+struct SelSmem {
+  unsigned long long key[32];     // winners so far: (ordered score, ~chunk)
+  unsigned long long sorted[32];  // final winners in rank order
+  unsigned long long surv[kSurvMax + 32];
+  unsigned long long wkey[kSelWaves][64];  // wave_select scratch
+  uint32_t tw[kSelWaves];         // per-wave lower bound of the threshold
+  uint32_t red[2][kSelWaves];     // per-wave partial sums / minima, double buffered
+  uint32_t red2[2][kSelWaves];
+  int nkey, nsurv;
+};
+
+__device__ __forceinline__ unsigned long long sel_key(uint32_t ord, int c) {
+  return (static_cast<unsigned long long>(ord) << 32) | static_cast<uint32_t>(~static_cast<uint32_t>(c));
+}
+
+// Sum (SUM) or minimum over the block of one value per wave (wave-uniform
+// inputs); `slot` alternates between calls so one barrier per call suffices.
+template <bool SUM>
+__device__ __forceinline__ uint32_t block_reduce_waves(uint32_t v, uint32_t (&red)[2][kSelWaves], int &slot) {
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) red[slot][wave] = v;
+  __syncthreads();
+  uint32_t r = red[slot][0];
+#pragma unroll
+  for (int w = 1; w < kSelWaves; ++w) r = SUM ? r + red[slot][w] : min(r, red[slot][w]);
+  slot ^= 1;
+  return r;
+}
+
+__device__ __forceinline__ uint32_t wave_usum(uint32_t v) { return wave_reduce_u32<2>(v); }
+__device__ __forceinline__ uint32_t wave_umin(uint32_t v) { return wave_reduce_u32<0>(v); }
+
+// Exact top-K of one tile with all threads: a bitwise search for the
+// keep-th largest ordered score theta (counting with ballots, summed over
+// the waves through LDS; it starts below the common leading bits of the
+// smallest and largest candidate and stops once exactly `keep` scores are at
+// or above the trial value), then every score above theta and the lowest
+// chunks tied at theta.  Candidates: ord[] (0 = none) and the nprev winners
+// kept from earlier tiles.  Leaves the winners, unordered, in ss.key[0..nkey).
+__device__ __forceinline__ void tile_select_exact(const uint32_t (&ord)[kSelVPT], int tile0, int K, SelSmem &ss,
+                                                  int &slot) {
+  const int t = threadIdx.x;
+  const int nprev = ss.nkey;
+  const unsigned long long xkey = t < nprev ? ss.key[t] : 0ull;
+  const uint32_t xo = static_cast<uint32_t>(xkey >> 32);
+  const int xc = static_cast<int>(~static_cast<uint32_t>(xkey));
+  uint32_t cnt = xo != 0u ? 1u : 0u, lo = xo != 0u ? xo : 0xFFFFFFFFu, hi = xo;
+#pragma unroll
+  for (int j = 0; j < kSelVPT; ++j) {
+    cnt += ord[j] != 0u ? 1u : 0u;
+    lo = min(lo, ord[j] != 0u ? ord[j] : 0xFFFFFFFFu);
+    hi = max(hi, ord[j]);
+  }
+  const uint32_t avail = block_reduce_waves<true>(wave_usum(cnt), ss.red, slot);
+  lo = block_reduce_waves<false>(wave_umin(lo), ss.red2, slot);
+  hi = ~block_reduce_waves<false>(wave_umin(~hi), ss.red, slot);
+  const int keep = min(K, static_cast<int>(avail));
+  uint32_t theta = 0u;
+  bool exact = false;
+  if (keep > 0) {
+    const uint32_t spread = lo ^ hi;
+    const int top = spread ? 31 - __clz(spread) : -1;
+    theta = top < 0 ? lo : (top == 31 ? 0u : lo & ~((2u << top) - 1u));
+    for (int bit = top; bit >= 0; --bit) {
+      const uint32_t cand = theta | (1u << bit);
+      uint32_t c = 0;
+#pragma unroll
+      for (int j = 0; j < kSelVPT; ++j) c += __popcll(__ballot(ord[j] >= cand));
+      c += __popcll(__ballot(xo >= cand && xo != 0u));
+      const uint32_t tot = block_reduce_waves<true>(c, ss.red, slot);
+      if (static_cast<int>(tot) >= keep) {
+        theta = cand;
+        if (static_cast<int>(tot) == keep) {
+          exact = true;
+          break;
+        }
+      }
+    }
+    if (top < 0) exact = static_cast<int>(avail) == keep;
+  }
+  uint32_t win = 0u;  // bit j: ord[j]
+  uint32_t ngt = 0;
+#pragma unroll
+  for (int j = 0; j < kSelVPT; ++j) {
+    const bool w = keep > 0 && ord[j] != 0u && (exact ? ord[j] >= theta : ord[j] > theta);
+    win |= w ? (1u << j) : 0u;
+    ngt += __popcll(__ballot(w));
+  }
+  bool xw = keep > 0 && xo != 0u && (exact ? xo >= theta : xo > theta);
+  ngt += __popcll(__ballot(xw));
+  int need = keep - static_cast<int>(block_reduce_waves<true>(ngt, ss.red, slot));
+  while (need > 0) {  // uniform: every thread sees the same counts
+    uint32_t best = 0xFFFFFFFFu;
+#pragma unroll
+    for (int j = 0; j < kSelVPT; ++j)
+      if (!((win >> j) & 1u) && ord[j] == theta && ord[j] != 0u)
+        best = min(best, static_cast<uint32_t>(tile0 + j * kDecThreads + t));
+    if (!xw && xo == theta && xo != 0u) best = min(best, static_cast<uint32_t>(xc));
+    best = block_reduce_waves<false>(wave_umin(best), ss.red2, slot);
+    if (best == 0xFFFFFFFFu) break;
+#pragma unroll
+    for (int j = 0; j < kSelVPT; ++j)
+      if (static_cast<uint32_t>(tile0 + j * kDecThreads + t) == best && ord[j] == theta) win |= 1u << j;
+    if (!xw && xo == theta && static_cast<uint32_t>(xc) == best) xw = true;
+    --need;
+  }
+  __syncthreads();  // every thread has read ss.key / ss.nkey
+  if (t == 0) ss.nkey = 0;
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < kSelVPT; ++j)
+    if ((win >> j) & 1u) ss.key[atomicAdd(&ss.nkey, 1)] = sel_key(ord[j], tile0 + j * kDecThreads + t);
+  if (xw) ss.key[atomicAdd(&ss.nkey, 1)] = xkey;
+  __syncthreads();
+}
+
+// One wave selects the top-K of the tot survivor keys in ss.surv into
+// ss.key (rank order), ss.nkey.
+template <int NJ>
+__device__ __forceinline__ void select_survivors(SelSmem &ss, int tot, int K) {
+  const int lane = threadIdx.x & 63;
+  uint32_t so[NJ];
+  int si[NJ];
+  bool sw[NJ];
+  int sr[NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int x = j * 64 + lane;
+    const unsigned long long kk = x < tot ? ss.surv[x] : 0ull;
+    so[j] = static_cast<uint32_t>(kk >> 32);
+    si[j] = x < tot ? static_cast<int>(~static_cast<uint32_t>(kk)) : 0x7FFFFFFF;
+  }
+  wave_select<NJ>(so, si, K, sw, sr, ss.wkey[0]);
+  int nw = 0;
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    if (sw[j]) ss.key[sr[j]] = sel_key(so[j], si[j]);
+    nw += __popcll(__ballot(sw[j]));
+  }
+  if (lane == 0) ss.nkey = nw;
+}
+
+// Block-wide top-K of the group scores sigma[0..n) by (sigma desc, chunk
+// asc), all kDecThreads threads, in tiles of kDecThreads * kSelVPT scores
+// (one tile covers a 512K-token cache: 8192 chunks).  Per tile:
+//  1. a lower bound of the threshold: in a wave whose lanes' maxima include
+//     at least K scores, the K-th largest lane maximum is exceeded or met by
+//     K distinct scores, so it cannot lie above the tile's K-th largest
+//     score; the largest such bound over the waves is taken;
+//  2. the scores at or above it (typically a few dozen) and the winners kept
+//     from earlier tiles are collected in LDS, and one wave selects exactly
+//     among them (wave_select: same order, same tie rule);
+//  3. when too many scores pass (many equal scores), the tile falls back to
+//     the exact block-wide search.
+// On return ss.sorted[0..keep) holds the winners in rank order; returns keep.
+__device__ __forceinline__ int block_topk(const float *sig, int n, int K, SelSmem &ss) {
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  int slot = 0;
+  if (t == 0) ss.nkey = 0;
+  __syncthreads();
+  for (int tile0 = 0; tile0 < n; tile0 += kDecThreads * kSelVPT) {
+    // loads without a lane-dependent branch (past n they re-read sigma[0]),
+    // all issued before the first is used
+    float sv[kSelVPT];
+#pragma unroll
+    for (int j = 0; j < kSelVPT; ++j) {
+      const int c = tile0 + j * kDecThreads + t;
+      sv[j] = sig[c < n ? c : 0];
+    }
+    uint32_t ord[kSelVPT];
+    uint32_t mx = 0u;
+#pragma unroll
+    for (int j = 0; j < kSelVPT; ++j) {
+      ord[j] = tile0 + j * kDecThreads + t < n ? orderable(sv[j]) : 0u;  // 0: no candidate
+      mx = max(mx, ord[j]);
+    }
+    // 1. per-wave bound: the K-th largest lane maximum (0 = no bound)
+    {
+      const uint32_t mo[1] = {mx};
+      const int mi[1] = {lane};
+      bool mw[1];
+      int mr[1];
+      const int nvalid = __popcll(__ballot(mx != 0u));
+      wave_select<1>(mo, mi, K, mw, mr, ss.wkey[wave]);
+      const bool kth = nvalid >= K && mw[0] && mr[0] == K - 1;
+      if (lane == 0) ss.tw[wave] = 0u;
+      __builtin_amdgcn_wave_barrier();
+      if (kth) ss.tw[wave] = mx;
+    }
+    if (t == 0) ss.nsurv = 0;
+    __syncthreads();
+    uint32_t bound = 1u;  // real scores are >= 1 in the ordered form
+#pragma unroll
+    for (int w = 0; w < kSelWaves; ++w) bound = max(bound, ss.tw[w]);
+    // 2. survivors: scores >= bound (none of the others can be among the
+    // tile's K largest), then the winners kept so far
+    const int nprev = ss.nkey;
+    {
+      uint32_t sm = 0u;
+#pragma unroll
+      for (int j = 0; j < kSelVPT; ++j) sm |= ord[j] >= bound ? (1u << j) : 0u;
+      int pos = sm ? atomicAdd(&ss.nsurv, __popc(sm)) : 0;  // one LDS atomic per thread
+#pragma unroll
+      for (int j = 0; j < kSelVPT; ++j) {
+        if ((sm >> j) & 1u) {
+          if (pos < kSurvMax) ss.surv[pos] = sel_key(ord[j], tile0 + j * kDecThreads + t);
+          ++pos;
+        }
+      }
+    }
+    __syncthreads();
+    const int ns = ss.nsurv;
+    if (ns <= kSurvMax) {
+      if (t < nprev) ss.surv[ns + t] = ss.key[t];
+      __syncthreads();
+      if (wave == 0) {
+        const int tot = ns + nprev;
+        if (tot <= 64)
+          select_survivors<1>(ss, tot, K);
+        else
+          select_survivors<kSurvNJ>(ss, tot, K);
+      }
+      __syncthreads();
+    } else {
+      // 3. many scores at the bound: the exact block-wide search, on the
+      // tile's scores read again
+      uint32_t ord2[kSelVPT];
+#pragma unroll
+      for (int j = 0; j < kSelVPT; ++j) {
+        const int c = tile0 + j * kDecThreads + t;
+        const float v = sig[c < n ? c : 0];
+        ord2[j] = c < n ? orderable(v) : 0u;
+      }
+      tile_select_exact(ord2, tile0, K, ss, slot);
+    }
+  }
+  // rank the winners: position = number of larger keys
+  const int keep = ss.nkey;
+  if (t < keep) {
+    const unsigned long long k0 = ss.key[t];
+    int r = 0;
+    for (int e = 0; e < keep; ++e) r += ss.key[e] > k0 ? 1 : 0;
+    ss.sorted[r] = k0;
+  }
+  __syncthreads();
+  return keep;
+}
+
+// D2: every slot workgroup of (b, g) selects the top-K from the group scores
+// (the same arithmetic in each, so they agree), slot 0 writes the lists,
+// and slot k attends the chunk of rank k; the last workgroup combines the
+// chunk and window partials in slot order.
 template <typename T, int D>
 __global__ void __launch_bounds__(kDecThreads)
 decode_attend_kernel(DecodeArgs a) {
   __shared__ UnitSmem<T, D> us;
+  __shared__ SelSmem ss;
   __shared__ int is_last;
   const int g = blockIdx.y, b = blockIdx.z, slot = blockIdx.x, t = threadIdx.x;
   const int G = a.Hq / a.Hkv, K = a.K;
   const int seq = clamp_seq(a.seq_lens, b, a.Tmax, a.err, false);
   const int i = seq - 1;
-  (void)i;
-  float *recs = a.parts + (static_cast<size_t>(b) * a.Hkv + g) * a.nslots * G * (D + 2);
-  if (slot < K) {
+  const int n = eligible_chunks(i, a.W, a.S);
+  const size_t bg = static_cast<size_t>(b) * a.Hkv + g;
+  float *recs = a.parts + bg * a.nslots * G * (D + 2);
+  if (K > 0) {
+    const int keep = block_topk(a.sig + bg * a.Cmax, n, K, ss);
+    if (slot == 0) {
+      // the lists: chunk ids, and each head's own score, in rank order
+      for (int x = t; x < K; x += kDecThreads)
+        a.topk_idx[bg * K + x] = x < keep ? static_cast<int>(~static_cast<uint32_t>(ss.sorted[x])) : -1;
+      for (int x = t; x < K * G; x += kDecThreads) {
+        const int k = x / G, hh = x % G;
+        const int c = k < keep ? static_cast<int>(~static_cast<uint32_t>(ss.sorted[k])) : -1;
+        a.topk_score[(static_cast<size_t>(b) * a.Hq + g * G + hh) * K + k] =
+            c >= 0 ? a.hsc[(bg * a.Cmax + c) * G + hh] : -INFINITY;
+      }
+    }
     float *rec = recs + static_cast<size_t>(slot) * G * (D + 2);
-    const int c = a.topk_idx[(static_cast<size_t>(b) * a.Hkv + g) * K + slot];
+    const int c = slot < keep ? static_cast<int>(~static_cast<uint32_t>(ss.sorted[slot])) : -1;
     if (c < 0) {
       for (int hh = t; hh < G; hh += kDecThreads) { publish(rec + hh * (D + 2), -INFINITY); publish(rec + hh * (D + 2) + 1, 0.f); }
     } else {
       load_q_rows<T, D>(us, static_cast<const T *>(a.q) + (static_cast<size_t>(b) * a.Hq + g * G) * D, D, G);
       __syncthreads();
-      const T *kc = static_cast<const T *>(a.k_cache) + ((static_cast<size_t>(b) * a.Hkv + g) * a.Tmax + static_cast<size_t>(c) * a.S) * D;
-      const T *vc = static_cast<const T *>(a.v_cache) + ((static_cast<size_t>(b) * a.Hkv + g) * a.Tmax + static_cast<size_t>(c) * a.S) * D;
+      const T *kc = static_cast<const T *>(a.k_cache) + (bg * a.Tmax + static_cast<size_t>(c) * a.S) * D;
+      const T *vc = static_cast<const T *>(a.v_cache) + (bg * a.Tmax + static_cast<size_t>(c) * a.S) * D;
       constexpr int NP = pairs_per_thread<D>();
       float2 ou[NP];
       attend_unit<T, D>(us, kc, vc, a.S, G, a.tau, ou);
@@ -391,13 +546,13 @@ decode_attend_kernel(DecodeArgs a) {
           const float inv = 1.f / us.l[hh];
           publish(rh + 2 + 2 * e2, ou[r].x * inv);
           publish(rh + 3 + 2 * e2, ou[r].y * inv);
-          if (e2 == 0) { publish(rh, a.topk_score[(static_cast<size_t>(b) * a.Hq + g * G + hh) * K + slot]); publish(rh + 1, 1.f); }
+          if (e2 == 0) { publish(rh, a.hsc[(bg * a.Cmax + c) * G + hh]); publish(rh + 1, 1.f); }
         }
       }
     }
   }
   {
-    const unsigned before = arrive(a.count2 + b * a.Hkv + g);
+    const unsigned before = arrive(a.count + b * a.Hkv + g);
     if (t == 0) is_last = (before == static_cast<unsigned>(a.nslot_blocks - 1));
   }
   __syncthreads();
@@ -405,7 +560,7 @@ decode_attend_kernel(DecodeArgs a) {
   // combine every slot (chunks 0..K-1, window units K..) in slot order
   combine_slots<T, D>(recs, a.nslots, G, reinterpret_cast<float *>(us.v),
                       static_cast<T *>(a.o) + (static_cast<size_t>(b) * a.Hq + g * G) * D);
-  if (t == 0) reset_counter(a.count2 + b * a.Hkv + g);
+  if (t == 0) reset_counter(a.count + b * a.Hkv + g);
 }
 
 // ------------------------------------------------------------------ dense comparator
@@ -464,23 +619,6 @@ dense_decode_kernel(DenseArgs a) {
 }
 
 // ------------------------------------------------------------------ launchers
-template <typename T, int D, bool QCAL, int SNJ, int MNJ>
-static void launch_d1(const DecodeArgs &a, hipStream_t st) {
-  decode_score_kernel<T, D, QCAL, SNJ, MNJ><<<dim3(a.P + a.NW, a.Hkv, a.B), kDecThreads, 0, st>>>(a);
-}
-
-// slice width SNJ = CPB / 64 in {1, 4, 16}; merge width MNJ = P*K / 256 rounded up to {4, 8, 16}
-template <typename T, int D, bool QCAL>
-static void dispatch_d1(const DecodeArgs &a, hipStream_t st) {
-  const int snj = a.CPB / 64, mnj_need = (a.P * a.K + kDecThreads - 1) / kDecThreads;
-  const int mnj = mnj_need <= 4 ? 4 : (mnj_need <= 8 ? 8 : 16);
-#define HILS_D1(S_, M_) \
-  if (snj == S_ && mnj == M_) return launch_d1<T, D, QCAL, S_, M_>(a, st);
-  HILS_D1(1, 4) HILS_D1(1, 8) HILS_D1(1, 16) HILS_D1(4, 4) HILS_D1(4, 8) HILS_D1(4, 16)
-  HILS_D1(16, 4) HILS_D1(16, 8) HILS_D1(16, 16)
-#undef HILS_D1
-}
-
 template <typename T, int D>
 static hipError_t decode_t(const DecodeArgs &a, hipStream_t st) {
   if (a.r > 0) {
@@ -489,9 +627,9 @@ static hipError_t decode_t(const DecodeArgs &a, hipStream_t st) {
         static_cast<const T *>(a.w_up), a.qhat, a.Hq, a.r, a.Dh);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    dispatch_d1<T, D, true>(a, st);
+    decode_score_kernel<T, D, true><<<dim3(a.P + a.NW, a.Hkv, a.B), kDecThreads, 0, st>>>(a);
   } else {
-    dispatch_d1<T, D, false>(a, st);
+    decode_score_kernel<T, D, false><<<dim3(a.P + a.NW, a.Hkv, a.B), kDecThreads, 0, st>>>(a);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

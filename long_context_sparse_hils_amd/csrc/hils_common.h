@@ -149,6 +149,29 @@ __device__ __forceinline__ uint32_t uprefix_rows4(uint32_t v) {
   return ((row & 1) ? static_cast<uint32_t>(r[0]) : 0u) + ((row & 2) ? static_cast<uint32_t>(s[0]) : 0u);
 }
 
+// Whole-wave min / max / sum of a uint32 without LDS traffic: DPP moves
+// inside each row of 16 lanes (xor 1, xor 2, then the half-row and row
+// mirrors), then the row swaps across the four rows.
+template <int OP, int CTRL>
+__device__ __forceinline__ uint32_t dpp_combine(uint32_t v) {
+  const uint32_t o = static_cast<uint32_t>(
+      __builtin_amdgcn_update_dpp(static_cast<int>(v), static_cast<int>(v), CTRL, 0xF, 0xF, false));
+  return OP == 0 ? min(v, o) : OP == 1 ? max(v, o) : v + o;
+}
+template <int OP>  // 0: min, 1: max, 2: sum
+__device__ __forceinline__ uint32_t wave_reduce_u32(uint32_t v) {
+  v = dpp_combine<OP, 0xB1>(v);   // quad_perm [1,0,3,2]
+  v = dpp_combine<OP, 0x4E>(v);   // quad_perm [2,3,0,1]
+  v = dpp_combine<OP, 0x141>(v);  // row_half_mirror
+  v = dpp_combine<OP, 0x140>(v);  // row_mirror
+  auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  const uint32_t a = r[0], b = r[1];
+  v = OP == 0 ? min(a, b) : OP == 1 ? max(a, b) : a + b;
+  auto q = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  const uint32_t c = q[0], d = q[1];
+  return OP == 0 ? min(c, d) : OP == 1 ? max(c, d) : c + d;
+}
+
 __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) {
@@ -241,11 +264,8 @@ __device__ __forceinline__ void wave_select(const uint32_t (&ord)[NJ], const int
     hi = max(hi, ord[j]);
     lo = min(lo, ord[j] != 0u ? ord[j] : 0xFFFFFFFFu);
   }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) {
-    lo = min(lo, static_cast<uint32_t>(__shfl_xor(static_cast<int>(lo), o, kWave)));
-    hi = max(hi, static_cast<uint32_t>(__shfl_xor(static_cast<int>(hi), o, kWave)));
-  }
+  lo = wave_reduce_u32<0>(lo);
+  hi = wave_reduce_u32<1>(hi);
   const int keep = min(k, avail);
   uint32_t theta = 0u;
   bool exact = false;  // exactly `keep` keys are >= theta

@@ -47,12 +47,12 @@ struct DecodeArgs {
   int32_t *topk_idx;
   float *topk_score;
   float *qhat;                   // [B, Hq, d] (Q-Cal only)
-  unsigned long long *cand_key;  // [B, Hkv, P, K]
-  float *cand_s;                 // [B, Hkv, P, K, G]
+  float *sig;                    // [B, Hkv, Cmax]: group score of each eligible chunk
+  float *hsc;                    // [B, Hkv, Cmax, G]: each head's own score
   float *parts;                  // [B, Hkv, nslots, G, d+2]
-  unsigned *count1, *count2, *err;
+  unsigned *count, *err;
   int B, Tmax, Hq, Hkv, d, S, K, W, r, Dh, Cmax;
-  int P, CPB, NW, nslots, nslot_blocks;
+  int P, NW, nslots, nslot_blocks;
   float tau;
   bool bf16;
 };

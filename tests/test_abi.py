@@ -120,7 +120,7 @@ def test_workspace_sizes_scale_with_the_problem():
     assert big > small > 0
     # 4M tokens still fits the merge capacity with top-16
     assert hils.hils_decode_workspace_bytes(_cfg(batch=1, seq_len=4194304, qcal_rank=0)) > 0
-    assert hils.hils_decode_error_offset(_cfg(batch=3, n_kv_heads=8)) == 4 * 2 * 3 * 8
+    assert hils.hils_decode_error_offset(_cfg(batch=3, n_kv_heads=8)) == 4 * 3 * 8
 
 
 def test_invalid_config_gives_zero_workspace():
