@@ -189,6 +189,28 @@ def test_decode_parity(name):
     print(f"{name}: near-tie rows {ties}")
 
 
+def test_decode_all_scores_tied():
+    """Every key equal: every chunk summary, hence every group score, is the
+    same, so the selection is decided by the tie rule alone (lowest chunk
+    first) over hundreds of equal scores."""
+    wl = wl_decode(B=2, T=32768, Hq=4, Hkv=1, d=64, K=8, W=128, needles="none")
+    sl = np.array([32768, 20000], dtype=np.int32)
+    inp = hs.decode_inputs(wl, 909, seq_lens=sl)
+    kc = inp["k_cache"]
+    inp["k_cache"] = np.ascontiguousarray(np.broadcast_to(kc[:, :, :1], kc.shape))
+    oc = ocfg(wl)
+    ks64, bs64 = oracle.summary(oc, inp["k_cache"], inp["q_lm"])
+    ks, bs = oracle.store(oc, ks64), bs64.astype(np.float32)
+    d = upload(inp)
+    res = gpu_decode(wl.config_dict(), d, dev(ks), dev(bs), d["seq_lens"])
+    r = oracle.decode(oc, inp, ks, bs)
+    gidx = host(res["idx"])
+    assert (gidx == r["idx"]).all()
+    assert (gidx[..., :wl.top_k] == np.arange(wl.top_k)).all()
+    check_scores(host(res["tsc"]), r["tsc"], gidx, r["idx"], wl.group)
+    check_out(host(res["o"]), r["o"], wl.dtype)
+
+
 def test_decode_matches_prefill_row():
     """A GPU decode step at seq_len = i+1 on the prefill's K/V and summaries
     selects what the GPU prefill selected for row i."""
