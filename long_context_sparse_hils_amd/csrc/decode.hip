@@ -95,7 +95,7 @@ decode_score_kernel(DecodeArgs a) {
     const int j0 = n * a.S + u * kUnitKeys;
     float *rec = a.parts + ((static_cast<size_t>(b) * a.Hkv + g) * a.nslots + K + u) * G * (D + 2);
     if (j0 > i) {
-      for (int hh = t; hh < G; hh += kDecThreads) { publish(rec + hh * (D + 2), -INFINITY); publish(rec + hh * (D + 2) + 1, 0.f); }
+      for (int hh = t; hh < G; hh += kDecThreads) publish2(rec + hh * (D + 2), -INFINITY, 0.f);
       return;
     }
     const int nk = min(kUnitKeys, i - j0 + 1);
@@ -109,9 +109,8 @@ decode_score_kernel(DecodeArgs a) {
       const int pr = t + r * kUnitThreads, hh = pr / (D / 2), e2 = pr % (D / 2);
       if (hh < G) {
         float *rh = rec + hh * (D + 2);
-        publish(rh + 2 + 2 * e2, ou[r].x);
-        publish(rh + 3 + 2 * e2, ou[r].y);
-        if (e2 == 0) { publish(rh, us.m[hh]); publish(rh + 1, us.l[hh]); }
+        publish2(rh + 2 + 2 * e2, ou[r].x, ou[r].y);
+        if (e2 == 0) publish2(rh, us.m[hh], us.l[hh]);
       }
     }
     return;
@@ -124,7 +123,10 @@ decode_score_kernel(DecodeArgs a) {
   constexpr int RPP = static_cast<int>(sizeof(T)) / 2;  // 16-byte loads per 8-element piece
   constexpr int U = 8 / RPP;                         // pieces in flight per thread
   constexpr int RS = U * kDecThreads / LPH;          // rows per batch
-  const int nrows = nch * G;
+  // rows are (head, chunk) in head-major order, row = hh * kCPB + cl: the 4
+  // rows one load instruction covers are 1 KB of one head's contiguous
+  // summaries
+  const int nrows = nch > 0 ? G * kCPB : 0;
   const T *ks = static_cast<const T *>(a.k_sum);
   const size_t hbase = static_cast<size_t>(b) * a.Hq + g * G;
   // Batches of RS rows, double buffered in registers: the loads of batch
@@ -139,8 +141,8 @@ decode_score_kernel(DecodeArgs a) {
     for (int u = 0; u < U; ++u) {
       const int p = u * kDecThreads + t;
       const int row = rb + p / LPH, seg = p % LPH;
-      const int rr = row < nrows ? row : 0;
-      const int cl = rr / G, hh = rr % G;
+      const int rr = (row < nrows && (row & (kCPB - 1)) < nch) ? row : 0;
+      const int cl = rr & (kCPB - 1), hh = rr / kCPB;
       const size_t ro = (hbase + hh) * a.Cmax + c0 + cl;
 #pragma unroll
       for (int r = 0; r < RPP; ++r) kv[u * RPP + r] = reinterpret_cast<const uint4 *>(ks + ro * D + seg * 8)[r];
@@ -152,7 +154,7 @@ decode_score_kernel(DecodeArgs a) {
     for (int u = 0; u < U; ++u) {
       const int p = u * kDecThreads + t;
       const int row = rb + p / LPH, seg = p % LPH;
-      const int hh = (row < nrows) ? row % G : 0;
+      const int hh = (row < nrows) ? row / kCPB : 0;
       float kf[8];
       Elem<T>::load8(reinterpret_cast<const T *>(&kv[u * RPP]), kf);
       const float *qv = sm.qh + hh * D + seg * 8;
@@ -160,7 +162,7 @@ decode_score_kernel(DecodeArgs a) {
 #pragma unroll
       for (int x = 0; x < 8; ++x) part += qv[x] * kf[x];
       const float dot = dpp_group_sum<LPH>(part);
-      if (seg == 0 && row < nrows) sm.s[row] = a.tau * dot + bs[u];
+      if (seg == 0 && row < nrows && (row & (kCPB - 1)) < nch) sm.s[row] = a.tau * dot + bs[u];
     }
   };
   {
@@ -185,15 +187,14 @@ decode_score_kernel(DecodeArgs a) {
     }
   }
   __syncthreads();
-  // sigma and the per-head scores of the slice's chunks: rows are (chunk,
-  // head) in chunk-major order, as hsc stores them
+  // sigma and the per-head scores of the slice's chunks (hsc is chunk-major)
   const size_t bg = static_cast<size_t>(b) * a.Hkv + g;
   for (int cl = t; cl < nch; cl += kDecThreads) {
     float m = -INFINITY;
-    for (int hh = 0; hh < G; ++hh) m = fmaxf(m, sm.s[cl * G + hh]);
+    for (int hh = 0; hh < G; ++hh) m = fmaxf(m, sm.s[hh * kCPB + cl]);
     a.sig[bg * a.Cmax + c0 + cl] = m;
   }
-  for (int x = t; x < nrows; x += kDecThreads) a.hsc[(bg * a.Cmax + c0) * G + x] = sm.s[x];
+  for (int x = t; x < nch * G; x += kDecThreads) a.hsc[(bg * a.Cmax + c0) * G + x] = sm.s[(x % G) * kCPB + x / G];
 }
 
 // ------------------------------------------------------------------ combine
@@ -206,10 +207,34 @@ __device__ __forceinline__ void combine_slots(const float *recs, int nslots, int
   const int t = threadIdx.x;
   float *w = scratch;                  // [nslots * G]: e^{m - M}
   float *lt = scratch + nslots * G;    // [G]: sum w * l
-  for (int x = t; x < nslots * G; x += kDecThreads) {
-    const float *rh = recs + static_cast<size_t>(x) * (D + 2);
-    w[x] = load_acquired(rh);
-    scratch[nslots * G + G + x] = load_acquired(rh + 1);
+  float *lv = scratch + nslots * G + G;  // [nslots * G]: l
+  // Loads first, in one round trip: (m, l) of every (slot, head), then the
+  // o pairs of every slot for this thread's first output pair (8-byte
+  // loads; no lane-dependent branch: a thread past the outputs re-reads
+  // pair 0).  The (m, l) loads are older, so the weights wait only for them.
+  constexpr int kPre = 32;
+  const int nml = nslots * G, npairs = G * D / 2, npre = min(nslots, kPre);
+  float2 ml[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int x = t + u * kDecThreads;
+    ml[u] = load_acquired2(recs + static_cast<size_t>(x < nml ? x : 0) * (D + 2));
+  }
+  const int p0 = t < npairs ? t : 0;
+  const int hh0 = p0 / (D / 2), e20 = p0 % (D / 2);
+  float2 ov[kPre];
+#pragma unroll
+  for (int q = 0; q < kPre; ++q)
+    if (q < npre) ov[q] = load_acquired2(recs + (static_cast<size_t>(q) * G + hh0) * (D + 2) + 2 + 2 * e20);
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int x = t + u * kDecThreads;
+    if (x < nml) { w[x] = ml[u].x; lv[x] = ml[u].y; }
+  }
+  for (int x = t + 2 * kDecThreads; x < nml; x += kDecThreads) {  // more than 2 per thread
+    const float2 v = load_acquired2(recs + static_cast<size_t>(x) * (D + 2));
+    w[x] = v.x;
+    lv[x] = v.y;
   }
   __syncthreads();
   for (int hh = t; hh < G; hh += kDecThreads) {
@@ -220,26 +245,36 @@ __device__ __forceinline__ void combine_slots(const float *recs, int nslots, int
       const float m = w[s * G + hh];
       const float e = (m == -INFINITY) ? 0.f : __expf(m - M);
       w[s * G + hh] = e;
-      L += e * scratch[nslots * G + G + s * G + hh];
+      L += e * lv[s * G + hh];
     }
     lt[hh] = L;
   }
   __syncthreads();
-  // every slot's o value of the thread's output: loads issued together
-  constexpr int kPre = 32;
-  for (int x = t; x < G * D; x += kDecThreads) {
-    const int hh = x / D, e = x % D;
-    float acc = 0.f;
-    for (int s0 = 0; s0 < nslots; s0 += kPre) {
-      float ov[kPre];
+  for (int p = t; p < npairs; p += kDecThreads) {
+    const int hh = p / (D / 2), e2 = p % (D / 2);
+    float2 acc = make_float2(0.f, 0.f);
+    if (p == t) {
 #pragma unroll
       for (int q = 0; q < kPre; ++q)
-        if (s0 + q < nslots) ov[q] = load_acquired(recs + (static_cast<size_t>(s0 + q) * G + hh) * (D + 2) + 2 + e);
-#pragma unroll
-      for (int q = 0; q < kPre; ++q)
-        if (s0 + q < nslots) acc += w[(s0 + q) * G + hh] * ov[q];
+        if (q < npre) {
+          const float wq = w[q * G + hh];
+          acc.x += wq * ov[q].x;
+          acc.y += wq * ov[q].y;
+        }
+    } else {
+      for (int q = 0; q < npre; ++q) {
+        const float2 v = load_acquired2(recs + (static_cast<size_t>(q) * G + hh) * (D + 2) + 2 + 2 * e2);
+        acc.x += w[q * G + hh] * v.x;
+        acc.y += w[q * G + hh] * v.y;
+      }
     }
-    Elem<T>::store(out, static_cast<size_t>(hh) * D + e, acc / lt[hh]);
+    for (int q = npre; q < nslots; ++q) {
+      const float2 v = load_acquired2(recs + (static_cast<size_t>(q) * G + hh) * (D + 2) + 2 + 2 * e2);
+      acc.x += w[q * G + hh] * v.x;
+      acc.y += w[q * G + hh] * v.y;
+    }
+    const float inv = 1.f / lt[hh];
+    Elem<T>::store2(out + static_cast<size_t>(hh) * D + 2 * e2, acc.x * inv, acc.y * inv);
   }
 }
 
@@ -514,6 +549,8 @@ decode_attend_kernel(DecodeArgs a) {
   const size_t bg = static_cast<size_t>(b) * a.Hkv + g;
   float *recs = a.parts + bg * a.nslots * G * (D + 2);
   if (K > 0) {
+    // the query rows go to LDS while the group scores are loaded
+    load_q_rows<T, D>(us, static_cast<const T *>(a.q) + (static_cast<size_t>(b) * a.Hq + g * G) * D, D, G);
     const int keep = block_topk(a.sig + bg * a.Cmax, n, K, ss);
     if (slot == 0) {
       // the lists: chunk ids, and each head's own score, in rank order
@@ -529,10 +566,8 @@ decode_attend_kernel(DecodeArgs a) {
     float *rec = recs + static_cast<size_t>(slot) * G * (D + 2);
     const int c = slot < keep ? static_cast<int>(~static_cast<uint32_t>(ss.sorted[slot])) : -1;
     if (c < 0) {
-      for (int hh = t; hh < G; hh += kDecThreads) { publish(rec + hh * (D + 2), -INFINITY); publish(rec + hh * (D + 2) + 1, 0.f); }
+      for (int hh = t; hh < G; hh += kDecThreads) publish2(rec + hh * (D + 2), -INFINITY, 0.f);
     } else {
-      load_q_rows<T, D>(us, static_cast<const T *>(a.q) + (static_cast<size_t>(b) * a.Hq + g * G) * D, D, G);
-      __syncthreads();
       const T *kc = static_cast<const T *>(a.k_cache) + (bg * a.Tmax + static_cast<size_t>(c) * a.S) * D;
       const T *vc = static_cast<const T *>(a.v_cache) + (bg * a.Tmax + static_cast<size_t>(c) * a.S) * D;
       constexpr int NP = pairs_per_thread<D>();
@@ -544,9 +579,8 @@ decode_attend_kernel(DecodeArgs a) {
         if (hh < G) {
           float *rh = rec + hh * (D + 2);
           const float inv = 1.f / us.l[hh];
-          publish(rh + 2 + 2 * e2, ou[r].x * inv);
-          publish(rh + 3 + 2 * e2, ou[r].y * inv);
-          if (e2 == 0) { publish(rh, a.hsc[(bg * a.Cmax + c) * G + hh]); publish(rh + 1, 1.f); }
+          publish2(rh + 2 + 2 * e2, ou[r].x * inv, ou[r].y * inv);
+          if (e2 == 0) publish2(rh, a.hsc[(bg * a.Cmax + c) * G + hh], 1.f);
         }
       }
     }
@@ -578,7 +612,7 @@ dense_decode_kernel(DenseArgs a) {
   const int j_lo = p * a.L, j_hi = min(i + 1, (p + 1) * a.L);
   constexpr int NP = pairs_per_thread<D>();
   if (j_lo >= j_hi) {
-    for (int hh = t; hh < G; hh += kDecThreads) { publish(rec + hh * (D + 2), -INFINITY); publish(rec + hh * (D + 2) + 1, 0.f); }
+    for (int hh = t; hh < G; hh += kDecThreads) publish2(rec + hh * (D + 2), -INFINITY, 0.f);
   } else {
     load_q_rows<T, D>(us, static_cast<const T *>(a.q) + (static_cast<size_t>(b) * a.Hq + g * G) * D, D, G);
     __syncthreads();
@@ -601,9 +635,8 @@ dense_decode_kernel(DenseArgs a) {
       const int pr = t + r * kUnitThreads, hh = pr / (D / 2), e2 = pr % (D / 2);
       if (hh < G) {
         float *rh = rec + hh * (D + 2);
-        publish(rh + 2 + 2 * e2, acc.o[r].x);
-        publish(rh + 3 + 2 * e2, acc.o[r].y);
-        if (e2 == 0) { publish(rh, acc.m[r]); publish(rh + 1, acc.l[r]); }
+        publish2(rh + 2 + 2 * e2, acc.o[r].x, acc.o[r].y);
+        if (e2 == 0) publish2(rh, acc.m[r], acc.l[r]);
       }
     }
   }

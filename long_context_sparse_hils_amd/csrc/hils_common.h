@@ -217,6 +217,17 @@ __device__ __forceinline__ void publish(float *p, float v) {
 __device__ __forceinline__ void publish(unsigned long long *p, unsigned long long v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// Two adjacent floats (8-byte aligned) in one write-through store / load.
+__device__ __forceinline__ void publish2(float *p, float x, float y) {
+  const unsigned long long v = static_cast<unsigned long long>(__float_as_uint(x)) |
+                               (static_cast<unsigned long long>(__float_as_uint(y)) << 32);
+  __hip_atomic_store(reinterpret_cast<unsigned long long *>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float2 load_acquired2(const float *p) {
+  const unsigned long long v =
+      __hip_atomic_load(reinterpret_cast<const unsigned long long *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return make_float2(__uint_as_float(static_cast<uint32_t>(v)), __uint_as_float(static_cast<uint32_t>(v >> 32)));
+}
 // Call from every thread after its publish() stores: returns, in thread 0 of
 // the workgroup, the number of workgroups that arrived before this one.
 __device__ __forceinline__ unsigned arrive(unsigned *counter) {
