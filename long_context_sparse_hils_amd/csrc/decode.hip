@@ -292,6 +292,7 @@ struct SelSmem {
   uint32_t red[2][kSelWaves];     // per-wave partial sums / minima, double buffered
   uint32_t red2[2][kSelWaves];
   int nkey, nsurv;
+  uint32_t sord[kDecThreads * kSelVPT];  // the tile's ordered scores (0 = none)
 };
 
 __device__ __forceinline__ unsigned long long sel_key(uint32_t ord, int c) {
@@ -399,30 +400,96 @@ __device__ __forceinline__ void tile_select_exact(const uint32_t (&ord)[kSelVPT]
   __syncthreads();
 }
 
+// The k-th largest of one ordered value per lane (0 = none), or 0 when
+// fewer than k lanes hold a value: a bitwise search from below the common
+// leading bits of the smallest and largest value, counting with ballots.
+__device__ __forceinline__ uint32_t wave_kth_u32(uint32_t v, int k) {
+  const int avail = __popcll(__ballot(v != 0u));
+  if (k <= 0 || avail < k) return 0u;
+  const uint32_t lo = wave_reduce_u32<0>(v != 0u ? v : 0xFFFFFFFFu), hi = wave_reduce_u32<1>(v);
+  const uint32_t spread = lo ^ hi;
+  if (!spread) return lo;
+  const int top = 31 - __clz(spread);
+  uint32_t theta = top == 31 ? 0u : lo & ~((2u << top) - 1u);
+  for (int bit = top; bit >= 0; --bit) {
+    const uint32_t cand = theta | (1u << bit);
+    if (__popcll(__ballot(v >= cand)) >= k) theta = cand;
+  }
+  return theta;
+}
+
 // One wave selects the top-K of the tot survivor keys in ss.surv into
-// ss.key (rank order), ss.nkey.
+// ss.key (unordered; block_topk ranks them) and ss.nkey: the K-th largest
+// key by a bitwise search over the 64-bit keys' ordered-score word, every
+// key above it, and the lowest chunks tied at it.
 template <int NJ>
 __device__ __forceinline__ void select_survivors(SelSmem &ss, int tot, int K) {
   const int lane = threadIdx.x & 63;
   uint32_t so[NJ];
   int si[NJ];
-  bool sw[NJ];
-  int sr[NJ];
+  int avail = 0;
+  uint32_t lo = 0xFFFFFFFFu, hi = 0u;
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
     const int x = j * 64 + lane;
     const unsigned long long kk = x < tot ? ss.surv[x] : 0ull;
     so[j] = static_cast<uint32_t>(kk >> 32);
     si[j] = x < tot ? static_cast<int>(~static_cast<uint32_t>(kk)) : 0x7FFFFFFF;
+    avail += __popcll(__ballot(so[j] != 0u));
+    lo = min(lo, so[j] != 0u ? so[j] : 0xFFFFFFFFu);
+    hi = max(hi, so[j]);
   }
-  wave_select<NJ>(so, si, K, sw, sr, ss.wkey[0]);
-  int nw = 0;
+  const int keep = min(K, avail);
+  lo = wave_reduce_u32<0>(lo);
+  hi = wave_reduce_u32<1>(hi);
+  uint32_t theta = 0u;
+  bool exact = false;
+  if (keep > 0) {
+    const uint32_t spread = lo ^ hi;
+    const int top = spread ? 31 - __clz(spread) : -1;
+    theta = top < 0 ? lo : (top == 31 ? 0u : lo & ~((2u << top) - 1u));
+    for (int bit = top; bit >= 0; --bit) {
+      const uint32_t cand = theta | (1u << bit);
+      int cnt = 0;
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) cnt += __popcll(__ballot(so[j] >= cand));
+      if (cnt >= keep) {
+        theta = cand;
+        if (cnt == keep) {
+          exact = true;
+          break;
+        }
+      }
+    }
+    if (top < 0) exact = avail == keep;
+  }
+  bool w[NJ];
+  int ngt = 0;
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
-    if (sw[j]) ss.key[sr[j]] = sel_key(so[j], si[j]);
-    nw += __popcll(__ballot(sw[j]));
+    w[j] = keep > 0 && so[j] != 0u && (exact ? so[j] >= theta : so[j] > theta);
+    ngt += __popcll(__ballot(w[j]));
   }
-  if (lane == 0) ss.nkey = nw;
+  for (int need = keep - ngt; need > 0; --need) {  // ties at theta: lowest chunk first
+    int best = 0x7FFFFFFF;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+      if (!w[j] && so[j] == theta && so[j] != 0u) best = min(best, si[j]);
+    best = static_cast<int>(wave_reduce_u32<0>(static_cast<uint32_t>(best)));
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+      if (!w[j] && so[j] == theta && si[j] == best) w[j] = true;
+  }
+  int base = 0;
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const unsigned long long m = __ballot(w[j]);
+    const int below = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
+                                                __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
+    if (w[j]) ss.key[base + below] = sel_key(so[j], si[j]);
+    base += __popcll(m);
+  }
+  if (lane == 0) ss.nkey = base;
 }
 
 // Block-wide top-K of the group scores sigma[0..n) by (sigma desc, chunk
@@ -452,25 +519,17 @@ __device__ __forceinline__ int block_topk(const float *sig, int n, int K, SelSme
       const int c = tile0 + j * kDecThreads + t;
       sv[j] = sig[c < n ? c : 0];
     }
-    uint32_t ord[kSelVPT];
     uint32_t mx = 0u;
 #pragma unroll
     for (int j = 0; j < kSelVPT; ++j) {
-      ord[j] = tile0 + j * kDecThreads + t < n ? orderable(sv[j]) : 0u;  // 0: no candidate
-      mx = max(mx, ord[j]);
+      const uint32_t o = tile0 + j * kDecThreads + t < n ? orderable(sv[j]) : 0u;  // 0: no candidate
+      ss.sord[j * kDecThreads + t] = o;
+      mx = max(mx, o);
     }
     // 1. per-wave bound: the K-th largest lane maximum (0 = no bound)
     {
-      const uint32_t mo[1] = {mx};
-      const int mi[1] = {lane};
-      bool mw[1];
-      int mr[1];
-      const int nvalid = __popcll(__ballot(mx != 0u));
-      wave_select<1>(mo, mi, K, mw, mr, ss.wkey[wave]);
-      const bool kth = nvalid >= K && mw[0] && mr[0] == K - 1;
-      if (lane == 0) ss.tw[wave] = 0u;
-      __builtin_amdgcn_wave_barrier();
-      if (kth) ss.tw[wave] = mx;
+      const uint32_t kth = wave_kth_u32(mx, K);
+      if (lane == 0) ss.tw[wave] = kth;
     }
     if (t == 0) ss.nsurv = 0;
     __syncthreads();
@@ -481,14 +540,16 @@ __device__ __forceinline__ int block_topk(const float *sig, int n, int K, SelSme
     // tile's K largest), then the winners kept so far
     const int nprev = ss.nkey;
     {
-      uint32_t sm = 0u;
+      // (a thread holds a survivor only when its lane maximum reaches the bound)
+      if (mx >= bound) {
+        uint32_t sm = 0u;
 #pragma unroll
-      for (int j = 0; j < kSelVPT; ++j) sm |= ord[j] >= bound ? (1u << j) : 0u;
-      int pos = sm ? atomicAdd(&ss.nsurv, __popc(sm)) : 0;  // one LDS atomic per thread
-#pragma unroll
-      for (int j = 0; j < kSelVPT; ++j) {
-        if ((sm >> j) & 1u) {
-          if (pos < kSurvMax) ss.surv[pos] = sel_key(ord[j], tile0 + j * kDecThreads + t);
+        for (int j = 0; j < kSelVPT; ++j) sm |= ss.sord[j * kDecThreads + t] >= bound ? (1u << j) : 0u;
+        int pos = atomicAdd(&ss.nsurv, __popc(sm));  // one LDS atomic per such thread
+        while (sm) {
+          const int j = __ffs(sm) - 1;
+          sm &= sm - 1u;
+          if (pos < kSurvMax) ss.surv[pos] = sel_key(ss.sord[j * kDecThreads + t], tile0 + j * kDecThreads + t);
           ++pos;
         }
       }
