@@ -54,24 +54,23 @@ __device__ __forceinline__ void attend_unit(UnitSmem<T, D> &sm, const T *__restr
   constexpr int QD = D / 4;  // elements per quarter
   constexpr int VPT = kUnitKeys * D * static_cast<int>(sizeof(T)) / 16 / kUnitThreads;  // 16-B pieces per thread
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  // value rows: issue the loads first, park them in LDS after the logits
+  // value rows: issue the loads first, park them in LDS after the logits.
+  // No load sits under a lane-dependent branch (a lane past the unit reads
+  // piece / row 0 again; those values are zeroed or masked afterwards), so
+  // every load is in flight before the first is used.
   const int vpieces = nk * D * static_cast<int>(sizeof(T)) / 16;
   uint4 vreg[VPT];
 #pragma unroll
   for (int r = 0; r < VPT; ++r) {
     const int pc = t + r * kUnitThreads;
-    vreg[r] = pc < vpieces ? reinterpret_cast<const uint4 *>(vrow)[pc] : make_uint4(0, 0, 0, 0);
+    vreg[r] = reinterpret_cast<const uint4 *>(vrow)[pc < vpieces ? pc : 0];
   }
   {
     const int j = t >> 2, qq = t & 3;
     float kv[QD];
-    if (j < nk) {
+    const int jr = j < nk ? j : 0;
 #pragma unroll
-      for (int e8 = 0; e8 < QD / 8; ++e8) Elem<T>::load8(krow + static_cast<size_t>(j) * D + qq * QD + e8 * 8, kv + e8 * 8);
-    } else {
-#pragma unroll
-      for (int e = 0; e < QD; ++e) kv[e] = 0.f;
-    }
+    for (int e8 = 0; e8 < QD / 8; ++e8) Elem<T>::load8(krow + static_cast<size_t>(jr) * D + qq * QD + e8 * 8, kv + e8 * 8);
     for (int h = 0; h < G; ++h) {
       float acc = 0.f;
 #pragma unroll
@@ -81,13 +80,16 @@ __device__ __forceinline__ void attend_unit(UnitSmem<T, D> &sm, const T *__restr
     }
   }
 #pragma unroll
-  for (int r = 0; r < VPT; ++r) sm.v[t + r * kUnitThreads] = vreg[r];
+  for (int r = 0; r < VPT; ++r) {
+    const int pc = t + r * kUnitThreads;
+    sm.v[pc] = pc < vpieces ? vreg[r] : make_uint4(0, 0, 0, 0);
+  }
   __syncthreads();
   for (int h = wave; h < G; h += kUnitThreads / 64) {
     const float lam = sm.p[h][lane];
-    const float m = wave_max(lam);
+    const float m = wave_reduce_f32<1>(lam);
     const float e = (lam == -INFINITY) ? 0.f : __expf(lam - m);
-    const float l = wave_sum(e);
+    const float l = wave_reduce_f32<2>(e);
     sm.p[h][lane] = e;
     if (lane == 0) { sm.m[h] = m; sm.l[h] = l; }
   }
@@ -98,13 +100,21 @@ __device__ __forceinline__ void attend_unit(UnitSmem<T, D> &sm, const T *__restr
     const int h = pr / (D / 2), e2 = pr % (D / 2);
     float2 acc = make_float2(0.f, 0.f);
     if (h < G) {
+      // eight keys per step, their LDS reads issued together (keys past nk
+      // have p = 0 and zero value rows)
       const T *vs = reinterpret_cast<const T *>(sm.v);
-      for (int j = 0; j < nk; ++j) {
-        float v2[2];
-        Elem<T>::load2(vs + j * D + 2 * e2, v2);
-        const float pj = sm.p[h][j];
-        acc.x += pj * v2[0];
-        acc.y += pj * v2[1];
+      for (int j0 = 0; j0 < nk; j0 += 8) {
+        float v2[8][2], pj[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          Elem<T>::load2(vs + (j0 + u) * D + 2 * e2, v2[u]);
+          pj[u] = sm.p[h][j0 + u];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          acc.x += pj[u] * v2[u][0];
+          acc.y += pj[u] * v2[u][1];
+        }
       }
     }
     o[r] = acc;

@@ -172,6 +172,22 @@ __device__ __forceinline__ uint32_t wave_reduce_u32(uint32_t v) {
   return OP == 0 ? min(c, d) : OP == 1 ? max(c, d) : c + d;
 }
 
+// The same over floats (max or sum).
+template <int OP, int CTRL>
+__device__ __forceinline__ float dpp_combine_f(float v) {
+  const float o = __int_as_float(
+      __builtin_amdgcn_update_dpp(__float_as_int(v), __float_as_int(v), CTRL, 0xF, 0xF, false));
+  return OP == 1 ? fmaxf(v, o) : v + o;
+}
+template <int OP>  // 1: max, 2: sum
+__device__ __forceinline__ float wave_reduce_f32(float v) {
+  v = dpp_combine_f<OP, 0xB1>(v);
+  v = dpp_combine_f<OP, 0x4E>(v);
+  v = dpp_combine_f<OP, 0x141>(v);
+  v = dpp_combine_f<OP, 0x140>(v);
+  return OP == 1 ? max_rows4(v) : sum_rows4(v);
+}
+
 __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) {
