@@ -237,17 +237,23 @@ __device__ __forceinline__ void combine_slots(const float *recs, int nslots, int
     lv[x] = v.y;
   }
   __syncthreads();
-  for (int hh = t; hh < G; hh += kDecThreads) {
-    float M = -INFINITY;
-    for (int s = 0; s < nslots; ++s) M = fmaxf(M, w[s * G + hh]);
-    float L = 0.f;
-    for (int s = 0; s < nslots; ++s) {
-      const float m = w[s * G + hh];
-      const float e = (m == -INFINITY) ? 0.f : __expf(m - M);
-      w[s * G + hh] = e;
-      L += e * lv[s * G + hh];
+  // weights e^{m - M} and the normaliser per head: wave 0, slots over lanes
+  if ((t >> 6) == 0) {
+    const int lane = t & 63;
+    for (int hh = 0; hh < G; ++hh) {
+      float mloc = -INFINITY;
+      for (int s = lane; s < nslots; s += 64) mloc = fmaxf(mloc, w[s * G + hh]);
+      const float M = wave_reduce_f32<1>(mloc);
+      float lloc = 0.f;
+      for (int s = lane; s < nslots; s += 64) {
+        const float m = w[s * G + hh];
+        const float e = (m == -INFINITY) ? 0.f : __expf(m - M);
+        w[s * G + hh] = e;
+        lloc += e * lv[s * G + hh];
+      }
+      const float L = wave_reduce_f32<2>(lloc);
+      if (lane == 0) lt[hh] = L;
     }
-    lt[hh] = L;
   }
   __syncthreads();
   for (int p = t; p < npairs; p += kDecThreads) {
@@ -610,9 +616,23 @@ decode_attend_kernel(DecodeArgs a) {
   const size_t bg = static_cast<size_t>(b) * a.Hkv + g;
   float *recs = a.parts + bg * a.nslots * G * (D + 2);
   if (K > 0) {
-    // the query rows go to LDS while the group scores are loaded
-    load_q_rows<T, D>(us, static_cast<const T *>(a.q) + (static_cast<size_t>(b) * a.Hq + g * G) * D, D, G);
+    // the query rows are loaded (into registers) together with the group
+    // scores, and parked in LDS after the selection
+    constexpr int QPT = (kMaxG * D + kDecThreads - 1) / kDecThreads;
+    const T *qsrc = static_cast<const T *>(a.q) + (static_cast<size_t>(b) * a.Hq + g * G) * D;
+    float qreg[QPT];
+#pragma unroll
+    for (int r = 0; r < QPT; ++r) {
+      const int x = t + r * kDecThreads;
+      if (r * kDecThreads < G * D) qreg[r] = Elem<T>::load(qsrc, x < G * D ? x : 0);
+    }
     const int keep = block_topk(a.sig + bg * a.Cmax, n, K, ss);
+#pragma unroll
+    for (int r = 0; r < QPT; ++r) {
+      const int x = t + r * kDecThreads;
+      if (x < G * D) us.q[x / D][x % D] = qreg[r];
+    }
+    __syncthreads();
     if (slot == 0) {
       // the lists: chunk ids, and each head's own score, in rank order
       for (int x = t; x < K; x += kDecThreads)
