@@ -289,6 +289,8 @@ attn_prefill_mfma_kernel(AttnArgs a, int ntiles, int xcd_map, int nblk) {
   using C = AttnCfg<D, G, WAVES, TPW>;
   extern __shared__ __align__(16) unsigned char smem_raw[];
   AttnSmem<D, G, WAVES, TPW> &sm = *reinterpret_cast<AttnSmem<D, G, WAVES, TPW> *>(smem_raw);
+  // the rows' fusion scores [kQT * G * K] follow the struct
+  float *wl = reinterpret_cast<float *>(smem_raw + sizeof(AttnSmem<D, G, WAVES, TPW>));
 
   const int T = a.T, K = a.K, W = a.W, Hq = a.Hq, Hkv = a.Hkv;
   const int C_chunks = T / kItemKeys;  // chunk size S = 64 on this path
@@ -435,30 +437,57 @@ attn_prefill_mfma_kernel(AttnArgs a, int ntiles, int xcd_map, int nblk) {
     }
   }
 
+  // ---- the tile's fusion scores into LDS: wl[(q * G + hh) * K + k] =
+  // topk_score[b, g G + hh, q0 + q, k], all loads issued before any store
+  // (no lane-dependent branch around them), so the row statistics and the
+  // cursors below read LDS instead of making dependent global loads
+  const float *tsc_b = a.topk_score + static_cast<size_t>(b) * Hq * T * K;
+  {
+    constexpr int kWPT = (C::kQT * G * C::kKMax + C::kThreads - 1) / C::kThreads;
+    constexpr int kStep = kWPT < 8 ? kWPT : 8;  // loads in flight per thread
+    const int total = C::kQT * G * K;
+#pragma unroll
+    for (int r0 = 0; r0 < kWPT; r0 += kStep) {
+      float wv[kStep];
+#pragma unroll
+      for (int r = 0; r < kStep; ++r) {
+        const int x = tid + (r0 + r) * C::kThreads;
+        const int xc = x < total ? x : 0;
+        const int q = xc / (G * K), rem = xc % (G * K), hh = rem / K, k = rem % K;
+        const int i = min(q0 + q, T - 1);
+        if ((r0 + r) * C::kThreads < total) wv[r] = tsc_b[(static_cast<size_t>(g * G + hh) * T + i) * K + k];
+      }
+#pragma unroll
+      for (int r = 0; r < kStep; ++r) {
+        const int x = tid + (r0 + r) * C::kThreads;
+        if (x < total) wl[x] = wv[r];
+      }
+    }
+  }
+  __syncthreads();
+
   // ---- row statistics from the selected chunk scores, and each row's
   // cursor into its ascending selection list
   int cur[TPW], nxt_pos[TPW];
   float nxt_alpha[TPW];
-  // this row's fusion scores, indexed by top-K slot: a.topk_score + tsc_off[t]
-  const float *tsc_b = a.topk_score + static_cast<size_t>(b) * Hq * T * K;
-  int tsc_off[TPW];
+  int wrow[TPW];  // this row's fusion scores: wl + wrow[t], indexed by top-K slot
 #pragma unroll
   for (int t = 0; t < TPW; ++t) {
     const int qk = row_q[t] * C::kKMax;
-    tsc_off[t] = (row_h * T + (row_ok[t] ? q0 + row_q[t] : 0)) * K;
+    wrow[t] = (row_q[t] * G + (ln % G)) * K;
     float mx = -INFINITY;
     if (row_ok[t])
-      for (int k = 0; k < K && sm.spos[qk + k] != kNoPos; ++k) mx = fmaxf(mx, tsc_b[tsc_off[t] + sm.sk[qk + k]]);
+      for (int k = 0; k < K && sm.spos[qk + k] != kNoPos; ++k) mx = fmaxf(mx, wl[wrow[t] + sm.sk[qk + k]]);
     float l = 0.f;
     if (row_ok[t] && mx != -INFINITY)
-      for (int k = 0; k < K && sm.spos[qk + k] != kNoPos; ++k) l += __expf(tsc_b[tsc_off[t] + sm.sk[qk + k]] - mx);
+      for (int k = 0; k < K && sm.spos[qk + k] != kNoPos; ++k) l += __expf(wl[wrow[t] + sm.sk[qk + k]] - mx);
     R.m_row[t] = mx;
     R.l_row[t] = l;
 #pragma unroll
     for (int dt = 0; dt < C::kDT; ++dt) R.acc[t][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     cur[t] = 0;
     nxt_pos[t] = (row_ok[t] && K > 0) ? sm.spos[qk] : kNoPos;
-    nxt_alpha[t] = nxt_pos[t] != kNoPos ? tsc_b[tsc_off[t] + sm.sk[qk]] : 0.f;
+    nxt_alpha[t] = nxt_pos[t] != kNoPos ? wl[wrow[t] + sm.sk[qk]] : 0.f;
   }
 
   // ---- staging: item x -> LDS buffer, straight from global memory.  Wave w
@@ -529,7 +558,7 @@ attn_prefill_mfma_kernel(AttnArgs a, int ntiles, int xcd_map, int nblk) {
           const int qk = row_q[t] * C::kKMax;
           ++cur[t];
           nxt_pos[t] = cur[t] < K ? sm.spos[qk + cur[t]] : kNoPos;
-          nxt_alpha[t] = nxt_pos[t] != kNoPos ? tsc_b[tsc_off[t] + sm.sk[qk + cur[t]]] : 0.f;
+          nxt_alpha[t] = nxt_pos[t] != kNoPos ? wl[wrow[t] + sm.sk[qk + cur[t]]] : 0.f;
         }
         const bool act = nxt_pos[t] == x;
         wgt[t] = act ? __expf(nxt_alpha[t] - R.m_row[t]) : 0.f;
@@ -540,7 +569,7 @@ attn_prefill_mfma_kernel(AttnArgs a, int ntiles, int xcd_map, int nblk) {
           const int qk = row_q[t] * C::kKMax;
           ++cur[t];
           nxt_pos[t] = cur[t] < K ? sm.spos[qk + cur[t]] : kNoPos;
-          nxt_alpha[t] = nxt_pos[t] != kNoPos ? tsc_b[tsc_off[t] + sm.sk[qk + cur[t]]] : 0.f;
+          nxt_alpha[t] = nxt_pos[t] != kNoPos ? wl[wrow[t] + sm.sk[qk + cur[t]]] : 0.f;
         }
       }
       run_item<D, TPW, true, false>(mask, R, ksb, vtb, koff, voff, wgt, lo, hi, j0, tau, tl2e, lg);
@@ -602,7 +631,7 @@ static hipError_t attn_mfma_t(const AttnArgs &a, hipStream_t st) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int xcd_map = (npairs % 8 == 0) ? 1 : 0;
-  const size_t smem = sizeof(AttnSmem<D, G, WAVES, TPW>);
+  const size_t smem = sizeof(AttnSmem<D, G, WAVES, TPW>) + static_cast<size_t>(C::kQT) * G * a.K * sizeof(float);
   auto kern = attn_prefill_mfma_kernel<D, G, WAVES, TPW>;
   e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                           static_cast<int>(smem));
