@@ -118,7 +118,7 @@ def check_scores(gpu_tsc, ora_tsc, gpu_idx, ora_idx, G, tol=1e-5):
     gi = np.repeat(gpu_idx, G, axis=1)
     oi = np.repeat(ora_idx, G, axis=1)
     match = (gi == oi) & (oi >= 0)
-    d = np.abs(gpu_tsc.astype(np.float64) - ora_tsc)[match]
+    d = np.abs(gpu_tsc.astype(np.float64)[match] - ora_tsc[match])
     assert d.size == 0 or d.max() <= tol, d.max()
     assert np.isneginf(gpu_tsc[oi < 0]).all()
 

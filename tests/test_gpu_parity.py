@@ -128,6 +128,28 @@ def test_sparse_attention_parity(name):
     print(f"{name}: max |d| {err:.3g}")
 
 
+def test_score_topk_all_scores_tied():
+    """Every key equal, so every chunk summary and every group score of a
+    query is the same: the prefill selection is decided by the tie rule
+    alone (lowest chunks first) for every query, through the threshold
+    search's tie rounds."""
+    wl = wl_prefill(T=2048, Hq=8, Hkv=2, d=128, K=16, W=128, r=32, Dh=256)
+    inp = hs.prefill_inputs(wl, 212)
+    kk = inp["k"]
+    inp["k"] = np.ascontiguousarray(np.broadcast_to(kk[:, :, :1], kk.shape))
+    ks, bs = _oracle_stage_inputs(wl, inp)
+    c = hils.Config.from_dict(wl.config_dict())
+    d = upload(inp)
+    gidx, gtsc = gpu_score(c, d["q"], dev(ks), dev(bs), d.get("h"), d.get("w_down"), d.get("w_up"))
+    gidx, gtsc = host(gidx), host(gtsc)
+    r = oracle.prefill(ocfg(wl), inp, k_sum=ks, b_sum=bs)
+    assert (gidx == r["idx"]).all()
+    n = np.array([oracle.eligible_chunks(i, wl.window, 64) for i in range(wl.seq_len)])
+    expect = np.where(np.arange(wl.top_k)[None, :] < n[:, None], np.arange(wl.top_k)[None, :], -1)
+    assert (gidx == expect[None, None]).all()
+    check_scores(gtsc, r["tsc"], gidx, r["idx"], wl.group)
+
+
 @pytest.mark.parametrize("name", ["tiny_f32", "sharp_bf16_qcal", "scaled_needles", "ragged_d64_g1"])
 def test_prefill_end_to_end(name):
     """summary -> score/top-K -> attention on the GPU against the oracle's
