@@ -293,7 +293,6 @@ struct SelSmem {
   unsigned long long key[32];     // winners so far: (ordered score, ~chunk)
   unsigned long long sorted[32];  // final winners in rank order
   unsigned long long surv[kSurvMax + 32];
-  unsigned long long wkey[kSelWaves][64];  // wave_select scratch
   uint32_t tw[kSelWaves];         // per-wave lower bound of the threshold
   uint32_t red[2][kSelWaves];     // per-wave partial sums / minima, double buffered
   uint32_t red2[2][kSelWaves];
@@ -507,7 +506,7 @@ __device__ __forceinline__ void select_survivors(SelSmem &ss, int tot, int K) {
 //     score; the largest such bound over the waves is taken;
 //  2. the scores at or above it (typically a few dozen) and the winners kept
 //     from earlier tiles are collected in LDS, and one wave selects exactly
-//     among them (wave_select: same order, same tie rule);
+//     among them (same order, same tie rule);
 //  3. when too many scores pass (many equal scores), the tile falls back to
 //     the exact block-wide search.
 // On return ss.sorted[0..keep) holds the winners in rank order; returns keep.

@@ -85,12 +85,6 @@ __device__ __forceinline__ float group_sum(float v) {
   for (int o = width / 2; o >= 1; o >>= 1) v += __shfl_xor(v, o, kWave);
   return v;
 }
-template <int width>
-__device__ __forceinline__ float group_max(float v) {
-#pragma unroll
-  for (int o = width / 2; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-  return v;
-}
 
 // Sums inside aligned groups of 8 or 16 lanes with DPP lane moves (no LDS
 // traffic): xor-1 and xor-2 inside quads, then mirror inside 8 and 16 lanes.
@@ -204,19 +198,12 @@ __device__ __forceinline__ uint32_t orderable(float f) {
   uint32_t u = __float_as_uint(f);
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
-__device__ __forceinline__ float from_orderable(uint32_t o) {
-  uint32_t u = (o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o;
-  return __uint_as_float(u);
-}
 __device__ __forceinline__ unsigned long long make_key(float score, int chunk) {
   return (static_cast<unsigned long long>(orderable(score)) << 32) |
          static_cast<uint32_t>(~static_cast<uint32_t>(chunk));
 }
 __device__ __forceinline__ int key_chunk(unsigned long long k) {
   return static_cast<int>(~static_cast<uint32_t>(k & 0xFFFFFFFFu));
-}
-__device__ __forceinline__ float key_score(unsigned long long k) {
-  return from_orderable(static_cast<uint32_t>(k >> 32));
 }
 constexpr unsigned long long kNoKey = 0ull;  // below every real key
 
@@ -226,14 +213,8 @@ constexpr unsigned long long kNoKey = 0ull;  // below every real key
 // workgroup is written with device-scope atomic stores (written through to
 // the coherent memory side), each thread waits for its stores before the
 // workgroup barrier that precedes the ticket, and the workgroup that takes the
-// last ticket reads the data with device-scope atomic loads.
-__device__ __forceinline__ void publish(float *p, float v) {
-  __hip_atomic_store(reinterpret_cast<uint32_t *>(p), __float_as_uint(v), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void publish(unsigned long long *p, unsigned long long v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-// Two adjacent floats (8-byte aligned) in one write-through store / load.
+// last ticket reads the data with device-scope atomic loads.  Both move two
+// adjacent floats (8-byte aligned) at a time.
 __device__ __forceinline__ void publish2(float *p, float x, float y) {
   const unsigned long long v = static_cast<unsigned long long>(__float_as_uint(x)) |
                                (static_cast<unsigned long long>(__float_as_uint(y)) << 32);
@@ -244,7 +225,7 @@ __device__ __forceinline__ float2 load_acquired2(const float *p) {
       __hip_atomic_load(reinterpret_cast<const unsigned long long *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   return make_float2(__uint_as_float(static_cast<uint32_t>(v)), __uint_as_float(static_cast<uint32_t>(v >> 32)));
 }
-// Call from every thread after its publish() stores: returns, in thread 0 of
+// Call from every thread after its publish2() stores: returns, in thread 0 of
 // the workgroup, the number of workgroups that arrived before this one.
 __device__ __forceinline__ unsigned arrive(unsigned *counter) {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
@@ -258,120 +239,11 @@ __device__ __forceinline__ void reset_counter(unsigned *counter) {
   __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Loads of data another workgroup published before an atomic ticket.
-__device__ __forceinline__ float load_acquired(const float *p) {
-  return __uint_as_float(__hip_atomic_load(reinterpret_cast<const uint32_t *>(p), __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT));
-}
-__device__ __forceinline__ unsigned long long load_acquired(const unsigned long long *p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Wave-wide top-k selection by (score desc, index asc) without sorting.
-// Each lane holds NJ candidates: ord[j] = orderable(score) (0 = no
-// candidate) and a unique index idx[j].  A bitwise binary search over the
-// 32-bit keys, counting with ballots, finds the k-th largest key theta; the
-// winners are every key above theta plus the lowest-index keys equal to it.
-// theta lies between the smallest and the largest candidate, so the search
-// starts below their common leading bits, and it stops early once exactly k
-// keys are at or above the trial value.
-// On return win[j] marks winners and rank[j] is the winner's position:
-// the winners' 64-bit keys (ord, ~idx) are compacted into `scratch` (LDS
-// private to the wave, >= min(k, 64 NJ) entries) and every lane counts the
-// larger keys there (broadcast reads, no cross-lane shuffles).
-template <int NJ>
-__device__ __forceinline__ void wave_select(const uint32_t (&ord)[NJ], const int (&idx)[NJ], int k,
-                                            bool (&win)[NJ], int (&rank)[NJ], unsigned long long *scratch) {
-  const int lane = threadIdx.x & 63;
-  int avail = 0;
-  uint32_t lo = 0xFFFFFFFFu, hi = 0u;
-#pragma unroll
-  for (int j = 0; j < NJ; ++j) {
-    avail += __popcll(__ballot(ord[j] != 0u));
-    hi = max(hi, ord[j]);
-    lo = min(lo, ord[j] != 0u ? ord[j] : 0xFFFFFFFFu);
-  }
-  lo = wave_reduce_u32<0>(lo);
-  hi = wave_reduce_u32<1>(hi);
-  const int keep = min(k, avail);
-  uint32_t theta = 0u;
-  bool exact = false;  // exactly `keep` keys are >= theta
-  if (keep > 0) {
-    const uint32_t spread = lo ^ hi;
-    const int top = spread ? 31 - __clz(spread) : -1;  // highest bit where lo and hi differ
-    theta = top < 0 ? lo : (top == 31 ? 0u : lo & ~((2u << top) - 1u));
-    for (int bit = top; bit >= 0; --bit) {
-      const uint32_t cand = theta | (1u << bit);
-      int cnt = 0;
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) cnt += __popcll(__ballot(ord[j] >= cand));
-      if (cnt >= keep) {
-        theta = cand;
-        if (cnt == keep) {
-          exact = true;
-          break;
-        }
-      }
-    }
-    if (top < 0) exact = avail == keep;
-  }
-  int cnt_gt = 0;
-#pragma unroll
-  for (int j = 0; j < NJ; ++j) {
-    win[j] = keep > 0 && (exact ? ord[j] >= theta : ord[j] > theta);
-    cnt_gt += __popcll(__ballot(win[j]));
-  }
-  // ties at theta: take the lowest indices first
-  for (int need = keep - cnt_gt; need > 0; --need) {
-    int best = 0x7FFFFFFF;
-#pragma unroll
-    for (int j = 0; j < NJ; ++j)
-      if (!win[j] && ord[j] == theta && ord[j] != 0u) best = min(best, idx[j]);
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) best = min(best, __shfl_xor(best, o, 64));
-#pragma unroll
-    for (int j = 0; j < NJ; ++j)
-      if (!win[j] && ord[j] == theta && idx[j] == best) win[j] = true;
-  }
-  unsigned long long key[NJ];
-  int nwin = 0;
-#pragma unroll
-  for (int j = 0; j < NJ; ++j) {
-    key[j] = (static_cast<unsigned long long>(ord[j]) << 32) | static_cast<uint32_t>(~static_cast<uint32_t>(idx[j]));
-    const unsigned long long m = __ballot(win[j]);
-    const int below = __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
-                                                __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u));
-    if (win[j]) scratch[nwin + below] = key[j];
-    nwin += __popcll(m);
-    rank[j] = 0;
-  }
-  __builtin_amdgcn_wave_barrier();  // (LDS operations of one wave complete in order)
-  for (int e = 0; e < nwin; ++e) {
-    const unsigned long long ke = scratch[e];
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) rank[j] += ke > key[j] ? 1 : 0;
-  }
-  __builtin_amdgcn_wave_barrier();  // scratch may be reused after this
-  (void)lane;
-}
 
 // R1 partition: complete chunks before query i's window
 __device__ __forceinline__ int eligible_chunks(int i, int W, int S) {
   int w0 = i - W + 1;
   return w0 > 0 ? w0 / S : 0;
-}
-
-// merge two online-softmax partials (m, l) into the first; returns the scale
-// that the first partial's accumulator must be multiplied by, and sets *sb to
-// the scale for the second.
-__device__ __forceinline__ float merge_ml(float &m, float &l, float m2, float l2, float *sb) {
-  float mn = fmaxf(m, m2);
-  float sa = (m == -INFINITY) ? 0.f : __expf(m - mn);
-  float s2 = (m2 == -INFINITY) ? 0.f : __expf(m2 - mn);
-  l = l * sa + l2 * s2;
-  m = mn;
-  *sb = s2;
-  return sa;
 }
 
 }  // namespace hils
