@@ -58,6 +58,7 @@ struct AttnCfg {
   static constexpr int kKS = D / 32;          // k-steps of S^T
   static constexpr int kDT = D / 16;          // d tiles of O^T
   static constexpr int kKMax = 32;            // largest top-K
+  static constexpr int kLS = kKMax + 1;       // per-query list stride: slot kKMax is a sentinel
   static constexpr int kRowPieces = D / 8;    // 16-byte pieces per K row
   // one staged item = 64 K rows + D V^T rows of 128 bytes, loaded straight
   // into LDS in 1 KB wave-wide pieces
@@ -71,9 +72,9 @@ struct AttnSmem {
   using C = AttnCfg<D, G, WAVES, TPW>;
   uint16_t ks[2][kItemKeys * D];   // K rows, 16-byte pieces XOR-swizzled per row
   uint16_t vt[2][D * kItemKeys];   // V^T rows, 16-byte pieces XOR-swizzled per row
-  int16_t spos[C::kQT * C::kKMax];   // per query: union positions of its chunks, ascending
-  int8_t sk[C::kQT * C::kKMax];      // their slots in the query's top-K list
-  int16_t ulist[C::kQT * C::kKMax];  // union of selected chunks, ascending
+  int16_t spos[C::kQT * C::kLS];     // per query: union positions of its chunks, ascending, then kNoPos
+  int8_t sk[C::kQT * C::kLS];        // their slots in the query's top-K list
+  alignas(16) int16_t ulist[C::kQT * C::kKMax];  // union of selected chunks, ascending (first: the raw lists)
   uint32_t umask[256];
   int wbase[256];                    // union positions before each 32-chunk word
   int nunion;
@@ -137,50 +138,44 @@ struct RowState {
   float m_row[TPW], l_row[TPW];
 };
 
-// Attend one staged item with one 16-row tile.  CHUNK: exact chunk softmax
-// weighted by wgt; otherwise a window block, masked to [lo, hi] per row when
-// MASKED.  The tile's S^T, softmax and O^T update are one straight-line block;
-// tiles of a wave run one after the other (each a wave-uniform branch).
-template <int D, bool CHUNK, bool MASKED>
-__device__ __forceinline__ void attend_tile(const bf16x8 (&qop)[D / 32], f32x4 (&acc)[D / 16], float &m_row,
-                                            float &l_row, const uint16_t *ksb, const uint16_t *vtb, int koff,
-                                            int voff, float wgt, int lo, int hi, int j0, float tau, float tl2e,
-                                            int lg) {
-  constexpr int KS = D / 32, DT = D / 16;
-  // S^T = K Q^T; the operands of k-step s + 1 are read while the MFMAs of
-  // step s run, and the scheduling barrier keeps later reads from being
-  // hoisted further (registers)
-  f32x4 st[4];
-  {
-    uint4 u[2][4];
-    auto load_k = [&](uint4 (&dst)[4], int s) {
+// S^T = K Q^T of one 16-row tile; the operands of k-step s + 1 are read
+// while the MFMAs of step s run, and the scheduling barrier keeps later reads
+// from being hoisted further (registers).
+template <int D>
+__device__ __forceinline__ void tile_scores(const bf16x8 (&qop)[D / 32], const uint16_t *ksb, int koff,
+                                            f32x4 (&st)[4]) {
+  constexpr int KS = D / 32;
+  uint4 u[2][4];
+  auto load_k = [&](uint4 (&dst)[4], int s) {
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-        dst[kt] = *reinterpret_cast<const uint4 *>(ksb + (koff ^ (32 * s)) + (32 * (kt >> 1) + 4 * (kt & 1)) * D);
-    };
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt) st[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    load_k(u[0], 0);
-#pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      if (s + 1 < KS) load_k(u[(s + 1) & 1], s + 1);
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt) st[kt] = mfma16(as_bf16x8(u[s & 1][kt]), qop[s], st[kt]);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  }
-  // V^T operands of the first d-tile pair, read while the softmax runs
-  uint4 v[2][2][2];
-  auto load_v = [&](uint4 (&dst)[2][2], int dt) {
-#pragma unroll
-    for (int d2 = 0; d2 < 2; ++d2)
-#pragma unroll
-      for (int sl = 0; sl < 2; ++sl)
-        dst[d2][sl] = *reinterpret_cast<const uint4 *>(vtb + (voff ^ (32 * sl)) + 16 * (dt + d2) * kItemKeys);
+    for (int kt = 0; kt < 4; ++kt)
+      dst[kt] = *reinterpret_cast<const uint4 *>(ksb + (koff ^ (32 * s)) + (32 * (kt >> 1) + 4 * (kt & 1)) * D);
   };
-  load_v(v[0], 0);
-  // softmax pieces: this lane holds keys perm_key(kt, 4 lg + i) of row ln
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt) st[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  load_k(u[0], 0);
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    if (s + 1 < KS) load_k(u[(s + 1) & 1], s + 1);
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) st[kt] = mfma16(as_bf16x8(u[s & 1][kt]), qop[s], st[kt]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// Softmax of one tile's S^T into the bf16 P^T operand (this lane holds keys
+// perm_key(kt, 4 lg + i) of row ln).  CHUNK: exact softmax over the chunk's
+// 64 keys, scaled by the fusion weight wgt.  Otherwise a window block against
+// the row's reference maximum m_row; when MASKED, only the lane's keys with
+// perm_key(kt, 4 lg + i) - 8 lg <= lim count (see window_limit);
+// the reference moves to the block's maximum only when that exceeds it by
+// more than kLazyRescale, and the returned factor (1 otherwise) rescales the
+// row's accumulator.
+template <bool CHUNK, bool MASKED>
+__device__ __forceinline__ float tile_softmax(const f32x4 (&st)[4], bf16x8 (&pb)[2], float &m_row, float &l_row,
+                                              float wgt, int lim, float tau, float tl2e) {
   float p[4][4];
+  float sc = 1.f;
   if (CHUNK) {
     float mc = -INFINITY;
 #pragma unroll
@@ -198,7 +193,7 @@ __device__ __forceinline__ void attend_tile(const bf16x8 (&qop)[D / 32], f32x4 (
         lc += p[kt][i];
       }
     lc = sum_rows4(lc);
-    const float w = wgt / lc;
+    const float w = wgt * __builtin_amdgcn_rcpf(lc);  // lc >= 1 (the maximum's term)
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
@@ -210,41 +205,33 @@ __device__ __forceinline__ void attend_tile(const bf16x8 (&qop)[D / 32], f32x4 (
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         float x = st[kt][i];
-        if (MASKED) {
-          const int j = j0 + perm_key(kt, 4 * lg + i);
-          x = (j >= lo && j <= hi) ? x : -INFINITY;
-        }
+        // perm_key(kt, 4 lg + i) - 8 lg, a constant
+        if (MASKED) x = (32 * (kt >> 1) + 4 * (kt & 1) + i <= lim) ? x : -INFINITY;
         p[kt][i] = x;
         mb = fmaxf(mb, x);
       }
     mb = max_rows4(mb);
     const float cand = mb * tau;  // the block's largest logit of this row
-    float ref = m_row;
-    float sc = 1.f;
-    if (cand > ref + kLazyRescale) {
-      sc = (ref == -INFINITY) ? 0.f : __expf(ref - cand);
-      ref = cand;
-    }
-    const float off = -ref * kLog2e;
+    const bool move = cand > m_row + kLazyRescale;
+    const float e = __expf(m_row - cand);  // 0 while m_row is -inf
+    sc = move ? e : 1.f;
+    const float ref = move ? cand : m_row;
+    // ref stays -inf only when every key of the row is masked so far; any
+    // finite offset then sends every masked logit to exp2(-inf) = 0
+    const float off = (MASKED && ref == -INFINITY) ? 0.f : -ref * kLog2e;
     float ls = 0.f;
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        float e = __builtin_amdgcn_exp2f(fmaf(p[kt][i], tl2e, off));
-        if (MASKED) e = (p[kt][i] == -INFINITY) ? 0.f : e;
-        p[kt][i] = e;
-        ls += e;
+        const float ex = __builtin_amdgcn_exp2f(fmaf(p[kt][i], tl2e, off));
+        p[kt][i] = ex;
+        ls += ex;
       }
     ls = sum_rows4(ls);
     l_row = l_row * sc + ls;
     m_row = ref;
-    if (__ballot(sc != 1.f)) {
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) acc[dt] *= sc;
-    }
   }
-  bf16x8 pb[2];
 #pragma unroll
   for (int sl = 0; sl < 2; ++sl) {
     uint4 u;
@@ -254,8 +241,31 @@ __device__ __forceinline__ void attend_tile(const bf16x8 (&qop)[D / 32], f32x4 (
     u.w = pack_bf16x2(p[2 * sl + 1][2], p[2 * sl + 1][3]);
     pb[sl] = as_bf16x8(u);
   }
-  // O^T += V^T P^T; the next d-tile pair's operands are read while this
-  // pair's MFMAs run
+  return sc;
+}
+
+template <int D>
+__device__ __forceinline__ void rescale_acc(f32x4 (&acc)[D / 16], float sc) {
+  if (__ballot(sc != 1.f)) {
+#pragma unroll
+    for (int dt = 0; dt < D / 16; ++dt) acc[dt] *= sc;
+  }
+}
+
+// O^T += V^T P^T; the next d-tile pair's operands are read while this pair's
+// MFMAs run
+template <int D>
+__device__ __forceinline__ void tile_pv(f32x4 (&acc)[D / 16], const bf16x8 (&pb)[2], const uint16_t *vtb, int voff) {
+  constexpr int DT = D / 16;
+  uint4 v[2][2][2];
+  auto load_v = [&](uint4 (&dst)[2][2], int dt) {
+#pragma unroll
+    for (int d2 = 0; d2 < 2; ++d2)
+#pragma unroll
+      for (int sl = 0; sl < 2; ++sl)
+        dst[d2][sl] = *reinterpret_cast<const uint4 *>(vtb + (voff ^ (32 * sl)) + 16 * (dt + d2) * kItemKeys);
+  };
+  load_v(v[0], 0);
 #pragma unroll
   for (int st2 = 0; st2 < DT / 2; ++st2) {
     const int dt = 2 * st2;
@@ -268,16 +278,29 @@ __device__ __forceinline__ void attend_tile(const bf16x8 (&qop)[D / 32], f32x4 (
   }
 }
 
+// Attend one staged item with one 16-row tile.
+template <int D, bool CHUNK, bool MASKED>
+__device__ __forceinline__ void attend_tile(const bf16x8 (&qop)[D / 32], f32x4 (&acc)[D / 16], float &m_row,
+                                            float &l_row, const uint16_t *ksb, const uint16_t *vtb, int koff,
+                                            int voff, float wgt, int lim, float tau, float tl2e) {
+  f32x4 st[4];
+  tile_scores<D>(qop, ksb, koff, st);
+  bf16x8 pb[2];
+  const float sc = tile_softmax<CHUNK, MASKED>(st, pb, m_row, l_row, wgt, lim, tau, tl2e);
+  if (!CHUNK) rescale_acc<D>(acc, sc);
+  tile_pv<D>(acc, pb, vtb, voff);
+}
+
 // Run the item for the wave's tiles that take part (bit t of `mask`).
 template <int D, int TPW, bool CHUNK, bool MASKED>
 __device__ __forceinline__ void run_item(int mask, RowState<D, TPW> &R, const uint16_t *ksb, const uint16_t *vtb,
-                                         int koff, int voff, const float (&wgt)[TPW], const int (&lo)[TPW],
-                                         const int (&hi)[TPW], int j0, float tau, float tl2e, int lg) {
+                                         int koff, int voff, const float (&wgt)[TPW], const int (&lim)[TPW], float tau,
+                                         float tl2e) {
 #pragma unroll
   for (int t = 0; t < TPW; ++t)
     if ((mask >> t) & 1)
-      attend_tile<D, CHUNK, MASKED>(R.qop[t], R.acc[t], R.m_row[t], R.l_row[t], ksb, vtb, koff, voff, wgt[t], lo[t],
-                                    hi[t], j0, tau, tl2e, lg);
+      attend_tile<D, CHUNK, MASKED>(R.qop[t], R.acc[t], R.m_row[t], R.l_row[t], ksb, vtb, koff, voff, wgt[t], lim[t],
+                                    tau, tl2e);
 }
 
 // ------------------------------------------------------------------ kernel
@@ -320,22 +343,107 @@ attn_prefill_mfma_kernel(AttnArgs a, int ntiles, int xcd_map, int nblk) {
   const uint16_t *kb = static_cast<const uint16_t *>(a.k) + (static_cast<size_t>(b) * Hkv + g) * T * D;
   const uint16_t *vtg = static_cast<const uint16_t *>(a.vt_ws) + (static_cast<size_t>(b) * Hkv + g) * nblk * D * kItemKeys;
 
+  // ---- every global load of the set-up is issued here, at once, with
+  // clamped indices and no lane-dependent branch (so that nothing waits for
+  // one load before issuing the next): the selections (query, slot) of the
+  // tile, the Q operands of the wave's rows and the rows' fusion scores.
+  constexpr int kPairs = (C::kQT * C::kKMax + C::kThreads - 1) / C::kThreads;
+  constexpr int kWPT = (C::kQT * G * C::kKMax + C::kThreads - 1) / C::kThreads;
+  const int kc_max = K > 0 ? K - 1 : 0;
+  int my_c[kPairs];
+  float wv[kWPT];
+  if (K > 0) {
+    const int *idx_bg = a.topk_idx + (static_cast<size_t>(b) * Hkv + g) * T * K;
+#pragma unroll
+    for (int r = 0; r < kPairs; ++r) {
+      const int x = tid + r * C::kThreads, q = x / C::kKMax, k = x % C::kKMax;
+      my_c[r] = idx_bg[static_cast<size_t>(min(q0 + q, T - 1)) * K + min(k, kc_max)];
+    }
+    const float *tsc_b = a.topk_score + static_cast<size_t>(b) * Hq * T * K;
+    const int total = C::kQT * G * K;
+#pragma unroll
+    for (int r = 0; r < kWPT; ++r) {
+      const int x = tid + r * C::kThreads;
+      const int xc = x < total ? x : 0;
+      const int q = xc / (G * K), rem = xc % (G * K), hh = rem / K, k = rem % K;
+      if (r * C::kThreads < total) wv[r] = tsc_b[(static_cast<size_t>(g * G + hh) * T + min(q0 + q, T - 1)) * K + k];
+    }
+  }
+  // per-lane row identity for the tiles
+  int row_q[TPW];
+  const int row_h = g * G + (ln % G);  // the same head in every tile
+  bool row_ok[TPW];
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) {
+    const int q = wave * C::kQPW + t * C::kQPT + ln / G;
+    row_q[t] = q;
+    row_ok[t] = (q0 + q) < T;
+  }
+  RowState<D, TPW> R;
+  // Q operands (B of S^T = K Q^T): lane holds row ln, d = 32 ks + 8 lg .. +8;
+  // rows past T read the last query (their results are not stored)
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) {
+    const size_t qo = ((static_cast<size_t>(b) * Hq + row_h) * T + min(q0 + row_q[t], T - 1)) * D;
+#pragma unroll
+    for (int s = 0; s < C::kKS; ++s) R.qop[t][s] = as_bf16x8(*reinterpret_cast<const uint4 *>(qb + qo + 32 * s + 8 * lg));
+  }
+
   // ---- the union of the tile's selected chunks (bit mask -> ascending list)
   for (int x = tid; x < 256; x += C::kThreads) sm.umask[x] = 0u;
   __syncthreads();
-  // selections in a register per (query, slot)
-  constexpr int kPairs = (C::kQT * C::kKMax + C::kThreads - 1) / C::kThreads;
-  int my_c[kPairs];
+  // the tile's fusion scores into LDS: wl[(q * G + hh) * K + k] =
+  // topk_score[b, g G + hh, q0 + q, k], read by the row statistics and the
+  // cursors below
+  {
+    const int total = C::kQT * G * K;
+#pragma unroll
+    for (int r = 0; r < kWPT; ++r) {
+      const int x = tid + r * C::kThreads;
+      if (r * C::kThreads < total && x < total) wl[x] = wv[r];
+    }
+  }
 #pragma unroll
   for (int r = 0; r < kPairs; ++r) {
-    const int x = tid + r * C::kThreads, q = x / C::kKMax, k = x % C::kKMax, i = q0 + q;
-    int c = -1;
-    if (q < C::kQT && k < K && i < T) c = a.topk_idx[((static_cast<size_t>(b) * Hkv + g) * T + i) * K + k];
+    const int x = tid + r * C::kThreads, q = x / C::kKMax, k = x % C::kKMax;
+    const int c = (q < C::kQT && k < K && q0 + q < T) ? my_c[r] : -1;
     my_c[r] = c;
     if (q < C::kQT) sm.ulist[x] = static_cast<int16_t>(c);  // scratch copy of the raw lists
     if (c >= 0) atomicOr(&sm.umask[c >> 5], 1u << (c & 31));
   }
   __syncthreads();
+  // ---- row statistics from the raw lists: M_row = max of the row's selected
+  // chunk scores, l_row = sum of e^{s_hat - M_row} over them (every valid
+  // slot counts), eight slots at a time with a running maximum
+  int wrow[TPW];  // this row's fusion scores: wl + wrow[t], indexed by top-K slot
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) {
+    wrow[t] = (row_q[t] * G + (ln % G)) * K;
+    const int16_t *raw = sm.ulist + row_q[t] * C::kKMax;
+    float mx = -INFINITY, l = 0.f;
+    for (int k0 = 0; k0 < K; k0 += 8) {
+      const uint4 cw = *reinterpret_cast<const uint4 *>(raw + k0);
+      const uint32_t cv[4] = {cw.x, cw.y, cw.z, cw.w};
+      float sv[8];
+      bool ok[8];
+      float m8 = -INFINITY;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int c = static_cast<int16_t>((cv[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+        ok[e] = (k0 + e < K) && c >= 0;
+        sv[e] = wl[wrow[t] + min(k0 + e, K - 1)];
+        m8 = ok[e] ? fmaxf(m8, sv[e]) : m8;
+      }
+      const float mn = fmaxf(mx, m8);
+      float l8 = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) l8 += ok[e] ? __expf(sv[e] - mn) : 0.f;
+      l = (mx == -INFINITY ? 0.f : l * __expf(mx - mn)) + l8;
+      mx = mn;
+    }
+    R.m_row[t] = mx;
+    R.l_row[t] = l;
+  }
   if (wave == 0) {
     const int nwords = (C_chunks + 31) >> 5;
     int base = 0;
@@ -384,12 +492,13 @@ attn_prefill_mfma_kernel(AttnArgs a, int ntiles, int xcd_map, int nblk) {
       const int rank = my_c[r];
       const int c = sm.ulist[q * C::kKMax + k];
       const int upos = sm.wbase[c >> 5] + __popc(sm.umask[c >> 5] & ((1u << (c & 31)) - 1u));
-      sm.spos[q * C::kKMax + rank] = static_cast<int16_t>(upos);
-      sm.sk[q * C::kKMax + rank] = static_cast<int8_t>(k);
+      sm.spos[q * C::kLS + rank] = static_cast<int16_t>(upos);
+      sm.sk[q * C::kLS + rank] = static_cast<int8_t>(k);
     } else {
-      sm.spos[q * C::kKMax + (-1 - my_c[r])] = kNoPos;
+      sm.spos[q * C::kLS + (-1 - my_c[r])] = kNoPos;
     }
   }
+  for (int q = tid; q < C::kQT; q += C::kThreads) sm.spos[q * C::kLS + C::kKMax] = kNoPos;
   __syncthreads();
   // the ascending union list (overwrites the scratch copy)
   if (wave == 0) {
@@ -413,80 +522,18 @@ attn_prefill_mfma_kernel(AttnArgs a, int ntiles, int xcd_map, int nblk) {
   const int nwin = (i_last - jw0) / kItemKeys + 1;
   const int nitems = nunion + nwin;
 
-  // ---- per-lane row identity for the tiles
-  int row_q[TPW];
-  const int row_h = g * G + (ln % G);  // the same head in every tile
-  bool row_ok[TPW];
-#pragma unroll
-  for (int t = 0; t < TPW; ++t) {
-    const int q = wave * C::kQPW + t * C::kQPT + ln / G;
-    row_q[t] = q;
-    row_ok[t] = (q0 + q) < T;
-  }
 
-  RowState<D, TPW> R;
-  // ---- Q operands (B of S^T = K Q^T): lane holds row ln, d = 32 ks + 8 lg .. +8
-#pragma unroll
-  for (int t = 0; t < TPW; ++t) {
-    const int i = q0 + row_q[t];
-    const size_t qo = ((static_cast<size_t>(b) * Hq + row_h) * T + (row_ok[t] ? i : 0)) * D;
-#pragma unroll
-    for (int s = 0; s < C::kKS; ++s) {
-      uint4 u = row_ok[t] ? *reinterpret_cast<const uint4 *>(qb + qo + 32 * s + 8 * lg) : make_uint4(0, 0, 0, 0);
-      R.qop[t][s] = as_bf16x8(u);
-    }
-  }
-
-  // ---- the tile's fusion scores into LDS: wl[(q * G + hh) * K + k] =
-  // topk_score[b, g G + hh, q0 + q, k], all loads issued before any store
-  // (no lane-dependent branch around them), so the row statistics and the
-  // cursors below read LDS instead of making dependent global loads
-  const float *tsc_b = a.topk_score + static_cast<size_t>(b) * Hq * T * K;
-  {
-    constexpr int kWPT = (C::kQT * G * C::kKMax + C::kThreads - 1) / C::kThreads;
-    constexpr int kStep = kWPT < 8 ? kWPT : 8;  // loads in flight per thread
-    const int total = C::kQT * G * K;
-#pragma unroll
-    for (int r0 = 0; r0 < kWPT; r0 += kStep) {
-      float wv[kStep];
-#pragma unroll
-      for (int r = 0; r < kStep; ++r) {
-        const int x = tid + (r0 + r) * C::kThreads;
-        const int xc = x < total ? x : 0;
-        const int q = xc / (G * K), rem = xc % (G * K), hh = rem / K, k = rem % K;
-        const int i = min(q0 + q, T - 1);
-        if ((r0 + r) * C::kThreads < total) wv[r] = tsc_b[(static_cast<size_t>(g * G + hh) * T + i) * K + k];
-      }
-#pragma unroll
-      for (int r = 0; r < kStep; ++r) {
-        const int x = tid + (r0 + r) * C::kThreads;
-        if (x < total) wl[x] = wv[r];
-      }
-    }
-  }
-  __syncthreads();
-
-  // ---- row statistics from the selected chunk scores, and each row's
-  // cursor into its ascending selection list
+  // ---- each row's cursor into its ascending selection list
+  // cur[t]: LDS index of the row's next list entry (a list ends in kNoPos)
   int cur[TPW], nxt_pos[TPW];
   float nxt_alpha[TPW];
-  int wrow[TPW];  // this row's fusion scores: wl + wrow[t], indexed by top-K slot
 #pragma unroll
   for (int t = 0; t < TPW; ++t) {
-    const int qk = row_q[t] * C::kKMax;
-    wrow[t] = (row_q[t] * G + (ln % G)) * K;
-    float mx = -INFINITY;
-    if (row_ok[t])
-      for (int k = 0; k < K && sm.spos[qk + k] != kNoPos; ++k) mx = fmaxf(mx, wl[wrow[t] + sm.sk[qk + k]]);
-    float l = 0.f;
-    if (row_ok[t] && mx != -INFINITY)
-      for (int k = 0; k < K && sm.spos[qk + k] != kNoPos; ++k) l += __expf(wl[wrow[t] + sm.sk[qk + k]] - mx);
-    R.m_row[t] = mx;
-    R.l_row[t] = l;
+    const int qk = row_q[t] * C::kLS;
 #pragma unroll
     for (int dt = 0; dt < C::kDT; ++dt) R.acc[t][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    cur[t] = 0;
-    nxt_pos[t] = (row_ok[t] && K > 0) ? sm.spos[qk] : kNoPos;
+    cur[t] = qk;
+    nxt_pos[t] = row_ok[t] ? sm.spos[qk] : kNoPos;
     nxt_alpha[t] = nxt_pos[t] != kNoPos ? wl[wrow[t] + sm.sk[qk]] : 0.f;
   }
 
@@ -549,51 +596,53 @@ attn_prefill_mfma_kernel(AttnArgs a, int ntiles, int xcd_map, int nblk) {
     const uint16_t *vtb = sm.vt[buf];
     const int j0 = j0_cur;
     float wgt[TPW];
-    int lo[TPW], hi[TPW];
+    int lim[TPW];
     int mask = 0;
     if (x < nunion) {
 #pragma unroll
       for (int t = 0; t < TPW; ++t) {
         if (nxt_pos[t] < x) {  // only after a repeated entry: skip it
-          const int qk = row_q[t] * C::kKMax;
           ++cur[t];
-          nxt_pos[t] = cur[t] < K ? sm.spos[qk + cur[t]] : kNoPos;
-          nxt_alpha[t] = nxt_pos[t] != kNoPos ? wl[wrow[t] + sm.sk[qk + cur[t]]] : 0.f;
+          nxt_pos[t] = sm.spos[cur[t]];
+          nxt_alpha[t] = nxt_pos[t] != kNoPos ? wl[wrow[t] + sm.sk[cur[t]]] : 0.f;
         }
         const bool act = nxt_pos[t] == x;
         wgt[t] = act ? __expf(nxt_alpha[t] - R.m_row[t]) : 0.f;
-        lo[t] = 0;
-        hi[t] = -1;
+        lim[t] = 0;
         if (__ballot(act)) mask |= 1 << t;
         if (act) {
-          const int qk = row_q[t] * C::kKMax;
           ++cur[t];
-          nxt_pos[t] = cur[t] < K ? sm.spos[qk + cur[t]] : kNoPos;
-          nxt_alpha[t] = nxt_pos[t] != kNoPos ? wl[wrow[t] + sm.sk[qk + cur[t]]] : 0.f;
+          nxt_pos[t] = sm.spos[cur[t]];
+          nxt_alpha[t] = nxt_pos[t] != kNoPos ? wl[wrow[t] + sm.sk[cur[t]]] : 0.f;
         }
       }
-      run_item<D, TPW, true, false>(mask, R, ksb, vtb, koff, voff, wgt, lo, hi, j0, tau, tl2e, lg);
+      run_item<D, TPW, true, false>(mask, R, ksb, vtb, koff, voff, wgt, lim, tau, tl2e);
     } else {
+      // Query i's window starts at n_i * S, a multiple of the block size
+      // (S = 64): a block lies in it from its first key on, up to key i, or
+      // not at all.  lim: the last key of the block the row takes, as a
+      // lane-relative offset (key - j0 - 8 lg); -1 takes none.
       bool edge = false;
 #pragma unroll
       for (int t = 0; t < TPW; ++t) {
         wgt[t] = 0.f;
-        lo[t] = 0;
-        hi[t] = -1;
+        lim[t] = -1;
+        bool mine = false;
         if (row_ok[t]) {
           const int i = q0 + row_q[t];
-          lo[t] = max(j0, (max(0, i - W + 1) >> 6) << 6);  // n_i * S with S = 64
-          hi[t] = min(j0 + kItemKeys - 1, i);
+          const int ws = (max(0, i - W + 1) >> 6) << 6;  // n_i * S
+          mine = ws <= j0 && j0 <= i;
+          const int hi = min(j0 + kItemKeys - 1, i);
+          if (mine) lim[t] = hi - j0 - 8 * lg;
+          // a row that does not take the whole block needs the mask
+          edge = edge || !mine || hi != j0 + kItemKeys - 1;
         }
-        const bool mine = lo[t] <= hi[t];
         if (__ballot(mine)) mask |= 1 << t;
-        // a row whose window does not cover the whole block needs the mask
-        edge = edge || (row_ok[t] && (lo[t] != j0 || hi[t] != j0 + kItemKeys - 1));
       }
       if (__ballot(edge))
-        run_item<D, TPW, false, true>(mask, R, ksb, vtb, koff, voff, wgt, lo, hi, j0, tau, tl2e, lg);
+        run_item<D, TPW, false, true>(mask, R, ksb, vtb, koff, voff, wgt, lim, tau, tl2e);
       else
-        run_item<D, TPW, false, false>(mask, R, ksb, vtb, koff, voff, wgt, lo, hi, j0, tau, tl2e, lg);
+        run_item<D, TPW, false, false>(mask, R, ksb, vtb, koff, voff, wgt, lim, tau, tl2e);
     }
     j0_cur = j0_nxt;
     j0_nxt = j0_nn;
