@@ -133,7 +133,8 @@ hils_status hils_chunk_score_topk(const hils_config *cfg, const void *q, const v
  *   q, o       [B, H_q, T, d]   dtype (o out)
  *   k, v       [B, H_kv, T, d]  dtype
  *   topk_idx   [B, H_kv, T, K]  int32 (as written by hils_chunk_score_topk;
- *                               entries must be -1 or eligible chunks < n_i)
+ *                               entries must be -1 or eligible chunks < n_i,
+ *                               no chunk twice in one list)
  *   topk_score [B, H_q, T, K]   f32
  *   workspace  >= hils_prefill_workspace_bytes(cfg) bytes, device memory
  *              (may be the one given to hils_chunk_score_topk: this call

@@ -73,7 +73,7 @@ struct AttnSmem {
   uint16_t ks[2][kItemKeys * D];   // K rows, 16-byte pieces XOR-swizzled per row
   uint16_t vt[2][D * kItemKeys];   // V^T rows, 16-byte pieces XOR-swizzled per row
   int16_t spos[C::kQT * C::kLS];     // per query: union positions of its chunks, ascending, then kNoPos
-  int8_t sk[C::kQT * C::kLS];        // their slots in the query's top-K list
+  int8_t sk[C::kQT * C::kLS];        // their slots in the query's top-K list (0 past the end)
   alignas(16) int16_t ulist[C::kQT * C::kKMax];  // union of selected chunks, ascending (first: the raw lists)
   uint32_t umask[256];
   int wbase[256];                    // union positions before each 32-chunk word
@@ -496,9 +496,13 @@ attn_prefill_mfma_kernel(AttnArgs a, int ntiles, int xcd_map, int nblk) {
       sm.sk[q * C::kLS + rank] = static_cast<int8_t>(k);
     } else {
       sm.spos[q * C::kLS + (-1 - my_c[r])] = kNoPos;
+      sm.sk[q * C::kLS + (-1 - my_c[r])] = 0;
     }
   }
-  for (int q = tid; q < C::kQT; q += C::kThreads) sm.spos[q * C::kLS + C::kKMax] = kNoPos;
+  for (int q = tid; q < C::kQT; q += C::kThreads) {
+    sm.spos[q * C::kLS + C::kKMax] = kNoPos;
+    sm.sk[q * C::kLS + C::kKMax] = 0;
+  }
   __syncthreads();
   // the ascending union list (overwrites the scratch copy)
   if (wave == 0) {
@@ -534,16 +538,13 @@ attn_prefill_mfma_kernel(AttnArgs a, int ntiles, int xcd_map, int nblk) {
     for (int dt = 0; dt < C::kDT; ++dt) R.acc[t][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
     cur[t] = qk;
     nxt_pos[t] = row_ok[t] ? sm.spos[qk] : kNoPos;
-    nxt_alpha[t] = nxt_pos[t] != kNoPos ? wl[wrow[t] + sm.sk[qk]] : 0.f;
+    nxt_alpha[t] = wl[wrow[t] + sm.sk[qk]];  // unused once the list has ended
   }
 
   // ---- staging: item x -> LDS buffer, straight from global memory.  Wave w
   // fills 1 KB slices w, w + WAVES, ... of each tensor; lane l's 16 bytes land
   // at byte 16 l of the slice, i.e. at one (row, physical piece) pair, and the
   // lane fetches the logical piece the swizzle puts there.
-  auto item_key0 = [&](int x) -> int {
-    return x < nunion ? static_cast<int>(sm.ulist[x]) * kItemKeys : jw0 + (x - nunion) * kItemKeys;
-  };
   auto issue_loads = [&](int j0, int buf) {
     const uint16_t *vsrc = vtg + static_cast<size_t>(j0 / kItemKeys) * D * kItemKeys;
 #pragma unroll
@@ -567,6 +568,18 @@ attn_prefill_mfma_kernel(AttnArgs a, int ntiles, int xcd_map, int nblk) {
     }
   };
 
+  // the union list, 64 entries at a time in a register (lane l holds entry
+  // ubase + l): an item's first key is a lane read, not an LDS round trip
+  int ubase = 0;
+  int ureg = lane < nunion ? sm.ulist[lane] : 0;
+  auto union_key0 = [&](int x) -> int {
+    if (x - ubase >= 64) {  // uniform: the next 64 entries
+      ubase += 64;
+      ureg = ubase + lane < nunion ? sm.ulist[ubase + lane] : 0;
+    }
+    return __builtin_amdgcn_readlane(ureg, x - ubase) * kItemKeys;
+  };
+  auto item_key0 = [&](int x) -> int { return x < nunion ? union_key0(x) : jw0 + (x - nunion) * kItemKeys; };
   int j0_cur = 0, j0_nxt = 0;
   if (nitems > 0) {
     j0_cur = item_key0(0);
@@ -599,24 +612,28 @@ attn_prefill_mfma_kernel(AttnArgs a, int ntiles, int xcd_map, int nblk) {
     int lim[TPW];
     int mask = 0;
     if (x < nunion) {
+      bool act[TPW];
 #pragma unroll
       for (int t = 0; t < TPW; ++t) {
-        if (nxt_pos[t] < x) {  // only after a repeated entry: skip it
+        while (nxt_pos[t] < x) {  // a chunk listed twice: attended once
           ++cur[t];
           nxt_pos[t] = sm.spos[cur[t]];
-          nxt_alpha[t] = nxt_pos[t] != kNoPos ? wl[wrow[t] + sm.sk[cur[t]]] : 0.f;
+          nxt_alpha[t] = wl[wrow[t] + sm.sk[cur[t]]];
         }
-        const bool act = nxt_pos[t] == x;
-        wgt[t] = act ? __expf(nxt_alpha[t] - R.m_row[t]) : 0.f;
+        act[t] = nxt_pos[t] == x;
+        wgt[t] = act[t] ? __expf(nxt_alpha[t] - R.m_row[t]) : 0.f;
         lim[t] = 0;
-        if (__ballot(act)) mask |= 1 << t;
-        if (act) {
-          ++cur[t];
-          nxt_pos[t] = sm.spos[cur[t]];
-          nxt_alpha[t] = nxt_pos[t] != kNoPos ? wl[wrow[t] + sm.sk[cur[t]]] : 0.f;
-        }
+        if (__ballot(act[t])) mask |= 1 << t;
       }
       run_item<D, TPW, true, false>(mask, R, ksb, vtb, koff, voff, wgt, lim, tau, tl2e);
+      // rows that took their entry move on; the reads land during the
+      // barrier wait instead of ahead of the tiles
+#pragma unroll
+      for (int t = 0; t < TPW; ++t) {
+        cur[t] += act[t] ? 1 : 0;
+        nxt_pos[t] = sm.spos[cur[t]];
+        nxt_alpha[t] = wl[wrow[t] + sm.sk[cur[t]]];
+      }
     } else {
       // Query i's window starts at n_i * S, a multiple of the block size
       // (S = 64): a block lies in it from its first key on, up to key i, or
