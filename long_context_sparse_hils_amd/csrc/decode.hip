@@ -117,6 +117,7 @@ decode_score_kernel(DecodeArgs a) {
   }
 
   // ---------------- score slice: chunks [c0, c0 + nch) of the G heads
+  if (a.Cmax == 0) return;  // no chunk summary is stored (k_sum may be absent)
   const int c0 = blk * kCPB;
   const int nch = max(0, min(c0 + kCPB, n) - c0);
   constexpr int LPH = D / 8;                         // lanes per (chunk, head) row, 8 elements each
@@ -131,19 +132,20 @@ decode_score_kernel(DecodeArgs a) {
   const size_t hbase = static_cast<size_t>(b) * a.Hq + g * G;
   // Batches of RS rows, double buffered in registers: the loads of batch
   // n + 1 are in flight while batch n is reduced.
-  // Branch-free: rows past the slice read its row 0 again (their dots are
-  // never stored; chunk c0 exists even when the slice is empty), and every
-  // lane of a row reads the row's b'.  A load under a
-  // lane-dependent branch would make the compiler wait for every load in
-  // flight at the branch's end.
+  // Branch-free, and independent of n (a dependent load: the sequence
+  // length): every row of the slice is read, its chunk clamped to the last
+  // one stored, and rows past the slice read its row 0 again.  Only the
+  // rows of eligible chunks are stored.  Every lane of a row reads the
+  // row's b'.  A load under a lane-dependent branch would make the compiler
+  // wait for every load in flight at the branch's end.
   auto load_batch = [&](int rb, uint4 (&kv)[U * RPP], float (&bs)[U]) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int p = u * kDecThreads + t;
       const int row = rb + p / LPH, seg = p % LPH;
-      const int rr = (row < nrows && (row & (kCPB - 1)) < nch) ? row : 0;
+      const int rr = row < G * kCPB ? row : 0;
       const int cl = rr & (kCPB - 1), hh = rr / kCPB;
-      const size_t ro = (hbase + hh) * a.Cmax + c0 + cl;
+      const size_t ro = (hbase + hh) * a.Cmax + min(c0 + cl, a.Cmax - 1);
 #pragma unroll
       for (int r = 0; r < RPP; ++r) kv[u * RPP + r] = reinterpret_cast<const uint4 *>(ks + ro * D + seg * 8)[r];
       bs[u] = a.b_sum[ro];
@@ -510,19 +512,30 @@ __device__ __forceinline__ void select_survivors(SelSmem &ss, int tot, int K) {
 //  3. when too many scores pass (many equal scores), the tile falls back to
 //     the exact block-wide search.
 // On return ss.sorted[0..keep) holds the winners in rank order; returns keep.
-__device__ __forceinline__ int block_topk(const float *sig, int n, int K, SelSmem &ss) {
+__device__ __forceinline__ int block_topk(const float *sig, int n, int cmax, int K, SelSmem &ss) {
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   int slot = 0;
+  // loads without a lane-dependent branch, all issued before the first is
+  // used; the first tile's go out before n is known (it follows from the
+  // sequence length, itself a load): they read every stored score (past
+  // cmax, sigma[0] again) and n masks them afterwards
+  float sv[kSelVPT];
+  if (cmax > 0) {
+#pragma unroll
+    for (int j = 0; j < kSelVPT; ++j) {
+      const int c = j * kDecThreads + t;
+      sv[j] = sig[c < cmax ? c : 0];
+    }
+  }
   if (t == 0) ss.nkey = 0;
   __syncthreads();
   for (int tile0 = 0; tile0 < n; tile0 += kDecThreads * kSelVPT) {
-    // loads without a lane-dependent branch (past n they re-read sigma[0]),
-    // all issued before the first is used
-    float sv[kSelVPT];
+    if (tile0 > 0) {  // (past n, sigma[0] again)
 #pragma unroll
-    for (int j = 0; j < kSelVPT; ++j) {
-      const int c = tile0 + j * kDecThreads + t;
-      sv[j] = sig[c < n ? c : 0];
+      for (int j = 0; j < kSelVPT; ++j) {
+        const int c = tile0 + j * kDecThreads + t;
+        sv[j] = sig[c < n ? c : 0];
+      }
     }
     uint32_t mx = 0u;
 #pragma unroll
@@ -625,7 +638,7 @@ decode_attend_kernel(DecodeArgs a) {
       const int x = t + r * kDecThreads;
       if (r * kDecThreads < G * D) qreg[r] = Elem<T>::load(qsrc, x < G * D ? x : 0);
     }
-    const int keep = block_topk(a.sig + bg * a.Cmax, n, K, ss);
+    const int keep = block_topk(a.sig + bg * a.Cmax, n, a.Cmax, K, ss);
 #pragma unroll
     for (int r = 0; r < QPT; ++r) {
       const int x = t + r * kDecThreads;

@@ -323,8 +323,10 @@ score_topk_mfma_kernel(ScoreArgs a, const uint16_t *__restrict__ u_hi, const uin
         src = ksb + ((static_cast<size_t>(b) * Hq + h) * C + c) * D + ((pp ^ score_swz(r, kPk)) << 3);
         dst = item_ks(buf) + sl * 512;
       } else {
-        const int y = sl - kSlK, lohi = y / slm, part = y % slm;
-        const int slot = part * 64 + lane, r = slot / Pm, pp = slot % Pm;
+        // (reached only with Q-Cal: slm, Pm > 0)
+        const int slm1 = slm > 0 ? slm : 1, Pm1 = Pm > 0 ? Pm : 1;
+        const int y = sl - kSlK, lohi = y / slm1, part = y % slm1;
+        const int slot = part * 64 + lane, r = slot / Pm1, pp = slot % Pm1;
         const int c = min(c0 + r, C - 1);
         src = (lohi ? m_lo : m_hi) + ((static_cast<size_t>(b) * Hq + h) * C + c) * RP + ((pp ^ score_swz(r, Pm)) << 3);
         dst = (lohi ? item_ml(buf) : item_mh(buf)) + part * 512;

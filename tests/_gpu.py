@@ -95,7 +95,7 @@ def check_topk(gpu_idx, ora_idx, sigma, tol=NEAR_TIE):
     [..., K], sigma [..., C] (oracle group scores, float64)."""
     g = gpu_idx.reshape(-1, gpu_idx.shape[-1])
     o = ora_idx.reshape(-1, ora_idx.shape[-1])
-    s = sigma.reshape(-1, sigma.shape[-1])
+    s = sigma.reshape(g.shape[0], -1)  # (also with no chunk at all)
     ties = 0
     for r in range(g.shape[0]):
         if np.array_equal(g[r], o[r]):

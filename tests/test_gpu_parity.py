@@ -180,6 +180,8 @@ DECODE_CASES = {
     "f32_d64_g1": (wl_decode(B=2, T=2048, Hq=2, Hkv=2, d=64, K=4, W=128, dtype="f32"), [2048, 191]),
     "k0": (wl_decode(B=2, K=0), [4096, 700]),
     "g8_k32": (wl_decode(B=1, T=8192, Hq=8, Hkv=1, d=64, K=32, W=256), [8000]),
+    # a cache shorter than one chunk: no summary stored, window only
+    "no_chunk": (wl_decode(B=2, T=48, Hq=4, Hkv=1, d=64, K=4, W=32, needles="none"), [48, 17]),
 }
 
 
