@@ -275,8 +275,14 @@ score_topk_mfma_kernel(ScoreArgs a, const uint16_t *__restrict__ u_hi, const uin
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int ln = lane & 15, lg = lane >> 4;
   const int T = a.T, C = a.C, K = a.K, Hq = a.Hq, Hkv = a.Hkv, G = Hq / Hkv;
-  const int g = blockIdx.y, b = blockIdx.z;
-  const int q_wg = blockIdx.x * QW;
+  // one-dimensional grid, query block slowest: the latest (heaviest: most
+  // eligible chunks) query blocks of every (b, g) go first, so that the
+  // light ones fill the tail
+  const int npair = Hkv * a.B;
+  const int xq = static_cast<int>(blockIdx.x) / npair, pair = static_cast<int>(blockIdx.x) % npair;
+  const int g = pair % Hkv, b = pair / Hkv;
+  const int nqb = (T + QW - 1) / QW;
+  const int q_wg = (nqb - 1 - xq) * QW;
   const int qw0 = q_wg + wave * 16;  // the wave's first query
   const bool qcal = QR >= 0 ? QR > 0 : a.r > 0;
   const int i_me = qw0 + ln;         // this lane's query (B column)
@@ -665,7 +671,7 @@ hipError_t launch_score_mfma(const ScoreArgs &a, hipStream_t st) {
     hipError_t e2 = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),                              \
                                         hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem)); \
     if (e2 != hipSuccess) return e2;                                                                      \
-    kern<<<dim3((a.T + WW * 16 - 1) / (WW * 16), a.Hkv, a.B), WW * 64, smem, st>>>(a, u_hi, u_lo, m_hi, m_lo, RPa); \
+    kern<<<dim3((a.T + WW * 16 - 1) / (WW * 16) * a.Hkv * a.B), WW * 64, smem, st>>>(a, u_hi, u_lo, m_hi, m_lo, RPa); \
     return hipGetLastError();                                                                             \
   }
   HILS_SCORE(128, 1, 8, 4, 0) HILS_SCORE(128, 1, 8, 4, 1) HILS_SCORE(128, 1, 8, 4, 2)
