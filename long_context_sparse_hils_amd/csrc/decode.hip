@@ -122,7 +122,8 @@ decode_score_kernel(DecodeArgs a) {
   const int nch = max(0, min(c0 + kCPB, n) - c0);
   constexpr int LPH = D / 8;                         // lanes per (chunk, head) row, 8 elements each
   constexpr int RPP = static_cast<int>(sizeof(T)) / 2;  // 16-byte loads per 8-element piece
-  constexpr int U = 8 / RPP;                         // pieces in flight per thread
+  constexpr int U = 4 / RPP;                         // pieces in flight per thread (80 registers:
+                                                     // five workgroups per CU, the whole grid at once)
   constexpr int RS = U * kDecThreads / LPH;          // rows per batch
   // rows are (head, chunk) in head-major order, row = hh * kCPB + cl: the 4
   // rows one load instruction covers are 1 KB of one head's contiguous
