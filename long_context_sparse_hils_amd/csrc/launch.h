@@ -33,7 +33,7 @@ struct AttnArgs {
   const int32_t *topk_idx;
   const float *topk_score;
   void *o;
-  void *vt_ws;  // prefill workspace: transposed value tiles of the MFMA path
+  void *vt_ws;  // prefill workspace: transposed value tiles of the MFMA path, then its query grouping
   int B, T, Hq, Hkv, d, S, K, W;
   float tau;
   bool bf16;

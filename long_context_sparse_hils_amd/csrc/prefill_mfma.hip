@@ -303,12 +303,119 @@ __device__ __forceinline__ void run_item(int mask, RowState<D, TPW> &R, const ui
                                     tau, tl2e);
 }
 
+// ------------------------------------------------------------------ query grouping
+// Which QPT of a workgroup's QT queries share a 16-row tile.  A tile runs a
+// chunk item when any of its queries selected the chunk, so tiles of
+// queries with overlapping selections run fewer items: greedily, each tile
+// starts from the lowest remaining query and takes, one at a time, the
+// query whose chunks add the fewest to the tile's union (ties: the lower
+// query).  Rows are independent, so every grouping gives the same outputs.
+// One wave per workgroup tile; plan[(pair * ntiles + tile) * QT + s] is the
+// local query of row slot s = tile_in_workgroup * QPT + query_in_tile.
+// Workgroups of more than 64 queries (one per lane) keep the identity.
+template <int QT, int QPT>
+__global__ void __launch_bounds__(64)
+attn_plan_kernel(const int32_t *__restrict__ topk_idx, uint8_t *__restrict__ plan, int T, int K, int ntiles) {
+  constexpr bool kGroup = QT <= 64 && QPT > 1;
+  constexpr int kNW = kGroup ? QT : 1;              // union words per query (K <= 32)
+  constexpr int kPer = kGroup ? QT * 32 / 64 : 1;   // (query, slot) entries per lane
+  __shared__ uint32_t umask[256];                   // chunk bit mask (at most 8192 chunks)
+  __shared__ int wbase[256];                        // union positions before each word
+  __shared__ uint32_t qm[kGroup ? QT : 1][kNW + 1]; // per query: its chunks' union positions (padded rows)
+  __shared__ uint32_t uni[kNW];                     // the tile being formed
+  const int L = blockIdx.x, lane = threadIdx.x;
+  const int tile = L % ntiles, pair = L / ntiles;
+  const int q0 = tile * QT;
+  uint8_t *out = plan + static_cast<size_t>(L) * QT;
+  if (!kGroup || K <= 0) {
+    for (int s = lane; s < QT; s += 64) out[s] = static_cast<uint8_t>(s);
+    return;
+  }
+  const int nwc = (T / kItemKeys + 31) >> 5;  // words of the chunk mask
+  for (int w = lane; w < 256; w += 64) umask[w] = 0u;
+  for (int x = lane; x < QT * (kNW + 1); x += 64) (&qm[0][0])[x] = 0u;
+  __syncthreads();
+  // the tile's selections: entry e = (query e / K, slot e % K); past T, none
+  const int32_t *idx = topk_idx + static_cast<size_t>(pair) * T * K;
+  int cv[kPer];
+#pragma unroll
+  for (int r = 0; r < kPer; ++r) {
+    const int e = lane + 64 * r, q = e / K;
+    const bool ok = e < QT * K && q0 + q < T;
+    const int c = idx[static_cast<size_t>(ok ? q0 + q : 0) * K + (ok ? e % K : 0)];
+    cv[r] = ok ? c : -1;
+  }
+#pragma unroll
+  for (int r = 0; r < kPer; ++r)
+    if (cv[r] >= 0) atomicOr(&umask[cv[r] >> 5], 1u << (cv[r] & 31));
+  __syncthreads();
+  // union positions: exclusive prefix of the words' popcounts (four words a lane)
+  {
+    int cnt[4], tot = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int w = 4 * lane + j;
+      cnt[j] = w < nwc ? __popc(umask[w]) : 0;
+      tot += cnt[j];
+    }
+    int incl = tot;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += y;
+    }
+    int run = incl - tot;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int w = 4 * lane + j;
+      if (w < 256) wbase[w] = run;
+      run += cnt[j];
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < kPer; ++r) {
+    const int c = cv[r];
+    if (c >= 0) {
+      const int upos = wbase[c >> 5] + __popc(umask[c >> 5] & ((1u << (c & 31)) - 1u));
+      atomicOr(&qm[(lane + 64 * r) / K][upos >> 5], 1u << (upos & 31));
+    }
+  }
+  __syncthreads();
+  const int last = nwc > 0 ? nwc - 1 : 0;
+  const int nu = wbase[last] + __popc(umask[last]);  // union size
+  const int nw = (nu + 31) >> 5;
+  // greedy grouping; lane q stands for query q
+  unsigned long long rem = QT == 64 ? ~0ull : ((1ull << QT) - 1ull);
+  for (int t = 0; t < QT / QPT; ++t) {
+    const int seed = __ffsll(static_cast<long long>(rem)) - 1;
+    rem &= ~(1ull << seed);
+    if (lane == 0) out[t * QPT] = static_cast<uint8_t>(seed);
+    for (int w = lane; w < nw; w += 64) uni[w] = qm[seed][w];
+    __syncthreads();
+    for (int k = 1; k < QPT; ++k) {
+      uint32_t key = 0xFFFFFFFFu;
+      if (lane < QT && ((rem >> lane) & 1ull)) {
+        uint32_t cost = 0;
+        for (int w = 0; w < nw; ++w) cost += __popc(uni[w] | qm[lane][w]);
+        key = (cost << 8) | static_cast<uint32_t>(lane);
+      }
+      key = wave_reduce_u32<0>(key);
+      const int best = static_cast<int>(key & 0xFFu);
+      rem &= ~(1ull << best);
+      if (lane == 0) out[t * QPT + k] = static_cast<uint8_t>(best);
+      for (int w = lane; w < nw; w += 64) uni[w] |= qm[best][w];
+      __syncthreads();
+    }
+  }
+}
+
 // ------------------------------------------------------------------ kernel
 // One tile per wave: four waves per SIMD (two workgroups per CU), at most 128
 // registers; two tiles per wave: two waves per SIMD, at most 256.
 template <int D, int G, int WAVES, int TPW>
 __global__ void __launch_bounds__(WAVES * 64, TPW == 1 ? 4 : 2)
-attn_prefill_mfma_kernel(AttnArgs a, int ntiles, int xcd_map, int nblk) {
+attn_prefill_mfma_kernel(AttnArgs a, const uint8_t *__restrict__ plan, int ntiles, int xcd_map, int nblk) {
   using C = AttnCfg<D, G, WAVES, TPW>;
   extern __shared__ __align__(16) unsigned char smem_raw[];
   AttnSmem<D, G, WAVES, TPW> &sm = *reinterpret_cast<AttnSmem<D, G, WAVES, TPW> *>(smem_raw);
@@ -319,10 +426,10 @@ attn_prefill_mfma_kernel(AttnArgs a, int ntiles, int xcd_map, int nblk) {
   const int C_chunks = T / kItemKeys;  // chunk size S = 64 on this path
   // ---- workgroup -> (tile, g, b); heaviest (latest) tiles first, and the
   // tiles of one (b, g) on one XCD so its K/V stay in that XCD's L2
-  int tile, g, b;
+  int tile, g, b, pair;
   {
     const int L = blockIdx.x;
-    int pair, slot;
+    int slot;
     if (xcd_map) {
       const int xcd = L & 7, s = L >> 3;
       pair = xcd + 8 * (s / ntiles);
@@ -345,8 +452,15 @@ attn_prefill_mfma_kernel(AttnArgs a, int ntiles, int xcd_map, int nblk) {
 
   // ---- every global load of the set-up is issued here, at once, with
   // clamped indices and no lane-dependent branch (so that nothing waits for
-  // one load before issuing the next): the selections (query, slot) of the
-  // tile, the Q operands of the wave's rows and the rows' fusion scores.
+  // one load before issuing the next): the rows' queries in the grouping of
+  // attn_plan_kernel (first: the Q loads need them), the selections (query,
+  // slot) of the tile, the rows' fusion scores, then the Q operands.
+  int row_q[TPW];
+  {
+    const uint8_t *pt = plan + (static_cast<size_t>(pair) * ntiles + tile) * C::kQT;
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) row_q[t] = min(static_cast<int>(pt[wave * C::kQPW + t * C::kQPT + ln / G]), C::kQT - 1);
+  }
   constexpr int kPairs = (C::kQT * C::kKMax + C::kThreads - 1) / C::kThreads;
   constexpr int kWPT = (C::kQT * G * C::kKMax + C::kThreads - 1) / C::kThreads;
   const int kc_max = K > 0 ? K - 1 : 0;
@@ -370,15 +484,10 @@ attn_prefill_mfma_kernel(AttnArgs a, int ntiles, int xcd_map, int nblk) {
     }
   }
   // per-lane row identity for the tiles
-  int row_q[TPW];
   const int row_h = g * G + (ln % G);  // the same head in every tile
   bool row_ok[TPW];
 #pragma unroll
-  for (int t = 0; t < TPW; ++t) {
-    const int q = wave * C::kQPW + t * C::kQPT + ln / G;
-    row_q[t] = q;
-    row_ok[t] = (q0 + q) < T;
-  }
+  for (int t = 0; t < TPW; ++t) row_ok[t] = (q0 + row_q[t]) < T;
   RowState<D, TPW> R;
   // Q operands (B of S^T = K Q^T): lane holds row ln, d = 32 ks + 8 lg .. +8;
   // rows past T read the last query (their results are not stored)
@@ -685,6 +794,12 @@ attn_prefill_mfma_kernel(AttnArgs a, int ntiles, int xcd_map, int nblk) {
   }
 }
 
+// value tiles (bf16), rounded up to 256 bytes
+static size_t attn_vt_bytes(int B, int Hkv, int T, int d) {
+  const size_t nblk = (static_cast<size_t>(T) + kItemKeys - 1) / kItemKeys;
+  return (static_cast<size_t>(B) * Hkv * nblk * kItemKeys * d * 2 + 255) / 256 * 256;
+}
+
 template <int D, int G>
 static hipError_t attn_mfma_t(const AttnArgs &a, hipStream_t st) {
   constexpr int WAVES = 4, TPW = 2;
@@ -696,13 +811,18 @@ static hipError_t attn_mfma_t(const AttnArgs &a, hipStream_t st) {
                                                              static_cast<uint16_t *>(a.vt_ws), a.T, nblk);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  // the query grouping, after the value tiles in the workspace
+  uint8_t *plan = static_cast<uint8_t *>(a.vt_ws) + attn_vt_bytes(a.B, a.Hkv, a.T, D);
+  attn_plan_kernel<C::kQT, C::kQPT><<<dim3(ntiles * npairs), 64, 0, st>>>(a.topk_idx, plan, a.T, a.K, ntiles);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
   const int xcd_map = (npairs % 8 == 0) ? 1 : 0;
   const size_t smem = sizeof(AttnSmem<D, G, WAVES, TPW>) + static_cast<size_t>(C::kQT) * G * a.K * sizeof(float);
   auto kern = attn_prefill_mfma_kernel<D, G, WAVES, TPW>;
   e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
                           static_cast<int>(smem));
   if (e != hipSuccess) return e;
-  kern<<<dim3(ntiles * npairs), C::kThreads, smem, st>>>(a, ntiles, xcd_map, nblk);
+  kern<<<dim3(ntiles * npairs), C::kThreads, smem, st>>>(a, plan, ntiles, xcd_map, nblk);
   return hipGetLastError();
 }
 
@@ -712,9 +832,10 @@ bool attn_mfma_supported(const AttnArgs &a) {
          a.S == kItemKeys && a.K <= 32 && a.T / a.S <= 8192;
 }
 
+// value tiles, then the grouping: one byte per (pair, query slot), at most
+// 128 slots of padding per pair
 size_t attn_mfma_ws_bytes(int B, int Hkv, int T, int d) {
-  const size_t nblk = (static_cast<size_t>(T) + kItemKeys - 1) / kItemKeys;
-  return static_cast<size_t>(B) * Hkv * nblk * kItemKeys * d * 2;
+  return attn_vt_bytes(B, Hkv, T, d) + static_cast<size_t>(B) * Hkv * (static_cast<size_t>(T) + 128);
 }
 
 hipError_t launch_attn_mfma(const AttnArgs &a, hipStream_t st) {
