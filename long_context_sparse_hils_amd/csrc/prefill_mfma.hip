@@ -310,104 +310,77 @@ __device__ __forceinline__ void run_item(int mask, RowState<D, TPW> &R, const ui
 // starts from the lowest remaining query and takes, one at a time, the
 // query whose chunks add the fewest to the tile's union (ties: the lower
 // query).  Rows are independent, so every grouping gives the same outputs.
-// One wave per workgroup tile; plan[(pair * ntiles + tile) * QT + s] is the
-// local query of row slot s = tile_in_workgroup * QPT + query_in_tile.
-// Workgroups of more than 64 queries (one per lane) keep the identity.
+// One wave per workgroup tile (four per block, independent: no LDS, no
+// barrier), lane q for query q, each query's chunks as a bit mask of the
+// chunk ids in four registers (up to 128 chunks: T <= 8192 with S = 64); the
+// forming tile's union in scalar registers (readlane), and lane s keeps the
+// query chosen for row slot s.
+// plan[(pair * ntiles + tile) * QT + s] is the local query of row slot
+// s = tile_in_workgroup * QPT + query_in_tile.  More chunks, or workgroups
+// of more than 64 queries, keep the identity.
 template <int QT, int QPT>
-__global__ void __launch_bounds__(64)
-attn_plan_kernel(const int32_t *__restrict__ topk_idx, uint8_t *__restrict__ plan, int T, int K, int ntiles) {
+__global__ void __launch_bounds__(256)
+attn_plan_kernel(const int32_t *__restrict__ topk_idx, uint8_t *__restrict__ plan, int T, int K, int ntiles,
+                 int nplans) {
   constexpr bool kGroup = QT <= 64 && QPT > 1;
-  constexpr int kNW = kGroup ? QT : 1;              // union words per query (K <= 32)
-  constexpr int kPer = kGroup ? QT * 32 / 64 : 1;   // (query, slot) entries per lane
-  __shared__ uint32_t umask[256];                   // chunk bit mask (at most 8192 chunks)
-  __shared__ int wbase[256];                        // union positions before each word
-  __shared__ uint32_t qm[kGroup ? QT : 1][kNW + 1]; // per query: its chunks' union positions (padded rows)
-  __shared__ uint32_t uni[kNW];                     // the tile being formed
-  const int L = blockIdx.x, lane = threadIdx.x;
+  const int L = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (L >= nplans) return;
   const int tile = L % ntiles, pair = L / ntiles;
   const int q0 = tile * QT;
   uint8_t *out = plan + static_cast<size_t>(L) * QT;
-  if (!kGroup || K <= 0) {
-    for (int s = lane; s < QT; s += 64) out[s] = static_cast<uint8_t>(s);
+  if (!kGroup || K <= 0 || K > 32 || T / kItemKeys > 128) {
+    for (int x = lane; x < QT; x += 64) out[x] = static_cast<uint8_t>(x);
     return;
   }
-  const int nwc = (T / kItemKeys + 31) >> 5;  // words of the chunk mask
-  for (int w = lane; w < 256; w += 64) umask[w] = 0u;
-  for (int x = lane; x < QT * (kNW + 1); x += 64) (&qm[0][0])[x] = 0u;
-  __syncthreads();
-  // the tile's selections: entry e = (query e / K, slot e % K); past T, none
-  const int32_t *idx = topk_idx + static_cast<size_t>(pair) * T * K;
-  int cv[kPer];
-#pragma unroll
-  for (int r = 0; r < kPer; ++r) {
-    const int e = lane + 64 * r, q = e / K;
-    const bool ok = e < QT * K && q0 + q < T;
-    const int c = idx[static_cast<size_t>(ok ? q0 + q : 0) * K + (ok ? e % K : 0)];
-    cv[r] = ok ? c : -1;
-  }
-#pragma unroll
-  for (int r = 0; r < kPer; ++r)
-    if (cv[r] >= 0) atomicOr(&umask[cv[r] >> 5], 1u << (cv[r] & 31));
-  __syncthreads();
-  // union positions: exclusive prefix of the words' popcounts (four words a lane)
+  // this lane's query: its selected chunks as a 128-bit mask (past T: none)
+  uint32_t mine[4] = {0u, 0u, 0u, 0u};
   {
-    int cnt[4], tot = 0;
+    const bool ok = lane < QT && q0 + lane < T;
+    const int32_t *row = topk_idx + (static_cast<size_t>(pair) * T + (ok ? q0 + lane : 0)) * K;
+    // all loads in flight at once: 16-byte pieces when K is a multiple of 4
+    // (rows are then 16-byte aligned), else single slots; pieces / slots past
+    // K re-read the last one and count for nothing
+    int cs[32];
+    if ((K & 3) == 0) {
+      const int4 *rv = reinterpret_cast<const int4 *>(row);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int w = 4 * lane + j;
-      cnt[j] = w < nwc ? __popc(umask[w]) : 0;
-      tot += cnt[j];
+      for (int v = 0; v < 8; ++v) {
+        const int4 x = rv[min(v, K / 4 - 1)];
+        cs[4 * v] = x.x; cs[4 * v + 1] = x.y; cs[4 * v + 2] = x.z; cs[4 * v + 3] = x.w;
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < 32; ++k) cs[k] = row[min(k, K - 1)];
     }
-    int incl = tot;
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int y = __shfl_up(incl, o, 64);
-      if (lane >= o) incl += y;
-    }
-    int run = incl - tot;
+    for (int k = 0; k < 32; ++k) {
+      const int c = (ok && k < K) ? cs[k] : -1;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int w = 4 * lane + j;
-      if (w < 256) wbase[w] = run;
-      run += cnt[j];
-    }
-  }
-  __syncthreads();
-#pragma unroll
-  for (int r = 0; r < kPer; ++r) {
-    const int c = cv[r];
-    if (c >= 0) {
-      const int upos = wbase[c >> 5] + __popc(umask[c >> 5] & ((1u << (c & 31)) - 1u));
-      atomicOr(&qm[(lane + 64 * r) / K][upos >> 5], 1u << (upos & 31));
+      for (int w = 0; w < 4; ++w) mine[w] |= (c >= 0 && (c >> 5) == w) ? (1u << (c & 31)) : 0u;
     }
   }
-  __syncthreads();
-  const int last = nwc > 0 ? nwc - 1 : 0;
-  const int nu = wbase[last] + __popc(umask[last]);  // union size
-  const int nw = (nu + 31) >> 5;
-  // greedy grouping; lane q stands for query q
   unsigned long long rem = QT == 64 ? ~0ull : ((1ull << QT) - 1ull);
+  int chosen = lane;  // the query of row slot `lane`
   for (int t = 0; t < QT / QPT; ++t) {
     const int seed = __ffsll(static_cast<long long>(rem)) - 1;
     rem &= ~(1ull << seed);
-    if (lane == 0) out[t * QPT] = static_cast<uint8_t>(seed);
-    for (int w = lane; w < nw; w += 64) uni[w] = qm[seed][w];
-    __syncthreads();
+    chosen = lane == t * QPT ? seed : chosen;
+    uint32_t u[4];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) u[w] = __builtin_amdgcn_readlane(mine[w], seed);
     for (int k = 1; k < QPT; ++k) {
-      uint32_t key = 0xFFFFFFFFu;
-      if (lane < QT && ((rem >> lane) & 1ull)) {
-        uint32_t cost = 0;
-        for (int w = 0; w < nw; ++w) cost += __popc(uni[w] | qm[lane][w]);
-        key = (cost << 8) | static_cast<uint32_t>(lane);
-      }
-      key = wave_reduce_u32<0>(key);
-      const int best = static_cast<int>(key & 0xFFu);
+      const bool cand = lane < QT && ((rem >> lane) & 1ull);
+      const uint32_t cost =
+          __popc(u[0] | mine[0]) + __popc(u[1] | mine[1]) + __popc(u[2] | mine[2]) + __popc(u[3] | mine[3]);
+      const uint32_t key = wave_reduce_u32<0>(cand ? (cost << 8) | static_cast<uint32_t>(lane) : 0xFFFFFFFFu);
+      const int best = static_cast<int>(__builtin_amdgcn_readfirstlane(key) & 0xFFu);
       rem &= ~(1ull << best);
-      if (lane == 0) out[t * QPT + k] = static_cast<uint8_t>(best);
-      for (int w = lane; w < nw; w += 64) uni[w] |= qm[best][w];
-      __syncthreads();
+      chosen = lane == t * QPT + k ? best : chosen;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) u[w] |= __builtin_amdgcn_readlane(mine[w], best);
     }
   }
+  if (lane < QT) out[lane] = static_cast<uint8_t>(chosen);
 }
 
 // ------------------------------------------------------------------ kernel
@@ -813,7 +786,8 @@ static hipError_t attn_mfma_t(const AttnArgs &a, hipStream_t st) {
   if (e != hipSuccess) return e;
   // the query grouping, after the value tiles in the workspace
   uint8_t *plan = static_cast<uint8_t *>(a.vt_ws) + attn_vt_bytes(a.B, a.Hkv, a.T, D);
-  attn_plan_kernel<C::kQT, C::kQPT><<<dim3(ntiles * npairs), 64, 0, st>>>(a.topk_idx, plan, a.T, a.K, ntiles);
+  attn_plan_kernel<C::kQT, C::kQPT><<<dim3((ntiles * npairs + 3) / 4), 256, 0, st>>>(a.topk_idx, plan, a.T, a.K,
+                                                                                     ntiles, ntiles * npairs);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int xcd_map = (npairs % 8 == 0) ? 1 : 0;
