@@ -138,7 +138,8 @@ hils_status hils_chunk_score_topk(const hils_config *cfg, const void *q, const v
  *   topk_score [B, H_q, T, K]   f32
  *   workspace  >= hils_prefill_workspace_bytes(cfg) bytes, device memory
  *              (may be the one given to hils_chunk_score_topk: this call
- *              overwrites it with transposed value tiles, in stream order).
+ *              overwrites it with transposed value tiles and its query
+ *              grouping, in stream order).
  */
 hils_status hils_sparse_attn_prefill(const hils_config *cfg, const void *q, const void *k,
                                      const void *v, const int32_t *topk_idx,
