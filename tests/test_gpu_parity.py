@@ -48,6 +48,8 @@ PREFILL_CASES = {
     "short_T_le_W": wl_prefill(T=300, Hq=4, Hkv=2, d=128, K=4, W=512),
     "k0_window_only": wl_prefill(T=1024, Hq=4, Hkv=2, d=64, K=0, W=192),
     "g8": wl_prefill(T=1024, Hq=8, Hkv=1, d=64, K=8, W=128),
+    # a top-K that is not a multiple of 4 (single-slot loads of the lists)
+    "bf16_k5": wl_prefill(T=1024, Hq=8, Hkv=2, d=128, K=5, W=128),
     # Q-Cal rank 48 (two 32-wide halves, the second part-filled) over a
     # hidden size with a 96-column tail past its 128-wide steps
     "qcal_r48_ragged_dh": wl_prefill(T=1024, Hq=4, Hkv=2, d=64, K=8, W=128, r=48, Dh=352),
