@@ -1,13 +1,14 @@
 // Prefill hierarchical sparse attention on the MFMA units (bf16 operands,
 // fp32 accumulation) -- HiLS-Attention, picx.dev summary, Methodology 2
-// (Eq. 10) and 3 (query packing: M adjacent queries x G heads share the
-// union of their selected chunks so that matrix tiles stay full).
+// (Eq. 10) and 3 (query packing: M queries x G heads share the union of
+// their selected chunks so that matrix tiles stay full).
 //
-// Workgroup = (tile of QT adjacent queries, KV head g, batch b), 4 waves (one
-// per SIMD) in under 80 KB of LDS, so that two workgroups share a CU and
-// fill each other's barrier waits and softmax phases with MFMA work.
-// Each wave owns 32 (query, head) rows = two 16-row MFMA tiles of
-// 16/G queries x G heads, with fp32 output accumulators in registers.
+// Workgroup = (QT consecutive queries, KV head g, batch b), 4 waves (one per
+// SIMD) in under 80 KB of LDS, so that two workgroups share a CU and fill
+// each other's barrier waits and softmax phases with MFMA work.  Each wave
+// owns 32 (query, head) rows = two 16-row MFMA tiles of 16/G queries x G
+// heads, with fp32 output accumulators in registers; which queries share a
+// tile comes from attn_plan_kernel (grouped by selection overlap).
 //
 // The workgroup walks a list of 64-key "items": first every chunk in the
 // union of its queries' selections, then the 64-key blocks of the window
@@ -15,8 +16,8 @@
 // ([d][key], padded rows; read from value tiles transposed once per call by
 // a small kernel) are staged once in LDS, double buffered, and shared by all
 // waves.  Per item, each wave runs only the row tiles that take part (one of
-// their rows selected the chunk / overlaps the window block), and the tiles
-// it runs share every K and V^T operand read:
+// their rows selected the chunk / overlaps the window block), one after the
+// other:
 //   S^T = K Q^T           16x16x32 bf16 MFMA, keys in M, rows in N
 //   chunk item:  p = softmax over the chunk's 64 keys (exact), scaled by the
 //                fusion weight e^{s_hat - M_row}; rows that did not select
