@@ -13,17 +13,19 @@
 // Kernels:
 //   qcal_u_mfma      u[token, a]   MFMA GEMM over D_h  -> u_hi/u_lo [B*T, RP]
 //   qcal_m           m[b, h, c, a] VALU (tiny)          -> m_hi/m_lo [B, Hq, C, RP]
-//   score_topk_mfma  per (128 queries, KV head, batch), 8 waves of 16 queries:
-//                    tiles of 16 chunks x (up to 4 heads) of k', m and b' are
-//                    staged once in LDS for all waves (double buffered, loaded
-//                    straight from global memory); each wave forms S^T tiles
-//                    of 16 chunks x 16 queries per head, keeps the max over
-//                    the group's heads in LDS, then per query runs a
-//                    ballot-driven radix select of the K-th largest group
-//                    score and a rank pass that orders the winners by (score
-//                    desc, chunk asc); a second pass over the tiles (same
-//                    arithmetic, bit-identical) writes each head's own score
-//                    for the winners.
+//   score_topk_mfma  per (128 queries, KV head, batch), 8 waves of 16 queries,
+//                    the latest (heaviest) query blocks first: items of 64
+//                    chunks x one head of k', m and b' are staged once in LDS
+//                    for all waves (double buffered, loaded straight from
+//                    global memory); each wave forms S^T tiles of 16 chunks x
+//                    16 queries per head.  Groups of at most 4 heads keep
+//                    every head's score in registers (one pass); larger
+//                    groups keep the group maximum and recompute the
+//                    winners' per-head scores in a second pass (the same
+//                    arithmetic, bit-identical).  Per query, a bitwise search
+//                    for the K-th largest group score (counts from row sums
+//                    of the 4 lanes of a query) and a rank pass order the
+//                    winners by (score desc, chunk asc).
 #include "hils_common.h"
 #include "launch.h"
 
