@@ -181,8 +181,48 @@ hils_status hils_sparse_attn_decode(const hils_config *cfg, const void *q, const
                                     void *stream);
 
 /* Byte offset, inside a decode workspace, of the uint32 that counts clamped
- * seq_lens entries (cumulative; the caller may reset it to zero). */
+ * seq_lens entries and, for the paged call, page indices outside the pool
+ * (cumulative; the caller may reset it to zero). */
 size_t hils_decode_error_offset(const hils_config *cfg);
+
+/*
+ * Paged caches for serving.  A page holds one chunk (S = 64 consecutive
+ * positions of one sequence) for every KV head:
+ *   k_pages, v_pages  [num_pages, H_kv, S, d]  dtype
+ *   block_table       [B, max_pages]           int32, device: page of chunk
+ *                     (64-position block) c of sequence b
+ * cfg->seq_len is the per-sequence capacity T_max; max_pages must be at least
+ * ceil(T_max / S) (INVALID_ARG otherwise).  Only the table entries of blocks
+ * a call reads must be valid; a page index outside [0, num_pages) is never
+ * dereferenced (see each call).  The pool, the table and its pages stay owned
+ * by the caller; the library does not allocate or free pages.
+ *
+ * hils_landmark_summary_paged: hils_landmark_summary on a paged key cache
+ * (same math, same k_sum / b_sum layout, which stay per sequence).  A chunk
+ * whose page index lies outside the pool gets NaN summaries for every head.
+ */
+hils_status hils_landmark_summary_paged(const hils_config *cfg, const void *k_pages,
+                                        const int32_t *block_table, int32_t max_pages,
+                                        int32_t num_pages, const void *q_lm,
+                                        int32_t chunk_begin, int32_t chunk_end, void *k_sum,
+                                        float *b_sum, void *stream);
+
+/*
+ * hils_sparse_attn_decode_paged: hils_sparse_attn_decode reading the window
+ * and the selected chunks from paged caches; same arguments otherwise, same
+ * workspace (hils_decode_workspace_bytes), bit-identical results for the
+ * same cache contents.  A block the step reads whose page index lies outside
+ * the pool contributes no keys and adds one to the error word at
+ * hils_decode_error_offset(cfg).
+ */
+hils_status hils_sparse_attn_decode_paged(const hils_config *cfg, const void *q, const void *h,
+                                          const void *w_down, const void *w_up,
+                                          const void *k_pages, const void *v_pages,
+                                          const int32_t *block_table, int32_t max_pages,
+                                          int32_t num_pages, const void *k_sum,
+                                          const float *b_sum, const int32_t *seq_lens, void *o,
+                                          int32_t *topk_idx, float *topk_score, void *workspace,
+                                          size_t workspace_bytes, void *stream);
 
 /* Bytes of the workspace hils_dense_attn_decode needs (zero it once, as for
  * the sparse decode workspace). */

@@ -21,6 +21,7 @@ ENTRY_POINTS = (
     "hils_landmark_summary", "hils_prefill_workspace_bytes", "hils_chunk_score_topk",
     "hils_sparse_attn_prefill", "hils_decode_workspace_bytes", "hils_sparse_attn_decode",
     "hils_decode_error_offset", "hils_dense_decode_workspace_bytes", "hils_dense_attn_decode",
+    "hils_landmark_summary_paged", "hils_sparse_attn_decode_paged",
     "hils_status_string", "hils_last_error",
 )
 
@@ -86,6 +87,8 @@ def _load() -> ctypes.CDLL:
         "hils_decode_error_offset": [C],
         "hils_dense_decode_workspace_bytes": [C],
         "hils_dense_attn_decode": [C, P, P, P, P, P, P, SZ, P],
+        "hils_landmark_summary_paged": [C, P, P, I32, I32, P, I32, I32, P, P, P],
+        "hils_sparse_attn_decode_paged": [C, P, P, P, P, P, P, P, I32, I32, P, P, P, P, P, P, P, SZ, P],
         "hils_status_string": [ctypes.c_int],
         "hils_last_error": [],
     }
@@ -178,6 +181,24 @@ def hils_sparse_attn_decode(cfg: Config, q, h, w_down, w_up, k_cache, v_cache, k
            "hils_sparse_attn_decode")
 
 
+def hils_landmark_summary_paged(cfg: Config, k_pages, block_table, max_pages, num_pages, q_lm, chunk_begin,
+                                chunk_end, k_sum, b_sum, stream=None):
+    _check(lib.hils_landmark_summary_paged(ctypes.byref(cfg), _ptr(k_pages), _ptr(block_table), max_pages,
+                                           num_pages, _ptr(q_lm), chunk_begin, chunk_end, _ptr(k_sum),
+                                           _ptr(b_sum), _stream(stream)), "hils_landmark_summary_paged")
+
+
+def hils_sparse_attn_decode_paged(cfg: Config, q, h, w_down, w_up, k_pages, v_pages, block_table, max_pages,
+                                  num_pages, k_sum, b_sum, seq_lens, o, topk_idx, topk_score, workspace,
+                                  stream=None):
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib.hils_sparse_attn_decode_paged(ctypes.byref(cfg), _ptr(q), _ptr(h), _ptr(w_down), _ptr(w_up),
+                                             _ptr(k_pages), _ptr(v_pages), _ptr(block_table), max_pages,
+                                             num_pages, _ptr(k_sum), _ptr(b_sum), _ptr(seq_lens), _ptr(o),
+                                             _ptr(topk_idx), _ptr(topk_score), _ptr(workspace), ws_bytes,
+                                             _stream(stream)), "hils_sparse_attn_decode_paged")
+
+
 def hils_dense_decode_workspace_bytes(cfg: Config) -> int:
     return int(lib.hils_dense_decode_workspace_bytes(ctypes.byref(cfg)))
 
@@ -193,5 +214,5 @@ __all__ = ["Config", "HilsError", "lib", "LIB_PATH", "ENTRY_POINTS", "last_error
            "hils_landmark_summary", "hils_prefill_workspace_bytes", "hils_chunk_score_topk",
            "hils_sparse_attn_prefill", "hils_decode_workspace_bytes", "hils_decode_error_offset",
            "hils_sparse_attn_decode", "hils_dense_decode_workspace_bytes", "hils_dense_attn_decode",
-           "HILS_OK", "HILS_ERR_INVALID_ARG", "HILS_ERR_UNSUPPORTED", "HILS_ERR_WORKSPACE",
+           "hils_landmark_summary_paged", "hils_sparse_attn_decode_paged", "HILS_OK", "HILS_ERR_INVALID_ARG", "HILS_ERR_UNSUPPORTED", "HILS_ERR_WORKSPACE",
            "HILS_ERR_HIP", "HILS_BF16", "HILS_F32"]

@@ -155,6 +155,42 @@ hils_status finish(hipError_t e, const char *what) {
   return HILS_OK;
 }
 
+// Paged caches: pages of S keys of every KV head, [num_pages, H_kv, S, d];
+// every position below seq_len (the per-sequence capacity) needs a slot of
+// the block table.
+hils_status check_pages(const hils_config *c, const int32_t *block_table, int32_t max_pages, int32_t num_pages) {
+  if (!block_table) return fail(HILS_ERR_INVALID_ARG, "block_table is NULL");
+  if (num_pages < 1) return fail(HILS_ERR_INVALID_ARG, "num_pages must be >= 1 (got %d)", num_pages);
+  const long long need = (static_cast<long long>(c->seq_len) + c->chunk_size - 1) / c->chunk_size;
+  if (max_pages < need)
+    return fail(HILS_ERR_INVALID_ARG, "max_pages (%d) below the %lld pages of seq_len %d", max_pages, need,
+                c->seq_len);
+  return HILS_OK;
+}
+
+hils_status summary_impl(const hils_config *cfg, const void *k, const int32_t *block_table, int32_t max_pages,
+                         int32_t num_pages, const void *q_lm, int32_t chunk_begin, int32_t chunk_end, void *k_sum,
+                         float *b_sum, void *stream) {
+  const int C = cfg->seq_len / cfg->chunk_size;
+  if (chunk_begin < 0 || chunk_end < chunk_begin || chunk_end > C)
+    return fail(HILS_ERR_INVALID_ARG, "chunk range [%d, %d) outside [0, %d]", chunk_begin, chunk_end, C);
+  if (chunk_end == chunk_begin) return HILS_OK;
+  CHECK(check_ptr(k, block_table ? "k_pages" : "k"));
+  CHECK(check_ptr(q_lm, "q_lm"));
+  CHECK(check_ptr(k_sum, "k_sum"));
+  CHECK(check_ptr(b_sum, "b_sum"));
+  hils::SummaryArgs a{k, q_lm, k_sum, b_sum, cfg->batch, cfg->seq_len, cfg->n_q_heads, cfg->n_kv_heads, C,
+                      cfg->head_dim, chunk_begin, chunk_end, tau_of(cfg), cfg->dtype == HILS_BF16,
+                      block_table, max_pages, num_pages};
+  return finish(hils::launch_summary(a, static_cast<hipStream_t>(stream)), "landmark summary launch");
+}
+
+hils_status decode_impl(const hils_config *cfg, const void *q, const void *h, const void *w_down, const void *w_up,
+                        const void *k_cache, const void *v_cache, const int32_t *block_table, int32_t max_pages,
+                        int32_t num_pages, const void *k_sum, const float *b_sum, const int32_t *seq_lens, void *o,
+                        int32_t *topk_idx, float *topk_score, void *workspace, size_t workspace_bytes,
+                        void *stream);
+
 }  // namespace
 
 extern "C" {
@@ -176,17 +212,17 @@ hils_status hils_landmark_summary(const hils_config *cfg, const void *k, const v
                                   int32_t chunk_end, void *k_sum, float *b_sum, void *stream) {
   g_last_error.clear();
   CHECK(check_config(cfg));
-  const int C = cfg->seq_len / cfg->chunk_size;
-  if (chunk_begin < 0 || chunk_end < chunk_begin || chunk_end > C)
-    return fail(HILS_ERR_INVALID_ARG, "chunk range [%d, %d) outside [0, %d]", chunk_begin, chunk_end, C);
-  if (chunk_end == chunk_begin) return HILS_OK;
-  CHECK(check_ptr(k, "k"));
-  CHECK(check_ptr(q_lm, "q_lm"));
-  CHECK(check_ptr(k_sum, "k_sum"));
-  CHECK(check_ptr(b_sum, "b_sum"));
-  hils::SummaryArgs a{k, q_lm, k_sum, b_sum, cfg->batch, cfg->seq_len, cfg->n_q_heads, cfg->n_kv_heads, C,
-                      cfg->head_dim, chunk_begin, chunk_end, tau_of(cfg), cfg->dtype == HILS_BF16};
-  return finish(hils::launch_summary(a, static_cast<hipStream_t>(stream)), "landmark summary launch");
+  return summary_impl(cfg, k, nullptr, 0, 0, q_lm, chunk_begin, chunk_end, k_sum, b_sum, stream);
+}
+
+hils_status hils_landmark_summary_paged(const hils_config *cfg, const void *k_pages, const int32_t *block_table,
+                                        int32_t max_pages, int32_t num_pages, const void *q_lm, int32_t chunk_begin,
+                                        int32_t chunk_end, void *k_sum, float *b_sum, void *stream) {
+  g_last_error.clear();
+  CHECK(check_config(cfg));
+  CHECK(check_pages(cfg, block_table, max_pages, num_pages));
+  return summary_impl(cfg, k_pages, block_table, max_pages, num_pages, q_lm, chunk_begin, chunk_end, k_sum, b_sum,
+                      stream);
 }
 
 size_t hils_prefill_workspace_bytes(const hils_config *cfg) {
@@ -277,10 +313,36 @@ hils_status hils_sparse_attn_decode(const hils_config *cfg, const void *q, const
                                     float *topk_score, void *workspace, size_t workspace_bytes, void *stream) {
   g_last_error.clear();
   CHECK(check_config(cfg));
+  return decode_impl(cfg, q, h, w_down, w_up, k_cache, v_cache, nullptr, 0, 0, k_sum, b_sum, seq_lens, o, topk_idx,
+                     topk_score, workspace, workspace_bytes, stream);
+}
+
+hils_status hils_sparse_attn_decode_paged(const hils_config *cfg, const void *q, const void *h, const void *w_down,
+                                          const void *w_up, const void *k_pages, const void *v_pages,
+                                          const int32_t *block_table, int32_t max_pages, int32_t num_pages,
+                                          const void *k_sum, const float *b_sum, const int32_t *seq_lens, void *o,
+                                          int32_t *topk_idx, float *topk_score, void *workspace,
+                                          size_t workspace_bytes, void *stream) {
+  g_last_error.clear();
+  CHECK(check_config(cfg));
+  CHECK(check_pages(cfg, block_table, max_pages, num_pages));
+  return decode_impl(cfg, q, h, w_down, w_up, k_pages, v_pages, block_table, max_pages, num_pages, k_sum, b_sum,
+                     seq_lens, o, topk_idx, topk_score, workspace, workspace_bytes, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+hils_status decode_impl(const hils_config *cfg, const void *q, const void *h, const void *w_down, const void *w_up,
+                        const void *k_cache, const void *v_cache, const int32_t *block_table, int32_t max_pages,
+                        int32_t num_pages, const void *k_sum, const float *b_sum, const int32_t *seq_lens, void *o,
+                        int32_t *topk_idx, float *topk_score, void *workspace, size_t workspace_bytes,
+                        void *stream) {
   CHECK(check_ptr(q, "q"));
   CHECK(check_qcal_ptrs(cfg, h, w_down, w_up));
-  CHECK(check_ptr(k_cache, "k_cache"));
-  CHECK(check_ptr(v_cache, "v_cache"));
+  CHECK(check_ptr(k_cache, block_table ? "k_pages" : "k_cache"));
+  CHECK(check_ptr(v_cache, block_table ? "v_pages" : "v_cache"));
   const int Cmax = cfg->seq_len / cfg->chunk_size;
   if (Cmax > 0) {
     CHECK(check_ptr(k_sum, "k_sum"));
@@ -314,9 +376,13 @@ hils_status hils_sparse_attn_decode(const hils_config *cfg, const void *q, const
   a.r = cfg->qcal_rank; a.Dh = cfg->hidden_dim; a.Cmax = Cmax;
   a.P = g.P; a.NW = g.NW; a.nslots = g.nslots; a.nslot_blocks = g.nslot_blocks;
   a.tau = tau_of(cfg); a.bf16 = cfg->dtype == HILS_BF16;
-  // topk buffers are also read back by the attend kernel: provide scratch when K == 0
+  a.block_table = block_table; a.max_pages = max_pages; a.num_pages = num_pages;
   return finish(hils::launch_decode(a, static_cast<hipStream_t>(stream)), "sparse decode launch");
 }
+
+}  // namespace
+
+extern "C" {
 
 size_t hils_dense_decode_workspace_bytes(const hils_config *cfg) {
   if (check_config(cfg) != HILS_OK) return 0;

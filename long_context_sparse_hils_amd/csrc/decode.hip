@@ -36,6 +36,23 @@ __device__ __forceinline__ int clamp_seq(const int32_t *seq_lens, int b, int Tma
   return s;
 }
 
+// First row of the 64-key block j0 .. j0 + 63 of (b, g) (j0 a multiple of
+// S = 64): in the contiguous cache [B, Hkv, Tmax, D], or in the page
+// [num_pages, Hkv, S, D] that the block table gives for block j0 / S.  A page
+// index outside [0, num_pages) gives nullptr (and, with count, one error).
+template <typename T, int D>
+__device__ __forceinline__ const T *kv_block(const DecodeArgs &a, const void *cache, int b, int g, int j0,
+                                             bool count) {
+  const T *base = static_cast<const T *>(cache);
+  if (!a.block_table) return base + ((static_cast<size_t>(b) * a.Hkv + g) * a.Tmax + j0) * D;
+  const int pg = a.block_table[static_cast<size_t>(b) * a.max_pages + j0 / a.S];
+  if (pg < 0 || pg >= a.num_pages) {
+    if (count) atomicAdd(a.err, 1u);
+    return nullptr;
+  }
+  return base + (static_cast<size_t>(pg) * a.Hkv + g) * a.S * D;
+}
+
 // ------------------------------------------------------------------ Q-Cal (decode)
 template <typename T, int D>
 __global__ void __launch_bounds__(kDecThreads)
@@ -87,14 +104,13 @@ decode_score_kernel(DecodeArgs a) {
   const int seq = clamp_seq(a.seq_lens, b, a.Tmax, a.err, blk == 0 && g == 0 && t == 0);
   const int i = seq - 1;
   const int n = eligible_chunks(i, a.W, a.S);
-  const T *kc = static_cast<const T *>(a.k_cache) + (static_cast<size_t>(b) * a.Hkv + g) * a.Tmax * D;
-  const T *vc = static_cast<const T *>(a.v_cache) + (static_cast<size_t>(b) * a.Hkv + g) * a.Tmax * D;
-
   if (blk >= a.P) {  // ---------------- window unit
     const int u = blk - a.P;
     const int j0 = n * a.S + u * kUnitKeys;
     float *rec = a.parts + ((static_cast<size_t>(b) * a.Hkv + g) * a.nslots + K + u) * G * (D + 2);
-    if (j0 > i) {
+    const T *kb = j0 > i ? nullptr : kv_block<T, D>(a, a.k_cache, b, g, j0, t == 0);
+    const T *vb = kb ? kv_block<T, D>(a, a.v_cache, b, g, j0, false) : nullptr;
+    if (!vb) {  // past the query, or a page outside the pool: no keys
       for (int hh = t; hh < G; hh += kDecThreads) publish2(rec + hh * (D + 2), -INFINITY, 0.f);
       return;
     }
@@ -103,7 +119,7 @@ decode_score_kernel(DecodeArgs a) {
     __syncthreads();
     constexpr int NP = pairs_per_thread<D>();
     float2 ou[NP];
-    attend_unit<T, D>(us, kc + static_cast<size_t>(j0) * D, vc + static_cast<size_t>(j0) * D, nk, G, a.tau, ou);
+    attend_unit<T, D>(us, kb, vb, nk, G, a.tau, ou);
 #pragma unroll
     for (int r = 0; r < NP; ++r) {
       const int pr = t + r * kUnitThreads, hh = pr / (D / 2), e2 = pr % (D / 2);
@@ -659,11 +675,11 @@ decode_attend_kernel(DecodeArgs a) {
     }
     float *rec = recs + static_cast<size_t>(slot) * G * (D + 2);
     const int c = slot < keep ? static_cast<int>(~static_cast<uint32_t>(ss.sorted[slot])) : -1;
-    if (c < 0) {
+    const T *kc = c < 0 ? nullptr : kv_block<T, D>(a, a.k_cache, b, g, c * a.S, t == 0);
+    const T *vc = kc ? kv_block<T, D>(a, a.v_cache, b, g, c * a.S, false) : nullptr;
+    if (!vc) {  // no chunk of this rank, or its page is outside the pool
       for (int hh = t; hh < G; hh += kDecThreads) publish2(rec + hh * (D + 2), -INFINITY, 0.f);
     } else {
-      const T *kc = static_cast<const T *>(a.k_cache) + (bg * a.Tmax + static_cast<size_t>(c) * a.S) * D;
-      const T *vc = static_cast<const T *>(a.v_cache) + (bg * a.Tmax + static_cast<size_t>(c) * a.S) * D;
       constexpr int NP = pairs_per_thread<D>();
       float2 ou[NP];
       attend_unit<T, D>(us, kc, vc, a.S, G, a.tau, ou);

@@ -14,6 +14,11 @@ struct SummaryArgs {
   int B, T, Hq, Hkv, C, d, c0, c1;
   float tau;
   bool bf16;
+  // paged K (null: contiguous [B, Hkv, T, d]): k holds pages
+  // [num_pages, Hkv, S, d] and block_table [B, max_pages] maps chunk c of
+  // sequence b to its page
+  const int32_t *block_table;
+  int max_pages, num_pages;
 };
 
 struct ScoreArgs {
@@ -55,6 +60,11 @@ struct DecodeArgs {
   int P, NW, nslots, nslot_blocks;
   float tau;
   bool bf16;
+  // paged caches (null: contiguous [B, Hkv, Tmax, d]): k_cache / v_cache hold
+  // pages [num_pages, Hkv, S, d]; block_table [B, max_pages] maps the 64-key
+  // block j / S of sequence b to its page
+  const int32_t *block_table;
+  int max_pages, num_pages;
 };
 
 struct DenseArgs {

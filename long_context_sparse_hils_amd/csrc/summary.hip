@@ -19,7 +19,7 @@ template <typename T, int D>
 __global__ void __launch_bounds__(kSumThreads)
 landmark_summary_kernel(const T *__restrict__ k, const T *__restrict__ q_lm, T *__restrict__ k_sum,
                         float *__restrict__ b_sum, int T_len, int Hq, int Hkv, int C, int c0,
-                        float tau) {
+                        float tau, const int32_t *__restrict__ block_table, int max_pages, int num_pages) {
   constexpr int LD = D + 1;  // padded fp32 row stride (conflict-free column reads)
   __shared__ float keys[kSumS * LD];
   __shared__ float qrow[4][D];
@@ -28,8 +28,26 @@ landmark_summary_kernel(const T *__restrict__ k, const T *__restrict__ q_lm, T *
   const int G = Hq / Hkv;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
+  const T *kc;
+  if (block_table) {
+    // paged keys: the chunk is one page; a page index outside the pool
+    // makes the chunk's summary NaN for every head of the group
+    const int pg = block_table[static_cast<size_t>(b) * max_pages + c];
+    if (pg < 0 || pg >= num_pages) {
+      for (int x = tid; x < G * (D + 1); x += kSumThreads) {
+        const size_t so = (static_cast<size_t>(b) * Hq + g * G + x / (D + 1)) * C + c;
+        if (x % (D + 1) == D)
+          b_sum[so] = NAN;
+        else
+          Elem<T>::store(k_sum, so * D + x % (D + 1), NAN);
+      }
+      return;
+    }
+    kc = k + (static_cast<size_t>(pg) * Hkv + g) * kSumS * D;
+  } else {
+    kc = k + ((static_cast<size_t>(b) * Hkv + g) * T_len + static_cast<size_t>(c) * kSumS) * D;
+  }
   // stage the chunk's keys: 64 x D elements, 8 per thread per step
-  const T *kc = k + ((static_cast<size_t>(b) * Hkv + g) * T_len + static_cast<size_t>(c) * kSumS) * D;
   for (int e8 = tid; e8 < kSumS * D / 8; e8 += kSumThreads) {
     float v[8];
     Elem<T>::load8(kc + e8 * 8, v);
@@ -81,7 +99,7 @@ static hipError_t launch_summary_t(const SummaryArgs &a, hipStream_t st) {
   dim3 grid(a.c1 - a.c0, a.Hkv, a.B);
   landmark_summary_kernel<T, D><<<grid, kSumThreads, 0, st>>>(
       static_cast<const T *>(a.k), static_cast<const T *>(a.q_lm), static_cast<T *>(a.k_sum),
-      a.b_sum, a.T, a.Hq, a.Hkv, a.C, a.c0, a.tau);
+      a.b_sum, a.T, a.Hq, a.Hkv, a.C, a.c0, a.tau, a.block_table, a.max_pages, a.num_pages);
   return hipGetLastError();
 }
 

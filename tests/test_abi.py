@@ -126,3 +126,31 @@ def test_workspace_sizes_scale_with_the_problem():
 def test_invalid_config_gives_zero_workspace():
     assert hils.hils_decode_workspace_bytes(_cfg(head_dim=100)) == 0
     assert hils.hils_prefill_workspace_bytes(_cfg(n_q_heads=3, n_kv_heads=2)) == 0
+
+
+def test_paged_calls_check_the_page_table():
+    """Paged calls: a block table is required and must cover the capacity."""
+    cfg = _cfg(batch=2, seq_len=4096, qcal_rank=0, hidden_dim=0)
+    need = 4096 // 64
+    L = hils.lib
+    assert L.hils_landmark_summary_paged(ctypes.byref(cfg), FAKE, None, need, 10, FAKE, 0, 1, FAKE, FAKE,
+                                         None) == hils.HILS_ERR_INVALID_ARG
+    assert "block_table" in hils.last_error()
+    assert L.hils_landmark_summary_paged(ctypes.byref(cfg), FAKE, FAKE, need - 1, 10, FAKE, 0, 1, FAKE, FAKE,
+                                         None) == hils.HILS_ERR_INVALID_ARG
+    assert "max_pages" in hils.last_error()
+    assert L.hils_landmark_summary_paged(ctypes.byref(cfg), FAKE, FAKE, need, 0, FAKE, 0, 1, FAKE, FAKE,
+                                         None) == hils.HILS_ERR_INVALID_ARG
+    assert L.hils_landmark_summary_paged(ctypes.byref(cfg), None, FAKE, need, 10, FAKE, 0, 1, FAKE, FAKE,
+                                         None) == hils.HILS_ERR_INVALID_ARG
+    assert "k_pages is NULL" in hils.last_error()
+    dneed = hils.hils_decode_workspace_bytes(cfg)
+    args = [FAKE, None, None, None, FAKE, FAKE]
+    tail = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, dneed, None]
+    assert L.hils_sparse_attn_decode_paged(ctypes.byref(cfg), *args, None, need, 10, *tail) == \
+        hils.HILS_ERR_INVALID_ARG
+    assert L.hils_sparse_attn_decode_paged(ctypes.byref(cfg), *args, FAKE, need - 1, 10, *tail) == \
+        hils.HILS_ERR_INVALID_ARG
+    tail[-2] = dneed - 1
+    assert L.hils_sparse_attn_decode_paged(ctypes.byref(cfg), *args, FAKE, need, 10, *tail) == \
+        hils.HILS_ERR_WORKSPACE

@@ -198,3 +198,85 @@ def test_prefill_graph_replay():
         return [res["k_sum"], res["b_sum"], res["idx"], res["tsc"], res["o"]]
 
     _replay_checks(g, fill, eager, [k_sum, b_sum, idx, tsc, o], len(qs))
+
+
+def _paged(cache: np.ndarray, pages_of: np.ndarray, num_pages: int, S: int, seed: int) -> np.ndarray:
+    """[B, H_kv, T, d] -> a page pool [num_pages, H_kv, S, d]: block c of
+    sequence b lands in page pages_of[b, c]; unused pages hold other values."""
+    B, Hkv, T, d = cache.shape
+    pool = hs.normal((num_pages, Hkv, S, d), seed, hs.STREAM_K, 3.0, dtype="bf16")
+    for b in range(B):
+        for c in range(T // S):
+            pool[pages_of[b, c]] = cache[b, :, c * S:(c + 1) * S]
+    return pool
+
+
+def test_paged_decode_matches_contiguous():
+    """The paged summary and decode calls on a shuffled page pool equal the
+    contiguous calls bit for bit; a page index outside the pool is counted and
+    skipped, and leaves the other sequences untouched."""
+    B, T, Hq, Hkv, d, K, W, S = 3, 4096, 8, 2, 128, 16, 512, 64
+    wl = _wl_decode(B, T, Hq, Hkv, d, K, W)
+    lens = np.array([4096, 1000, 300], dtype=np.int32)
+    inp = hs.decode_inputs(wl, 525, seq_lens=lens)
+    c = hils.Config.from_dict(wl.config_dict())
+    C = T // S
+    max_pages, num_pages = C + 3, B * C + 11
+    rng = np.random.default_rng(5)
+    pages_of = np.full((B, max_pages), -1, dtype=np.int32)
+    pages_of[:, :C] = rng.permutation(num_pages)[:B * C].reshape(B, C)
+    kp = dev(_paged(inp["k_cache"], pages_of, num_pages, S, 31))
+    vp = dev(_paged(inp["v_cache"], pages_of, num_pages, S, 32))
+    table = dev(pages_of)
+    kc, vc, qlm = dev(inp["k_cache"]), dev(inp["v_cache"]), dev(inp["q_lm"])
+
+    ks, bs = (torch.empty((B, Hq, C, d), dtype=torch.bfloat16, device="cuda"),
+              torch.empty((B, Hq, C), dtype=torch.float32, device="cuda"))
+    hils.hils_landmark_summary(c, kc, qlm, 0, C, ks, bs)
+    ksp, bsp = torch.empty_like(ks), torch.empty_like(bs)
+    hils.hils_landmark_summary_paged(c, kp, table, max_pages, num_pages, qlm, 0, C, ksp, bsp)
+    assert torch.equal(ks, ksp) and torch.equal(bs, bsp)
+
+    def paged_step(sl, tab, ws):
+        o = torch.empty((B, Hq, d), dtype=torch.bfloat16, device="cuda")
+        idx = torch.empty((B, Hkv, K), dtype=torch.int32, device="cuda")
+        tsc = torch.empty((B, Hq, K), dtype=torch.float32, device="cuda")
+        hils.hils_sparse_attn_decode_paged(c, dev(inp["q"]), None, None, None, kp, vp, tab, max_pages, num_pages,
+                                           ks, bs, sl, o, idx, tsc, ws)
+        return dict(o=o, idx=idx, tsc=tsc)
+
+    off = hils.hils_decode_error_offset(c)
+    for sl_np in (lens, np.array([1, 4095, 2113], dtype=np.int32)):
+        sl = dev(sl_np)
+        ref = gpu_decode(wl.config_dict(), dict(q=dev(inp["q"]), k_cache=kc, v_cache=vc), ks, bs, sl)
+        ws = torch.zeros((hils.hils_decode_workspace_bytes(c),), dtype=torch.uint8, device="cuda")
+        got = paged_step(sl, table, ws)
+        for key in ("o", "idx", "tsc"):
+            assert torch.equal(got[key], ref[key]), key
+        assert int(ws[off:off + 4].cpu().numpy().view(np.uint32)[0]) == 0
+    oc = oracle.OracleConfig.from_dict(wl.config_dict())
+    _check_step(wl, oc, inp, got, ks, bs, sl_np)
+
+    # sequence 1's last window block points outside the pool
+    sl = dev(lens)
+    ref = paged_step(sl, table, torch.zeros((hils.hils_decode_workspace_bytes(c),), dtype=torch.uint8,
+                                            device="cuda"))
+    bad = pages_of.copy()
+    bad[1, (int(lens[1]) - 1) // S] = num_pages + 5
+    ws = torch.zeros((hils.hils_decode_workspace_bytes(c),), dtype=torch.uint8, device="cuda")
+    got = paged_step(sl, dev(bad), ws)
+    torch.cuda.synchronize()
+    assert int(ws[off:off + 4].cpu().numpy().view(np.uint32)[0]) == Hkv  # one window unit per group
+    assert torch.isfinite(got["o"].float()).all()
+    for b in (0, 2):
+        assert torch.equal(got["o"][b], ref["o"][b]) and torch.equal(got["idx"][b], ref["idx"][b])
+    # ... and a summary whose page is outside the pool is NaN, the rest as before
+    bad = pages_of.copy()
+    bad[2, 7] = -3
+    ksb, bsb = torch.empty_like(ks), torch.empty_like(bs)
+    hils.hils_landmark_summary_paged(c, kp, dev(bad), max_pages, num_pages, qlm, 0, C, ksb, bsb)
+    assert torch.isnan(ksb[2, :, 7].float()).all() and torch.isnan(bsb[2, :, 7]).all()
+    keep = torch.ones((B, C), dtype=torch.bool, device="cuda")
+    keep[2, 7] = False
+    assert torch.equal(ksb.permute(0, 2, 1, 3)[keep], ks.permute(0, 2, 1, 3)[keep])
+    assert torch.equal(bsb.permute(0, 2, 1)[keep], bs.permute(0, 2, 1)[keep])
