@@ -52,6 +52,7 @@ def parse():
     p.add_argument("--no-dense", action="store_true")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-flush", action="store_true")
+    p.add_argument("--no-paged", action="store_true", help="skip the paged-cache decode leg")
     p.add_argument("--only", choices=["prefill", "decode"], default=None,
                    help="profile one path (for rocprofv3 runs)")
     p.add_argument("--decode-batches", default="1,4")
@@ -255,6 +256,30 @@ def bench_decode(args, torch, hils, hs, flush, batch):
                              traffic=traffic_record("decode_512k_b%d" % B, DECODE_SOURCES),
                              kernel="decode step (score+select kernel, attend+combine kernel)"),
                needle_hits=f"{hits}/{len(inp['needles'])}")
+    if not args.no_paged:
+        # the same caches as a shuffled pool of 64-key pages behind a block table
+        S = wl.chunk_size
+        perm = torch.randperm(B * C, generator=torch.Generator().manual_seed(args.seed), dtype=torch.int64)
+        table = perm.to(torch.int32).reshape(B, C).to("cuda")
+        pools = []
+        for name in ("k_cache", "v_cache"):
+            blocks = d[name].view(B, Hkv, C, S, D).permute(0, 2, 1, 3, 4).reshape(B * C, Hkv, S, D)
+            pool = torch.empty(tuple(blocks.shape), dtype=blocks.dtype, device="cuda")
+            pool[perm.to("cuda")] = blocks
+            pools.append(pool)
+            del blocks
+        po, pidx, ptsc = torch.empty_like(o), torch.empty_like(idx), torch.empty_like(tsc)
+        pws = torch.zeros_like(ws)
+
+        def pstep():
+            hils.hils_sparse_attn_decode_paged(c, d["q"], None, None, None, pools[0], pools[1], table, C, B * C,
+                                               k_sum, b_sum, d["seq_lens"], po, pidx, ptsc, pws, stream)
+        pms, _ = timed(pstep, args.steps, args.warmup)
+        same = bool(torch.equal(po, o) and torch.equal(pidx, idx) and torch.equal(ptsc, tsc))
+        out["paged"] = dict(ms_per_step=pms, value=B / (pms * 1e-3),
+                            frac_hbm=nb["total"] * B / (pms * 1e-3) / 1e9 / PEAK_HBM_GBS, equal_to_contiguous=same)
+        log(f"[decode b{batch}] paged {pms * 1e3:.1f} us, outputs equal to the contiguous call: {same}")
+        del pools, table, pws
     if not args.no_dense:
         dws = torch.zeros((hils.hils_dense_decode_workspace_bytes(c),), dtype=torch.uint8, device="cuda")
         do = torch.empty_like(o)
