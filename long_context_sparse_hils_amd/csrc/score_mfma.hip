@@ -621,9 +621,307 @@ score_topk_mfma_kernel(ScoreArgs a, const uint16_t *__restrict__ u_hi, const uin
   }
 }
 
+// ------------------------------------------------------------------ scores + top-K, long sequences
+// More chunks than one pass of the kernel above keeps in registers (C up to
+// 8192 per sequence): the summaries stream through in blocks of 64 chunks,
+// every head of the group per block, and each query keeps a running top-K
+// of keys (score, chunk) with every head's own score of the kept chunks.
+//
+// Lane (ln, lg) works on query ln of the wave's 16, as above; the running
+// list of a query is spread over its four lanes, KPL slots each (slot s of
+// row lg is list entry 4 s + lg; entries at or past K are never used).
+// After each block the query's candidates above its current K-th key (the
+// smallest kept key; empty slots hold key 0) replace that smallest entry one
+// at a time, best first, so the list always holds the K largest keys seen.
+// Keys are unique (the chunk is in the low word), so the result is the
+// exact top-K by (score descending, chunk ascending) of all eligible chunks.
+
+__device__ __forceinline__ unsigned long long umax64_rows4(unsigned long long v) {
+  uint32_t lo = static_cast<uint32_t>(v), hi = static_cast<uint32_t>(v >> 32);
+  auto rl = __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+  auto rh = __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+  unsigned long long x = (static_cast<unsigned long long>(rh[0]) << 32) | rl[0];
+  unsigned long long y = (static_cast<unsigned long long>(rh[1]) << 32) | rl[1];
+  v = x > y ? x : y;
+  lo = static_cast<uint32_t>(v);
+  hi = static_cast<uint32_t>(v >> 32);
+  auto sl = __builtin_amdgcn_permlane32_swap(lo, lo, false, false);
+  auto sh = __builtin_amdgcn_permlane32_swap(hi, hi, false, false);
+  x = (static_cast<unsigned long long>(sh[0]) << 32) | sl[0];
+  y = (static_cast<unsigned long long>(sh[1]) << 32) | sl[1];
+  return x > y ? x : y;
+}
+__device__ __forceinline__ unsigned long long umin64_rows4(unsigned long long v) { return ~umax64_rows4(~v); }
+
+template <int D, int WAVES, int KPL>
+__global__ void __launch_bounds__(WAVES * 64)
+score_topk_stream_kernel(ScoreArgs a, const uint16_t *__restrict__ u_hi, const uint16_t *__restrict__ u_lo,
+                         const uint16_t *__restrict__ m_hi, const uint16_t *__restrict__ m_lo, int RP) {
+  constexpr int KS = D / 32;
+  constexpr int IC = 64;         // chunks per block
+  constexpr int QW = WAVES * 16;  // queries per workgroup
+  constexpr int GM = 4;           // heads per group handled here
+  constexpr unsigned long long kFull = ~0ull;  // a slot past K: never the smallest
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  const ScoreItemLayout lay(D, IC, RP);
+  auto item_ks = [&](int buf) { return reinterpret_cast<uint16_t *>(smem_raw + buf * lay.bytes + lay.ks); };
+  auto item_mh = [&](int buf) { return reinterpret_cast<uint16_t *>(smem_raw + buf * lay.bytes + lay.mh); };
+  auto item_ml = [&](int buf) { return reinterpret_cast<uint16_t *>(smem_raw + buf * lay.bytes + lay.ml); };
+  auto item_bs = [&](int buf) { return reinterpret_cast<float *>(smem_raw + buf * lay.bytes + lay.bs); };
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int ln = lane & 15, lg = lane >> 4;
+  const int T = a.T, C = a.C, K = a.K, Hq = a.Hq, Hkv = a.Hkv, G = Hq / Hkv;
+  // heaviest (latest) query blocks first, as above
+  const int npair = Hkv * a.B;
+  const int xq = static_cast<int>(blockIdx.x) / npair, pair = static_cast<int>(blockIdx.x) % npair;
+  const int g = pair % Hkv, b = pair / Hkv;
+  const int nqb = (T + QW - 1) / QW;
+  const int q_wg = (nqb - 1 - xq) * QW;
+  const int qw0 = q_wg + wave * 16;
+  const bool qcal = a.r > 0;
+  const int i_me = qw0 + ln;
+  const bool q_ok = i_me < T;
+  const int n_me = q_ok ? min(eligible_chunks(i_me, a.W, a.S), C) : 0;
+  const int n_wave = qw0 < T ? min(eligible_chunks(min(qw0 + 15, T - 1), a.W, a.S), C) : 0;
+  const int n_wg = min(eligible_chunks(min(q_wg + QW - 1, T - 1), a.W, a.S), C);
+  const int nblk = (n_wg + IC - 1) / IC;
+  const int nitems = nblk * G;  // block outer, head inner
+
+  uint4 uh[2], ul[2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) { uh[s] = make_uint4(0, 0, 0, 0); ul[s] = make_uint4(0, 0, 0, 0); }
+  if (qcal) {
+    const size_t uo = (static_cast<size_t>(b) * T + (q_ok ? i_me : 0)) * RP + 8 * lg;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const bool ok = q_ok && s < RP / 32;
+      uh[s] = ok ? *reinterpret_cast<const uint4 *>(u_hi + uo + 32 * s) : make_uint4(0, 0, 0, 0);
+      ul[s] = ok ? *reinterpret_cast<const uint4 *>(u_lo + uo + 32 * s) : make_uint4(0, 0, 0, 0);
+    }
+  }
+  const uint16_t *qb = static_cast<const uint16_t *>(a.q);
+  const uint16_t *ksb = static_cast<const uint16_t *>(a.k_sum);
+  // every head's Q operand: lane holds query ln, d = 32 s + 8 lg .. +8
+  uint4 qv[GM][KS];
+#pragma unroll
+  for (int hh = 0; hh < GM; ++hh) {
+    const size_t qo = ((static_cast<size_t>(b) * Hq + g * G + min(hh, G - 1)) * T + (q_ok ? i_me : 0)) * D + 8 * lg;
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+      qv[hh][s] = (q_ok && hh < G) ? *reinterpret_cast<const uint4 *>(qb + qo + 32 * s) : make_uint4(0, 0, 0, 0);
+  }
+
+  // ---- staging of item x = (chunk block x / G, head x % G), as above
+  constexpr int kPk = D / 8;
+  constexpr int kSlK = IC * D * 2 / 1024;
+  const int Pm = RP / 8;
+  const int slm = qcal ? IC * RP * 2 / 1024 : 0;
+  float bs_reg = 0.f;
+  auto issue_item = [&](int x, int buf) {
+    const int hh = x % G, cb = x / G;
+    const int h = g * G + hh, c0 = cb * IC;
+    const int nsl = kSlK + 2 * slm;
+    for (int sl = wave; sl < nsl; sl += WAVES) {
+      const uint16_t *src;
+      uint16_t *dst;
+      if (sl < kSlK) {
+        const int slot = sl * 64 + lane, r = slot / kPk, pp = slot % kPk;
+        const int c = min(c0 + r, C - 1);  // rows past C are never used
+        src = ksb + ((static_cast<size_t>(b) * Hq + h) * C + c) * D + ((pp ^ score_swz(r, kPk)) << 3);
+        dst = item_ks(buf) + sl * 512;
+      } else {
+        const int slm1 = slm > 0 ? slm : 1, Pm1 = Pm > 0 ? Pm : 1;
+        const int y = sl - kSlK, lohi = y / slm1, part = y % slm1;
+        const int slot = part * 64 + lane, r = slot / Pm1, pp = slot % Pm1;
+        const int c = min(c0 + r, C - 1);
+        src = (lohi ? m_lo : m_hi) + ((static_cast<size_t>(b) * Hq + h) * C + c) * RP + ((pp ^ score_swz(r, Pm)) << 3);
+        dst = (lohi ? item_ml(buf) : item_mh(buf)) + part * 512;
+      }
+      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)dst, 16, 0, 0);
+    }
+    if (wave == WAVES - 1) {
+      const int c = c0 + lane;
+      bs_reg = c < C ? a.b_sum[(static_cast<size_t>(b) * Hq + h) * C + c] : 0.f;
+    }
+  };
+  auto finish_item = [&](int buf) {
+    if (wave == WAVES - 1) item_bs(buf)[lane] = bs_reg;
+  };
+  // s of chunk tile ctl of the staged item for head hh
+  auto score_tile = [&](int buf, int ctl, const uint4 (&qh)[KS]) -> f32x4s {
+    const uint16_t *iks = item_ks(buf), *imh = item_mh(buf), *iml = item_ml(buf);
+    const float *ibs = item_bs(buf);
+    const int r = 16 * ctl + ln;
+    f32x4s acc = f32x4s{0.f, 0.f, 0.f, 0.f};
+    uint4 av[KS];
+#pragma unroll
+    for (int s = 0; s < KS; ++s)
+      av[s] = *reinterpret_cast<const uint4 *>(iks + r * D + (((4 * s + lg) ^ score_swz(r, kPk)) << 3));
+#pragma unroll
+    for (int s = 0; s < KS; ++s) acc = mfma_s(av[s], qh[s], acc);
+    if (qcal) {
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {  // RP / 32 of them (u, m registers stay unrolled)
+        if (s >= RP / 32) break;
+        const int off = r * RP + (((4 * s + lg) ^ score_swz(r, Pm)) << 3);
+        const uint4 mh = *reinterpret_cast<const uint4 *>(imh + off);
+        const uint4 ml = *reinterpret_cast<const uint4 *>(iml + off);
+        acc = mfma_s(mh, uh[s], acc);
+        acc = mfma_s(mh, ul[s], acc);
+        acc = mfma_s(ml, uh[s], acc);
+      }
+    }
+    f32x4s sv;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sv[i] = a.tau * acc[i] + ibs[16 * ctl + 4 * lg + i];
+    return sv;
+  };
+
+  // the running list: slot s of this lane = entry 4 s + lg of the query's list
+  unsigned long long skey[KPL];
+  float ssc[KPL][GM];
+#pragma unroll
+  for (int s = 0; s < KPL; ++s) {
+    skey[s] = 4 * s + lg < K ? kNoKey : kFull;
+#pragma unroll
+    for (int hh = 0; hh < GM; ++hh) ssc[s][hh] = -INFINITY;
+  }
+  unsigned long long theta = kNoKey;  // the query's smallest kept key
+  float scb[GM][16];                  // this block's scores: candidate v = chunk 16 (v >> 2) + 4 lg + (v & 3)
+
+  if (nitems > 0) {
+    issue_item(0, 0);
+    __builtin_amdgcn_s_waitcnt(0);
+    finish_item(0);
+  }
+  __syncthreads();
+  for (int x = 0; x < nitems; ++x) {
+    const int buf = x & 1;
+    const int hh = x % G, cb = x / G;
+    if (x + 1 < nitems) issue_item(x + 1, buf ^ 1);
+    if (IC * cb < n_wave) {  // wave-uniform: some query of the wave has eligible chunks here
+#pragma unroll
+      for (int h2 = 0; h2 < GM; ++h2) {
+        if (h2 != hh) continue;
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct) {
+          const f32x4s sv = score_tile(buf, ct, qv[h2]);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) scb[h2][4 * ct + i] = sv[i];
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    if (x + 1 < nitems) finish_item(buf ^ 1);
+    __syncthreads();
+    if (hh != G - 1 || IC * cb >= n_wave) continue;
+    // ---- block cb complete: merge its candidates into the running lists
+    unsigned long long kv[16];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int c = IC * cb + 16 * (v >> 2) + 4 * lg + (v & 3);
+      float sg = scb[0][v];
+#pragma unroll
+      for (int h2 = 1; h2 < GM; ++h2)
+        if (h2 < G) sg = fmaxf(sg, scb[h2][v]);
+      kv[v] = c < n_me ? make_key(sg, c) : kNoKey;
+    }
+    for (int round = 0; round < 64; ++round) {
+      // this lane's best candidate above theta, and its heads' scores
+      unsigned long long mb = kNoKey;
+      float bs[GM];
+#pragma unroll
+      for (int h2 = 0; h2 < GM; ++h2) bs[h2] = -INFINITY;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const bool take = kv[v] > theta && kv[v] > mb;
+        mb = take ? kv[v] : mb;
+#pragma unroll
+        for (int h2 = 0; h2 < GM; ++h2) bs[h2] = take ? scb[h2][v] : bs[h2];
+      }
+      const unsigned long long qbest = umax64_rows4(mb);
+      const bool ins = qbest > theta;  // the query takes qbest this round
+      if (!__ballot(ins)) break;
+      const bool owner = ins && mb == qbest;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) kv[v] = (owner && kv[v] == qbest) ? kNoKey : kv[v];
+#pragma unroll
+      for (int h2 = 0; h2 < GM; ++h2) bs[h2] = max_rows4(owner ? bs[h2] : -INFINITY);
+      // the slot to replace: the smallest key (= theta) of the lowest row holding it
+      unsigned long long lmin = kFull;
+      int lslot = 0;
+#pragma unroll
+      for (int s = 0; s < KPL; ++s) {
+        const bool lt = skey[s] < lmin;
+        lmin = lt ? skey[s] : lmin;
+        lslot = lt ? s : lslot;
+      }
+      const uint32_t row_take = umin_rows4(lmin == theta ? static_cast<uint32_t>(lg) : 4u);
+      const bool rep = ins && static_cast<uint32_t>(lg) == row_take;
+#pragma unroll
+      for (int s = 0; s < KPL; ++s) {
+        const bool here = rep && s == lslot;
+        skey[s] = here ? qbest : skey[s];
+#pragma unroll
+        for (int h2 = 0; h2 < GM; ++h2) ssc[s][h2] = here ? bs[h2] : ssc[s][h2];
+      }
+      unsigned long long m2 = kFull;
+#pragma unroll
+      for (int s = 0; s < KPL; ++s) m2 = skey[s] < m2 ? skey[s] : m2;
+      theta = umin64_rows4(m2);
+    }
+  }
+
+  // ---- the lists in selection order: an entry's position = number of the
+  // query's kept keys above it (the staging buffers are free now)
+  if (!q_ok) return;
+  unsigned long long *lk = reinterpret_cast<unsigned long long *>(smem_raw) + (wave * 16 + ln) * (4 * KPL);
+#pragma unroll
+  for (int s = 0; s < KPL; ++s) lk[4 * s + lg] = skey[s] == kFull ? kNoKey : skey[s];
+  __builtin_amdgcn_wave_barrier();
+  const int keep = min(K, n_me);
+  const size_t ibase = ((static_cast<size_t>(b) * Hkv + g) * T + i_me) * K;
+#pragma unroll
+  for (int s = 0; s < KPL; ++s) {
+    const unsigned long long k0 = skey[s];
+    if (k0 == kFull || k0 == kNoKey) continue;
+    int rk = 0;
+    for (int e = 0; e < 4 * KPL; ++e) rk += lk[e] > k0 ? 1 : 0;
+    a.topk_idx[ibase + rk] = key_chunk(k0);
+#pragma unroll
+    for (int h2 = 0; h2 < GM; ++h2)
+      if (h2 < G) a.topk_score[((static_cast<size_t>(b) * Hq + g * G + h2) * T + i_me) * K + rk] = ssc[s][h2];
+  }
+  for (int k = keep + lg; k < K; k += 4) a.topk_idx[ibase + k] = -1;
+  for (int x = lg; x < G * (K - keep); x += 4) {
+    const int h2 = x / (K - keep), k = keep + x % (K - keep);
+    a.topk_score[((static_cast<size_t>(b) * Hq + g * G + h2) * T + i_me) * K + k] = -INFINITY;
+  }
+}
+
+constexpr int kStreamMaxC = 8192;  // chunk ids fit the key's low word; 512K positions at S = 64
+
 bool score_mfma_supported(const ScoreArgs &a) {
-  return a.bf16 && (a.d == 64 || a.d == 128) && a.C <= kScoreMaxC && a.K <= 32 && a.K > 0 &&
+  const bool fits = a.C <= kScoreMaxC || (a.C <= kStreamMaxC && a.Hq / a.Hkv <= 4);
+  return a.bf16 && (a.d == 64 || a.d == 128) && fits && a.K <= 32 && a.K > 0 &&
          (a.r == 0 || (a.Dh % 32 == 0 && a.r <= 64));
+}
+
+template <int D, int KPL>
+static hipError_t launch_score_stream(const ScoreArgs &a, const uint16_t *u_hi, const uint16_t *u_lo,
+                                      const uint16_t *m_hi, const uint16_t *m_lo, int RPa, hipStream_t st) {
+  constexpr int WAVES = 8;
+  auto kern = score_topk_stream_kernel<D, WAVES, KPL>;
+  const size_t items = 2 * static_cast<size_t>(ScoreItemLayout(D, 64, RPa).bytes);
+  const size_t lists = static_cast<size_t>(WAVES) * 16 * 4 * KPL * sizeof(unsigned long long);
+  const size_t smem = items > lists ? items : lists;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     static_cast<int>(smem));
+  if (e != hipSuccess) return e;
+  kern<<<dim3((a.T + WAVES * 16 - 1) / (WAVES * 16) * a.Hkv * a.B), WAVES * 64, smem, st>>>(a, u_hi, u_lo, m_hi,
+                                                                                            m_lo, RPa);
+  return hipGetLastError();
 }
 
 size_t score_mfma_ws_bytes(int B, int T, int Hq, int C, int r) {
@@ -658,6 +956,14 @@ hipError_t launch_score_mfma(const ScoreArgs &a, hipStream_t st) {
                                              m_hi, m_lo, a.Hq, a.C, a.r, RP);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
+  }
+  if (a.C > kScoreMaxC) {  // long sequences: the streaming selection
+    const int RPs = a.r > 0 ? RP : 0;
+    if (a.d == 128)
+      return a.K <= 16 ? launch_score_stream<128, 4>(a, u_hi, u_lo, m_hi, m_lo, RPs, st)
+                       : launch_score_stream<128, 8>(a, u_hi, u_lo, m_hi, m_lo, RPs, st);
+    return a.K <= 16 ? launch_score_stream<64, 4>(a, u_hi, u_lo, m_hi, m_lo, RPs, st)
+                     : launch_score_stream<64, 8>(a, u_hi, u_lo, m_hi, m_lo, RPs, st);
   }
   // candidates per lane in the selection: ceil(C / 64) rounded to 1, 2 or 4
   const int nj = a.C <= 64 ? 1 : (a.C <= 128 ? 2 : 4);
