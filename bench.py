@@ -53,7 +53,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-flush", action="store_true")
     p.add_argument("--no-paged", action="store_true", help="skip the paged-cache decode leg")
-    p.add_argument("--only", choices=["prefill", "decode"], default=None,
+    p.add_argument("--no-long", action="store_true", help="skip the 512K-token prefill leg")
+    p.add_argument("--only", choices=["prefill", "decode", "long"], default=None,
                    help="profile one path (for rocprofv3 runs)")
     p.add_argument("--decode-batches", default="1,4")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle sample time")
@@ -193,6 +194,89 @@ def bench_prefill(args, torch, hils, hs, flush):
                                     attention=float(stage_ms[2])),
                wall_s_incl_flush=wall, flops=fl, wl=wl, inp=inp)
     return res
+
+
+def bench_prefill_long(args, torch, hils, hs, flush):
+    """Long prefill: one 512K-token sequence through the three calls, and the
+    dense causal attention at the same shape through the same attention call
+    (top-K 0, window = T: every query attends all of its prefix)."""
+    wl = hs.WORKLOADS["prefill_512k"]
+    log(f"[prefill 512k] generating inputs {wl}")
+    t0 = time.time()
+    inp = hs.prefill_inputs(wl, args.seed + 20)
+    log(f"[prefill 512k] inputs in {time.time() - t0:.1f}s")
+
+    def dev(a):
+        return torch.from_numpy(a.view(np.int16)).to("cuda").view(torch.bfloat16) if a.dtype == np.uint16 \
+            else torch.from_numpy(a).to("cuda")
+    d = {}
+    for k_, v_ in list(inp.items()):
+        if isinstance(v_, np.ndarray):
+            d[k_] = dev(v_)
+            inp[k_] = None
+    c = hils.Config.from_dict(wl.config_dict())
+    B, T, Hq, Hkv, D, C, K = wl.batch, wl.seq_len, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.n_chunks, wl.top_k
+    k_sum = torch.empty((B, Hq, C, D), dtype=torch.bfloat16, device="cuda")
+    b_sum = torch.empty((B, Hq, C), dtype=torch.float32, device="cuda")
+    ws = torch.empty((hils.hils_prefill_workspace_bytes(c),), dtype=torch.uint8, device="cuda")
+    idx = torch.empty((B, Hkv, T, K), dtype=torch.int32, device="cuda")
+    tsc = torch.empty((B, Hq, T, K), dtype=torch.float32, device="cuda")
+    o = torch.empty((B, Hq, T, D), dtype=torch.bfloat16, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(tm=None):
+        if tm: tm.mark()
+        hils.hils_landmark_summary(c, d["k"], d["q_lm"], 0, C, k_sum, b_sum, stream)
+        if tm: tm.mark()
+        hils.hils_chunk_score_topk(c, d["q"], d["h"], d["w_down"], d["w_up"], k_sum, b_sum, idx, tsc, ws, stream)
+        if tm: tm.mark()
+        hils.hils_sparse_attn_prefill(c, d["q"], d["k"], d["v"], idx, tsc, o, ws, stream)
+        if tm: tm.mark()
+
+    step()
+    torch.cuda.synchronize()
+    per = []
+    for s in range(max(1, min(args.steps, 3))):
+        flush()
+        tm = Timer(torch, stream)
+        step(tm)
+        torch.cuda.synchronize()
+        ev = tm.events
+        per.append([ev[j].elapsed_time(ev[j + 1]) for j in range(3)])
+        log(f"[prefill 512k] step {s}: summary {per[-1][0]:.2f} ms, score {per[-1][1]:.2f} ms, "
+            f"attention {per[-1][2]:.2f} ms")
+    stage = np.array(per).mean(axis=0)
+    ms = float(stage.sum())
+    fl = algorithmic_prefill(wl)
+    out = dict(workload="prefill_512k", batch=B, seq_len=T, ms_per_step=ms, value=B * T / (ms * 1e-3),
+               unit="query-tokens/s",
+               stage_ms=dict(summary=float(stage[0]), score_topk=float(stage[1]), attention=float(stage[2])),
+               attention_tflops=fl["attn"] / (stage[2] * 1e-3) / 1e12,
+               attention_frac_mfma=fl["attn"] / (stage[2] * 1e-3) / 1e12 / PEAK_MFMA_BF16_TFLOPS,
+               score_tflops=(fl["score"] + fl["qcal"]) / (stage[1] * 1e-3) / 1e12)
+    if not args.no_dense:
+        dc = hils.Config.from_dict(dict(wl.config_dict(), top_k=0, window=T))
+        dws = torch.empty((hils.hils_prefill_workspace_bytes(dc),), dtype=torch.uint8, device="cuda")
+        do = torch.empty_like(o)
+        flush()
+        a_ = torch.cuda.Event(enable_timing=True)
+        b_ = torch.cuda.Event(enable_timing=True)
+        a_.record(stream)
+        hils.hils_sparse_attn_prefill(dc, d["q"], d["k"], d["v"], None, None, do, dws, stream)
+        b_.record(stream)
+        torch.cuda.synchronize()
+        dms = a_.elapsed_time(b_)
+        dflops = 4.0 * D * (T * (T + 1) / 2) * B * Hq
+        out["dense"] = dict(ms=dms, tflops=dflops / (dms * 1e-3) / 1e12,
+                            what="causal attention over every prefix, same attention call with top_k 0, window T")
+        out["speedup_vs_dense_attention"] = dms / float(stage[2])
+        out["speedup_vs_dense_step"] = dms / ms
+        log(f"[prefill 512k] dense attention {dms:.1f} ms; sparse step {ms:.1f} ms "
+            f"({dms / ms:.1f}x), attention alone {dms / stage[2]:.1f}x")
+        del dws, do
+    del d, k_sum, b_sum, ws, idx, tsc, o
+    torch.cuda.empty_cache()
+    return out
 
 
 def bench_decode(args, torch, hils, hs, flush, batch):
@@ -357,7 +441,7 @@ def main():
 
     line = dict(metric=METRIC, unit="query-tokens/s", n_gpus=1, steps=args.steps, warmup=args.warmup,
                 higher_is_better=True, scaling="weak", vs_baseline=None, dtype="bf16", data="synthetic")
-    if args.only != "decode":
+    if args.only in (None, "prefill"):
         res = bench_prefill(args, torch, hils, hs, flush)
         wl, fl = res["wl"], res["flops"]
         ms = res["ms"]
@@ -380,7 +464,7 @@ def main():
             log("[cpu] timing the oracle")
             line["cpu_baseline"] = cpu_baseline(args, res)
         del res
-    if args.only != "prefill" and not args.no_decode:
+    if args.only in (None, "decode") and not args.no_decode:
         dec = {}
         for b in [int(x) for x in args.decode_batches.split(",") if x]:
             dec[f"b{b}"] = bench_decode(args, torch, hils, hs, flush, b)
@@ -389,6 +473,12 @@ def main():
             first = dec[next(iter(dec))]
             line.update(value=first["value"], ms_per_step=first["ms_per_step"], roofline=first["roofline"],
                         config=dict(workload="decode_512k", batch=first["batch"], seq_len=first["seq_len"]))
+    if args.only in (None, "long") and not args.no_long:
+        lg = bench_prefill_long(args, torch, hils, hs, flush)
+        line["prefill_512k"] = lg
+        if args.only == "long":
+            line.update(value=lg["value"], ms_per_step=lg["ms_per_step"],
+                        config=dict(workload="prefill_512k", batch=lg["batch"], seq_len=lg["seq_len"]))
     print(json.dumps(line))
 
 

@@ -74,6 +74,11 @@ WORKLOADS = {
     "prefill_8k": Workload("prefill_8k", "prefill", 2, 8192, 32, 8, 128, top_k=16,
                            window=512, qcal_rank=32, hidden_dim=4096,
                            qkv_std=1.0 / math.sqrt(128.0), needles="frac:0.1"),
+    # The same recipe at 512K tokens in one sequence (long prefill: 8192
+    # chunks, up to 8184 eligible per query).
+    "prefill_512k": Workload("prefill_512k", "prefill", 1, 524288, 32, 8, 128, top_k=16,
+                             window=512, qcal_rank=32, hidden_dim=4096,
+                             qkv_std=1.0 / math.sqrt(128.0), needles="frac:0.1"),
     # Decode at 128K: B=8, one needle chunk per sequence at a uniform depth.
     "decode_128k": Workload("decode_128k", "decode", 8, 131072, 32, 8, 128,
                             needles="uniform:1"),

@@ -1,6 +1,7 @@
 """GPU parity at the benchmark shapes, in the launch configuration bench.py
 times: the 8K-token prefill (B=2, 32/8 heads, d=128, K=16, W=512, Q-Cal r=32)
-on sampled query rows plus properties of every row, and decode steps at
+and the same recipe at 512K tokens (B=1) on sampled query rows plus
+properties of every row, and decode steps at
 128K (B=8), 512K (B=4) and 4M (B=1) tokens against the oracle's decode.
 
 Both sides of a decode comparison read the same stored chunk summaries (the
@@ -84,6 +85,42 @@ def test_prefill_8k_sampled_rows():
     err = check_out(go[:, :, qpos], r["o"], "bf16", mask=mask)
     hits = sum(int(n["chunk"] in gidx[n["b"], n["g"], n["query"]]) for n in inp["needles"])
     log(f"prefill 8K: near-tie rows {ties}/{same.size}, max|d| {err:.3g}, needle hits {hits}/{len(inp['needles'])}")
+
+
+def test_prefill_512k_sampled_rows():
+    """One 512K-token sequence (8192 chunks): the streaming scorer and the
+    attention at their longest shape, every row's list checked for validity
+    and sampled rows against the oracle."""
+    wl = hs.WORKLOADS["prefill_512k"]
+    t0 = time.time()
+    inp = hs.prefill_inputs(wl, 7)
+    d = {k: dev(v) for k, v in inp.items() if isinstance(v, np.ndarray)}
+    log(f"prefill 512K: inputs {time.time() - t0:.1f}s")
+    res = gpu_prefill(wl.config_dict(), d)
+    torch.cuda.synchronize()
+    assert bool(torch.isfinite(res["o"]).all())
+    gidx, gtsc = host(res["idx"]), host(res["tsc"])
+    log(f"gpu prefill done ({time.time() - t0:.1f}s)")
+    check_rows_valid(gidx, gtsc, wl.seq_len, wl.window, wl.chunk_size, wl.group)
+    T = wl.seq_len
+    rows = set(np.linspace(0, T - 1, 24).astype(int).tolist())
+    rows |= {0, 575, 576, 640, T // 2, T - 64, T - 1}
+    rows |= {n["query"] for n in inp["needles"][::997]}
+    qpos = np.array(sorted(rows), dtype=np.int32)
+    go = host(res["o"][:, :, torch.from_numpy(qpos).long().cuda()])
+    del res, d
+    gc.collect()
+    torch.cuda.empty_cache()
+    oc = ocfg(wl)
+    r = oracle.prefill(oc, inp, qpos=qpos)
+    log(f"oracle on {qpos.size} rows ({time.time() - t0:.1f}s)")
+    gi = gidx[:, :, qpos]
+    ties = check_topk(gi, r["idx"], r["sigma"])
+    check_scores(gtsc[:, :, qpos], r["tsc"], gi, r["idx"], wl.group)
+    same = (gi == r["idx"]).all(-1)
+    mask = np.repeat(same, wl.group, axis=1)[..., None] & np.ones((1, 1, 1, wl.head_dim), bool)
+    err = check_out(go, r["o"], "bf16", mask=mask)
+    log(f"prefill 512K: near-tie rows {ties}/{same.size}, max|d| {err:.3g}")
 
 
 def _decode_case(name, batch=None, synthetic=False, check_summary_chunks=0):
