@@ -791,7 +791,11 @@ static hipError_t attn_mfma_t(const AttnArgs &a, hipStream_t st) {
                                                                                      ntiles, ntiles * npairs);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int xcd_map = (npairs % 8 == 0) ? 1 : 0;
+  // a (b, g) pair's K and V^T fit one XCD's 4 MB L2: keep each pair on one
+  // XCD; longer sequences: every XCD works on the same pair at a time, so
+  // that the chunks its queries gather stay in the shared memory-side cache
+  const bool pair_fits_l2 = static_cast<size_t>(a.T) * D * 2 * 2 <= (size_t{4} << 20);
+  const int xcd_map = (npairs % 8 == 0 && pair_fits_l2) ? 1 : 0;
   const size_t smem = sizeof(AttnSmem<D, G, WAVES, TPW>) + static_cast<size_t>(C::kQT) * G * a.K * sizeof(float);
   auto kern = attn_prefill_mfma_kernel<D, G, WAVES, TPW>;
   e = hipFuncSetAttribute(reinterpret_cast<const void *>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
