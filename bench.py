@@ -54,6 +54,7 @@ def parse():
     p.add_argument("--no-flush", action="store_true")
     p.add_argument("--no-paged", action="store_true", help="skip the paged-cache decode leg")
     p.add_argument("--no-long", action="store_true", help="skip the 512K-token prefill leg")
+    p.add_argument("--no-decode-more", action="store_true", help="skip the 128K and 4M decode legs")
     p.add_argument("--only", choices=["prefill", "decode", "long"], default=None,
                    help="profile one path (for rocprofv3 runs)")
     p.add_argument("--decode-batches", default="1,4")
@@ -279,14 +280,14 @@ def bench_prefill_long(args, torch, hils, hs, flush):
     return out
 
 
-def bench_decode(args, torch, hils, hs, flush, batch):
-    wl = hs.WORKLOADS["decode_512k_b1" if batch == 1 else "decode_512k_b4"]
+def bench_decode(args, torch, hils, hs, flush, batch, name=None, paged=True):
+    wl = hs.WORKLOADS[name or ("decode_512k_b1" if batch == 1 else "decode_512k_b4")]
     if wl.batch != batch:
         wl = wl.with_(batch=batch)
-    log(f"[decode b{batch}] generating inputs")
+    log(f"[{wl.name} b{batch}] generating inputs")
     t0 = time.time()
     inp = hs.decode_inputs(wl, args.seed + 10)
-    log(f"[decode b{batch}] inputs in {time.time() - t0:.1f}s")
+    log(f"[{wl.name} b{batch}] inputs in {time.time() - t0:.1f}s")
 
     def dev(a):
         return torch.from_numpy(a.view(np.int16)).to("cuda").view(torch.bfloat16) if a.dtype == np.uint16 \
@@ -328,7 +329,7 @@ def bench_decode(args, torch, hils, hs, flush, batch):
         return float(np.mean(ts)), ts
 
     ms, ts = timed(step, args.steps, args.warmup)
-    log(f"[decode b{batch}] step {ms * 1e3:.1f} us ({', '.join(f'{t * 1e3:.1f}' for t in ts)})")
+    log(f"[{wl.name} b{batch}] step {ms * 1e3:.1f} us ({', '.join(f'{t * 1e3:.1f}' for t in ts)})")
     # needle hits (information only)
     gidx = idx.cpu().numpy()
     hits = sum(int(n["chunk"] in gidx[n["b"], n["g"]]) for n in inp["needles"])
@@ -337,10 +338,11 @@ def bench_decode(args, torch, hils, hs, flush, batch):
                bytes_per_step=nb["total"] * B,
                roofline=dict(bound="hbm", achieved=nb["total"] * B / (ms * 1e-3) / 1e9, peak=PEAK_HBM_GBS,
                              unit="GB/s", frac=nb["total"] * B / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
-                             traffic=traffic_record("decode_512k_b%d" % B, DECODE_SOURCES),
+                             traffic=(traffic_record("decode_512k_b%d" % B, DECODE_SOURCES)
+                                      if T == 524288 else None),
                              kernel="decode step (score+select kernel, attend+combine kernel)"),
                needle_hits=f"{hits}/{len(inp['needles'])}")
-    if not args.no_paged:
+    if paged and not args.no_paged:
         # the same caches as a shuffled pool of 64-key pages behind a block table
         S = wl.chunk_size
         perm = torch.randperm(B * C, generator=torch.Generator().manual_seed(args.seed), dtype=torch.int64)
@@ -362,7 +364,7 @@ def bench_decode(args, torch, hils, hs, flush, batch):
         same = bool(torch.equal(po, o) and torch.equal(pidx, idx) and torch.equal(ptsc, tsc))
         out["paged"] = dict(ms_per_step=pms, value=B / (pms * 1e-3),
                             frac_hbm=nb["total"] * B / (pms * 1e-3) / 1e9 / PEAK_HBM_GBS, equal_to_contiguous=same)
-        log(f"[decode b{batch}] paged {pms * 1e3:.1f} us, outputs equal to the contiguous call: {same}")
+        log(f"[{wl.name} b{batch}] paged {pms * 1e3:.1f} us, outputs equal to the contiguous call: {same}")
         del pools, table, pws
     if not args.no_dense:
         dws = torch.zeros((hils.hils_dense_decode_workspace_bytes(c),), dtype=torch.uint8, device="cuda")
@@ -375,7 +377,7 @@ def bench_decode(args, torch, hils, hs, flush, batch):
         out["dense"] = dict(ms_per_step=dms, achieved_GBs=db / (dms * 1e-3) / 1e9,
                             frac_hbm=db / (dms * 1e-3) / 1e9 / PEAK_HBM_GBS)
         out["speedup_vs_dense"] = dms / ms
-        log(f"[decode b{batch}] dense {dms * 1e3:.1f} us, speedup {dms / ms:.1f}x")
+        log(f"[{wl.name} b{batch}] dense {dms * 1e3:.1f} us, speedup {dms / ms:.1f}x")
     del d, k_sum, b_sum, ws
     torch.cuda.empty_cache()
     return out
@@ -469,6 +471,13 @@ def main():
         for b in [int(x) for x in args.decode_batches.split(",") if x]:
             dec[f"b{b}"] = bench_decode(args, torch, hils, hs, flush, b)
         line["decode_512k"] = dec
+        if not args.no_decode_more:
+            # the other decode shapes of the method's efficiency study: 128K
+            # tokens at batch 8, and one 4M-token sequence
+            more = {}
+            for nm, bb in (("decode_128k", 8), ("decode_4m", 1)):
+                more[f"{nm}_b{bb}"] = bench_decode(args, torch, hils, hs, flush, bb, name=nm, paged=False)
+            line["decode_more"] = more
         if args.only == "decode":
             first = dec[next(iter(dec))]
             line.update(value=first["value"], ms_per_step=first["ms_per_step"], roofline=first["roofline"],

@@ -92,7 +92,7 @@ hils_status check_qcal_ptrs(const hils_config *c, const void *h, const void *wd,
 // ------------------------------------------------------------ decode geometry
 struct DecodeGeom {
   int P, NW, nslots, nslot_blocks;
-  size_t off_counts, off_qhat, off_sig, off_hsc, off_parts, total;
+  size_t off_counts, off_qhat, off_sig, off_hsc, off_smax, off_parts, total;
 };
 
 constexpr int kDecodeCPB = 64;      // chunks per score slice
@@ -119,6 +119,8 @@ hils_status decode_geom(const hils_config *c, DecodeGeom *g) {
   off = align_up(off + sizeof(float) * B * Hkv * Cmax);
   g->off_hsc = off;
   off = align_up(off + sizeof(float) * B * Hkv * Cmax * G);
+  g->off_smax = off;
+  off = align_up(off + sizeof(float) * B * Hkv * g->P);
   g->off_parts = off;
   off = align_up(off + sizeof(float) * B * Hkv * g->nslots * G * (D + 2));
   g->total = off;
@@ -369,6 +371,7 @@ hils_status decode_impl(const hils_config *cfg, const void *q, const void *h, co
   a.qhat = reinterpret_cast<float *>(ws + g.off_qhat);
   a.sig = reinterpret_cast<float *>(ws + g.off_sig);
   a.hsc = reinterpret_cast<float *>(ws + g.off_hsc);
+  a.smax = reinterpret_cast<float *>(ws + g.off_smax);
   a.parts = reinterpret_cast<float *>(ws + g.off_parts);
   a.count = counts; a.err = counts + BH;
   a.B = cfg->batch; a.Tmax = cfg->seq_len; a.Hq = cfg->n_q_heads; a.Hkv = cfg->n_kv_heads;

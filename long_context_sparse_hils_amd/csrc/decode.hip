@@ -208,10 +208,19 @@ decode_score_kernel(DecodeArgs a) {
   __syncthreads();
   // sigma and the per-head scores of the slice's chunks (hsc is chunk-major)
   const size_t bg = static_cast<size_t>(b) * a.Hkv + g;
+  // (nch <= kCPB: the slice's chunks are the lanes of wave 0, whose maximum
+  // is the slice's, for the selection's first bound)
   for (int cl = t; cl < nch; cl += kDecThreads) {
     float m = -INFINITY;
     for (int hh = 0; hh < G; ++hh) m = fmaxf(m, sm.s[hh * kCPB + cl]);
     a.sig[bg * a.Cmax + c0 + cl] = m;
+  }
+  if (t < 64) {
+    float m = -INFINITY;
+    if (t < nch)
+      for (int hh = 0; hh < G; ++hh) m = fmaxf(m, sm.s[hh * kCPB + t]);
+    m = wave_reduce_f32<1>(m);
+    if (t == 0) a.smax[bg * a.P + blk] = m;
   }
   for (int x = t; x < nch * G; x += kDecThreads) a.hsc[(bg * a.Cmax + c0) * G + x] = sm.s[(x % G) * kCPB + x / G];
 }
@@ -315,8 +324,8 @@ struct SelSmem {
   uint32_t tw[kSelWaves];         // per-wave lower bound of the threshold
   uint32_t red[2][kSelWaves];     // per-wave partial sums / minima, double buffered
   uint32_t red2[2][kSelWaves];
-  int nkey, nsurv;
-  uint32_t sord[kDecThreads * kSelVPT];  // the tile's ordered scores (0 = none)
+  int nkey, nsurv, nslice;
+  uint32_t sord[kDecThreads * kSelVPT];  // the tile's ordered scores (0 = none); or surviving slices
 };
 
 __device__ __forceinline__ unsigned long long sel_key(uint32_t ord, int c) {
@@ -627,6 +636,94 @@ __device__ __forceinline__ int block_topk(const float *sig, int n, int cmax, int
   return keep;
 }
 
+// The same selection, narrowed first by the slices' maxima (each the largest
+// group score of 64 consecutive chunks, stored by D1):
+//  1. a lower bound of the threshold from the maxima, as in step 1 above:
+//     K lanes whose maximum over their slices reaches it hold K distinct
+//     chunks' scores at or above it;
+//  2. only slices whose maximum reaches the bound can hold a winner; their
+//     scores at or above the bound are the survivors;
+//  3. one wave selects exactly among them.
+// Too many surviving slices or scores (many equal scores): block_topk.
+constexpr int kSlicePT = 8;                          // slice maxima per thread
+constexpr int kSliceMax = kDecThreads * kSelVPT;     // surviving slices kept (LDS: ss.sord)
+__device__ __forceinline__ int block_topk_sliced(const float *sig, const float *smax, int n, int cmax, int K,
+                                                 SelSmem &ss) {
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int ns = (n + kCPB - 1) / kCPB;  // slices holding eligible chunks
+  uint32_t mx = 0u, so[kSlicePT];
+#pragma unroll
+  for (int j = 0; j < kSlicePT; ++j) {
+    const int s = j * kDecThreads + t;
+    const float v = smax[s < ns ? s : 0];
+    so[j] = s < ns ? orderable(v) : 0u;
+    mx = max(mx, so[j]);
+  }
+  {
+    const uint32_t kth = wave_kth_u32(mx, K);
+    if (lane == 0) ss.tw[wave] = kth;
+  }
+  if (t == 0) {
+    ss.nkey = 0;
+    ss.nsurv = 0;
+    ss.nslice = 0;
+  }
+  __syncthreads();
+  uint32_t bound = 1u;
+#pragma unroll
+  for (int w = 0; w < kSelWaves; ++w) bound = max(bound, ss.tw[w]);
+#pragma unroll
+  for (int j = 0; j < kSlicePT; ++j) {
+    if (so[j] >= bound) {
+      const int p = atomicAdd(&ss.nslice, 1);
+      if (p < kSliceMax) ss.sord[p] = static_cast<uint32_t>(j * kDecThreads + t);
+    }
+  }
+  __syncthreads();
+  const int nsl = ss.nslice;
+  if (nsl > kSliceMax) return block_topk(sig, n, cmax, K, ss);
+  // the surviving slices' scores: loads first, then the filter
+  constexpr int kPT = 8;  // scores per thread per round
+  for (int x0 = 0; x0 < nsl * kCPB; x0 += kDecThreads * kPT) {
+    float v[kPT];
+    int c[kPT];
+#pragma unroll
+    for (int j = 0; j < kPT; ++j) {
+      const int x = x0 + j * kDecThreads + t;
+      const int sl = x < nsl * kCPB ? static_cast<int>(ss.sord[x / kCPB]) : 0;
+      c[j] = x < nsl * kCPB ? sl * kCPB + x % kCPB : n;
+      v[j] = sig[c[j] < n ? c[j] : 0];
+    }
+#pragma unroll
+    for (int j = 0; j < kPT; ++j) {
+      const uint32_t o = c[j] < n ? orderable(v[j]) : 0u;
+      if (o >= bound) {
+        const int p = atomicAdd(&ss.nsurv, 1);
+        if (p < kSurvMax) ss.surv[p] = sel_key(o, c[j]);
+      }
+    }
+  }
+  __syncthreads();
+  const int tot = ss.nsurv;
+  if (tot > kSurvMax) return block_topk(sig, n, cmax, K, ss);
+  if (wave == 0) {
+    if (tot <= 64)
+      select_survivors<1>(ss, tot, K);
+    else
+      select_survivors<kSurvNJ>(ss, tot, K);
+  }
+  __syncthreads();
+  const int keep = ss.nkey;
+  if (t < keep) {
+    const unsigned long long k0 = ss.key[t];
+    int r = 0;
+    for (int e = 0; e < keep; ++e) r += ss.key[e] > k0 ? 1 : 0;
+    ss.sorted[r] = k0;
+  }
+  __syncthreads();
+  return keep;
+}
+
 // D2: every slot workgroup of (b, g) selects the top-K from the group scores
 // (the same arithmetic in each, so they agree), slot 0 writes the lists,
 // and slot k attends the chunk of rank k; the last workgroup combines the
@@ -655,7 +752,9 @@ decode_attend_kernel(DecodeArgs a) {
       const int x = t + r * kDecThreads;
       if (r * kDecThreads < G * D) qreg[r] = Elem<T>::load(qsrc, x < G * D ? x : 0);
     }
-    const int keep = block_topk(a.sig + bg * a.Cmax, n, a.Cmax, K, ss);
+    const int keep = (n > kCPB * K && (n + kCPB - 1) / kCPB <= kSlicePT * kDecThreads)
+                         ? block_topk_sliced(a.sig + bg * a.Cmax, a.smax + bg * a.P, n, a.Cmax, K, ss)
+                         : block_topk(a.sig + bg * a.Cmax, n, a.Cmax, K, ss);
 #pragma unroll
     for (int r = 0; r < QPT; ++r) {
       const int x = t + r * kDecThreads;

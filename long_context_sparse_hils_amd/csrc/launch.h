@@ -54,6 +54,7 @@ struct DecodeArgs {
   float *qhat;                   // [B, Hq, d] (Q-Cal only)
   float *sig;                    // [B, Hkv, Cmax]: group score of each eligible chunk
   float *hsc;                    // [B, Hkv, Cmax, G]: each head's own score
+  float *smax;                   // [B, Hkv, P]: the largest group score of each 64-chunk slice
   float *parts;                  // [B, Hkv, nslots, G, d+2]
   unsigned *count, *err;
   int B, Tmax, Hq, Hkv, d, S, K, W, r, Dh, Cmax;
