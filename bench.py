@@ -55,6 +55,8 @@ def parse():
     p.add_argument("--no-paged", action="store_true", help="skip the paged-cache decode leg")
     p.add_argument("--no-long", action="store_true", help="skip the 512K-token prefill leg")
     p.add_argument("--no-decode-more", action="store_true", help="skip the 128K and 4M decode legs")
+    p.add_argument("--decode-shapes", default="decode_128k:8,decode_4m:1",
+                   help="the further decode legs, workload:batch, comma separated")
     p.add_argument("--only", choices=["prefill", "decode", "long"], default=None,
                    help="profile one path (for rocprofv3 runs)")
     p.add_argument("--decode-batches", default="1,4")
@@ -475,10 +477,11 @@ def main():
             # the other decode shapes of the method's efficiency study: 128K
             # tokens at batch 8, and one 4M-token sequence
             more = {}
-            for nm, bb in (("decode_128k", 8), ("decode_4m", 1)):
-                more[f"{nm}_b{bb}"] = bench_decode(args, torch, hils, hs, flush, bb, name=nm, paged=False)
+            for spec in [x for x in args.decode_shapes.split(",") if x]:
+                nm, bb = spec.split(":")
+                more[f"{nm}_b{bb}"] = bench_decode(args, torch, hils, hs, flush, int(bb), name=nm, paged=False)
             line["decode_more"] = more
-        if args.only == "decode":
+        if args.only == "decode" and dec:
             first = dec[next(iter(dec))]
             line.update(value=first["value"], ms_per_step=first["ms_per_step"], roofline=first["roofline"],
                         config=dict(workload="decode_512k", batch=first["batch"], seq_len=first["seq_len"]))
