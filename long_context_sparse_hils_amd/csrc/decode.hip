@@ -313,7 +313,7 @@ __device__ __forceinline__ void combine_slots(const float *recs, int nslots, int
 }
 
 // ------------------------------------------------------------------ D2
-constexpr int kSelVPT = 32;
+constexpr int kSelVPT = 8;  // a 2048-score tile: D2 then fits four workgroups per CU (LDS, registers)
 constexpr int kSelWaves = kDecThreads / 64;
 constexpr int kSurvMax = 256;  // survivors the one-wave exact select takes (plus the kept winners)
 constexpr int kSurvNJ = (kSurvMax + 32 + 63) / 64;
@@ -527,7 +527,7 @@ __device__ __forceinline__ void select_survivors(SelSmem &ss, int tot, int K) {
 
 // Block-wide top-K of the group scores sigma[0..n) by (sigma desc, chunk
 // asc), all kDecThreads threads, in tiles of kDecThreads * kSelVPT scores
-// (one tile covers a 512K-token cache: 8192 chunks).  Per tile:
+// (2048 chunks; longer lists go through block_topk_sliced first).  Per tile:
 //  1. a lower bound of the threshold: in a wave whose lanes' maxima include
 //     at least K scores, the K-th largest lane maximum is exceeded or met by
 //     K distinct scores, so it cannot lie above the tile's K-th largest
