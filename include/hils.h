@@ -114,6 +114,9 @@ size_t hils_prefill_workspace_bytes(const hils_config *cfg);
  *   topk_score [B, H_q, T, K]     f32    out: each head's own s of those
  *                                        chunks, -inf pad
  *   workspace  >= hils_prefill_workspace_bytes(cfg) bytes, device memory.
+ * C = floor(T/S) may reach 8192 (T = 512K at S = 64; UNSUPPORTED above);
+ * sequences of more than 256 chunks stream the summaries and keep a running
+ * top-K per query (same result, same order).
  */
 hils_status hils_chunk_score_topk(const hils_config *cfg, const void *q, const void *h,
                                   const void *w_down, const void *w_up, const void *k_sum,
