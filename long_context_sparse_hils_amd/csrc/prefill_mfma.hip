@@ -489,7 +489,9 @@ attn_prefill_mfma_kernel(AttnArgs a, const uint8_t *__restrict__ plan, int ntile
 #pragma unroll
   for (int r = 0; r < kPairs; ++r) {
     const int x = tid + r * C::kThreads, q = x / C::kKMax, k = x % C::kKMax;
-    const int c = (q < C::kQT && k < K && q0 + q < T) ? my_c[r] : -1;
+    // (an id outside the sequence's chunks counts as no chunk: the union
+    // masks below are never indexed out of range)
+    const int c = (q < C::kQT && k < K && q0 + q < T && my_c[r] < C_chunks) ? my_c[r] : -1;
     my_c[r] = c;
     if (q < C::kQT) sm.ulist[x] = static_cast<int16_t>(c);  // scratch copy of the raw lists
     if (c >= 0) atomicOr(&sm.umask[c >> 5], 1u << (c & 31));

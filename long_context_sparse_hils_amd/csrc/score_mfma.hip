@@ -26,6 +26,8 @@
 //                    for the K-th largest group score (counts from row sums
 //                    of the 4 lanes of a query) and a rank pass order the
 //                    winners by (score desc, chunk asc).
+#include <type_traits>
+
 #include "hils_common.h"
 #include "launch.h"
 
@@ -510,12 +512,14 @@ score_topk_mfma_kernel(ScoreArgs a, const uint16_t *__restrict__ u_hi, const uin
     }
   }
   // winners as a bit mask over the lane's candidates
-  uint32_t winm = 0u;
+  // winners as a bit mask over the lane's NV candidates (64 when NJ = 4)
+  using WMask = typename std::conditional<(NV > 32), unsigned long long, uint32_t>::type;
+  WMask winm = 0;
   uint32_t ngt = 0;
 #pragma unroll
   for (int v = 0; v < NV; ++v) {
     const bool w = keep > 0 && (done ? ord[v] >= theta : ord[v] > theta);
-    winm |= w ? (1u << v) : 0u;
+    winm |= w ? (WMask{1} << v) : WMask{0};
     ngt += w ? 1u : 0u;
   }
   // ties at theta (queries not done): the lowest chunks first, one per round
@@ -532,14 +536,14 @@ score_topk_mfma_kernel(ScoreArgs a, const uint16_t *__restrict__ u_hi, const uin
 #pragma unroll
       for (int v = 0; v < NV; ++v) {
         const uint32_t c = 16 * (v >> 2) + 4 * lg + (v & 3);
-        if (c == m) winm |= 1u << v;
+        if (c == m) winm |= WMask{1} << v;
       }
       need_eq = m == 0xFFFFu ? 0 : need_eq - 1;
     }
   }
   // compact each query's winners (in lane-row order) into LDS
   {
-    uint32_t pos = uprefix_rows4(static_cast<uint32_t>(__popc(winm)));
+    uint32_t pos = uprefix_rows4(static_cast<uint32_t>(NV > 32 ? __popcll(winm) : __popc(static_cast<uint32_t>(winm))));
 #pragma unroll
     for (int v = 0; v < NV; ++v) {
       if ((winm >> v) & 1u) {

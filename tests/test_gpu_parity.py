@@ -53,6 +53,9 @@ PREFILL_CASES = {
     # Q-Cal rank 48 (two 32-wide halves, the second part-filled) over a
     # hidden size with a 96-column tail past its 128-wide steps
     "qcal_r48_ragged_dh": wl_prefill(T=1024, Hq=4, Hkv=2, d=64, K=8, W=128, r=48, Dh=352),
+    # 129..256 chunks: 64 candidates per lane in the one-pass scorer
+    "c140_d64_k20": wl_prefill(T=9000, Hq=4, Hkv=1, d=64, K=20, W=128),
+    "c156_d128_qcal": wl_prefill(T=10000, Hq=4, Hkv=1, d=128, K=8, W=256, r=32, Dh=256),
 }
 
 
