@@ -25,7 +25,19 @@ from _gpu import check_out, check_scores, check_topk, dev, gpu_attn, gpu_decode,
 
 @pytest.mark.parametrize("case", range(16))
 def test_random_shape(case):
-    rng = np.random.default_rng(1000 + case)
+    _run_case(case, np.random.default_rng(1000 + case))
+
+
+EDGE_T = [1, 63, 64, 65, 511, 512, 513, 575, 576, 577, 8191, 8192, 8193, 16384]
+
+
+@pytest.mark.parametrize("T", EDGE_T)
+def test_edge_length(T):
+    """Lengths at chunk and window boundaries (other parameters random)."""
+    _run_case(100 + EDGE_T.index(T), np.random.default_rng(2000 + T), T_fixed=T)
+
+
+def _run_case(case, rng, T_fixed=None):
     G = int(rng.choice([1, 2, 4, 8]))
     Hkv = int(rng.choice([1, 2]))
     d = int(rng.choice([64, 128]))
@@ -39,6 +51,8 @@ def test_random_shape(case):
         T = int(rng.integers(4100, 16400))
     else:
         T = int(rng.integers(40, 4000))
+    if T_fixed is not None:
+        T = T_fixed
     K = int(rng.integers(1, 33))
     W = int(rng.choice([64, 128, 200, 512, 1000]))
     B = int(rng.choice([1, 2]))
