@@ -1,6 +1,6 @@
 """Randomised shapes on the GPU: each case draws a configuration (batch,
-length from tens of tokens to past 256 chunks, group size, head dim, top-K,
-window, Q-Cal rank and hidden size, bf16 or fp32) from a fixed seed and
+length from tens of tokens to past 256 chunks, group size 1-16, head dim,
+top-K, window, Q-Cal rank and hidden size, bf16 or fp32) from a fixed seed and
 checks the prefill stages on sampled rows and a decode step at random
 lengths against the oracle, and the paged decode against the contiguous
 one, bit for bit."""
@@ -38,7 +38,7 @@ def test_edge_length(T):
 
 
 def _run_case(case, rng, T_fixed=None):
-    G = int(rng.choice([1, 2, 4, 8]))
+    G = int(rng.choice([1, 2, 4, 8, 16]))
     Hkv = int(rng.choice([1, 2]))
     d = int(rng.choice([64, 128]))
     u = rng.random()
@@ -83,13 +83,19 @@ def _run_case(case, rng, T_fixed=None):
                           host(gidx)[:, :, rows], host(gtsc)[:, :, rows].astype(np.float64))
     err = check_out(host(o)[:, :, rows], oref, dt)
     # decode on the same caches at random lengths, contiguous and paged
-    dwl = hs.Workload("d", "decode", B, T, G * Hkv, Hkv, d, top_k=K, window=W, needles="none", dtype=dt)
+    dwl = hs.Workload("d", "decode", B, T, G * Hkv, Hkv, d, top_k=K, window=W, needles="none", dtype=dt,
+                      qcal_rank=r, hidden_dim=Dh)
     dc = hils.Config.from_dict(dwl.config_dict())
     doc = oracle.OracleConfig.from_dict(dwl.config_dict())
     sl = rng.integers(1, T + 1, size=B).astype(np.int32)
     q1 = hs.normal((B, G * Hkv, d), 500 + case, hs.STREAM_Q, 1.0, dtype=dt)
     dinp = dict(q=q1, k_cache=inp["k"], v_cache=inp["v"], seq_lens=sl)
-    res = gpu_decode(dwl.config_dict(), dict(q=dev(q1), k_cache=dd["k"], v_cache=dd["v"]), dev(ks), dev(bs), dev(sl))
+    dq = dict(q=dev(q1), k_cache=dd["k"], v_cache=dd["v"])
+    if r:
+        h1 = hs.normal((B, Dh), 600 + case, hs.STREAM_H, 1.0, dtype=dt)
+        dinp.update(h=h1, w_down=inp["w_down"], w_up=inp["w_up"])
+        dq.update(h=dev(h1), w_down=dd["w_down"], w_up=dd["w_up"])
+    res = gpu_decode(dwl.config_dict(), dq, dev(ks), dev(bs), dev(sl))
     r2 = oracle.decode(doc, dinp, ks, bs)
     dties = check_topk(host(res["idx"]), r2["idx"], r2["sigma"]) if K else 0
     same = (host(res["idx"]) == r2["idx"]).all(-1)
@@ -111,7 +117,7 @@ def _run_case(case, rng, T_fixed=None):
         kp, vp = pool(inp["k"]), pool(inp["v"])
         ws = torch.zeros((hils.hils_decode_workspace_bytes(dc),), dtype=torch.uint8, device="cuda")
         po = torch.empty_like(res["o"]); pi = torch.empty_like(res["idx"]); pt = torch.empty_like(res["tsc"])
-        hils.hils_sparse_attn_decode_paged(dc, dev(q1), None, None, None, kp, vp, dev(perm), mp, npg, dev(ks), dev(bs),
+        hils.hils_sparse_attn_decode_paged(dc, dev(q1), dq.get("h"), dq.get("w_down"), dq.get("w_up"), kp, vp, dev(perm), mp, npg, dev(ks), dev(bs),
                                            dev(sl), po, pi, pt, ws)
         torch.cuda.synchronize()
         assert torch.equal(po, res["o"]) and torch.equal(pi, res["idx"]), "paged != contiguous"
