@@ -76,6 +76,51 @@ def test_qcal_is_linear_in_the_hidden_state():
     assert np.allclose(f(inp["h"] + h2), f(inp["h"]) + f(h2), atol=1e-12, rtol=0)
 
 
+def test_qcal_leaves_the_token_logits_on_the_raw_query():
+    """Q-Cal calibrates the query for chunk-level scoring only (picx.dev
+    summary, Methodology 3); the per-token logits inside a chunk and in the
+    window use the raw q (Eq. 10's first factor).  With every chunk selected
+    and exact chunk masses, the pipeline must therefore give causal softmax
+    attention over the RAW query even with a large calibration residual; an
+    oracle that fed q-hat to the token logits would give attention over q-hat."""
+    cfg = _cfg(seq_len=120, qcal_rank=3, hidden_dim=12)
+    inp = _prefill_inputs(cfg, 21, std=1.5, qcal=True)
+    r = oracle.prefill(cfg, inp, select_all=True, exact_mass=True)
+    assert np.abs(r["qhat"] - inp["q"]).max() > 0.5       # the residual is not small
+    tau = 1 / math.sqrt(cfg.head_dim)
+    for h in range(4):
+        ref = causal_attention_rows(inp["q"][0, h], inp["k"][0, h // 2], inp["v"][0, h // 2],
+                                    np.arange(cfg.seq_len), tau)
+        assert np.abs(r["o"][0, h] - ref).max() < 1e-12
+
+
+def test_qcal_query_is_the_one_that_scores_chunks():
+    """Eq. 7 is exact at q = q'_c (picx.dev summary, Methodology 1).  Build a
+    rank-one calibration that moves query i exactly onto chunk c's landmark
+    queries: W_down reads hidden unit a, h_i[a] = 1, and W_up's column is
+    q'_c - q_i for every head.  The pipeline's score of chunk c for query i
+    must then be the exact chunk log-sum-exp, which it is not for the raw q;
+    so this fails if the scores were taken from q instead of q-hat."""
+    cfg = _cfg(seq_len=160, qcal_rank=1, hidden_dim=6)
+    inp = _prefill_inputs(cfg, 22, std=1.5, qcal=True)
+    i, c, a = 150, 5, 4
+    d, S, G = cfg.head_dim, cfg.chunk_size, 2
+    inp["w_down"][:] = 0
+    inp["w_down"][0, a] = 1.0
+    inp["h"][0, i, :] = 0
+    inp["h"][0, i, a] = 1.0
+    inp["w_up"][:, 0] = (inp["q_lm"][0, :, c] - inp["q"][0, :, i]).reshape(-1)
+    r = oracle.prefill(cfg, inp)
+    tau = 1 / math.sqrt(d)
+    assert np.abs(r["qhat"][0, :, i] - inp["q_lm"][0, :, c]).max() < 1e-12
+    for h in range(4):
+        kc = inp["k"][0, h // G, c * S:(c + 1) * S]
+        exact = lse(tau * kc @ inp["q_lm"][0, h, c])
+        raw = lse(tau * kc @ inp["q"][0, h, i])
+        assert abs(r["s"][0, h, i, c] - exact) < 1e-12
+        assert abs(raw - exact) > 1e-3                      # the raw query would miss it
+
+
 # ----------------------------------------------------------------------- scores
 def test_score_at_the_landmark_query_is_the_exact_chunk_mass():
     """Eq. 7 read with q = q'_c is exact: when a query equals chunk c's
