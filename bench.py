@@ -12,12 +12,15 @@ input resident in HBM:
     decode on the same data for the speedup.
 
 Timing: HIP events on the library's stream around each call; every timed
-step starts from cold caches (a 1 GiB read-modify-write sweep outside the
-events evicts L2 and the 256 MB Infinity Cache).  The JSON line reports the
-mean over the timed steps.  Roofline: algorithmic work of the dominant
-kernel per launch over its measured duration, against MI355X peaks (bf16
-dense MFMA 2.5 PFLOP/s, HBM 8 TB/s).  The CPU baseline is the float64 oracle
-timed on a bounded sample of the same prefill workload on the host cores.
+step starts from cold caches (a 1 GiB read-only sweep outside the events
+evicts L2 and the 256 MB Infinity Cache and leaves no dirty lines behind).
+The JSON line reports the mean over the timed steps.  Roofline: algorithmic
+work of the dominant kernel per launch over its measured duration, against
+MI355X peaks (bf16 dense MFMA 2.5 PFLOP/s, HBM 8 TB/s).  The CPU baseline is
+the float64 oracle timed on a bounded sample of the same prefill workload
+(and on one 512K decode step) on the host cores; where it ran the whole
+prefill workload, its top-K lists and outputs are compared with the GPU's
+and the near-tie count is reported under "parity_8k".
 """
 from __future__ import annotations
 
@@ -189,13 +192,15 @@ def bench_prefill(args, torch, hils, hs, flush):
         log(f"[prefill] step {s}: summary {per[-1][0]:.3f} ms, score {per[-1][1]:.3f} ms, "
             f"attention {per[-1][2]:.3f} ms")
     wall = time.time() - wall0
+    gpu_out = dict(idx=idx.cpu().numpy(), tsc=tsc.cpu().numpy(),
+                   o=o.view(torch.int16).cpu().numpy().view(np.uint16))
     per = np.array(per)
     stage_ms = per.mean(axis=0)
     ms = float(stage_ms.sum())
     fl = algorithmic_prefill(wl)
     res = dict(ms=ms, stage_ms=dict(summary=float(stage_ms[0]), score_topk=float(stage_ms[1]),
                                     attention=float(stage_ms[2])),
-               wall_s_incl_flush=wall, flops=fl, wl=wl, inp=inp)
+               wall_s_incl_flush=wall, flops=fl, wl=wl, inp=inp, gpu_out=gpu_out)
     return res
 
 
@@ -340,8 +345,8 @@ def bench_decode(args, torch, hils, hs, flush, batch, name=None, paged=True):
                bytes_per_step=nb["total"] * B,
                roofline=dict(bound="hbm", achieved=nb["total"] * B / (ms * 1e-3) / 1e9, peak=PEAK_HBM_GBS,
                              unit="GB/s", frac=nb["total"] * B / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
-                             traffic=(traffic_record("decode_512k_b%d" % B, DECODE_SOURCES)
-                                      if T == 524288 else None),
+                             traffic=traffic_record(f"{wl.name.replace('_b1', '').replace('_b4', '')}_b{B}",
+                                                    DECODE_SOURCES),
                              kernel="decode step (score+select kernel, attend+combine kernel)"),
                needle_hits=f"{hits}/{len(inp['needles'])}")
     if paged and not args.no_paged:
@@ -385,6 +390,69 @@ def bench_decode(args, torch, hils, hs, flush, batch, name=None, paged=True):
     return out
 
 
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def parity_8k(wl, gpu, ref):
+    """Top-K lists and outputs of the timed GPU step against the oracle's
+    whole forward: rows with an identical list, rows accepted as near ties
+    (every chunk in the symmetric difference within 1e-5 of the oracle's
+    K-th group score), rows that fail that rule, and the largest output
+    difference on rows whose list matches."""
+    import hils_synth as hs
+    gi, oi, sig = gpu["idx"], ref["idx"], ref["sigma"]
+    same = (gi == oi).all(-1)
+    ties = bad = 0
+    for b, g, i in zip(*np.nonzero(~same)):
+        want, got = oi[b, g, i], gi[b, g, i]
+        keep = int((want >= 0).sum())
+        ok = int((got >= 0).sum()) == keep
+        if ok:
+            kth = sig[b, g, i, want[keep - 1]]
+            ok = all(abs(sig[b, g, i, c] - kth) <= 1e-5
+                     for c in set(got[:keep].tolist()) ^ set(want[:keep].tolist()))
+        ties += int(ok)
+        bad += int(not ok)
+    m = np.repeat(same, wl.group, axis=1)
+    diff = np.abs(hs.as_f64(gpu["o"])[m] - ref["o"][m])
+    tol_bad = int((diff > 1e-2 + 1e-2 * np.abs(ref["o"][m])).sum())
+    return dict(rows=int(same.size), identical_rows=int(same.sum()), near_tie_rows=ties,
+                mismatched_rows=bad, max_abs_diff=float(diff.max()) if diff.size else 0.0,
+                out_of_tolerance_elements=tol_bad, tolerance="1e-2 + 1e-2 |ref| (bf16)")
+
+
+def cpu_baseline_decode(args, oracle, hs):
+    """The oracle's decode step (scoring every eligible chunk from the given
+    summaries, top-K, fusion with the window) at 512K tokens, batch 1, on
+    the same seeded inputs as the GPU leg; the summaries it reads are built
+    by the oracle beforehand and not timed (the GPU leg does not time them
+    either)."""
+    wl = hs.WORKLOADS["decode_512k_b1"]
+    inp = hs.decode_inputs(wl, args.seed + 10)
+    oc = oracle.OracleConfig.from_dict(wl.config_dict())
+    ks64, bs64 = oracle.summary(oc, inp["k_cache"], inp["q_lm"])
+    ks, bs = oracle.store(oc, ks64), bs64.astype(np.float32)
+    del ks64, bs64
+    t0 = time.time()
+    n = 0
+    while True:
+        oracle.decode(oc, inp, ks, bs)
+        n += 1
+        if time.time() - t0 > 2.0:
+            break
+    dt = (time.time() - t0) / n
+    return dict(value=wl.batch / dt, unit="query-tokens/s", cores=oracle.threads(), kind="oracle",
+                sample=f"decode_512k batch 1: {n} oracle decode steps (scores over 8184 chunks x 32 heads, "
+                       f"top-16 per group, fusion with the 512-key window); {dt * 1e3:.0f} ms per step")
+
+
 def cpu_baseline(args, res):
     """The float64 oracle, as it stands, on a bounded sample of the prefill
     workload: all chunk summaries of batch 0, then scoring, selection and
@@ -408,11 +476,14 @@ def cpu_baseline(args, res):
         # the whole workload fits the time target: every sequence, every query
         ocf = oracle.OracleConfig.from_dict(wl.config_dict())
         t0 = time.time()
-        oracle.prefill(ocf, inp)
+        ref = oracle.prefill(ocf, inp)
         dt = time.time() - t0
-        return dict(value=wl.batch * wl.seq_len / dt, unit="query-tokens/s", cores=oracle.threads(), kind="oracle",
-                    sample=f"the whole prefill_8k workload: {wl.batch} sequences x {wl.seq_len} queries "
-                           f"(summaries, Q-Cal, scoring, top-K, fusion); {dt:.1f} s")
+        out = dict(value=wl.batch * wl.seq_len / dt, unit="query-tokens/s", cores=oracle.threads(), kind="oracle",
+                   cpu_model=cpu_model(),
+                   sample=f"the whole prefill_8k workload: {wl.batch} sequences x {wl.seq_len} queries "
+                          f"(summaries, Q-Cal, scoring, top-K, fusion); {dt:.1f} s")
+        res["parity_8k"] = parity_8k(wl, res["gpu_out"], ref)
+        return out
     nq = int(min(wl.seq_len, max(probe.size, nq)))
     stride = max(1, wl.seq_len // nq)
     qpos = np.arange(stride // 2, wl.seq_len, stride, dtype=np.int32)
@@ -420,6 +491,7 @@ def cpu_baseline(args, res):
     oracle.prefill(oc, sub, qpos=qpos)
     dt = time.time() - t0
     return dict(value=qpos.size / dt, unit="query-tokens/s", cores=oracle.threads(), kind="oracle",
+                cpu_model=cpu_model(),
                 sample=f"prefill_8k batch 0: all {wl.n_chunks} chunk summaries, then scoring/top-K/fusion for "
                        f"{qpos.size} of {wl.seq_len} query positions (stride {stride}); {dt:.1f} s")
 
@@ -467,6 +539,13 @@ def main():
         if not args.no_cpu_baseline:
             log("[cpu] timing the oracle")
             line["cpu_baseline"] = cpu_baseline(args, res)
+            if "parity_8k" in res:
+                line["parity_8k"] = res["parity_8k"]
+                log(f"[cpu] parity of the timed step: {res['parity_8k']}")
+            if not args.no_decode:
+                import hils_synth as hs_
+                import oracle
+                line["cpu_baseline"]["decode_512k_b1"] = cpu_baseline_decode(args, oracle, hs_)
         del res
     if args.only in (None, "decode") and not args.no_decode:
         dec = {}

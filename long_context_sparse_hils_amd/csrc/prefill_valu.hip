@@ -152,9 +152,13 @@ attn_valu_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__re
   win.init();
   float2 ou[NP];
   const size_t ibase = ((static_cast<size_t>(b) * Hkv + g) * T_len + i) * K;
+  const int n = eligible_chunks(i, W, S);
   for (int kk = 0; kk < K; ++kk) {
     const int c = topk_idx[ibase + kk];
-    if (c < 0) continue;  // uniform across the block
+    // -1 pads; an id outside the eligible chunks [0, n_i) is no chunk (it
+    // would overlap the window or lie past the sequence).  Uniform across
+    // the block.
+    if (c < 0 || c >= n) continue;
     attend_unit<T, D>(sm, kb + static_cast<size_t>(c) * S * D, vb + static_cast<size_t>(c) * S * D, S, G, tau, ou);
 #pragma unroll
     for (int r = 0; r < NP; ++r) {
@@ -167,7 +171,6 @@ attn_valu_kernel(const T *__restrict__ q, const T *__restrict__ k, const T *__re
     }
     __syncthreads();
   }
-  const int n = eligible_chunks(i, W, S);
   for (int j0 = n * S; j0 <= i; j0 += kUnitKeys) {
     const int nk = min(kUnitKeys, i - j0 + 1);
     attend_unit<T, D>(sm, kb + static_cast<size_t>(j0) * D, vb + static_cast<size_t>(j0) * D, nk, G, tau, ou);

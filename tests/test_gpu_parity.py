@@ -56,6 +56,14 @@ PREFILL_CASES = {
     # 129..256 chunks: 64 candidates per lane in the one-pass scorer
     "c140_d64_k20": wl_prefill(T=9000, Hq=4, Hkv=1, d=64, K=20, W=128),
     "c156_d128_qcal": wl_prefill(T=10000, Hq=4, Hkv=1, d=128, K=8, W=256, r=32, Dh=256),
+    # bf16 shapes the MFMA kernels do not tile, served by the VALU kernels:
+    # group sizes that are not powers of two (attention) ...
+    "bf16_g3_valu_attn": wl_prefill(T=1536, Hq=6, Hkv=2, d=128, K=8, W=256, r=16, Dh=128),
+    "bf16_g6_d64_valu_attn": wl_prefill(T=1100, Hq=6, Hkv=1, d=64, K=8, W=128),
+    # ... more than 256 chunks with a group above 4 (scoring) ...
+    "bf16_g8_c300_valu_score": wl_prefill(T=19237, Hq=8, Hkv=1, d=64, K=16, W=256),
+    # ... and Q-Cal over a hidden size that is not a multiple of 32 (scoring)
+    "bf16_qcal_dh100_valu_score": wl_prefill(T=1024, Hq=4, Hkv=2, d=128, K=8, W=128, r=16, Dh=100),
 }
 
 
@@ -155,7 +163,8 @@ def test_score_topk_all_scores_tied():
     check_scores(gtsc, r["tsc"], gidx, r["idx"], wl.group)
 
 
-@pytest.mark.parametrize("name", ["tiny_f32", "sharp_bf16_qcal", "scaled_needles", "ragged_d64_g1"])
+@pytest.mark.parametrize("name", ["tiny_f32", "sharp_bf16_qcal", "scaled_needles", "ragged_d64_g1",
+                                  "bf16_g3_valu_attn", "bf16_qcal_dh100_valu_score"])
 def test_prefill_end_to_end(name):
     """summary -> score/top-K -> attention on the GPU against the oracle's
     whole forward from the same inputs; rows with an accepted near-tie swap
