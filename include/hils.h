@@ -16,7 +16,8 @@
  *               CUDA/HIP tensor), contiguous, in the layouts stated per call,
  *               16-byte aligned.  The caller owns every buffer.  The library
  *               allocates nothing and keeps no state between calls; the only
- *               persistent object is the caller-owned decode workspace.
+ *               persistent objects are the caller-owned decode workspace and
+ *               the fixed scratch array of the allocation-free decode call.
  *   Streams     `stream` is a hipStream_t passed as void* (NULL = the default
  *               stream).  Calls only enqueue work; outputs are valid once the
  *               stream has been synchronised.  No call synchronises the host.
@@ -240,6 +241,34 @@ size_t hils_dense_decode_workspace_bytes(const hils_config *cfg);
 hils_status hils_dense_attn_decode(const hils_config *cfg, const void *q, const void *k_cache,
                                    const void *v_cache, const int32_t *seq_lens, void *o,
                                    void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Allocation-free decode step, for callers that cannot allocate device
+ * memory or pass a workspace: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc.  Same arguments and results as
+ * hils_sparse_attn_decode (contiguous caches), without the workspace: the
+ * step's scratch lives in a device array inside the library, of
+ * hils_noalloc_scratch_bytes() bytes per GPU (48 MiB), which each GPU the
+ * library runs on holds until the process ends.  The first call on a device
+ * looks the array up on that device (the current device); the call itself
+ * allocates nothing and calls no allocating routine.
+ *   A configuration whose decode workspace (hils_decode_workspace_bytes)
+ *   exceeds the array returns HILS_ERR_UNSUPPORTED and enqueues nothing
+ *   (128K x 8, 512K x 4 and 4M x 1 at 32/8 heads, d = 128, K = 16 fit).
+ *   Every call on one GPU shares that GPU's array: calls that may overlap
+ *   on one GPU (two streams, two threads) race and must be serialised by
+ *   the caller.  Each call clears the array's tickets and error word on its
+ *   stream first (a kernel, not a memset, so graph replays stay correct);
+ *   out-of-range seq_lens are clamped as in hils_sparse_attn_decode, and
+ *   their count is not reported.
+ */
+hils_status hils_sparse_attn_decode_noalloc(const hils_config *cfg, const void *q, const void *h,
+                                            const void *w_down, const void *w_up,
+                                            const void *k_cache, const void *v_cache,
+                                            const void *k_sum, const float *b_sum,
+                                            const int32_t *seq_lens, void *o, int32_t *topk_idx,
+                                            float *topk_score, void *stream);
+size_t hils_noalloc_scratch_bytes(void);
 
 const char *hils_status_string(hils_status status);
 const char *hils_last_error(void); /* thread-local, "" when none */

@@ -22,6 +22,7 @@ ENTRY_POINTS = (
     "hils_sparse_attn_prefill", "hils_decode_workspace_bytes", "hils_sparse_attn_decode",
     "hils_decode_error_offset", "hils_dense_decode_workspace_bytes", "hils_dense_attn_decode",
     "hils_landmark_summary_paged", "hils_sparse_attn_decode_paged",
+    "hils_sparse_attn_decode_noalloc", "hils_noalloc_scratch_bytes",
     "hils_status_string", "hils_last_error",
 )
 
@@ -89,6 +90,8 @@ def _load() -> ctypes.CDLL:
         "hils_dense_attn_decode": [C, P, P, P, P, P, P, SZ, P],
         "hils_landmark_summary_paged": [C, P, P, I32, I32, P, I32, I32, P, P, P],
         "hils_sparse_attn_decode_paged": [C, P, P, P, P, P, P, P, I32, I32, P, P, P, P, P, P, P, SZ, P],
+        "hils_sparse_attn_decode_noalloc": [C, P, P, P, P, P, P, P, P, P, P, P, P, P],
+        "hils_noalloc_scratch_bytes": [],
         "hils_status_string": [ctypes.c_int],
         "hils_last_error": [],
     }
@@ -179,6 +182,19 @@ def hils_sparse_attn_decode(cfg: Config, q, h, w_down, w_up, k_cache, v_cache, k
                                        _ptr(seq_lens), _ptr(o), _ptr(topk_idx), _ptr(topk_score),
                                        _ptr(workspace), ws_bytes, _stream(stream)),
            "hils_sparse_attn_decode")
+
+
+def hils_sparse_attn_decode_noalloc(cfg: Config, q, h, w_down, w_up, k_cache, v_cache, k_sum, b_sum, seq_lens,
+                                    o, topk_idx, topk_score, stream=None):
+    _check(lib.hils_sparse_attn_decode_noalloc(ctypes.byref(cfg), _ptr(q), _ptr(h), _ptr(w_down), _ptr(w_up),
+                                               _ptr(k_cache), _ptr(v_cache), _ptr(k_sum), _ptr(b_sum),
+                                               _ptr(seq_lens), _ptr(o), _ptr(topk_idx), _ptr(topk_score),
+                                               _stream(stream)),
+           "hils_sparse_attn_decode_noalloc")
+
+
+def hils_noalloc_scratch_bytes() -> int:
+    return int(lib.hils_noalloc_scratch_bytes())
 
 
 def hils_landmark_summary_paged(cfg: Config, k_pages, block_table, max_pages, num_pages, q_lm, chunk_begin,

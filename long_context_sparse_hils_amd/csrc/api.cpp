@@ -6,6 +6,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <mutex>
 #include <string>
 
 #include "../../include/hils.h"
@@ -416,6 +417,83 @@ hils_status hils_dense_attn_decode(const hils_config *cfg, const void *q, const 
                     counts + BH, cfg->batch, cfg->seq_len, cfg->n_q_heads, cfg->n_kv_heads, cfg->head_dim,
                     g.P, g.L, tau_of(cfg), cfg->dtype == HILS_BF16};
   return finish(hils::launch_dense_decode(a, static_cast<hipStream_t>(stream)), "dense decode launch");
+}
+
+}  // extern "C"
+
+// ------------------------------------------------------------ allocation-free decode
+// For callers that cannot allocate device memory (code under HIP graph
+// capture, tight serving loops): the decode step's scratch -- group scores,
+// per-head scores, slice maxima, partial records, arrival tickets -- lives
+// in one file-scope device array instead of a caller workspace.  Each GPU
+// the library runs on holds its own copy of the array until the process
+// ends.  Its address is looked up once per device (hipGetSymbolAddress, with
+// that device current) and only that address is handed to kernels; the
+// array's name in host code is a host-side stand-in, not a device address.
+namespace {
+
+constexpr size_t kScratchBytes = size_t(48) << 20;  // 48 MiB per device
+constexpr int kMaxDevices = 64;
+
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+hils_status scratch_for_current_device(void **out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(HILS_ERR_UNSUPPORTED, "device index %d out of range", dev);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!p) return fail(HILS_ERR_HIP, "hipGetSymbolAddress(scratch) gave a null address");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return HILS_OK;
+}
+
+// Zeroes the first n words of the scratch (the arrival tickets and the error
+// word): a kernel rather than hipMemsetAsync, so the step stays correct when
+// a caller captures it into a graph and replays it.
+__global__ void zero_words_kernel(unsigned *p, int n) {
+  for (int x = blockIdx.x * blockDim.x + threadIdx.x; x < n; x += gridDim.x * blockDim.x) p[x] = 0u;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t hils_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
+hils_status hils_sparse_attn_decode_noalloc(const hils_config *cfg, const void *q, const void *h, const void *w_down,
+                                            const void *w_up, const void *k_cache, const void *v_cache,
+                                            const void *k_sum, const float *b_sum, const int32_t *seq_lens, void *o,
+                                            int32_t *topk_idx, float *topk_score, void *stream) {
+  g_last_error.clear();
+  CHECK(check_config(cfg));
+  DecodeGeom g;
+  CHECK(decode_geom(cfg, &g));
+  if (g.total > kScratchBytes)
+    return fail(HILS_ERR_UNSUPPORTED,
+                "decode scratch of %zu bytes needed, the allocation-free call holds %zu (use "
+                "hils_sparse_attn_decode with a workspace)",
+                g.total, kScratchBytes);
+  void *ws = nullptr;
+  CHECK(scratch_for_current_device(&ws));
+  // the previous call may have had another batch or head count, so its
+  // tickets and error word need not sit where this call's do
+  const int nwords = static_cast<int>(static_cast<size_t>(cfg->batch) * cfg->n_kv_heads + 1);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  zero_words_kernel<<<1, 256, 0, st>>>(static_cast<unsigned *>(ws), nwords);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "scratch clear launch");
+  return decode_impl(cfg, q, h, w_down, w_up, k_cache, v_cache, nullptr, 0, 0, k_sum, b_sum, seq_lens, o, topk_idx,
+                     topk_score, ws, g.total, stream);
 }
 
 }  // extern "C"

@@ -154,3 +154,17 @@ def test_paged_calls_check_the_page_table():
     tail[-2] = dneed - 1
     assert L.hils_sparse_attn_decode_paged(ctypes.byref(cfg), *args, FAKE, need, 10, *tail) == \
         hils.HILS_ERR_WORKSPACE
+
+
+def test_noalloc_decode_rejects_configs_beyond_its_scratch():
+    """The allocation-free decode call checks its fixed scratch size on the
+    host: a configuration whose decode workspace exceeds it fails with
+    UNSUPPORTED before any HIP call (this runs without a GPU)."""
+    cap = hils.hils_noalloc_scratch_bytes()
+    assert cap == 48 << 20
+    cfg = _cfg(batch=64, seq_len=1 << 22, qcal_rank=0, hidden_dim=0)
+    assert hils.hils_decode_workspace_bytes(cfg) > cap
+    st = hils.lib.hils_sparse_attn_decode_noalloc(ctypes.byref(cfg), FAKE, None, None, None, FAKE, FAKE, FAKE,
+                                                  FAKE, FAKE, FAKE, FAKE, FAKE, None)
+    assert st == hils.HILS_ERR_UNSUPPORTED
+    assert "allocation-free" in hils.last_error()
