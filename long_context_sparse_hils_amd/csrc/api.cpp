@@ -237,7 +237,8 @@ size_t hils_prefill_workspace_bytes(const hils_config *cfg) {
                        align_up(hils::score_mfma_ws_bytes(cfg->batch, cfg->seq_len, cfg->n_q_heads, C, cfg->qcal_rank)) +
                        kAlign;
   const size_t attn = cfg->dtype == HILS_BF16
-                          ? align_up(hils::attn_mfma_ws_bytes(cfg->batch, cfg->n_kv_heads, cfg->seq_len, cfg->head_dim))
+                          ? align_up(hils::attn_mfma_ws_bytes(cfg->batch, cfg->n_q_heads, cfg->n_kv_heads, cfg->seq_len,
+                                              cfg->head_dim))
                           : 0;
   return score > attn ? score : attn;
 }
@@ -292,7 +293,7 @@ hils_status hils_sparse_attn_prefill(const hils_config *cfg, const void *q, cons
   if (!aligned16(workspace)) return fail(HILS_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
   hils::AttnArgs a{q, k, v, topk_idx, topk_score, o, workspace, cfg->batch, cfg->seq_len, cfg->n_q_heads,
                    cfg->n_kv_heads, cfg->head_dim, cfg->chunk_size, cfg->top_k, cfg->window, tau_of(cfg),
-                   cfg->dtype == HILS_BF16};
+                   cfg->dtype == HILS_BF16, nullptr};
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (hils::attn_mfma_supported(a)) return finish(hils::launch_attn_mfma(a, st), "sparse attention launch");
   return finish(hils::launch_attn_valu(a, st), "sparse attention launch");

@@ -38,10 +38,13 @@ struct AttnArgs {
   const int32_t *topk_idx;
   const float *topk_score;
   void *o;
-  void *vt_ws;  // prefill workspace: transposed value tiles of the MFMA path, then its query grouping
+  void *vt_ws;  // prefill workspace: transposed value tiles of the MFMA path, then the rows' chunk log-mass
   int B, T, Hq, Hkv, d, S, K, W;
   float tau;
   bool bf16;
+  // set by the MFMA path between its two passes: each row's chunk log-mass
+  // [B, Hq, T] (o then holds the rows' normalised chunk parts)
+  const float *lse_c;
 };
 
 struct DecodeArgs {
@@ -86,7 +89,13 @@ size_t score_mfma_ws_bytes(int B, int T, int Hq, int C, int r);
 hipError_t launch_score_mfma(const ScoreArgs &a, hipStream_t st);
 hipError_t launch_attn_valu(const AttnArgs &a, hipStream_t st);
 bool attn_mfma_supported(const AttnArgs &a);
-size_t attn_mfma_ws_bytes(int B, int Hkv, int T, int d);
+size_t attn_mfma_ws_bytes(int B, int Hq, int Hkv, int T, int d);
+hipError_t launch_attn_chunks(const AttnArgs &a, uint16_t *ops, float *lse, const float *vmax, int nblk,
+                              hipStream_t st);
+inline int eligible_chunks_host(int i, int W, int S) {
+  const int w0 = i - W + 1;
+  return w0 > 0 ? w0 / S : 0;
+}
 hipError_t launch_attn_mfma(const AttnArgs &a, hipStream_t st);
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t st);
 hipError_t launch_dense_decode(const DenseArgs &a, hipStream_t st);

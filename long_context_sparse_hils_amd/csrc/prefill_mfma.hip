@@ -101,23 +101,37 @@ __device__ __forceinline__ int v_swz(int d) { return (d >> 1) & 7; }
 
 // ------------------------------------------------------------------ V^T tiles
 // v [B, Hkv, T, D] -> vt [B, Hkv, nblk, D, 64]: block blk holds keys
-// 64 blk .. 64 blk + 63 transposed (keys at or past T are zero).
+// 64 blk .. 64 blk + 63 transposed (keys at or past T are zero); vmax
+// [B, Hkv, nblk] (when given): the largest |v| element of each block.
 template <int D>
 __global__ void __launch_bounds__(256)
-vt_transpose_kernel(const uint16_t *__restrict__ v, uint16_t *__restrict__ vt, int T, int nblk) {
+vt_transpose_kernel(const uint16_t *__restrict__ v, uint16_t *__restrict__ vt, float *__restrict__ vmax, int T,
+                    int nblk) {
   constexpr int LD = D + 2;  // padded row (4-byte aligned, spreads column reads over banks)
   __shared__ uint16_t tile[kItemKeys * LD];
+  __shared__ uint32_t wmax[4];
   const int blk = blockIdx.x, pair = blockIdx.y;
   const uint16_t *src = v + static_cast<size_t>(pair) * T * D;
   const int j0 = blk * kItemKeys;
+  uint32_t amax = 0u;  // |v| as bf16 bits: the order of non-negative floats
   for (int p = threadIdx.x; p < kItemKeys * D / 8; p += 256) {
     const int key = p / (D / 8), seg = p % (D / 8);
     const uint4 u = (j0 + key < T) ? *reinterpret_cast<const uint4 *>(src + static_cast<size_t>(j0 + key) * D + seg * 8)
                                    : make_uint4(0u, 0u, 0u, 0u);
     uint32_t *row = reinterpret_cast<uint32_t *>(tile + key * LD + seg * 8);
     row[0] = u.x; row[1] = u.y; row[2] = u.z; row[3] = u.w;
+    const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) amax = max(amax, max(w4[e] & 0x7FFFu, (w4[e] >> 16) & 0x7FFFu));
+  }
+  if (vmax) {
+    amax = wave_reduce_u32<1>(amax);
+    if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = amax;
   }
   __syncthreads();
+  if (vmax && threadIdx.x == 0)
+    vmax[static_cast<size_t>(pair) * nblk + blk] =
+        bf16_to_f32(static_cast<uint16_t>(max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]))));
   uint16_t *dst = vt + (static_cast<size_t>(pair) * nblk + blk) * D * kItemKeys;
   for (int p = threadIdx.x; p < D * kItemKeys / 8; p += 256) {
     const int d = p / 8, kp = p % 8;
@@ -430,10 +444,13 @@ attn_prefill_mfma_kernel(AttnArgs a, const uint8_t *__restrict__ plan, int ntile
   // attn_plan_kernel (first: the Q loads need them), the selections (query,
   // slot) of the tile, the rows' fusion scores, then the Q operands.
   int row_q[TPW];
-  {
+  if (plan) {
     const uint8_t *pt = plan + (static_cast<size_t>(pair) * ntiles + tile) * C::kQT;
 #pragma unroll
     for (int t = 0; t < TPW; ++t) row_q[t] = min(static_cast<int>(pt[wave * C::kQPW + t * C::kQPT + ln / G]), C::kQT - 1);
+  } else {  // adjacent queries share a tile
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) row_q[t] = wave * C::kQPW + t * C::kQPT + ln / G;
   }
   constexpr int kPairs = (C::kQT * C::kKMax + C::kThreads - 1) / C::kThreads;
   constexpr int kWPT = (C::kQT * G * C::kKMax + C::kThreads - 1) / C::kThreads;
@@ -753,21 +770,49 @@ attn_prefill_mfma_kernel(AttnArgs a, const uint8_t *__restrict__ plan, int ntile
     __syncthreads();
   }
 
-  // ---- epilogue: o = acc / l, lane holds d = 16 dt + 4 lg + (0..3) of row ln
+  // ---- epilogue: o = acc / l, lane holds d = 16 dt + 4 lg + (0..3) of row ln.
+  // With a chunk pass before this one (a.lse_c), o holds each row's chunk
+  // part normalised by its chunk mass e^{lse_C}: the two parts meet under
+  // the joint normaliser,
+  //   o = (acc e^{m} + o_C e^{lse_C}) / (l e^{m} + e^{lse_C}),
+  // both scaled by e^{-max(m, lse_C)} (m, l: the row's window reference and
+  // sum; the window always holds key i itself, so m is finite).
   uint16_t *ob = static_cast<uint16_t *>(a.o);
 #pragma unroll
   for (int t = 0; t < TPW; ++t) {
     if (!row_ok[t]) continue;
-    const float inv = 1.f / R.l_row[t];
-    const size_t oo = ((static_cast<size_t>(b) * Hq + row_h) * T + (q0 + row_q[t])) * D;
+    const size_t ro = (static_cast<size_t>(b) * Hq + row_h) * T + (q0 + row_q[t]);
+    const size_t oo = ro * D;
+    float fw = 1.f, fc = 0.f, inv = 1.f / R.l_row[t];
+    if (a.lse_c) {
+      const float lc = a.lse_c[ro];
+      const float mx = fmaxf(R.m_row[t], lc);
+      fw = __expf(R.m_row[t] - mx);
+      fc = lc == -INFINITY ? 0.f : __expf(lc - mx);
+      inv = 1.f / (R.l_row[t] * fw + fc);
+    }
 #pragma unroll
     for (int dt = 0; dt < C::kDT; ++dt) {
+      float c4[4] = {0.f, 0.f, 0.f, 0.f};
+      if (fc != 0.f) {
+        const uint2 pc = *reinterpret_cast<const uint2 *>(ob + oo + 16 * dt + 4 * lg);
+        c4[0] = __uint_as_float(pc.x << 16);
+        c4[1] = __uint_as_float(pc.x & 0xFFFF0000u);
+        c4[2] = __uint_as_float(pc.y << 16);
+        c4[3] = __uint_as_float(pc.y & 0xFFFF0000u);
+      }
       uint2 w;
-      w.x = pack_bf16x2(R.acc[t][dt][0] * inv, R.acc[t][dt][1] * inv);
-      w.y = pack_bf16x2(R.acc[t][dt][2] * inv, R.acc[t][dt][3] * inv);
+      w.x = pack_bf16x2((R.acc[t][dt][0] * fw + c4[0] * fc) * inv, (R.acc[t][dt][1] * fw + c4[1] * fc) * inv);
+      w.y = pack_bf16x2((R.acc[t][dt][2] * fw + c4[2] * fc) * inv, (R.acc[t][dt][3] * fw + c4[3] * fc) * inv);
       *reinterpret_cast<uint2 *>(ob + oo + 16 * dt + 4 * lg) = w;
     }
   }
+}
+
+// the chunk log-mass and block maxima of |v|, rounded up to 256 bytes
+static size_t attn_chunk_meta_bytes(int B, int Hq, int Hkv, int T) {
+  const size_t nblk = (static_cast<size_t>(T) + kItemKeys - 1) / kItemKeys;
+  return ((static_cast<size_t>(B) * Hq * T + static_cast<size_t>(B) * Hkv * nblk) * sizeof(float) + 255) / 256 * 256;
 }
 
 // value tiles (bf16), rounded up to 256 bytes
@@ -777,22 +822,37 @@ static size_t attn_vt_bytes(int B, int Hkv, int T, int d) {
 }
 
 template <int D, int G>
-static hipError_t attn_mfma_t(const AttnArgs &a, hipStream_t st) {
+static hipError_t attn_mfma_t(const AttnArgs &a_in, hipStream_t st) {
   constexpr int WAVES = 4, TPW = 2;
   using C = AttnCfg<D, G, WAVES, TPW>;
-  const int ntiles = (a.T + C::kQT - 1) / C::kQT;
-  const int npairs = a.Hkv * a.B;
-  const int nblk = (a.T + kItemKeys - 1) / kItemKeys;
-  vt_transpose_kernel<D><<<dim3(nblk, npairs), 256, 0, st>>>(static_cast<const uint16_t *>(a.v),
-                                                             static_cast<uint16_t *>(a.vt_ws), a.T, nblk);
+  const int ntiles = (a_in.T + C::kQT - 1) / C::kQT;
+  const int npairs = a_in.Hkv * a_in.B;
+  const int nblk = (a_in.T + kItemKeys - 1) / kItemKeys;
+  // The chunk terms first (chunk-major, rows compacted per chunk): each
+  // row's chunk part into o, its chunk log-mass into the workspace after the
+  // value tiles.  Then the window band through the kernel below, which
+  // combines the two.  No query has an eligible chunk when T - W < S.
+  const bool chunks = a_in.K > 0 && eligible_chunks_host(a_in.T - 1, a_in.W, kItemKeys) > 0;
+  uint8_t *ws_after_vt = static_cast<uint8_t *>(a_in.vt_ws) + attn_vt_bytes(a_in.B, a_in.Hkv, a_in.T, D);
+  float *lse = reinterpret_cast<float *>(ws_after_vt);
+  float *vmax = lse + static_cast<size_t>(a_in.B) * a_in.Hq * a_in.T;
+  uint16_t *ops = reinterpret_cast<uint16_t *>(ws_after_vt + attn_chunk_meta_bytes(a_in.B, a_in.Hq, a_in.Hkv, a_in.T));
+  vt_transpose_kernel<D><<<dim3(nblk, npairs), 256, 0, st>>>(static_cast<const uint16_t *>(a_in.v),
+                                                             static_cast<uint16_t *>(a_in.vt_ws),
+                                                             chunks ? vmax : nullptr, a_in.T, nblk);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // the query grouping, after the value tiles in the workspace
-  uint8_t *plan = static_cast<uint8_t *>(a.vt_ws) + attn_vt_bytes(a.B, a.Hkv, a.T, D);
-  attn_plan_kernel<C::kQT, C::kQPT><<<dim3((ntiles * npairs + 3) / 4), 256, 0, st>>>(a.topk_idx, plan, a.T, a.K,
-                                                                                     ntiles, ntiles * npairs);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  AttnArgs a = a_in;
+  a.lse_c = nullptr;
+  if (chunks) {
+    e = launch_attn_chunks(a_in, ops, lse, vmax, nblk, st);
+    if (e != hipSuccess) return e;
+    a.lse_c = lse;
+  }
+  a.K = 0;
+  a.topk_idx = nullptr;
+  a.topk_score = nullptr;
+  const uint8_t *plan = nullptr;
   // a (b, g) pair's K and V^T fit one XCD's 4 MB L2: keep each pair on one
   // XCD; longer sequences: every XCD works on the same pair at a time, so
   // that the chunks its queries gather stay in the shared memory-side cache
@@ -813,10 +873,12 @@ bool attn_mfma_supported(const AttnArgs &a) {
          a.S == kItemKeys && a.K <= 32 && a.T / a.S <= 8192;
 }
 
-// value tiles, then the grouping: one byte per (pair, query slot), at most
-// 128 slots of padding per pair
-size_t attn_mfma_ws_bytes(int B, int Hkv, int T, int d) {
-  return attn_vt_bytes(B, Hkv, T, d) + static_cast<size_t>(B) * Hkv * (static_cast<size_t>(T) + 128);
+// value tiles, then the chunk log-mass of every (b, query head, query) and
+// the largest |v| of every 64-key block, then every complete chunk's K and
+// V^T in operand order
+size_t attn_mfma_ws_bytes(int B, int Hq, int Hkv, int T, int d) {
+  const size_t chunks = static_cast<size_t>(B) * Hkv * (T / kItemKeys);
+  return attn_vt_bytes(B, Hkv, T, d) + attn_chunk_meta_bytes(B, Hq, Hkv, T) + chunks * kItemKeys * d * 2 * 2;
 }
 
 hipError_t launch_attn_mfma(const AttnArgs &a, hipStream_t st) {

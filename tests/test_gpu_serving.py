@@ -6,8 +6,9 @@
   every step matches the float64 oracle run on the summaries the GPU built;
 - the decode step and the three prefill calls captured once into a HIP graph
   (torch.cuda.CUDAGraph) and replayed on new inputs: every replay equals an
-  eager call on the same inputs, bit for bit (the kernels are deterministic
-  and the decode workspace's counters return to zero by themselves).
+  eager call on the same inputs, bit for bit (the decode workspace's
+  counters return to zero by themselves), except the prefill output, whose
+  chunk sums are added in a timing-dependent order: within one bf16 ulp.
 """
 import os
 import sys
@@ -25,7 +26,8 @@ sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
 import hils_synth as hs  # noqa: E402
 import long_context_sparse_hils_amd as hils  # noqa: E402
 import oracle  # noqa: E402
-from _gpu import check_out, check_scores, check_topk, dev, gpu_decode, gpu_prefill, host  # noqa: E402
+from _gpu import (bf16_ulps, check_out, check_scores, check_topk, dev, gpu_decode, gpu_prefill,  # noqa: E402
+                  host)
 
 
 def _wl_decode(B, T, Hq, Hkv, d, K, W):
@@ -88,10 +90,13 @@ def test_decode_incremental_generation():
     print(f"incremental: {steps} steps, {completed} chunk completions, near-tie rows {ties}")
 
 
-def _replay_checks(g, fill, eager, outs, n):
+def _replay_checks(g, fill, eager, outs, n, ulp_ok=()):
     """Replay graph g n times; before each replay fill(r) writes new inputs
     into the captured buffers, and eager(r) recomputes the same step outside
-    the graph.  Between replays the program does eager work of its own."""
+    the graph.  Between replays the program does eager work of its own.
+    Outputs are bit-equal, except those listed in ulp_ok (bf16 outputs whose
+    fp32 sums are accumulated in a timing-dependent order), which may differ
+    by one bf16 ulp."""
     for r in range(n):
         fill(r)
         g.replay()
@@ -99,8 +104,11 @@ def _replay_checks(g, fill, eager, outs, n):
         got = [t.clone() for t in outs]
         ref = eager(r)
         torch.cuda.synchronize()
-        for a, b in zip(got, ref):
-            assert torch.equal(a, b), r
+        for j, (a, b) in enumerate(zip(got, ref)):
+            if j in ulp_ok:
+                assert bf16_ulps(host(a), host(b)).max() <= 1, r
+            else:
+                assert torch.equal(a, b), r
         _ = (torch.randn(1 << 16, device="cuda") * 2).sum().item()  # unrelated eager work
 
 
@@ -197,7 +205,7 @@ def test_prefill_graph_replay():
         res = gpu_prefill(cfgd, dd)
         return [res["k_sum"], res["b_sum"], res["idx"], res["tsc"], res["o"]]
 
-    _replay_checks(g, fill, eager, [k_sum, b_sum, idx, tsc, o], len(qs))
+    _replay_checks(g, fill, eager, [k_sum, b_sum, idx, tsc, o], len(qs), ulp_ok=(4,))
 
 
 def _paged(cache: np.ndarray, pages_of: np.ndarray, num_pages: int, S: int, seed: int) -> np.ndarray:
