@@ -1,4 +1,4 @@
-"""HiLS-Attention forward pass -- float64 CPU oracle (Python front end).
+"""HiLS-Attention forward pass and its backward -- float64 CPU oracle (Python front end).
 
 TEST INFRASTRUCTURE ONLY: imported by ``tests/``, by ``__graft_entry__.smoke()``
 and by the CPU-baseline leg of ``bench.py``, never by the library itself.  The
@@ -101,11 +101,13 @@ def _load():
         lib.orc_select.argtypes = [C, _P, _P, _I, _P, _P, _P]
         lib.orc_fuse.argtypes = [C, _P, _I, _P, _P, _I, _P, _I, _P, _P, _I, _P, _P, _I]
         lib.orc_causal_attention.argtypes = [C, _P, _I, _P, _P, _I, _P, _I, _P, _I]
+        lib.orc_backward.argtypes = [C, _P, _I, _P, _P, _I, _P, _I, _P, _I, _P, _P, _I, _P, _P, _I, _P, _I,
+                                     _P, _I, _P, _P, _P, _P, _P, _P, _P, _I]
         lib.orc_round_bf16.argtypes = [_P, _P, ctypes.c_long]
         lib.orc_round_bf16.restype = None
         lib.orc_eligible_chunks.argtypes = [_I, _I, _I]
         for f in ("orc_summary", "orc_qcal", "orc_scores", "orc_select", "orc_fuse",
-                  "orc_causal_attention", "orc_eligible_chunks"):
+                  "orc_causal_attention", "orc_eligible_chunks", "orc_backward"):
             getattr(lib, f).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -298,6 +300,58 @@ def dense_decode(cfg: OracleConfig, inp: dict, seq_lens=None) -> np.ndarray:
     return o[:, :, 0]
 
 
+def prefill_fixed(cfg: OracleConfig, inp: dict, idx) -> np.ndarray:
+    """The prefill forward with a GIVEN selection idx [B,Hkv,T,K] (the
+    function whose gradient the backward returns): Eq. 8 summaries of every
+    chunk (kept in float64), Q-Cal, the scores s-hat of the listed chunks,
+    and Eq. 10 fusion with the window.  Returns o [B,Hq,T,d]."""
+    B, T, G, K = cfg.batch, cfg.seq_len, cfg.group, idx.shape[-1]
+    qpos = np.arange(T, dtype=np.int32)
+    ks, bs = summary(cfg, inp["k"], inp["q_lm"])
+    if cfg.qcal_rank > 0:
+        qhat = qcal(cfg, inp["q"], inp["h"], inp["w_down"], inp["w_up"])
+    else:
+        qhat = qcal(cfg, inp["q"])
+    qp = np.broadcast_to(qpos, (B, T))
+    s = scores(cfg, qhat, qp, ks, bs)                                   # [B,Hq,T,C]
+    idx = np.asarray(idx, dtype=np.int32)
+    ih = np.repeat(idx, G, axis=1)                                      # [B,Hq,T,K]
+    tsc = np.where(ih >= 0, np.take_along_axis(s, np.maximum(ih, 0), axis=-1), -np.inf)
+    o, _ = fuse(cfg, inp["q"], inp["k"], inp["v"], qp, idx, tsc)
+    return o
+
+
+def backward(cfg: OracleConfig, inp: dict, idx, k_sum, b_sum, dout) -> dict:
+    """Gradients of L = sum(dout * O) for the prefill forward with the fixed
+    selection idx, given the stored summaries k_sum/b_sum that the forward
+    scored: dq, dk, dv, dq_lm and (Q-Cal) dh, dw_down, dw_up, float64."""
+    B, T, Hq, Hkv, d = cfg.batch, cfg.seq_len, cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
+    C = cfg.n_chunks
+    q, k, v, q_lm = _c(inp["q"]), _c(inp["k"]), _c(inp["v"]), _c(inp["q_lm"])
+    assert k.dtype == v.dtype
+    idx = _c(np.asarray(idx, dtype=np.int32))
+    k_sum, b_sum, dout = _c(k_sum), _c(b_sum), _c(dout)
+    out = dict(dq=np.empty((B, Hq, T, d)), dk=np.empty((B, Hkv, T, d)), dv=np.empty((B, Hkv, T, d)),
+               dq_lm=np.empty((B, Hq, C, d)))
+    if cfg.qcal_rank > 0:
+        h, wd, wu = _c(inp["h"]), _c(inp["w_down"]), _c(inp["w_up"])
+        assert wd.dtype == wu.dtype
+        out.update(dh=np.empty(h.shape), dw_down=np.empty(wd.shape), dw_up=np.empty(wu.shape))
+        cc = cfg.c(K=idx.shape[-1])
+        hp, wdp, wup, hdt, wdt = _ptr(h), _ptr(wd), _ptr(wu), _dt(h), _dt(wd)
+        dhp, dwdp, dwup = _ptr(out["dh"]), _ptr(out["dw_down"]), _ptr(out["dw_up"])
+    else:
+        cc = cfg.c(K=idx.shape[-1], r=0, Dh=0)
+        hp = wdp = wup = dhp = dwdp = dwup = None
+        hdt = wdt = 2
+    _load().orc_backward(ctypes.byref(cc), _ptr(q), _dt(q), _ptr(k), _ptr(v), _dt(k), _ptr(q_lm), _dt(q_lm),
+                         hp, hdt, wdp, wup, wdt, _ptr(idx), _ptr(k_sum), _dt(k_sum), _ptr(b_sum), _dt(b_sum),
+                         _ptr(dout), _dt(dout), _ptr(out["dq"]), _ptr(out["dk"]), _ptr(out["dv"]),
+                         _ptr(out["dq_lm"]), dhp, dwdp, dwup, threads())
+    return out
+
+
 __all__ = ["OracleConfig", "build", "eligible_chunks", "round_bf16", "store", "summary", "qcal",
-           "scores", "select", "fuse", "causal_attention", "prefill", "decode", "dense_decode"]
+           "scores", "select", "fuse", "causal_attention", "prefill", "decode", "dense_decode",
+           "prefill_fixed", "backward"]
 

@@ -1,5 +1,5 @@
 /*
- * HiLS-Attention forward pass -- float64 CPU oracle.
+ * HiLS-Attention forward pass and its backward -- float64 CPU oracle.
  *
  * TEST INFRASTRUCTURE ONLY.  Only the test-suite, the smoke check and the
  * benchmark's CPU-baseline leg may load this library.  It shares no code with
@@ -455,4 +455,318 @@ static uint16_t round_to_bf16(double x) {
 
 void orc_round_bf16(const double *x, uint16_t *out, long n) {
   for (long i = 0; i < n; ++i) out[i] = round_to_bf16(x[i]);
+}
+
+/* ======================================================================== */
+/* Backward pass of the forward above, for a FIXED selection.
+ *
+ * The pages train chunk selection through the forward weights: the score
+ * s-hat of each selected chunk sits inside the joint softmax of Eq. 10
+ * ([p1] Methodology 2), so the loss reaches s-hat, hence k'_c and b'_c,
+ * hence (Eq. 8, [p1] Methodology 1) the landmark query q'_c and the chunk's
+ * keys, and (Q-Cal, [p1] Methodology 3) the calibration weights.  The top-K
+ * choice itself is a discrete step and carries no gradient.  Given dO =
+ * dL/dO for every output row, this returns the exact gradients of
+ * L = sum(dO * O) with respect to q, k, v, the landmark queries and, with
+ * Q-Cal, h, W_down and W_up.
+ *
+ * Per row (b, h, i), with the entries of the row's selection list (c >= 0)
+ * and the window tokens j, and logZ = log( sum_c e^{s_c} + sum_j e^{l_j} ):
+ *   w_c = e^{s_c - logZ},  u_j = e^{l_j - logZ},  o = sum_c w_c o_c + sum_j u_j v_j
+ *   Delta = dO . o
+ *   ds_c           = w_c (dO . o_c - Delta)                  (joint softmax)
+ *   dl_j (chunk c) = w_c P_cj (dO . v_j - dO . o_c)          (chunk softmax)
+ *   dl_j (window)  = u_j (dO . v_j - Delta)
+ *   dv_j += w_c P_cj dO  or  u_j dO
+ *   dq += tau sum_j dl_j k_j,    dk_j += tau dl_j q          (l_j = tau q.k_j)
+ *   dq-hat += tau ds_c k'_c,  dk'_c += tau ds_c q-hat,  db'_c += ds_c
+ * Summary (Eq. 8) per (b, h, c), l_j = tau q'_c.k_j, p = softmax(l),
+ * k' = sum_j p_j k_j, b' = -sum_j p_j log p_j = LSE(l) - E_p[l]:
+ *   dl_j = p_j ( dk'.(k_j - k') - db' (l_j - E_p[l]) )
+ *   dq'_c += tau sum_j dl_j k_j,   dk_j += p_j dk' + tau dl_j q'_c
+ * The stored k' (rounded to the storage type in the forward) enters s-hat
+ * as given; the rounding is taken as the identity in the chain.
+ * Q-Cal: q-hat_h = q_h + (W_up u)[h d : h d + d], u = W_down h_i:
+ *   dq_h += dq-hat_h,   du = sum_h W_up[h d + e, :]^T dq-hat_h[e],
+ *   dW_up[h d + e, a] += dq-hat_h[e] u_a,  dW_down += du h_i^T,  dh_i = W_down^T du.
+ *
+ * Inputs as in the forward: q [B,Hq,T,d], k, v [B,Hkv,T,d], q_lm
+ * [B,Hq,C,d], h [B,T,Dh], w_down [r,Dh], w_up [Hq*d, r], idx [B,Hkv,T,K],
+ * k_sum [B,Hq,C,d] (stored), b_sum [B,Hq,C], dO [B,Hq,T,d].  Outputs are
+ * float64, overwritten: dq, dk, dv, dq_lm and (r > 0) dh, dw_down, dw_up. */
+typedef struct {
+  const orc_cfg *c;
+  const void *q; int qdt; const void *k; const void *v; int kvdt; const void *qlm; int lmdt;
+  const int *idx; const void *ksum; int ksdt; const void *bsum; int bsdt; const void *dout; int dodt;
+  const double *qhat; /* [B,Hq,T,d] */
+  double *dq, *dk, *dv, *dqlm, *dqhat, *dks, *dbs;
+} bwd_ctx;
+
+/* one (b, g) pair: every row of its heads, then its chunk summaries */
+static void bwd_pair_unit(void *vctx, long unit) {
+  bwd_ctx *x = (bwd_ctx *)vctx;
+  const orc_cfg *c = x->c;
+  int d = c->d, S = c->S, K = c->K, T = c->T, C = c->T / c->S, G = c->Hq / c->Hkv;
+  int b = (int)(unit / c->Hkv), g = (int)(unit % c->Hkv);
+  double tau = tau_of(c);
+  size_t kvbase = ((size_t)b * c->Hkv + g) * T;
+  int kk = K > 0 ? K : 1;
+  double *lam = (double *)malloc(sizeof(double) * ((size_t)kk * S + T));
+  double *P = (double *)malloc(sizeof(double) * (size_t)kk * S);
+  double *ob = (double *)malloc(sizeof(double) * (size_t)kk * d);
+  double *s_hat = (double *)malloc(sizeof(double) * kk);
+  int *chunk = (int *)malloc(sizeof(int) * kk);
+  double *o = (double *)malloc(sizeof(double) * d);
+  double *dO = (double *)malloc(sizeof(double) * d);
+  double *qv = (double *)malloc(sizeof(double) * d);
+  for (int hh = 0; hh < G; ++hh) {
+    int h = g * G + hh;
+    for (int i = 0; i < T; ++i) {
+      size_t qoff = (((size_t)b * c->Hq + h) * T + i) * d;
+      int n = orc_eligible_chunks(i, c->W, S);
+      int w_lo = n * S, nw = i - w_lo + 1;
+      for (int e = 0; e < d; ++e) { qv[e] = ld(x->q, x->qdt, qoff + e); dO[e] = ld(x->dout, x->dodt, qoff + e); }
+      const double *qh = x->qhat + qoff;
+      /* the selected chunks: s-hat from the stored summaries, token logits,
+       * chunk softmax P_c and chunk output o_c */
+      int nsel = 0;
+      for (int k = 0; k < K; ++k) {
+        int ch = x->idx[(kvbase + i) * K + k];
+        if (ch < 0) continue;
+        size_t so = ((size_t)b * c->Hq + h) * C + ch;
+        double acc = 0;
+        for (int e = 0; e < d; ++e) acc += qh[e] * ld(x->ksum, x->ksdt, so * d + e);
+        s_hat[nsel] = tau * acc + ld(x->bsum, x->bsdt, so);
+        double *l = lam + (size_t)nsel * S, *p = P + (size_t)nsel * S;
+        for (int j = 0; j < S; ++j) {
+          size_t koff = (kvbase + (size_t)ch * S + j) * d;
+          double a2 = 0;
+          for (int e = 0; e < d; ++e) a2 += qv[e] * ld(x->k, x->kvdt, koff + e);
+          l[j] = tau * a2;
+        }
+        double m = l[0];
+        for (int j = 1; j < S; ++j) if (l[j] > m) m = l[j];
+        double z = 0;
+        for (int j = 0; j < S; ++j) z += exp(l[j] - m);
+        for (int j = 0; j < S; ++j) p[j] = exp(l[j] - m) / z;
+        double *oc = ob + (size_t)nsel * d;
+        for (int e = 0; e < d; ++e) {
+          double a3 = 0;
+          for (int j = 0; j < S; ++j) a3 += p[j] * ld(x->v, x->kvdt, (kvbase + (size_t)ch * S + j) * d + e);
+          oc[e] = a3;
+        }
+        chunk[nsel++] = ch;
+      }
+      /* window logits and the joint log-normaliser */
+      double *lw = lam + (size_t)nsel * S;
+      for (int j = 0; j < nw; ++j) {
+        size_t koff = (kvbase + (size_t)(w_lo + j)) * d;
+        double a2 = 0;
+        for (int e = 0; e < d; ++e) a2 += qv[e] * ld(x->k, x->kvdt, koff + e);
+        lw[j] = tau * a2;
+      }
+      double M = -INFINITY;
+      for (int a = 0; a < nsel; ++a) if (s_hat[a] > M) M = s_hat[a];
+      for (int j = 0; j < nw; ++j) if (lw[j] > M) M = lw[j];
+      double z = 0;
+      for (int a = 0; a < nsel; ++a) z += exp(s_hat[a] - M);
+      for (int j = 0; j < nw; ++j) z += exp(lw[j] - M);
+      double logZ = M + log(z);
+      /* the output row and Delta = dO . o */
+      for (int e = 0; e < d; ++e) o[e] = 0;
+      for (int a = 0; a < nsel; ++a) {
+        double w = exp(s_hat[a] - logZ);
+        for (int e = 0; e < d; ++e) o[e] += w * ob[(size_t)a * d + e];
+      }
+      for (int j = 0; j < nw; ++j) {
+        double u = exp(lw[j] - logZ);
+        for (int e = 0; e < d; ++e) o[e] += u * ld(x->v, x->kvdt, (kvbase + (size_t)(w_lo + j)) * d + e);
+      }
+      double Delta = 0;
+      for (int e = 0; e < d; ++e) Delta += dO[e] * o[e];
+      double *dq = x->dq + qoff, *dqh = x->dqhat + qoff;
+      /* chunk terms */
+      for (int a = 0; a < nsel; ++a) {
+        int ch = chunk[a];
+        double w = exp(s_hat[a] - logZ);
+        const double *oc = ob + (size_t)a * d, *p = P + (size_t)a * S;
+        double dOo = 0;
+        for (int e = 0; e < d; ++e) dOo += dO[e] * oc[e];
+        double ds = w * (dOo - Delta);
+        size_t so = ((size_t)b * c->Hq + h) * C + ch;
+        for (int e = 0; e < d; ++e) {
+          dqh[e] += tau * ds * ld(x->ksum, x->ksdt, so * d + e);
+          x->dks[so * d + e] += tau * ds * qh[e];
+        }
+        x->dbs[so] += ds;
+        for (int j = 0; j < S; ++j) {
+          size_t koff = (kvbase + (size_t)ch * S + j) * d;
+          double dOv = 0;
+          for (int e = 0; e < d; ++e) dOv += dO[e] * ld(x->v, x->kvdt, koff + e);
+          double dl = w * p[j] * (dOv - dOo);
+          for (int e = 0; e < d; ++e) {
+            dq[e] += tau * dl * ld(x->k, x->kvdt, koff + e);
+            x->dk[koff + e] += tau * dl * qv[e];
+            x->dv[koff + e] += w * p[j] * dO[e];
+          }
+        }
+      }
+      /* window terms */
+      for (int j = 0; j < nw; ++j) {
+        size_t koff = (kvbase + (size_t)(w_lo + j)) * d;
+        double u = exp(lw[j] - logZ);
+        double dOv = 0;
+        for (int e = 0; e < d; ++e) dOv += dO[e] * ld(x->v, x->kvdt, koff + e);
+        double dl = u * (dOv - Delta);
+        for (int e = 0; e < d; ++e) {
+          dq[e] += tau * dl * ld(x->k, x->kvdt, koff + e);
+          x->dk[koff + e] += tau * dl * qv[e];
+          x->dv[koff + e] += u * dO[e];
+        }
+      }
+      /* q-hat = q + calibration: dq also receives dq-hat */
+      for (int e = 0; e < d; ++e) dq[e] += dqh[e];
+    }
+    /* the chunk summaries of head h (Eq. 8) */
+    double *l = lam, *p = P;
+    double *kp = ob; /* unrounded k' of the chunk */
+    for (int ch = 0; ch < C; ++ch) {
+      size_t so = ((size_t)b * c->Hq + h) * C + ch;
+      size_t lmo = so * d;
+      for (int j = 0; j < S; ++j) {
+        size_t koff = (kvbase + (size_t)ch * S + j) * d;
+        double acc = 0;
+        for (int e = 0; e < d; ++e) acc += ld(x->qlm, x->lmdt, lmo + e) * ld(x->k, x->kvdt, koff + e);
+        l[j] = tau * acc;
+      }
+      double m = l[0];
+      for (int j = 1; j < S; ++j) if (l[j] > m) m = l[j];
+      double z = 0;
+      for (int j = 0; j < S; ++j) z += exp(l[j] - m);
+      double El = 0;
+      for (int j = 0; j < S; ++j) { p[j] = exp(l[j] - m) / z; El += p[j] * l[j]; }
+      for (int e = 0; e < d; ++e) {
+        double acc = 0;
+        for (int j = 0; j < S; ++j) acc += p[j] * ld(x->k, x->kvdt, (kvbase + (size_t)ch * S + j) * d + e);
+        kp[e] = acc;
+      }
+      const double *dkp = x->dks + so * d;
+      double dbp = x->dbs[so];
+      for (int j = 0; j < S; ++j) {
+        size_t koff = (kvbase + (size_t)ch * S + j) * d;
+        double proj = 0;
+        for (int e = 0; e < d; ++e) proj += dkp[e] * (ld(x->k, x->kvdt, koff + e) - kp[e]);
+        double dl = p[j] * (proj - dbp * (l[j] - El));
+        for (int e = 0; e < d; ++e) {
+          x->dqlm[lmo + e] += tau * dl * ld(x->k, x->kvdt, koff + e);
+          x->dk[koff + e] += p[j] * dkp[e] + tau * dl * ld(x->qlm, x->lmdt, lmo + e);
+        }
+      }
+    }
+  }
+  free(lam); free(P); free(ob); free(s_hat); free(chunk); free(o); free(dO); free(qv);
+}
+
+/* Q-Cal weight gradients: one unit per output row of dW_up (Hq*d rows),
+ * then per row of dW_down (r rows), then per token of dh (B*T rows). */
+typedef struct {
+  const orc_cfg *c; const void *h; int hdt; const void *wd; const void *wu; int wdt;
+  const double *u, *du, *dqhat; double *dh, *dwd, *dwu;
+} qcal_bwd_ctx;
+
+static void dwu_unit(void *vctx, long row) { /* row = h*d + e */
+  qcal_bwd_ctx *x = (qcal_bwd_ctx *)vctx;
+  const orc_cfg *c = x->c;
+  int d = c->d, hh = (int)(row / d), e = (int)(row % d);
+  for (int a = 0; a < c->r; ++a) {
+    double acc = 0;
+    for (int b = 0; b < c->B; ++b)
+      for (int i = 0; i < c->T; ++i)
+        acc += x->dqhat[(((size_t)b * c->Hq + hh) * c->T + i) * d + e] * x->u[((size_t)b * c->T + i) * c->r + a];
+    x->dwu[(size_t)row * c->r + a] = acc;
+  }
+}
+static void dwd_unit(void *vctx, long a) {
+  qcal_bwd_ctx *x = (qcal_bwd_ctx *)vctx;
+  const orc_cfg *c = x->c;
+  for (int f = 0; f < c->Dh; ++f) {
+    double acc = 0;
+    for (int b = 0; b < c->B; ++b)
+      for (int i = 0; i < c->T; ++i)
+        acc += x->du[((size_t)b * c->T + i) * c->r + a] * ld(x->h, x->hdt, ((size_t)b * c->T + i) * c->Dh + f);
+    x->dwd[(size_t)a * c->Dh + f] = acc;
+  }
+}
+static void dh_unit(void *vctx, long tok) {
+  qcal_bwd_ctx *x = (qcal_bwd_ctx *)vctx;
+  const orc_cfg *c = x->c;
+  for (int f = 0; f < c->Dh; ++f) {
+    double acc = 0;
+    for (int a = 0; a < c->r; ++a) acc += x->du[(size_t)tok * c->r + a] * ld(x->wd, x->wdt, (size_t)a * c->Dh + f);
+    x->dh[(size_t)tok * c->Dh + f] = acc;
+  }
+}
+
+int orc_backward(const orc_cfg *c, const void *q, int qdt, const void *k, const void *v, int kvdt,
+                 const void *q_lm, int lmdt, const void *h, int hdt, const void *w_down, const void *w_up,
+                 int wdt, const int *idx, const void *k_sum, int ksdt, const void *b_sum, int bsdt,
+                 const void *dout, int dodt, double *dq, double *dk, double *dv, double *dq_lm, double *dh,
+                 double *dw_down, double *dw_up, int nthreads) {
+  int d = c->d, C = c->T / c->S;
+  size_t nq = (size_t)c->B * c->Hq * c->T * d, nkv = (size_t)c->B * c->Hkv * c->T * d;
+  size_t nlm = (size_t)c->B * c->Hq * C * d, ns = (size_t)c->B * c->Hq * C;
+  double *qhat = (double *)malloc(sizeof(double) * (nq ? nq : 1));
+  double *dqhat = (double *)calloc(nq ? nq : 1, sizeof(double));
+  double *dks = (double *)calloc(nlm ? nlm : 1, sizeof(double));
+  double *dbs = (double *)calloc(ns ? ns : 1, sizeof(double));
+  double *u = 0;
+  /* q-hat = q + slice_h(W_up (W_down h_i)) */
+  if (c->r > 0) {
+    u = (double *)malloc(sizeof(double) * (size_t)c->B * c->T * c->r);
+    for (size_t tok = 0; tok < (size_t)c->B * c->T; ++tok)
+      for (int a = 0; a < c->r; ++a) {
+        double acc = 0;
+        for (int f = 0; f < c->Dh; ++f) acc += ld(w_down, wdt, (size_t)a * c->Dh + f) * ld(h, hdt, tok * c->Dh + f);
+        u[tok * c->r + a] = acc;
+      }
+  }
+  for (int b = 0; b < c->B; ++b)
+    for (int hh = 0; hh < c->Hq; ++hh)
+      for (int i = 0; i < c->T; ++i) {
+        size_t off = (((size_t)b * c->Hq + hh) * c->T + i) * d;
+        for (int e = 0; e < d; ++e) {
+          double acc = 0;
+          if (c->r > 0)
+            for (int a = 0; a < c->r; ++a)
+              acc += ld(w_up, wdt, ((size_t)hh * d + e) * c->r + a) * u[((size_t)b * c->T + i) * c->r + a];
+          qhat[off + e] = ld(q, qdt, off + e) + acc;
+        }
+      }
+  memset(dq, 0, sizeof(double) * nq);
+  memset(dk, 0, sizeof(double) * nkv);
+  memset(dv, 0, sizeof(double) * nkv);
+  memset(dq_lm, 0, sizeof(double) * nlm);
+  bwd_ctx x = {c, q, qdt, k, v, kvdt, q_lm, lmdt, idx, k_sum, ksdt, b_sum, bsdt, dout, dodt,
+               qhat, dq, dk, dv, dq_lm, dqhat, dks, dbs};
+  parallel_for((long)c->B * c->Hkv, nthreads, bwd_pair_unit, &x);
+  if (c->r > 0) {
+    double *du = (double *)malloc(sizeof(double) * (size_t)c->B * c->T * c->r);
+    for (int b = 0; b < c->B; ++b)
+      for (int i = 0; i < c->T; ++i)
+        for (int a = 0; a < c->r; ++a) {
+          double acc = 0;
+          for (int hh = 0; hh < c->Hq; ++hh)
+            for (int e = 0; e < d; ++e)
+              acc += ld(w_up, wdt, ((size_t)hh * d + e) * c->r + a) * dqhat[(((size_t)b * c->Hq + hh) * c->T + i) * d + e];
+          du[((size_t)b * c->T + i) * c->r + a] = acc;
+        }
+    qcal_bwd_ctx y = {c, h, hdt, w_down, w_up, wdt, u, du, dqhat, dh, dw_down, dw_up};
+    parallel_for((long)c->Hq * d, nthreads, dwu_unit, &y);
+    parallel_for((long)c->r, nthreads, dwd_unit, &y);
+    parallel_for((long)c->B * c->T, nthreads, dh_unit, &y);
+    free(du);
+    free(u);
+  }
+  free(qhat); free(dqhat); free(dks); free(dbs);
+  return 0;
 }
