@@ -39,6 +39,7 @@ sys.path.insert(0, ROOT)
 METRIC = "HiLS fwd query-tokens/s + % HBM peak (decode 512K) / % MFMA peak (prefill 8K)"
 PEAK_MFMA_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
+PEAK_F32_VALU_TFLOPS = 157.3
 
 
 def log(*a):
@@ -60,7 +61,8 @@ def parse():
     p.add_argument("--no-decode-more", action="store_true", help="skip the 128K and 4M decode legs")
     p.add_argument("--decode-shapes", default="decode_128k:8,decode_4m:1",
                    help="the further decode legs, workload:batch, comma separated")
-    p.add_argument("--only", choices=["prefill", "decode", "long"], default=None,
+    p.add_argument("--no-backward", action="store_true", help="skip the 8K backward leg")
+    p.add_argument("--only", choices=["prefill", "decode", "long", "backward"], default=None,
                    help="profile one path (for rocprofv3 runs)")
     p.add_argument("--decode-batches", default="1,4")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle sample time")
@@ -202,6 +204,71 @@ def bench_prefill(args, torch, hils, hs, flush):
                                     attention=float(stage_ms[2])),
                wall_s_incl_flush=wall, flops=fl, wl=wl, inp=inp, gpu_out=gpu_out)
     return res
+
+
+def bench_backward(args, torch, hils, hs, flush):
+    """Backward pass at the 8K prefill workload: the forward runs once
+    (untimed) to fix the selection and the stored summaries, then each timed
+    step is one hils_sparse_attn_backward call (all seven gradients, Q-Cal
+    included).  Algorithmic work: five d-long products per (query, key) pair
+    the forward attends (q.k recomputed, dO.v, and the dq, dk, dv updates),
+    2 flops each, i.e. 2.5x the forward attention's count; the summary and
+    Q-Cal terms are small beside it and are not counted."""
+    wl = hs.WORKLOADS["prefill_8k"]
+    inp = hs.prefill_inputs(wl, args.seed)
+
+    def dev(a):
+        return torch.from_numpy(a.view(np.int16)).to("cuda").view(torch.bfloat16) if a.dtype == np.uint16 \
+            else torch.from_numpy(a).to("cuda")
+    d = {k: dev(v) for k, v in inp.items() if isinstance(v, np.ndarray)}
+    del inp
+    c = hils.Config.from_dict(wl.config_dict())
+    B, T, Hq, Hkv, D, C, K = wl.batch, wl.seq_len, wl.n_q_heads, wl.n_kv_heads, wl.head_dim, wl.n_chunks, wl.top_k
+    r, Dh = wl.qcal_rank, wl.hidden_dim
+    bf, f32 = torch.bfloat16, torch.float32
+    k_sum = torch.empty((B, Hq, C, D), dtype=bf, device="cuda")
+    b_sum = torch.empty((B, Hq, C), dtype=f32, device="cuda")
+    ws = torch.empty((hils.hils_prefill_workspace_bytes(c),), dtype=torch.uint8, device="cuda")
+    idx = torch.empty((B, Hkv, T, K), dtype=torch.int32, device="cuda")
+    tsc = torch.empty((B, Hq, T, K), dtype=f32, device="cuda")
+    stream = torch.cuda.current_stream()
+    hils.hils_landmark_summary(c, d["k"], d["q_lm"], 0, C, k_sum, b_sum, stream)
+    hils.hils_chunk_score_topk(c, d["q"], d["h"], d["w_down"], d["w_up"], k_sum, b_sum, idx, tsc, ws, stream)
+    del ws
+    dout = dev(hs.normal((B, Hq, T, D), args.seed, 40, 1.0, dtype="bf16"))
+    g = dict(dq=torch.empty((B, Hq, T, D), dtype=f32, device="cuda"),
+             dk=torch.empty((B, Hkv, T, D), dtype=f32, device="cuda"),
+             dv=torch.empty((B, Hkv, T, D), dtype=f32, device="cuda"),
+             dq_lm=torch.empty((B, Hq, C, D), dtype=f32, device="cuda"),
+             dh=torch.empty((B, T, Dh), dtype=f32, device="cuda"),
+             dw_down=torch.empty((r, Dh), dtype=f32, device="cuda"),
+             dw_up=torch.empty((Hq * D, r), dtype=f32, device="cuda"))
+    bws = torch.empty((hils.hils_backward_workspace_bytes(c),), dtype=torch.uint8, device="cuda")
+
+    def step():
+        hils.hils_sparse_attn_backward(c, d["q"], d["k"], d["v"], d["q_lm"], d["h"], d["w_down"], d["w_up"],
+                                       k_sum, b_sum, idx, dout, g["dq"], g["dk"], g["dv"], g["dq_lm"], g["dh"],
+                                       g["dw_down"], g["dw_up"], bws, stream)
+
+    for _ in range(max(1, args.warmup)):
+        step()
+    torch.cuda.synchronize()
+    per = []
+    for s in range(args.steps):
+        flush()
+        tm = Timer(torch, stream)
+        tm.mark()
+        step()
+        tm.mark()
+        torch.cuda.synchronize()
+        per.append(tm.events[0].elapsed_time(tm.events[1]))
+        log(f"[backward] step {s}: {per[-1]:.3f} ms")
+    ms = float(np.mean(per))
+    fl = 2.5 * algorithmic_prefill(wl)["attn"]
+    return dict(workload="prefill_8k backward (fixed selection)", value=B * T / (ms * 1e-3),
+                unit="query-tokens/s", ms_per_step=ms, dtype="bf16 in, f32 gradients",
+                algorithmic_tflop=fl / 1e12, achieved_tflops=fl / (ms * 1e-3) / 1e12,
+                peak_f32_vector_tflops=PEAK_F32_VALU_TFLOPS)
 
 
 def bench_prefill_long(args, torch, hils, hs, flush):
@@ -564,6 +631,12 @@ def main():
             first = dec[next(iter(dec))]
             line.update(value=first["value"], ms_per_step=first["ms_per_step"], roofline=first["roofline"],
                         config=dict(workload="decode_512k", batch=first["batch"], seq_len=first["seq_len"]))
+    if args.only in (None, "backward") and not args.no_backward:
+        bw = bench_backward(args, torch, hils, hs, flush)
+        line["backward_8k"] = bw
+        if args.only == "backward":
+            line.update(value=bw["value"], ms_per_step=bw["ms_per_step"],
+                        config=dict(workload="prefill_8k_backward", batch=2, seq_len=8192))
     if args.only in (None, "long") and not args.no_long:
         lg = bench_prefill_long(args, torch, hils, hs, flush)
         line["prefill_512k"] = lg

@@ -150,6 +150,45 @@ hils_status hils_sparse_attn_prefill(const hils_config *cfg, const void *q, cons
                                      const float *topk_score, void *o, void *workspace,
                                      size_t workspace_bytes, void *stream);
 
+/* Workspace bytes needed by hils_sparse_attn_backward (0 for an invalid or
+ * unsupported configuration). */
+size_t hils_backward_workspace_bytes(const hils_config *cfg);
+
+/*
+ * Backward pass of the prefill forward for a FIXED selection -- the chunk
+ * score s-hat sits inside the joint softmax of [p1] Methodology 2 (Eq. 10),
+ * so the loss reaches the landmark summary (Methodology 1, Eq. 8), the
+ * landmark queries and, with Q-Cal, the calibration weights (Methodology 3);
+ * the top-K choice itself is discrete and carries no gradient.  Given
+ * d_o = dL/dO, returns the gradients of L = sum(d_o * O) where O is the
+ * output of hils_sparse_attn_prefill with topk_score = each head's s-hat of
+ * the selected chunks, recomputed here as tau * q-hat . k_sum + b_sum from the
+ * STORED summaries (as hils_chunk_score_topk computes it).  The rounding of
+ * k_sum to dtype is taken as the identity in the chain rule.
+ *   q, d_o     [B, H_q, T, d]   dtype
+ *   k, v       [B, H_kv, T, d]  dtype
+ *   q_lm       [B, H_q, C, d]   dtype  (NULL allowed iff C == 0)
+ *   h, w_down, w_up                    as for hils_chunk_score_topk (NULL iff r == 0)
+ *   k_sum      [B, H_q, C, d]   dtype  } the summaries the forward scored;
+ *   b_sum      [B, H_q, C]      f32    } NULL allowed iff C == 0 or K == 0
+ *   topk_idx   [B, H_kv, T, K]  int32  the forward's selection (-1 pad; an id
+ *                                      outside [0, n_i) counts as no chunk)
+ * Outputs, all float32 and overwritten (no accumulation into them):
+ *   dq [B, H_q, T, d], dk / dv [B, H_kv, T, d], dq_lm [B, H_q, C, d]
+ *   (NULL allowed iff C == 0), and with r > 0: dh [B, T, D_h],
+ *   dw_down [r, D_h], dw_up [H_q*d, r] (all three NULL iff r == 0).
+ *   workspace  >= hils_backward_workspace_bytes(cfg) bytes, device memory.
+ * Every sum runs in a fixed order: repeated calls give identical bits.
+ * T is limited to 32768 (C <= 512; UNSUPPORTED above).
+ */
+hils_status hils_sparse_attn_backward(const hils_config *cfg, const void *q, const void *k,
+                                      const void *v, const void *q_lm, const void *h,
+                                      const void *w_down, const void *w_up, const void *k_sum,
+                                      const float *b_sum, const int32_t *topk_idx, const void *d_o,
+                                      float *dq, float *dk, float *dv, float *dq_lm, float *dh,
+                                      float *dw_down, float *dw_up, void *workspace,
+                                      size_t workspace_bytes, void *stream);
+
 /* Bytes of the decode workspace.  The caller zeroes it ONCE after allocating
  * it (hipMemset / torch.zeros); the library leaves its counters at zero after
  * every call.  A decode workspace must not be shared with another call kind

@@ -23,6 +23,7 @@ ENTRY_POINTS = (
     "hils_decode_error_offset", "hils_dense_decode_workspace_bytes", "hils_dense_attn_decode",
     "hils_landmark_summary_paged", "hils_sparse_attn_decode_paged",
     "hils_sparse_attn_decode_noalloc", "hils_noalloc_scratch_bytes",
+    "hils_backward_workspace_bytes", "hils_sparse_attn_backward",
     "hils_status_string", "hils_last_error",
 )
 
@@ -92,6 +93,8 @@ def _load() -> ctypes.CDLL:
         "hils_sparse_attn_decode_paged": [C, P, P, P, P, P, P, P, I32, I32, P, P, P, P, P, P, P, SZ, P],
         "hils_sparse_attn_decode_noalloc": [C, P, P, P, P, P, P, P, P, P, P, P, P, P],
         "hils_noalloc_scratch_bytes": [],
+        "hils_backward_workspace_bytes": [C],
+        "hils_sparse_attn_backward": [C] + [P] * 19 + [SZ, P],
         "hils_status_string": [ctypes.c_int],
         "hils_last_error": [],
     }
@@ -193,6 +196,20 @@ def hils_sparse_attn_decode_noalloc(cfg: Config, q, h, w_down, w_up, k_cache, v_
            "hils_sparse_attn_decode_noalloc")
 
 
+def hils_backward_workspace_bytes(cfg: Config) -> int:
+    return int(lib.hils_backward_workspace_bytes(ctypes.byref(cfg)))
+
+
+def hils_sparse_attn_backward(cfg: Config, q, k, v, q_lm, h, w_down, w_up, k_sum, b_sum, topk_idx, d_o,
+                              dq, dk, dv, dq_lm, dh, dw_down, dw_up, workspace, stream=None):
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(lib.hils_sparse_attn_backward(ctypes.byref(cfg), _ptr(q), _ptr(k), _ptr(v), _ptr(q_lm), _ptr(h),
+                                         _ptr(w_down), _ptr(w_up), _ptr(k_sum), _ptr(b_sum), _ptr(topk_idx),
+                                         _ptr(d_o), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dq_lm), _ptr(dh),
+                                         _ptr(dw_down), _ptr(dw_up), _ptr(workspace), ws_bytes, _stream(stream)),
+           "hils_sparse_attn_backward")
+
+
 def hils_noalloc_scratch_bytes() -> int:
     return int(lib.hils_noalloc_scratch_bytes())
 
@@ -230,5 +247,7 @@ __all__ = ["Config", "HilsError", "lib", "LIB_PATH", "ENTRY_POINTS", "last_error
            "hils_landmark_summary", "hils_prefill_workspace_bytes", "hils_chunk_score_topk",
            "hils_sparse_attn_prefill", "hils_decode_workspace_bytes", "hils_decode_error_offset",
            "hils_sparse_attn_decode", "hils_dense_decode_workspace_bytes", "hils_dense_attn_decode",
-           "hils_landmark_summary_paged", "hils_sparse_attn_decode_paged", "HILS_OK", "HILS_ERR_INVALID_ARG", "HILS_ERR_UNSUPPORTED", "HILS_ERR_WORKSPACE",
+           "hils_landmark_summary_paged", "hils_sparse_attn_decode_paged",
+           "hils_sparse_attn_decode_noalloc", "hils_noalloc_scratch_bytes",
+           "hils_backward_workspace_bytes", "hils_sparse_attn_backward", "HILS_OK", "HILS_ERR_INVALID_ARG", "HILS_ERR_UNSUPPORTED", "HILS_ERR_WORKSPACE",
            "HILS_ERR_HIP", "HILS_BF16", "HILS_F32"]

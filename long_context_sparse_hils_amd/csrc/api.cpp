@@ -299,6 +299,113 @@ hils_status hils_sparse_attn_prefill(const hils_config *cfg, const void *q, cons
   return finish(hils::launch_attn_valu(a, st), "sparse attention launch");
 }
 
+// ------------------------------------------------------------ backward
+namespace {
+
+struct BwdGeom {
+  size_t off_u, off_du, off_qhat, off_dqhat, off_logz, off_delta, off_lw, off_doo, off_ds;
+  size_t off_cnt, off_qboff, off_choff, off_list, total;
+};
+
+BwdGeom bwd_geom(const hils_config *c) {
+  const size_t B = c->batch, T = c->seq_len, Hq = c->n_q_heads, Hkv = c->n_kv_heads, d = c->head_dim;
+  const size_t K = c->top_k, r = c->qcal_rank, C = T / c->chunk_size, nqb = (T + 255) / 256;
+  BwdGeom g{};
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o += align_up(bytes);
+    return at;
+  };
+  g.off_u = take(sizeof(float) * B * T * r);
+  g.off_du = take(sizeof(float) * B * T * r);
+  g.off_qhat = take(r ? sizeof(float) * B * Hq * T * d : 0);
+  g.off_dqhat = take(r ? sizeof(float) * B * Hq * T * d : 0);
+  g.off_logz = take(sizeof(float) * B * Hq * T);
+  g.off_delta = take(sizeof(float) * B * Hq * T);
+  g.off_lw = take(sizeof(float) * B * Hq * T * K);
+  g.off_doo = take(sizeof(float) * B * Hq * T * K);
+  g.off_ds = take(sizeof(float) * B * Hq * T * K);
+  g.off_cnt = take(sizeof(int32_t) * B * Hkv * nqb * C);
+  g.off_qboff = take(sizeof(int32_t) * B * Hkv * nqb * C);
+  g.off_choff = take(sizeof(int32_t) * B * Hkv * (C + 1));
+  g.off_list = take(sizeof(int32_t) * B * Hkv * T * K);
+  g.total = o + kAlign;
+  return g;
+}
+
+hils_status check_backward_shape(const hils_config *c) {
+  const int C = c->seq_len / c->chunk_size;
+  if (C > hils::kMaxBwdChunks)
+    return fail(HILS_ERR_UNSUPPORTED, "backward supports at most %d chunks (T <= %d), got %d", hils::kMaxBwdChunks,
+                hils::kMaxBwdChunks * c->chunk_size, C);
+  return HILS_OK;
+}
+
+}  // namespace
+
+size_t hils_backward_workspace_bytes(const hils_config *cfg) {
+  if (check_config(cfg) != HILS_OK || check_backward_shape(cfg) != HILS_OK) return 0;
+  return bwd_geom(cfg).total;
+}
+
+hils_status hils_sparse_attn_backward(const hils_config *cfg, const void *q, const void *k, const void *v,
+                                      const void *q_lm, const void *h, const void *w_down, const void *w_up,
+                                      const void *k_sum, const float *b_sum, const int32_t *topk_idx,
+                                      const void *d_o, float *dq, float *dk, float *dv, float *dq_lm, float *dh,
+                                      float *dw_down, float *dw_up, void *workspace, size_t workspace_bytes,
+                                      void *stream) {
+  g_last_error.clear();
+  CHECK(check_config(cfg));
+  CHECK(check_backward_shape(cfg));
+  CHECK(check_ptr(q, "q"));
+  CHECK(check_ptr(k, "k"));
+  CHECK(check_ptr(v, "v"));
+  CHECK(check_ptr(d_o, "d_o"));
+  CHECK(check_ptr(dq, "dq"));
+  CHECK(check_ptr(dk, "dk"));
+  CHECK(check_ptr(dv, "dv"));
+  CHECK(check_qcal_ptrs(cfg, h, w_down, w_up));
+  if (cfg->qcal_rank == 0) {
+    if (dh || dw_down || dw_up)
+      return fail(HILS_ERR_INVALID_ARG, "dh, dw_down and dw_up must be NULL when qcal_rank == 0");
+  } else {
+    CHECK(check_ptr(dh, "dh"));
+    CHECK(check_ptr(dw_down, "dw_down"));
+    CHECK(check_ptr(dw_up, "dw_up"));
+  }
+  const int C = cfg->seq_len / cfg->chunk_size;
+  if (C > 0) {
+    CHECK(check_ptr(q_lm, "q_lm"));
+    CHECK(check_ptr(dq_lm, "dq_lm"));
+    if (cfg->top_k > 0) {
+      CHECK(check_ptr(k_sum, "k_sum"));
+      CHECK(check_ptr(b_sum, "b_sum"));
+    }
+  }
+  if (cfg->top_k > 0) CHECK(check_ptr(topk_idx, "topk_idx"));
+  const BwdGeom g = bwd_geom(cfg);
+  if (!workspace || workspace_bytes < g.total)
+    return fail(HILS_ERR_WORKSPACE, "backward workspace of %zu bytes given, %zu needed", workspace_bytes, g.total);
+  if (!aligned16(workspace)) return fail(HILS_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
+  char *ws = static_cast<char *>(workspace);
+  auto f = [&](size_t off) { return reinterpret_cast<float *>(ws + off); };
+  auto n = [&](size_t off) { return reinterpret_cast<int32_t *>(ws + off); };
+  hils::BwdArgs a{};
+  a.q = q; a.k = k; a.v = v; a.q_lm = q_lm; a.h = h; a.w_down = w_down; a.w_up = w_up;
+  a.k_sum = k_sum; a.d_o = d_o; a.b_sum = b_sum; a.topk_idx = topk_idx;
+  a.dq = dq; a.dk = dk; a.dv = dv; a.dq_lm = dq_lm; a.dh = dh; a.dw_down = dw_down; a.dw_up = dw_up;
+  a.u = f(g.off_u); a.du = f(g.off_du); a.qhat = f(g.off_qhat); a.dqhat = f(g.off_dqhat);
+  a.logz = f(g.off_logz); a.delta = f(g.off_delta);
+  a.slot_lw = f(g.off_lw); a.slot_doo = f(g.off_doo); a.slot_ds = f(g.off_ds);
+  a.inv_cnt = n(g.off_cnt); a.inv_qboff = n(g.off_qboff); a.inv_choff = n(g.off_choff); a.inv_list = n(g.off_list);
+  a.B = cfg->batch; a.T = cfg->seq_len; a.Hq = cfg->n_q_heads; a.Hkv = cfg->n_kv_heads; a.d = cfg->head_dim;
+  a.K = cfg->top_k; a.W = cfg->window; a.r = cfg->qcal_rank; a.Dh = cfg->hidden_dim;
+  a.tau = tau_of(cfg);
+  a.bf16 = cfg->dtype == HILS_BF16;
+  return finish(hils::launch_backward(a, static_cast<hipStream_t>(stream)), "backward launch");
+}
+
 size_t hils_decode_workspace_bytes(const hils_config *cfg) {
   if (check_config(cfg) != HILS_OK) return 0;
   DecodeGeom g;

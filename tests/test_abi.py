@@ -168,3 +168,34 @@ def test_noalloc_decode_rejects_configs_beyond_its_scratch():
                                                   FAKE, FAKE, FAKE, FAKE, FAKE, None)
     assert st == hils.HILS_ERR_UNSUPPORTED
     assert "allocation-free" in hils.last_error()
+
+
+def test_backward_host_checks():
+    """The backward call: its sequence-length limit, the Q-Cal gradient
+    pointers that must match the rank, and its workspace size, all checked on
+    the host before any launch."""
+    L = hils.lib
+    cfg = _cfg(batch=2, seq_len=8192, qcal_rank=32, hidden_dim=4096)
+    need = hils.hils_backward_workspace_bytes(cfg)
+    # q-hat and its gradient in fp32 dominate: 2 x B Hq T d x 4 bytes
+    assert need >= 2 * 2 * 32 * 8192 * 128 * 4
+    assert hils.hils_backward_workspace_bytes(_cfg(seq_len=65536)) == 0
+    assert hils.hils_backward_workspace_bytes(_cfg(seq_len=32768)) > 0
+
+    def call(c, ws_bytes, dh=FAKE, **over):
+        a = dict(q=FAKE, k=FAKE, v=FAKE, q_lm=FAKE, h=FAKE, w_down=FAKE, w_up=FAKE, k_sum=FAKE, b_sum=FAKE,
+                 idx=FAKE, d_o=FAKE, dq=FAKE, dk=FAKE, dv=FAKE, dq_lm=FAKE, dh=dh, dwd=dh, dwu=dh)
+        a.update(over)
+        return L.hils_sparse_attn_backward(ctypes.byref(c), *a.values(), FAKE, ws_bytes, None)
+
+    assert call(cfg, need - 1) == hils.HILS_ERR_WORKSPACE
+    assert call(cfg, need, d_o=None) == hils.HILS_ERR_INVALID_ARG
+    assert "d_o is NULL" in hils.last_error()
+    assert call(cfg, need, dh=None) == hils.HILS_ERR_INVALID_ARG
+    c0 = _cfg(qcal_rank=0, hidden_dim=0)
+    n0 = hils.hils_backward_workspace_bytes(c0)
+    assert 0 < n0 < need
+    assert call(c0, n0, h=None, w_down=None, w_up=None) == hils.HILS_ERR_INVALID_ARG  # dh given at rank 0
+    long_cfg = _cfg(seq_len=65536)
+    assert call(long_cfg, 1 << 40) == hils.HILS_ERR_UNSUPPORTED
+    assert "at most 512 chunks" in hils.last_error()
