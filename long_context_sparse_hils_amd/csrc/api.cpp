@@ -303,8 +303,8 @@ hils_status hils_sparse_attn_prefill(const hils_config *cfg, const void *q, cons
 namespace {
 
 struct BwdGeom {
-  size_t off_u, off_du, off_qhat, off_dqhat, off_logz, off_delta, off_lw, off_doo, off_ds;
-  size_t off_cnt, off_qboff, off_choff, off_list, total;
+  size_t off_u, off_du, off_qhat, off_dqhat, off_logz, off_delta, off_lw, off_doo, off_ds, off_z, off_zb;
+  size_t off_cnt, off_qboff, off_choff, off_list, off_pos, total;
 };
 
 BwdGeom bwd_geom(const hils_config *c) {
@@ -323,13 +323,16 @@ BwdGeom bwd_geom(const hils_config *c) {
   g.off_dqhat = take(r ? sizeof(float) * B * Hq * T * d : 0);
   g.off_logz = take(sizeof(float) * B * Hq * T);
   g.off_delta = take(sizeof(float) * B * Hq * T);
-  g.off_lw = take(sizeof(float) * B * Hq * T * K);
+  g.off_lw = take(sizeof(float) * B * Hq * T * K);  // per list entry and head: B Hkv (T K) G
   g.off_doo = take(sizeof(float) * B * Hq * T * K);
   g.off_ds = take(sizeof(float) * B * Hq * T * K);
+  g.off_z = take(sizeof(float) * B * Hq * C * r);
+  g.off_zb = take(sizeof(float) * B * Hq * C);
   g.off_cnt = take(sizeof(int32_t) * B * Hkv * nqb * C);
   g.off_qboff = take(sizeof(int32_t) * B * Hkv * nqb * C);
   g.off_choff = take(sizeof(int32_t) * B * Hkv * (C + 1));
   g.off_list = take(sizeof(int32_t) * B * Hkv * T * K);
+  g.off_pos = take(sizeof(int32_t) * B * Hkv * T * K);
   g.total = o + kAlign;
   return g;
 }
@@ -397,8 +400,10 @@ hils_status hils_sparse_attn_backward(const hils_config *cfg, const void *q, con
   a.dq = dq; a.dk = dk; a.dv = dv; a.dq_lm = dq_lm; a.dh = dh; a.dw_down = dw_down; a.dw_up = dw_up;
   a.u = f(g.off_u); a.du = f(g.off_du); a.qhat = f(g.off_qhat); a.dqhat = f(g.off_dqhat);
   a.logz = f(g.off_logz); a.delta = f(g.off_delta);
-  a.slot_lw = f(g.off_lw); a.slot_doo = f(g.off_doo); a.slot_ds = f(g.off_ds);
+  a.ent_lw = f(g.off_lw); a.ent_doo = f(g.off_doo); a.ent_ds = f(g.off_ds);
+  a.zsum = f(g.off_z); a.zb = f(g.off_zb);
   a.inv_cnt = n(g.off_cnt); a.inv_qboff = n(g.off_qboff); a.inv_choff = n(g.off_choff); a.inv_list = n(g.off_list);
+  a.inv_pos = n(g.off_pos);
   a.B = cfg->batch; a.T = cfg->seq_len; a.Hq = cfg->n_q_heads; a.Hkv = cfg->n_kv_heads; a.d = cfg->head_dim;
   a.K = cfg->top_k; a.W = cfg->window; a.r = cfg->qcal_rank; a.Dh = cfg->hidden_dim;
   a.tau = tau_of(cfg);

@@ -1,5 +1,5 @@
 // Backward pass of the HiLS-Attention prefill forward, for a fixed top-K
-// selection (VALU kernels, fp32 accumulation).
+// selection (fp32 accumulation).
 //
 // The pages train chunk selection through the forward weights: each selected
 // chunk's score s_hat sits in the joint softmax of Eq. 10 (picx.dev
@@ -21,267 +21,153 @@
 // E = sum p_j l_j:
 //   dl_j = p_j ( dk'.(k_j - k') - db' (l_j - E) ),
 //   dq'_c = tau sum_j dl_j k_j,   dk_j += p_j dk' + tau dl_j q'_c.
+// Q-Cal: q_hat = q + W_up u, u = W_down h, so dk'_c = tau sum ds q +
+// tau W_up_h z_c with z_c = sum ds u over the rows that selected chunk c.
 //
 // Kernels (all on the caller's stream):
-//   [qcal]  u = W_down h, q_hat = q + W_up u                          (r > 0)
-//   rows    one workgroup per (i, g, b), one wave per head (4 at a time):
-//           two passes over the row's selected chunks and window blocks
-//           (staged in LDS): the first gives logZ, Delta and per chunk its
-//           log-weight and dO.o_c; the second the dl_j and dq.  Writes dq,
-//           the per-row and per-slot values the key pass needs, and dq_hat.
+//   [qcal]  u = h W_down^T, q_hat = q + u W_up^T           (tiled fp32 GEMM)
 //   lists   the inverse of the selection: for every (b, g, chunk) the
 //           (query, slot) entries that selected it, ordered by query
-//           (counted per 256-query block, no atomics on the order).
-//   keys    one workgroup per 64-key block (b, g): every row whose window
-//           covers the block, then (complete chunks) every entry of the
-//           chunk's list with its G heads; thread (key, quarter of d) keeps
-//           dk, dv in registers.  Then the chunk's summary backward.
-//   [qcal]  du, dh, dW_down, dW_up.
+//           (counted per 256-query block, no atomics on the order), and
+//           each slot's place in its list.
+//   rows    one workgroup per (i, g, b), one wave per head (4 at a time), one
+//           pass over the row's selected chunks and window blocks (staged in
+//           LDS): logZ and Delta, and dq and dq_hat from running sums that
+//           the normaliser scales at the end.  Writes dq, dq_hat, logZ and
+//           Delta, and each list entry's log-weight, dO.o_c and ds_c.
+//   z       per (b, g, chunk): z = sum ds u and sum ds over the chunk's list.
+//   keys    per 64-key block (b, g): every row whose window covers the block,
+//           then (complete chunks) every entry of the chunk's list with its
+//           G heads; accumulates dk, dv (bf16 MFMA kernel where the shape
+//           allows, else the VALU kernel below), then the chunk's summary
+//           backward.
+//   [qcal]  du = dq_hat W_up, dW_up = dq_hat^T u, dW_down = du^T h,
+//           dh = du W_down                                  (tiled fp32 GEMM)
 // Every sum runs in a fixed order: the results are the same on every run.
-#include "hils_common.h"
-#include "launch.h"
+#include "bwd_common.h"
 
 namespace hils {
 
+using bwd::kBK;
+using bwd::kBT;
+using bwd::kQBlk;
+using bwd::sum4;
+
 namespace {
 
-constexpr int kBT = 256;     // threads per workgroup
-constexpr int kBK = 64;      // keys per block (= chunk size S)
-constexpr int kQBlk = 256;   // queries per block of the inverse-list build
 constexpr int kRowsPerBatch = 8;
 
-// Reduce over the 4 consecutive lanes 4m .. 4m+3.
-__device__ __forceinline__ float sum4(float v) {
-  v += __shfl_xor(v, 1, 64);
-  v += __shfl_xor(v, 2, 64);
-  return v;
-}
-
-// One row of a staged key / value tile, stored with one spare pair of
-// elements per row so that lane j reading row j hits bank j + const.
+// Rows j0 .. j0 + 63 of a [T, D] matrix into an fp32 LDS tile with rows
+// D + 2 floats apart (8-byte aligned pairs; lane j of a wave reading row j
+// meets bank 2 j + const); rows past T are zero.  Pieces of 8 elements.
 template <typename T, int D>
-struct Tile {
-  static constexpr int kLD = D + (sizeof(T) == 2 ? 2 : 1);
-  T x[kBK * kLD];
-  __device__ __forceinline__ float at(int j, int e) const { return to_f(x[j * kLD + e]); }
-  __device__ __forceinline__ static float to_f(float v) { return v; }
-  __device__ __forceinline__ static float to_f(uint16_t v) { return bf16_to_f32(v); }
-};
-
-// Rows j0 .. j0 + 63 of a [T, D] matrix into a tile (rows past T are zero).
-template <typename T, int D>
-__device__ __forceinline__ void stage_tile(Tile<T, D> &tl, const T *src, int j0, int T_len) {
-  constexpr int EPV = 16 / sizeof(T);  // elements per 16-byte piece
-  for (int p = threadIdx.x; p < kBK * D / EPV; p += kBT) {
-    const int r = p / (D / EPV), s = p % (D / EPV);
-    uint4 u = make_uint4(0u, 0u, 0u, 0u);
-    if (j0 + r < T_len) u = *reinterpret_cast<const uint4 *>(src + static_cast<size_t>(j0 + r) * D + s * EPV);
-    const T *e = reinterpret_cast<const T *>(&u);
+__device__ __forceinline__ void stage_tile(float (*tl)[D + 2], const T *src, int j0, int T_len) {
+  for (int p = threadIdx.x; p < kBK * D / 8; p += kBT) {
+    const int r = p / (D / 8), s = p % (D / 8);
+    float e[8];
+    if (j0 + r < T_len) {
+      Elem<T>::load8(src + static_cast<size_t>(j0 + r) * D + s * 8, e);
+    } else {
 #pragma unroll
-    for (int x = 0; x < EPV; ++x) tl.x[r * Tile<T, D>::kLD + s * EPV + x] = e[x];
+      for (int x = 0; x < 8; ++x) e[x] = 0.f;
+    }
+#pragma unroll
+    for (int x = 0; x < 8; x += 2) *reinterpret_cast<float2 *>(&tl[r][s * 8 + x]) = make_float2(e[x], e[x + 1]);
   }
 }
 
 }  // namespace
 
-// ------------------------------------------------------------------ Q-Cal
-// q_hat [B, Hq, T, D] fp32 = q + (W_up u)[h D + e], u [B*T, r] fp32.
-template <typename T>
-__global__ void __launch_bounds__(kBT)
-bwd_qhat_kernel(const T *__restrict__ q, const T *__restrict__ w_up, const float *__restrict__ u,
-                float *__restrict__ qhat, int Hq, int T_len, int D, int r, size_t total) {
-  for (size_t x = blockIdx.x * static_cast<size_t>(kBT) + threadIdx.x; x < total;
-       x += static_cast<size_t>(gridDim.x) * kBT) {
-    const int e = static_cast<int>(x % D);
-    const size_t row = x / D;  // (b, h, i)
-    const int i = static_cast<int>(row % T_len), h = static_cast<int>((row / T_len) % Hq);
-    const int b = static_cast<int>(row / (static_cast<size_t>(T_len) * Hq));
-    const float *ur = u + (static_cast<size_t>(b) * T_len + i) * r;
-    const T *wr = w_up + (static_cast<size_t>(h) * D + e) * r;
-    float acc = 0.f;
-    for (int a = 0; a < r; ++a) acc += Elem<T>::load(wr, a) * ur[a];
-    qhat[x] = Elem<T>::load(q, x) + acc;
+// ------------------------------------------------------------------ fp32 GEMM
+// C[m, n] = sum_k A(m, k) B(k, n) with A(m, k) = A[m lam + k lak] and
+// B(k, n) = B[k lbk + n lbn] (any strides), fp32 accumulation in a fixed k
+// order.  64 x 64 output tiles per 256-thread workgroup (4 x 4 per thread),
+// k in slabs of 16 staged in LDS.  MODE 0 stores C[m lcm + n lcn]; MODE 1 is
+// the Q-Cal q_hat: m = token b T + i, n = h D + e, and the tile adds
+// q[b, h, i, e] and stores q_hat in the same [B, Hq, T, D] layout.
+template <typename TA, typename TB, int MODE>
+__global__ void __launch_bounds__(256)
+bwd_gemm_kernel(const TA *__restrict__ A, long lam, long lak, const TB *__restrict__ Bm, long lbk, long lbn,
+                float *__restrict__ Cm, long lcm, long lcn, int M, int N, int Kd, const TB *__restrict__ qadd, int Hq,
+                int T_len, int D) {
+  __shared__ float As[16][64 + 4];
+  __shared__ float Bs[16][64 + 4];
+  const int t = threadIdx.x, tm = t >> 4, tn = t & 15;
+  const int m0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
+  const bool a_kfast = lak == 1, b_nfast = lbn == 1;
+  float acc[4][4];
+#pragma unroll
+  for (int x = 0; x < 4; ++x)
+#pragma unroll
+    for (int y = 0; y < 4; ++y) acc[x][y] = 0.f;
+  for (int k0 = 0; k0 < Kd; k0 += 16) {
+    float av[4], bv[4];
+    int am[4], ak[4], bk[4], bn[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int x = t + 256 * j;  // 1024 elements of each slab
+      am[j] = a_kfast ? x / 16 : x % 64;
+      ak[j] = a_kfast ? x % 16 : x / 64;
+      bk[j] = b_nfast ? x / 64 : x % 16;
+      bn[j] = b_nfast ? x % 64 : x / 16;
+      const int gm = m0 + am[j], gk = k0 + ak[j];
+      av[j] = (gm < M && gk < Kd) ? Elem<TA>::load(A, gm * lam + gk * lak) : 0.f;
+      const int gk2 = k0 + bk[j], gn = n0 + bn[j];
+      bv[j] = (gk2 < Kd && gn < N) ? Elem<TB>::load(Bm, gk2 * lbk + gn * lbn) : 0.f;
+    }
+    __syncthreads();  // the previous slab is no longer read
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      As[ak[j]][am[j]] = av[j];
+      Bs[bk[j]][bn[j]] = bv[j];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) {
+      const float4 a4 = *reinterpret_cast<const float4 *>(&As[kk][tm * 4]);
+      const float4 b4 = *reinterpret_cast<const float4 *>(&Bs[kk][tn * 4]);
+      const float a_[4] = {a4.x, a4.y, a4.z, a4.w}, b_[4] = {b4.x, b4.y, b4.z, b4.w};
+#pragma unroll
+      for (int x = 0; x < 4; ++x)
+#pragma unroll
+        for (int y = 0; y < 4; ++y) acc[x][y] += a_[x] * b_[y];
+    }
+  }
+#pragma unroll
+  for (int x = 0; x < 4; ++x) {
+    const int m = m0 + tm * 4 + x;
+    if (m >= M) continue;
+#pragma unroll
+    for (int y = 0; y < 4; ++y) {
+      const int n = n0 + tn * 4 + y;
+      if (n >= N) continue;
+      if (MODE == 0) {
+        Cm[m * lcm + n * lcn] = acc[x][y];
+      } else {
+        const int b = m / T_len, i = m % T_len, h = n / D, e = n % D;
+        const size_t o = ((static_cast<size_t>(b) * Hq + h) * T_len + i) * D + e;
+        Cm[o] = Elem<TB>::load(qadd, o) + acc[x][y];
+      }
+    }
   }
 }
 
-// ------------------------------------------------------------------ rows
-template <typename T, int D>
-struct RowSmem {
-  Tile<T, D> kt, vt;
-  float qs[4][D], qhs[4][D], dos[4][D];
-  float dls[4][kBK];                  // dl_j of the current block, per head
-  float sl_m[4][32], sl_l[4][32];     // per selected chunk: max and sum of e^{l - max}
-  float sl_doo[4][32], sl_s[4][32];   // dO.o_c and s_hat
-  int sel[32];                        // the row's chunks (list order; -1: none)
-};
-
-template <typename T, int D, bool QCAL>
-__global__ void __launch_bounds__(kBT)
-bwd_rows_kernel(BwdArgs a) {
-  __shared__ RowSmem<T, D> sm;
-  const int i = blockIdx.x, g = blockIdx.y, b = blockIdx.z, t = threadIdx.x;
-  const int lane = t & 63, w = t >> 6;
-  const int T_len = a.T, K = a.K, Hq = a.Hq, Hkv = a.Hkv, C = T_len / kBK;
-  const int G = Hq / Hkv;
-  const float tau = a.tau;
-  const int n = eligible_chunks(i, a.W, kBK), w_lo = n * kBK;
-  const int nwb = (i - w_lo) / kBK + 1;
-  const T *kb = static_cast<const T *>(a.k) + (static_cast<size_t>(b) * Hkv + g) * T_len * D;
-  const T *vb = static_cast<const T *>(a.v) + (static_cast<size_t>(b) * Hkv + g) * T_len * D;
-  const T *ksum = static_cast<const T *>(a.k_sum);
-  // the row's selection (an id outside [0, n_i) is no chunk)
-  if (t < 32) {
-    int c = -1;
-    if (t < K) c = a.topk_idx[((static_cast<size_t>(b) * Hkv + g) * T_len + i) * K + t];
-    sm.sel[t] = (c >= 0 && c < n) ? c : -1;
-  }
-  __syncthreads();
-  constexpr int EPL = D / 64;  // elements of d per lane
-  for (int h0 = 0; h0 < G; h0 += 4) {
-    const int hh = h0 + w, h = g * G + hh;
-    const bool act = hh < G;
-    const size_t ro = (static_cast<size_t>(b) * Hq + (act ? h : g * G)) * T_len + i;  // row (b, h, i)
-    for (int x = lane; x < D; x += 64) {
-      sm.qs[w][x] = Elem<T>::load(static_cast<const T *>(a.q), ro * D + x);
-      sm.qhs[w][x] = QCAL ? a.qhat[ro * D + x] : sm.qs[w][x];
-      sm.dos[w][x] = Elem<T>::load(static_cast<const T *>(a.d_o), ro * D + x);
-    }
-    // ---- pass 1: logZ, Delta; per chunk its statistics and dO.o_c
-    float mw = -INFINITY, lw = 0.f, dw = 0.f;  // window: max, sum e^{l - mw}, sum e^{l - mw} dO.v
-    for (int x = 0; x < K + nwb; ++x) {
-      const bool chunk = x < K;
-      if (chunk && sm.sel[x] < 0) continue;  // uniform across the workgroup
-      const int j0 = chunk ? sm.sel[x] * kBK : w_lo + (x - K) * kBK;
-      __syncthreads();  // the previous block's tiles are no longer read
-      stage_tile<T, D>(sm.kt, kb, j0, T_len);
-      stage_tile<T, D>(sm.vt, vb, j0, T_len);
-      __syncthreads();
-      if (act) {
-        float l = 0.f, dov = 0.f;
-        for (int e = 0; e < D; ++e) {
-          l += sm.qs[w][e] * sm.kt.at(lane, e);
-          dov += sm.dos[w][e] * sm.vt.at(lane, e);
-        }
-        l *= tau;
-        if (chunk) {
-          const float m = wave_max(l);
-          const float p = __expf(l - m);
-          const float lsum = wave_sum(p);
-          const float doo = wave_sum(p * dov) / lsum;
-          // s_hat = tau q_hat . k'_c + b'_c from the stored summary
-          const int c = sm.sel[x];
-          const size_t so = (static_cast<size_t>(b) * Hq + h) * C + c;
-          float sp = 0.f;
-#pragma unroll
-          for (int u = 0; u < EPL; ++u) sp += sm.qhs[w][lane * EPL + u] * Elem<T>::load(ksum, so * D + lane * EPL + u);
-          sp = wave_sum(sp);
-          if (lane == 0) {
-            sm.sl_m[w][x] = m;
-            sm.sl_l[w][x] = lsum;
-            sm.sl_doo[w][x] = doo;
-            sm.sl_s[w][x] = tau * sp + a.b_sum[so];
-          }
-        } else {
-          const int jj = j0 + lane;
-          const float lm = jj <= i ? l : -INFINITY;
-          const float mb = wave_max(lm);
-          const float mn = fmaxf(mw, mb);
-          const float e = jj <= i ? __expf(lm - mn) : 0.f;
-          const float sc = mw == -INFINITY ? 0.f : __expf(mw - mn);
-          lw = lw * sc + wave_sum(e);
-          dw = dw * sc + wave_sum(e * dov);
-          mw = mn;
-        }
-      }
-    }
-    __syncthreads();
-    // ---- the joint normaliser, Delta, and the per-slot values
-    float logZ = 0.f, Delta = 0.f;
-    if (act) {
-      float M = mw;
-      for (int x = 0; x < K; ++x)
-        if (sm.sel[x] >= 0) M = fmaxf(M, sm.sl_s[w][x]);
-      float z = lw * __expf(mw - M);
-      for (int x = 0; x < K; ++x)
-        if (sm.sel[x] >= 0) z += __expf(sm.sl_s[w][x] - M);
-      logZ = M + __logf(z);
-      Delta = dw * __expf(mw - logZ);
-      for (int x = 0; x < K; ++x)
-        if (sm.sel[x] >= 0) Delta += __expf(sm.sl_s[w][x] - logZ) * sm.sl_doo[w][x];
-      if (lane == 0) {
-        a.logz[ro] = logZ;
-        a.delta[ro] = Delta;
-      }
-      for (int x = lane; x < K; x += 64) {
-        const bool ok = sm.sel[x] >= 0;
-        const float wc = ok ? __expf(sm.sl_s[w][x] - logZ) : 0.f;
-        // w_c P_cj = e^{l_j + lwt}: lwt = s_hat - logZ - max - log(sum)
-        a.slot_lw[ro * K + x] = ok ? sm.sl_s[w][x] - logZ - sm.sl_m[w][x] - __logf(sm.sl_l[w][x]) : -INFINITY;
-        a.slot_doo[ro * K + x] = ok ? sm.sl_doo[w][x] : 0.f;
-        a.slot_ds[ro * K + x] = ok ? wc * (sm.sl_doo[w][x] - Delta) : 0.f;
-      }
-    }
-    // ---- pass 2: dl_j of every block, dq
-    float dq[EPL], dqh[EPL];
-#pragma unroll
-    for (int u = 0; u < EPL; ++u) dq[u] = dqh[u] = 0.f;
-    for (int x = 0; x < K + nwb; ++x) {
-      const bool chunk = x < K;
-      if (chunk && sm.sel[x] < 0) continue;
-      const int j0 = chunk ? sm.sel[x] * kBK : w_lo + (x - K) * kBK;
-      __syncthreads();
-      stage_tile<T, D>(sm.kt, kb, j0, T_len);
-      stage_tile<T, D>(sm.vt, vb, j0, T_len);
-      __syncthreads();
-      if (act) {
-        float l = 0.f, dov = 0.f;
-        for (int e = 0; e < D; ++e) {
-          l += sm.qs[w][e] * sm.kt.at(lane, e);
-          dov += sm.dos[w][e] * sm.vt.at(lane, e);
-        }
-        l *= tau;
-        float dl;
-        if (chunk) {
-          const float wc = __expf(sm.sl_s[w][x] - logZ);
-          const float pw = wc * __expf(l - sm.sl_m[w][x]) / sm.sl_l[w][x];  // w_c P_cj
-          dl = pw * (dov - sm.sl_doo[w][x]);
-          // dq_hat += tau ds_c k'_c
-          const int c = sm.sel[x];
-          const size_t so = (static_cast<size_t>(b) * Hq + h) * C + c;
-          const float ds = wc * (sm.sl_doo[w][x] - Delta);
-#pragma unroll
-          for (int u = 0; u < EPL; ++u) dqh[u] += tau * ds * Elem<T>::load(ksum, so * D + lane * EPL + u);
-        } else {
-          const int jj = j0 + lane;
-          dl = jj <= i ? __expf(l - logZ) * (dov - Delta) : 0.f;
-        }
-        sm.dls[w][lane] = dl;
-      }
-      __syncthreads();
-      if (act) {
-        for (int j = 0; j < kBK; ++j) {
-          const float dlj = sm.dls[w][j];
-#pragma unroll
-          for (int u = 0; u < EPL; ++u) dq[u] += dlj * sm.kt.at(j, lane * EPL + u);
-        }
-      }
-    }
-    if (act) {
-#pragma unroll
-      for (int u = 0; u < EPL; ++u) {
-        a.dq[ro * D + lane * EPL + u] = tau * dq[u] + dqh[u];
-        if (QCAL) a.dqhat[ro * D + lane * EPL + u] = dqh[u];
-      }
-    }
-    __syncthreads();
-  }
+template <typename TA, typename TB, int MODE = 0>
+static hipError_t gemm(const TA *A, long lam, long lak, const TB *Bm, long lbk, long lbn, float *Cm, long lcm, long lcn,
+                       int M, int N, int Kd, hipStream_t st, const TB *qadd = nullptr, int Hq = 0, int T_len = 1,
+                       int D = 1) {
+  const dim3 grid((N + 63) / 64, (M + 63) / 64);
+  bwd_gemm_kernel<TA, TB, MODE><<<grid, 256, 0, st>>>(A, lam, lak, Bm, lbk, lbn, Cm, lcm, lcn, M, N, Kd, qadd, Hq,
+                                                      T_len, D);
+  return hipGetLastError();
 }
 
 // ------------------------------------------------------------------ inverse lists
 // For each (b, g) and chunk c, the entries (i, slot) with topk_idx[b,g,i,slot]
 // == c (and c < n_i), ordered by i.  cnt [B, Hkv, nqb, C]: entries per
 // 256-query block; qboff: their offset inside the chunk's list; choff
-// [B, Hkv, C + 1]: each chunk's first entry; list [B, Hkv, T K]: i * 32 + slot.
+// [B, Hkv, C + 1]: each chunk's first entry; list [B, Hkv, T K]: i * 32 + slot;
+// pos [B, Hkv, T, K]: the entry's place in the list (-1 for no chunk).
 struct InvSmem {
   uint32_t mask[kMaxBwdChunks][kQBlk / 32];
 };
@@ -347,38 +233,262 @@ __global__ void __launch_bounds__(kBT) bwd_inv_fill_kernel(BwdArgs a) {
   const size_t pg = static_cast<size_t>(b) * a.Hkv + g;
   const int n = eligible_chunks(i, a.W, kBK);
   const int32_t *ir = a.topk_idx + (pg * a.T + i) * a.K;
+  int32_t *pr = a.inv_pos + (pg * a.T + i) * a.K;
   for (int k = 0; k < a.K; ++k) {
     const int c = ir[k];
-    if (c < 0 || c >= n) continue;
+    if (c < 0 || c >= n) {
+      pr[k] = -1;
+      continue;
+    }
     int rank = 0;
     for (int x = 0; x < (t >> 5); ++x) rank += __popc(sm.mask[c][x]);
     rank += __popc(sm.mask[c][t >> 5] & ((1u << (t & 31)) - 1u));
     const int pos = a.inv_choff[pg * (C + 1) + c] + a.inv_qboff[(pg * nqb + qb) * C + c] + rank;
     a.inv_list[pg * static_cast<size_t>(a.T) * a.K + pos] = i * 32 + k;
+    pr[k] = pos;
   }
 }
 
-// ------------------------------------------------------------------ keys
-template <typename T, int D>
-struct KeySmem {
-  float kt[kBK][D + 1];                  // the block's keys (fp32)
-  float rq[kRowsPerBatch][D];            // a batch of rows: q, dO, and q_hat (summary)
-  float rdo[kRowsPerBatch][D];
-  float rqh[kRowsPerBatch][D];
-  float ra[kRowsPerBatch], rb[kRowsPerBatch], rds[kRowsPerBatch];
-  int ri[kRowsPerBatch], rh[kRowsPerBatch], rwin[kRowsPerBatch];
-  float red[4][kMaxBwdG];                   // cross-wave reductions
-  float dkp[kMaxBwdG][D], dbp[kMaxBwdG];       // per head: dk'_c and db'_c of the chunk
-  float qlm[D], kp[D], pl[kBK], dlj[kBK];
-  float stat[4];
+// ------------------------------------------------------------------ rows
+template <int D>
+struct RowSmem {
+  float kt[kBK][D + 2], vt[kBK][D + 2];
+  float qs[4][D], qhs[4][D], dos[4][D];
+  float ew[4][kBK], dvw[4][kBK];      // per head: the block's weights and dO.v_j
+  float sl_m[4][32], sl_l[4][32];     // per selected chunk: max and sum of e^{l - max}
+  float sl_doo[4][32], sl_s[4][32];   // dO.o_c and s_hat
+  int sel[32];                        // the row's chunks (list order; -1: none)
 };
 
+// One pass over the row's blocks.  The chunk scores are computed first (from
+// the stored summaries), so their maximum Mc is known before any chunk is
+// read; the window keeps an online maximum mw.  Running sums, per lane's
+// elements e of d:
+//   window  A1 = sum e^{l_j - mw} dO.v_j k_j,  A2 = sum e^{l_j - mw} k_j
+//   chunks  Bq = sum_c e^{s_c - Mc} sum_j P_cj (dO.v_j - dO.o_c) k_j,
+//           B1 = sum_c e^{s_c - Mc} dO.o_c k'_c,  B2 = sum_c e^{s_c - Mc} k'_c
+// and at the end, with logZ and Delta:
+//   dq_hat = tau e^{Mc - logZ} (B1 - Delta B2)
+//   dq     = tau (e^{Mc - logZ} Bq + e^{mw - logZ} (A1 - Delta A2)) + dq_hat.
 template <typename T, int D, bool QCAL>
 __global__ void __launch_bounds__(kBT)
+bwd_rows_kernel(BwdArgs a) {
+  __shared__ RowSmem<D> sm;
+  const int i = blockIdx.x, g = blockIdx.y, b = blockIdx.z, t = threadIdx.x;
+  const int lane = t & 63, w = t >> 6;
+  const int T_len = a.T, K = a.K, Hq = a.Hq, Hkv = a.Hkv, C = T_len / kBK;
+  const int G = Hq / Hkv;
+  const float tau = a.tau;
+  const int n = eligible_chunks(i, a.W, kBK), w_lo = n * kBK;
+  const int nwb = (i - w_lo) / kBK + 1;
+  const size_t pg = static_cast<size_t>(b) * Hkv + g;
+  const T *kb = static_cast<const T *>(a.k) + pg * T_len * D;
+  const T *vb = static_cast<const T *>(a.v) + pg * T_len * D;
+  const T *ksum = static_cast<const T *>(a.k_sum);
+  // the row's selection (an id outside [0, n_i) is no chunk)
+  if (t < 32) {
+    int c = -1;
+    if (t < K) c = a.topk_idx[(pg * T_len + i) * K + t];
+    sm.sel[t] = (c >= 0 && c < n) ? c : -1;
+  }
+  __syncthreads();
+  constexpr int EPL = D / 64;  // elements of d per lane
+  for (int h0 = 0; h0 < G; h0 += 4) {
+    const int hh = h0 + w, h = g * G + hh;
+    const bool act = hh < G;
+    const size_t ro = (static_cast<size_t>(b) * Hq + (act ? h : g * G)) * T_len + i;  // row (b, h, i)
+    for (int x = lane; x < D; x += 64) {
+      sm.qs[w][x] = Elem<T>::load(static_cast<const T *>(a.q), ro * D + x);
+      sm.qhs[w][x] = QCAL ? a.qhat[ro * D + x] : sm.qs[w][x];
+      sm.dos[w][x] = Elem<T>::load(static_cast<const T *>(a.d_o), ro * D + x);
+    }
+    // the chunk scores s_hat = tau q_hat . k'_c + b'_c and their maximum
+    float Mc = -INFINITY;
+    if (act) {
+      for (int x = 0; x < K; ++x) {
+        if (sm.sel[x] < 0) continue;
+        const size_t so = (static_cast<size_t>(b) * Hq + h) * C + sm.sel[x];
+        float sp = 0.f;
+#pragma unroll
+        for (int u = 0; u < EPL; ++u) sp += sm.qhs[w][lane * EPL + u] * Elem<T>::load(ksum, so * D + lane * EPL + u);
+        const float s = tau * wave_sum(sp) + a.b_sum[so];
+        if (lane == 0) sm.sl_s[w][x] = s;
+        Mc = fmaxf(Mc, s);
+      }
+    }
+    float mw = -INFINITY, zw = 0.f, dw = 0.f;  // window: max, sum e^{l - mw}, sum e^{l - mw} dO.v
+    float A1[EPL], A2[EPL], Bq[EPL], B1[EPL], B2[EPL];
+#pragma unroll
+    for (int u = 0; u < EPL; ++u) A1[u] = A2[u] = Bq[u] = B1[u] = B2[u] = 0.f;
+    for (int x = 0; x < K + nwb; ++x) {
+      const bool chunk = x < K;
+      if (chunk && sm.sel[x] < 0) continue;  // uniform across the workgroup
+      const int j0 = chunk ? sm.sel[x] * kBK : w_lo + (x - K) * kBK;
+      __syncthreads();  // the previous block's tiles are no longer read
+      stage_tile<T, D>(sm.kt, kb, j0, T_len);
+      stage_tile<T, D>(sm.vt, vb, j0, T_len);
+      __syncthreads();
+      if (!act) continue;
+      // lane = key j of the block: l_j and dO.v_j
+      float l = 0.f, dov = 0.f;
+#pragma unroll 8
+      for (int e = 0; e < D; e += 4) {
+        const float4 q4 = *reinterpret_cast<const float4 *>(&sm.qs[w][e]);
+        const float4 o4 = *reinterpret_cast<const float4 *>(&sm.dos[w][e]);
+        const float2 k0 = *reinterpret_cast<const float2 *>(&sm.kt[lane][e]);
+        const float2 k1 = *reinterpret_cast<const float2 *>(&sm.kt[lane][e + 2]);
+        const float2 v0 = *reinterpret_cast<const float2 *>(&sm.vt[lane][e]);
+        const float2 v1 = *reinterpret_cast<const float2 *>(&sm.vt[lane][e + 2]);
+        l += q4.x * k0.x + q4.y * k0.y + q4.z * k1.x + q4.w * k1.y;
+        dov += o4.x * v0.x + o4.y * v0.y + o4.z * v1.x + o4.w * v1.y;
+      }
+      l *= tau;
+      float wj, cj;  // the key's weight and the value it is compared against
+      if (chunk) {
+        const float m = wave_max(l);
+        const float p = __expf(l - m);
+        const float lsum = wave_sum(p);
+        const float doo = wave_sum(p * dov) / lsum;
+        if (lane == 0) {
+          sm.sl_m[w][x] = m;
+          sm.sl_l[w][x] = lsum;
+          sm.sl_doo[w][x] = doo;
+        }
+        wj = p / lsum;
+        cj = doo;
+        // dq_hat terms: e^{s - Mc} dO.o_c k'_c and e^{s - Mc} k'_c
+        const float sw = __expf(sm.sl_s[w][x] - Mc);
+        const size_t so = (static_cast<size_t>(b) * Hq + h) * C + sm.sel[x];
+#pragma unroll
+        for (int u = 0; u < EPL; ++u) {
+          const float kp = Elem<T>::load(ksum, so * D + lane * EPL + u);
+          B1[u] += sw * doo * kp;
+          B2[u] += sw * kp;
+        }
+        sm.ew[w][lane] = wj * (dov - cj);
+      } else {
+        const int jj = j0 + lane;
+        const float lm = jj <= i ? l : -INFINITY;
+        const float mn = fmaxf(mw, wave_max(lm));
+        const float sc = mw == -INFINITY ? 0.f : __expf(mw - mn);
+        const float e = jj <= i ? __expf(lm - mn) : 0.f;
+        zw = zw * sc + wave_sum(e);
+        dw = dw * sc + wave_sum(e * dov);
+        mw = mn;
+#pragma unroll
+        for (int u = 0; u < EPL; ++u) {
+          A1[u] *= sc;
+          A2[u] *= sc;
+        }
+        sm.ew[w][lane] = e;
+        sm.dvw[w][lane] = dov;
+      }
+      // the wave's own LDS rows, written and read by its lanes (LDS
+      // operations of one wave complete in order: no wait needed)
+      __builtin_amdgcn_wave_barrier();
+      if (chunk) {
+        const float sw = __expf(sm.sl_s[w][x] - Mc);
+        float acc[EPL];
+#pragma unroll
+        for (int u = 0; u < EPL; ++u) acc[u] = 0.f;
+        for (int j = 0; j < kBK; ++j) {
+          const float c = sm.ew[w][j];
+#pragma unroll
+          for (int u = 0; u < EPL; ++u) acc[u] += c * sm.kt[j][lane * EPL + u];
+        }
+#pragma unroll
+        for (int u = 0; u < EPL; ++u) Bq[u] += sw * acc[u];
+      } else {
+        for (int j = 0; j < kBK; ++j) {
+          const float e = sm.ew[w][j], ed = e * sm.dvw[w][j];
+#pragma unroll
+          for (int u = 0; u < EPL; ++u) {
+            const float kv = sm.kt[j][lane * EPL + u];
+            A1[u] += ed * kv;
+            A2[u] += e * kv;
+          }
+        }
+      }
+    }
+    __syncthreads();
+    if (act) {
+      // ---- the joint normaliser, Delta, the list entries' values, dq
+      const float M = fmaxf(Mc, mw);
+      float z = zw * __expf(mw - M);
+      for (int x = 0; x < K; ++x)
+        if (sm.sel[x] >= 0) z += __expf(sm.sl_s[w][x] - M);
+      const float logZ = M + __logf(z);
+      float Delta = dw * __expf(mw - logZ);
+      for (int x = 0; x < K; ++x)
+        if (sm.sel[x] >= 0) Delta += __expf(sm.sl_s[w][x] - logZ) * sm.sl_doo[w][x];
+      if (lane == 0) {
+        a.logz[ro] = logZ;
+        a.delta[ro] = Delta;
+      }
+      for (int x = lane; x < K; x += 64) {
+        if (sm.sel[x] < 0) continue;
+        const int pos = a.inv_pos[(pg * T_len + i) * K + x];
+        const size_t eo = (pg * T_len * K + pos) * G + hh;
+        // w_c P_cj = e^{l_j + lw}: lw = s_hat - logZ - max - log(sum)
+        a.ent_lw[eo] = sm.sl_s[w][x] - logZ - sm.sl_m[w][x] - __logf(sm.sl_l[w][x]);
+        a.ent_doo[eo] = sm.sl_doo[w][x];
+        a.ent_ds[eo] = __expf(sm.sl_s[w][x] - logZ) * (sm.sl_doo[w][x] - Delta);
+      }
+      const float fc = Mc == -INFINITY ? 0.f : __expf(Mc - logZ), fw = __expf(mw - logZ);
+#pragma unroll
+      for (int u = 0; u < EPL; ++u) {
+        const float dqh = tau * fc * (B1[u] - Delta * B2[u]);
+        a.dq[ro * D + lane * EPL + u] = tau * (fc * Bq[u] + fw * (A1[u] - Delta * A2[u])) + dqh;
+        if (QCAL) a.dqhat[((static_cast<size_t>(b) * T_len + i) * Hq + h) * D + lane * EPL + u] = dqh;
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// ------------------------------------------------------------------ z
+// Per (b, g, chunk c) and head: z = sum over the chunk's list entries of
+// ds u_i (Q-Cal) and zb = sum ds, in list order.
+__global__ void __launch_bounds__(kBT) bwd_z_kernel(BwdArgs a) {
+  const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z, t = threadIdx.x;
+  const int G = a.Hq / a.Hkv, C = a.T / kBK, r = a.r, K = a.K;
+  const size_t pg = static_cast<size_t>(b) * a.Hkv + g;
+  const int e_lo = a.inv_choff[pg * (C + 1) + c], e_hi = a.inv_choff[pg * (C + 1) + c + 1];
+  const int32_t *list = a.inv_list + pg * static_cast<size_t>(a.T) * K;
+  const float *ds = a.ent_ds + pg * static_cast<size_t>(a.T) * K * G;
+  if (t < G) {
+    float acc = 0.f;
+    for (int e = e_lo; e < e_hi; ++e) acc += ds[static_cast<size_t>(e) * G + t];
+    a.zb[(static_cast<size_t>(b) * a.Hq + g * G + t) * C + c] = acc;
+  }
+  for (int x = t; x < G * r; x += kBT) {
+    const int hh = x / r, q = x % r;
+    float acc = 0.f;
+    for (int e = e_lo; e < e_hi; ++e) {
+      const int i = list[e] >> 5;
+      acc += ds[static_cast<size_t>(e) * G + hh] * a.u[(static_cast<size_t>(b) * a.T + i) * r + q];
+    }
+    a.zsum[((static_cast<size_t>(b) * a.Hq + g * G + hh) * C + c) * r + q] = acc;
+  }
+}
+
+// ------------------------------------------------------------------ keys (VALU)
+template <int D>
+struct KeySmem {
+  float kt[kBK][D + 1];                  // the block's keys (fp32)
+  float rq[kRowsPerBatch][D];            // a batch of rows: q and dO
+  float rdo[kRowsPerBatch][D];
+  float ra[kRowsPerBatch], rb[kRowsPerBatch], rds[kRowsPerBatch];
+  int ri[kRowsPerBatch], rh[kRowsPerBatch], rwin[kRowsPerBatch];
+  float dkp[kMaxBwdG][D];                // per head: tau sum ds q (the raw-q part of dk'_c)
+  bwd::SummaryScratch<D> ss;
+};
+
+template <typename T, int D>
+__global__ void __launch_bounds__(kBT)
 bwd_keys_kernel(BwdArgs a) {
-  __shared__ KeySmem<T, D> sm;
+  __shared__ KeySmem<D> sm;
   const int kb = blockIdx.x, g = blockIdx.y, b = blockIdx.z, t = threadIdx.x;
-  const int lane = t & 63, wv = t >> 6;
   const int T_len = a.T, K = a.K, Hq = a.Hq, Hkv = a.Hkv, W = a.W, C = T_len / kBK;
   const int G = Hq / Hkv;
   const float tau = a.tau;
@@ -400,7 +510,6 @@ bwd_keys_kernel(BwdArgs a) {
   const bool full_chunk = kb < C;
   if (full_chunk)
     for (int x = t; x < G * D; x += kBT) sm.dkp[x / D][x % D] = 0.f;
-  if (t < kMaxBwdG) sm.dbp[t] = 0.f;
   // the rows this block serves: every (i, h) whose window holds the block,
   // i in [j0, j0 + S + W - 2] with n_i S <= j0; then the chunk's entries
   const int iw_lo = j0, iw_hi = min(T_len - 1, j0 + kBK + W - 2);
@@ -412,36 +521,36 @@ bwd_keys_kernel(BwdArgs a) {
   }
   const int nrows = nwin + e_n * G;
   const int *list = a.inv_list + pg * static_cast<size_t>(T_len) * K;
+  const size_t ebase = pg * static_cast<size_t>(T_len) * K;
   for (int r0 = 0; r0 < nrows; r0 += kRowsPerBatch) {
     __syncthreads();
     // a batch of rows into LDS: row r -> (i, head) and its scalars
     if (t < kRowsPerBatch) {
       const int r = r0 + t;
-      int i = 0, hh = 0, win = -1, slot = 0;
+      int i = 0, hh = 0, win = -1;
       if (r < nwin) {
         i = iw_lo + r / G;
         hh = r % G;
         win = (eligible_chunks(i, W, kBK) * kBK <= j0) ? 1 : -1;  // the block lies in i's window
+        const size_t ro = (static_cast<size_t>(b) * Hq + g * G + hh) * T_len + i;
+        if (win == 1) {
+          sm.ra[t] = a.logz[ro];
+          sm.rb[t] = a.delta[ro];
+          sm.rds[t] = 0.f;
+        }
       } else if (r < nrows) {
-        const int en = list[e_lo + (r - nwin) / G];
-        i = en >> 5;
-        slot = en & 31;
+        const int e = e_lo + (r - nwin) / G;
+        i = list[e] >> 5;
         hh = (r - nwin) % G;
         win = 0;
+        const size_t eo = (ebase + e) * G + hh;
+        sm.ra[t] = a.ent_lw[eo];
+        sm.rb[t] = a.ent_doo[eo];
+        sm.rds[t] = a.ent_ds[eo];
       }
-      const size_t ro = (static_cast<size_t>(b) * Hq + g * G + hh) * T_len + i;
       sm.ri[t] = i;
       sm.rh[t] = hh;
       sm.rwin[t] = win;
-      if (win == 1) {
-        sm.ra[t] = a.logz[ro];
-        sm.rb[t] = a.delta[ro];
-        sm.rds[t] = 0.f;
-      } else if (win == 0) {
-        sm.ra[t] = a.slot_lw[ro * K + slot];
-        sm.rb[t] = a.slot_doo[ro * K + slot];
-        sm.rds[t] = a.slot_ds[ro * K + slot];
-      }
     }
     __syncthreads();
     for (int x = t; x < kRowsPerBatch * D; x += kBT) {
@@ -450,7 +559,6 @@ bwd_keys_kernel(BwdArgs a) {
       const size_t ro = (static_cast<size_t>(b) * Hq + g * G + sm.rh[r]) * T_len + sm.ri[r];
       sm.rq[r][e] = Elem<T>::load(static_cast<const T *>(a.q), ro * D + e);
       sm.rdo[r][e] = Elem<T>::load(static_cast<const T *>(a.d_o), ro * D + e);
-      if (sm.rwin[r] == 0) sm.rqh[r][e] = QCAL ? a.qhat[ro * D + e] : sm.rq[r][e];
     }
     __syncthreads();
     for (int r = 0; r < kRowsPerBatch; ++r) {
@@ -477,70 +585,16 @@ bwd_keys_kernel(BwdArgs a) {
         dv[u] += cv * sm.rdo[r][qd * QD + u];
         dk[u] += tau * dl * sm.rq[r][qd * QD + u];
       }
-      // the chunk's summary gradients: dk'_c += tau ds q_hat, db'_c += ds
-      // (threads of key slot hh keep head hh's sums)
+      // the raw-q part of the chunk's dk'_c: tau ds q (threads of key slot
+      // hh keep head hh's sums)
       if (win == 0 && j == sm.rh[r]) {
 #pragma unroll
-        for (int u = 0; u < QD; ++u) sm.dkp[j][qd * QD + u] += tau * sm.rds[r] * sm.rqh[r][qd * QD + u];
-        if (qd == 0) sm.dbp[j] += sm.rds[r];
+        for (int u = 0; u < QD; ++u) sm.dkp[j][qd * QD + u] += tau * sm.rds[r] * sm.rq[r][qd * QD + u];
       }
     }
   }
   __syncthreads();
-  // ---- the chunk summary (Eq. 8) of each head of the group
-  if (full_chunk) {
-    for (int hh = 0; hh < G; ++hh) {
-      const int h = g * G + hh;
-      const size_t so = (static_cast<size_t>(b) * Hq + h) * C + kb;
-      for (int x = t; x < D; x += kBT) sm.qlm[x] = Elem<T>::load(static_cast<const T *>(a.q_lm), so * D + x);
-      __syncthreads();
-      float l = 0.f;
-#pragma unroll
-      for (int u = 0; u < QD; ++u) l += sm.qlm[qd * QD + u] * kr[u];
-      l = tau * sum4(l);
-      // softmax over the 64 keys (4 lanes per key): block maximum and sum
-      float m = wave_max(l);
-      if (lane == 0) sm.red[wv][0] = m;
-      __syncthreads();
-      m = fmaxf(fmaxf(sm.red[0][0], sm.red[1][0]), fmaxf(sm.red[2][0], sm.red[3][0]));
-      __syncthreads();
-      const float ex = __expf(l - m);
-      float s = wave_sum(ex) * 0.25f;  // each key counted by its 4 lanes
-      float sl = wave_sum(ex * l) * 0.25f;
-      if (lane == 0) {
-        sm.red[wv][0] = s;
-        sm.red[wv][1] = sl;
-      }
-      __syncthreads();
-      const float z = sm.red[0][0] + sm.red[1][0] + sm.red[2][0] + sm.red[3][0];
-      const float El = (sm.red[0][1] + sm.red[1][1] + sm.red[2][1] + sm.red[3][1]) / z;
-      const float p = ex / z;
-      if (qd == 0) sm.pl[j] = p;
-      __syncthreads();
-      // k' (unrounded) = sum_j p_j k_j, a fixed key order per element
-      for (int e = t; e < D; e += kBT) {
-        float acc = 0.f;
-        for (int jk = 0; jk < kBK; ++jk) acc += sm.pl[jk] * sm.kt[jk][e];
-        sm.kp[e] = acc;
-      }
-      __syncthreads();
-      float proj = 0.f;
-#pragma unroll
-      for (int u = 0; u < QD; ++u) proj += sm.dkp[hh][qd * QD + u] * (kr[u] - sm.kp[qd * QD + u]);
-      proj = sum4(proj);
-      const float dl = p * (proj - sm.dbp[hh] * (l - El));
-#pragma unroll
-      for (int u = 0; u < QD; ++u) dk[u] += p * sm.dkp[hh][qd * QD + u] + tau * dl * sm.qlm[qd * QD + u];
-      if (qd == 0) sm.dlj[j] = dl;
-      __syncthreads();
-      for (int e = t; e < D; e += kBT) {
-        float acc = 0.f;
-        for (int jk = 0; jk < kBK; ++jk) acc += sm.dlj[jk] * sm.kt[jk][e];
-        a.dq_lm[so * D + e] = tau * acc;
-      }
-      __syncthreads();
-    }
-  }
+  if (full_chunk) bwd::summary_backward<T, D>(a, b, g, kb, sm.kt, kr, dk, sm.dkp, sm.ss);
   if (jj < T_len) {
 #pragma unroll
     for (int u = 0; u < QD; ++u) {
@@ -550,90 +604,27 @@ bwd_keys_kernel(BwdArgs a) {
   }
 }
 
-// ------------------------------------------------------------------ Q-Cal weights
-// du [B*T, r] = sum over heads of W_up[h D + e, :]^T dq_hat[b, h, i, e]:
-// one workgroup per token, each thread a slice of the H_q D rows with all r
-// sums in registers, then a fixed-order reduction over the threads.
-template <typename T>
-__global__ void __launch_bounds__(kBT)
-bwd_du_kernel(const T *__restrict__ w_up, const float *__restrict__ dqhat, float *__restrict__ du, int Hq, int T_len,
-              int D, int r) {
-  __shared__ float part[kBT / 64][64];
-  const int tok = blockIdx.x, t = threadIdx.x, lane = t & 63, wv = t >> 6;
-  const int b = tok / T_len, i = tok % T_len;
-  float acc[64];
-#pragma unroll
-  for (int a = 0; a < 64; ++a) acc[a] = 0.f;
-  for (int x = t; x < Hq * D; x += kBT) {
-    const int h = x / D, e = x % D;
-    const float g = dqhat[((static_cast<size_t>(b) * Hq + h) * T_len + i) * D + e];
-    const T *wr = w_up + static_cast<size_t>(x) * r;
-#pragma unroll
-    for (int a = 0; a < 64; ++a)
-      if (a < r) acc[a] += Elem<T>::load(wr, a) * g;
-  }
-#pragma unroll
-  for (int a = 0; a < 64; ++a) {
-    if (a < r) {
-      const float v = wave_sum(acc[a]);
-      if (lane == 0) part[wv][a] = v;
-    }
-  }
-  __syncthreads();
-  if (t < r) du[static_cast<size_t>(tok) * r + t] = part[0][t] + part[1][t] + part[2][t] + part[3][t];
-}
-
-// dW_up [Hq D, r]: entry (h D + e, a) = sum over tokens of dq_hat[b, h, i, e] u[b, i, a]
-__global__ void __launch_bounds__(kBT)
-bwd_dwup_kernel(const float *__restrict__ dqhat, const float *__restrict__ u, float *__restrict__ dwu, int B, int Hq,
-                int T_len, int D, int r) {
-  const int row = blockIdx.x * kBT + threadIdx.x, a = blockIdx.y;
-  if (row >= Hq * D) return;
-  const int h = row / D, e = row % D;
-  float acc = 0.f;
-  for (int b = 0; b < B; ++b)
-    for (int i = 0; i < T_len; ++i)
-      acc += dqhat[((static_cast<size_t>(b) * Hq + h) * T_len + i) * D + e] * u[(static_cast<size_t>(b) * T_len + i) * r + a];
-  dwu[static_cast<size_t>(row) * r + a] = acc;
-}
-
-// dW_down [r, Dh] = sum over tokens of du h;  dh [B*T, Dh] = du W_down
-template <typename T>
-__global__ void __launch_bounds__(kBT)
-bwd_dwdown_kernel(const float *__restrict__ du, const T *__restrict__ hin, float *__restrict__ dwd, int ntok, int r,
-                  int Dh) {
-  const int f = blockIdx.x * kBT + threadIdx.x, a = blockIdx.y;
-  if (f >= Dh) return;
-  float acc = 0.f;
-  for (int tok = 0; tok < ntok; ++tok) acc += du[static_cast<size_t>(tok) * r + a] * Elem<T>::load(hin, static_cast<size_t>(tok) * Dh + f);
-  dwd[static_cast<size_t>(a) * Dh + f] = acc;
-}
-
-template <typename T>
-__global__ void __launch_bounds__(kBT)
-bwd_dh_kernel(const float *__restrict__ du, const T *__restrict__ w_down, float *__restrict__ dh, int ntok, int r,
-              int Dh) {
-  const size_t x = blockIdx.x * static_cast<size_t>(kBT) + threadIdx.x;
-  if (x >= static_cast<size_t>(ntok) * Dh) return;
-  const size_t tok = x / Dh;
-  const int f = static_cast<int>(x % Dh);
-  float acc = 0.f;
-  for (int a = 0; a < r; ++a) acc += du[tok * r + a] * Elem<T>::load(w_down, static_cast<size_t>(a) * Dh + f);
-  dh[x] = acc;
-}
-
 // ------------------------------------------------------------------ launchers
 template <typename T, int D>
 static hipError_t bwd_t(const BwdArgs &a, hipStream_t st) {
   hipError_t e;
   const bool qcal = a.r > 0;
+  const int ntok = a.B * a.T, HD = a.Hq * D;
+  const T *h = static_cast<const T *>(a.h), *wd = static_cast<const T *>(a.w_down),
+          *wu = static_cast<const T *>(a.w_up);
   if (qcal) {
-    e = launch_qcal_down(a.h, a.w_down, a.u, a.B * a.T, a.r, a.Dh, a.bf16, st);
-    if (e != hipSuccess) return e;
-    const size_t total = static_cast<size_t>(a.B) * a.Hq * a.T * D;
-    bwd_qhat_kernel<T><<<static_cast<unsigned>((total + kBT - 1) / kBT < 65535 ? (total + kBT - 1) / kBT : 65535), kBT,
-                         0, st>>>(static_cast<const T *>(a.q), static_cast<const T *>(a.w_up), a.u, a.qhat, a.Hq,
-                                  a.T, D, a.r, total);
+    // u [ntok, r] = h [ntok, Dh] . W_down^T
+    if ((e = gemm<T, T>(h, a.Dh, 1, wd, 1, a.Dh, a.u, a.r, 1, ntok, a.r, a.Dh, st)) != hipSuccess) return e;
+    // q_hat = q + u . W_up^T   (stored [B, Hq, T, D])
+    if ((e = gemm<float, T, 1>(a.u, a.r, 1, wu, 1, a.r, a.qhat, 0, 0, ntok, HD, a.r, st, static_cast<const T *>(a.q),
+                               a.Hq, a.T, D)) != hipSuccess)
+      return e;
+  }
+  const int C = a.T / kBK, nqb = (a.T + kQBlk - 1) / kQBlk;
+  if (a.K > 0 && C > 0) {
+    bwd_inv_count_kernel<<<dim3(nqb, a.Hkv, a.B), kBT, 0, st>>>(a);
+    bwd_inv_scan_kernel<<<dim3(a.Hkv, a.B), kBT, 0, st>>>(a, nqb);
+    bwd_inv_fill_kernel<<<dim3(nqb, a.Hkv, a.B), kBT, 0, st>>>(a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   const dim3 rows(a.T, a.Hkv, a.B);
@@ -642,29 +633,27 @@ static hipError_t bwd_t(const BwdArgs &a, hipStream_t st) {
   else
     bwd_rows_kernel<T, D, false><<<rows, kBT, 0, st>>>(a);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  const int C = a.T / kBK, nqb = (a.T + kQBlk - 1) / kQBlk;
-  if (a.K > 0 && C > 0) {
-    bwd_inv_count_kernel<<<dim3(nqb, a.Hkv, a.B), kBT, 0, st>>>(a);
-    bwd_inv_scan_kernel<<<dim3(a.Hkv, a.B), kBT, 0, st>>>(a, nqb);
-    bwd_inv_fill_kernel<<<dim3(nqb, a.Hkv, a.B), kBT, 0, st>>>(a);
+  if (C > 0 && a.K > 0) {
+    bwd_z_kernel<<<dim3(C, a.Hkv, a.B), kBT, 0, st>>>(a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  const dim3 keys((a.T + kBK - 1) / kBK, a.Hkv, a.B);
-  if (qcal)
-    bwd_keys_kernel<T, D, true><<<keys, kBT, 0, st>>>(a);
-  else
-    bwd_keys_kernel<T, D, false><<<keys, kBT, 0, st>>>(a);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  if (qcal) {
-    const int ntok = a.B * a.T;
-    bwd_du_kernel<T><<<ntok, kBT, 0, st>>>(static_cast<const T *>(a.w_up), a.dqhat, a.du, a.Hq, a.T, D, a.r);
-    bwd_dwup_kernel<<<dim3((a.Hq * D + kBT - 1) / kBT, a.r), kBT, 0, st>>>(a.dqhat, a.u, a.dw_up, a.B, a.Hq, a.T, D, a.r);
-    bwd_dwdown_kernel<T><<<dim3((a.Dh + kBT - 1) / kBT, a.r), kBT, 0, st>>>(a.du, static_cast<const T *>(a.h),
-                                                                           a.dw_down, ntok, a.r, a.Dh);
-    const size_t nh = static_cast<size_t>(ntok) * a.Dh;
-    bwd_dh_kernel<T><<<static_cast<unsigned>((nh + kBT - 1) / kBT), kBT, 0, st>>>(
-        a.du, static_cast<const T *>(a.w_down), a.dh, ntok, a.r, a.Dh);
+  if (bwd_keys_mfma_supported(a)) {
+    if ((e = launch_bwd_keys_mfma(a, st)) != hipSuccess) return e;
+  } else {
+    bwd_keys_kernel<T, D><<<dim3((a.T + kBK - 1) / kBK, a.Hkv, a.B), kBT, 0, st>>>(a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  if (qcal) {
+    // du [ntok, r] = dq_hat [ntok, Hq D] . W_up
+    if ((e = gemm<float, T>(a.dqhat, HD, 1, wu, a.r, 1, a.du, a.r, 1, ntok, a.r, HD, st)) != hipSuccess) return e;
+    // dW_up [Hq D, r] = dq_hat^T . u
+    if ((e = gemm<float, float>(a.dqhat, 1, HD, a.u, a.r, 1, a.dw_up, a.r, 1, HD, a.r, ntok, st)) != hipSuccess)
+      return e;
+    // dW_down [r, Dh] = du^T . h
+    if ((e = gemm<float, T>(a.du, 1, a.r, h, a.Dh, 1, a.dw_down, a.Dh, 1, a.r, a.Dh, ntok, st)) != hipSuccess)
+      return e;
+    // dh [ntok, Dh] = du . W_down
+    if ((e = gemm<float, T>(a.du, a.r, 1, wd, a.Dh, 1, a.dh, a.Dh, 1, ntok, a.Dh, a.r, st)) != hipSuccess) return e;
   }
   return hipSuccess;
 }

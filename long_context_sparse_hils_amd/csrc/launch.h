@@ -92,12 +92,14 @@ struct BwdArgs {
   // outputs: dq [B,Hq,T,d], dk / dv [B,Hkv,T,d], dq_lm [B,Hq,C,d],
   // dh [B*T,Dh], dw_down [r,Dh], dw_up [Hq*d,r]
   float *dq, *dk, *dv, *dq_lm, *dh, *dw_down, *dw_up;
-  // workspace: u / du [B*T,r]; qhat / dqhat [B,Hq,T,d]; logz / delta
-  // [B,Hq,T]; slot_lw / slot_doo / slot_ds [B,Hq,T,K]
-  float *u, *du, *qhat, *dqhat, *logz, *delta, *slot_lw, *slot_doo, *slot_ds;
+  // workspace: u / du [B*T,r]; qhat [B,Hq,T,d]; dqhat [B,T,Hq,d] (token
+  // major); logz / delta [B,Hq,T]; per selection-list entry and head
+  // ent_lw / ent_doo / ent_ds [B,Hkv,T*K,G]; zsum [B,Hq,C,r], zb [B,Hq,C]
+  float *u, *du, *qhat, *dqhat, *logz, *delta, *ent_lw, *ent_doo, *ent_ds, *zsum, *zb;
   // inverse selection lists: inv_cnt / inv_qboff [B,Hkv,nqb,C],
-  // inv_choff [B,Hkv,C+1], inv_list [B,Hkv,T*K]
-  int32_t *inv_cnt, *inv_qboff, *inv_choff, *inv_list;
+  // inv_choff [B,Hkv,C+1], inv_list [B,Hkv,T*K] (query << 5 | slot),
+  // inv_pos [B,Hkv,T,K] (each slot's place in its list, -1: none)
+  int32_t *inv_cnt, *inv_qboff, *inv_choff, *inv_list, *inv_pos;
   int B, T, Hq, Hkv, d, K, W, r, Dh;
   float tau;
   bool bf16;
@@ -105,10 +107,9 @@ struct BwdArgs {
 
 hipError_t launch_summary(const SummaryArgs &a, hipStream_t st);
 hipError_t launch_score_valu(const ScoreArgs &a, hipStream_t st);
-// u [Ntok, r] fp32 = h W_down^T (Q-Cal down projection), r <= 64
-hipError_t launch_qcal_down(const void *h, const void *w_down, float *u, int Ntok, int r, int Dh, bool bf16,
-                            hipStream_t st);
 hipError_t launch_backward(const BwdArgs &a, hipStream_t st);
+bool bwd_keys_mfma_supported(const BwdArgs &a);
+hipError_t launch_bwd_keys_mfma(const BwdArgs &a, hipStream_t st);
 bool score_mfma_supported(const ScoreArgs &a);
 size_t score_mfma_ws_bytes(int B, int T, int Hq, int C, int r);
 hipError_t launch_score_mfma(const ScoreArgs &a, hipStream_t st);

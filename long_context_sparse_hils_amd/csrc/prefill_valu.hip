@@ -212,18 +212,6 @@ static hipError_t score_valu_t(const ScoreArgs &a, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_qcal_down(const void *h, const void *w_down, float *u, int Ntok, int r, int Dh, bool bf16,
-                            hipStream_t st) {
-  const dim3 g1((Ntok + kQcalTok - 1) / kQcalTok);
-  if (bf16)
-    qcal_down_kernel<uint16_t><<<g1, 256, 0, st>>>(static_cast<const uint16_t *>(h),
-                                                   static_cast<const uint16_t *>(w_down), u, Ntok, r, Dh);
-  else
-    qcal_down_kernel<float><<<g1, 256, 0, st>>>(static_cast<const float *>(h), static_cast<const float *>(w_down), u,
-                                                Ntok, r, Dh);
-  return hipGetLastError();
-}
-
 hipError_t launch_score_valu(const ScoreArgs &a, hipStream_t st) {
   if (a.bf16) return a.d == 128 ? score_valu_t<uint16_t, 128>(a, st) : score_valu_t<uint16_t, 64>(a, st);
   return a.d == 128 ? score_valu_t<float, 128>(a, st) : score_valu_t<float, 64>(a, st);

@@ -3,11 +3,13 @@ float64 oracle's backward, on seeded inputs.
 
 Both sides take the same selection and the same stored summaries, which come
 from the oracle (its forward over the seeded inputs), and the same seeded
-upstream gradient dO.  The gradients are float32 on the GPU in both storage
-modes (every product and sum in fp32 from the stored bf16 or fp32 inputs), so
-one tolerance serves both: |gpu - oracle| <= 1e-4 (max|ref| + |ref|) per
-tensor, the fp32-mode output bound applied to the tensor's own scale.  Sums
-run in a fixed order: a second call gives the same bits."""
+upstream gradient dO.  The gradients are float32.  In fp32 mode every product
+and sum is fp32: |gpu - oracle| <= 1e-4 (max|ref| + |ref|) per tensor, the
+fp32-mode output bound applied to the tensor's own scale.  In bf16 mode the
+key-major products run on the matrix cores with the weights P and their
+gradients dS rounded to bf16 as MFMA operands (as the forward rounds P for
+its P.V product), so the bound is the bf16-mode output bound, 1e-2 on the
+same scale.  Sums run in a fixed order: a second call gives the same bits."""
 import math
 import os
 import sys
@@ -27,7 +29,7 @@ import long_context_sparse_hils_amd as hils  # noqa: E402
 import oracle  # noqa: E402
 from _gpu import dev, empty, host  # noqa: E402
 
-TOL = 1e-4
+TOL = {"f32": 1e-4, "bf16": 1e-2}
 
 
 def wl(B=1, T=1024, Hq=4, Hkv=2, d=128, K=8, W=256, r=0, Dh=0, dtype="bf16", std=1.0, needles="none"):
@@ -46,6 +48,10 @@ CASES = {
     "f32_g3_qcal": wl(T=768, Hq=6, Hkv=2, d=128, K=5, W=200, r=8, Dh=64, dtype="f32"),
     # group of 8: two passes of four heads in the row kernel
     "bf16_g8_d64": wl(T=1024, Hq=8, Hkv=1, d=64, K=8, W=128),
+    # the largest group (MFMA key pass, 16 heads per summary product)
+    "bf16_g16": wl(T=640, Hq=16, Hkv=1, d=128, K=4, W=128),
+    # bf16 with a group of 3: the VALU key pass, and Q-Cal
+    "bf16_g3_valu_keys": wl(T=768, Hq=6, Hkv=2, d=64, K=5, W=200, r=8, Dh=64),
     # window only
     "bf16_k0": wl(T=640, Hq=4, Hkv=2, d=64, K=0, W=192),
     # every query inside the window: no chunk is eligible
@@ -81,15 +87,20 @@ def gpu_backward(c, d, ks, bs, idx, dout):
     return out
 
 
-def _compare(name, gpu, ref):
+def _compare(name, gpu, ref, tol):
+    """Returns the failure (or None), after printing the tensor's errors."""
     gpu = gpu.astype(np.float64)
     scale = float(np.abs(ref).max())
     err = np.abs(gpu - ref)
     worst = float((err / (scale + np.abs(ref) + 1e-30)).max()) if ref.size else 0.0
-    print(f"  {name}: max|ref| {scale:.3e}  max|d| {float(err.max()) if err.size else 0:.3e}  "
+    where = np.unravel_index(int(np.argmax(err)), err.shape) if err.size else ()
+    print(f"  {name}: max|ref| {scale:.3e}  max|d| {float(err.max()) if err.size else 0:.3e} at {where}  "
           f"worst d/(max|ref|+|ref|) {worst:.2e}")
-    assert np.isfinite(gpu).all(), name
-    assert (err <= TOL * (scale + np.abs(ref))).all(), (name, worst)
+    if not np.isfinite(gpu).all():
+        return (name, "not finite")
+    if not (err <= tol * (scale + np.abs(ref))).all():
+        return (name, worst)
+    return None
 
 
 @pytest.mark.parametrize("name", list(CASES))
@@ -104,9 +115,13 @@ def test_backward_parity(name):
     torch.cuda.synchronize()
     ref = oracle.backward(oc, inp, idx, ks, bs, dout)
     print(f"{name}: selected entries {(idx >= 0).sum()}")
+    bad = []
     for k in ("dq", "dk", "dv", "dq_lm", "dh", "dw_down", "dw_up"):
         if g1.get(k) is None:
             continue
         a, b = host(g1[k]), host(g2[k])
         assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), f"{k} differs between two calls"
-        _compare(k, a, ref[k])
+        f = _compare(k, a, ref[k], TOL[w.dtype])
+        if f:
+            bad.append(f)
+    assert not bad, bad
