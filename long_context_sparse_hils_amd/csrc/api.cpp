@@ -303,7 +303,7 @@ hils_status hils_sparse_attn_prefill(const hils_config *cfg, const void *q, cons
 namespace {
 
 struct BwdGeom {
-  size_t off_u, off_du, off_qhat, off_dqhat, off_logz, off_delta, off_lw, off_doo, off_ds, off_z, off_zb;
+  size_t off_u, off_du, off_qhat, off_dqhat, off_logz, off_delta, off_lw, off_doo, off_ds, off_z, off_zb, off_gpart;
   size_t off_cnt, off_qboff, off_choff, off_list, off_pos, total;
 };
 
@@ -328,6 +328,10 @@ BwdGeom bwd_geom(const hils_config *c) {
   g.off_ds = take(sizeof(float) * B * Hq * T * K);
   g.off_z = take(sizeof(float) * B * Hq * C * r);
   g.off_zb = take(sizeof(float) * B * Hq * C);
+  const size_t Dh = c->qcal_rank ? c->hidden_dim : 0;
+  size_t gp = hils::kBwdSplitW * (Hq * d * r > r * Dh ? Hq * d * r : r * Dh);
+  if (hils::kBwdSplitDu * B * T * r > gp) gp = hils::kBwdSplitDu * B * T * r;
+  g.off_gpart = take(sizeof(float) * gp);
   g.off_cnt = take(sizeof(int32_t) * B * Hkv * nqb * C);
   g.off_qboff = take(sizeof(int32_t) * B * Hkv * nqb * C);
   g.off_choff = take(sizeof(int32_t) * B * Hkv * (C + 1));
@@ -401,7 +405,7 @@ hils_status hils_sparse_attn_backward(const hils_config *cfg, const void *q, con
   a.u = f(g.off_u); a.du = f(g.off_du); a.qhat = f(g.off_qhat); a.dqhat = f(g.off_dqhat);
   a.logz = f(g.off_logz); a.delta = f(g.off_delta);
   a.ent_lw = f(g.off_lw); a.ent_doo = f(g.off_doo); a.ent_ds = f(g.off_ds);
-  a.zsum = f(g.off_z); a.zb = f(g.off_zb);
+  a.zsum = f(g.off_z); a.zb = f(g.off_zb); a.gpart = f(g.off_gpart);
   a.inv_cnt = n(g.off_cnt); a.inv_qboff = n(g.off_qboff); a.inv_choff = n(g.off_choff); a.inv_list = n(g.off_list);
   a.inv_pos = n(g.off_pos);
   a.B = cfg->batch; a.T = cfg->seq_len; a.Hq = cfg->n_q_heads; a.Hkv = cfg->n_kv_heads; a.d = cfg->head_dim;

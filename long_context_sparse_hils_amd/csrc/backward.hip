@@ -57,24 +57,74 @@ namespace {
 
 constexpr int kRowsPerBatch = 8;
 
-// Rows j0 .. j0 + 63 of a [T, D] matrix into an fp32 LDS tile with rows
-// D + 2 floats apart (8-byte aligned pairs; lane j of a wave reading row j
-// meets bank 2 j + const); rows past T are zero.  Pieces of 8 elements.
+// A 64-row key or value tile of the row kernel in LDS, in the storage type:
+// bf16 rows D + 4 elements apart (8-byte aligned groups of 4), fp32 rows
+// D + 2 apart (8-byte aligned pairs); lane j of a wave reading row j meets
+// bank 2 j + const.  Rows past T are zero.
 template <typename T, int D>
-__device__ __forceinline__ void stage_tile(float (*tl)[D + 2], const T *src, int j0, int T_len) {
-  for (int p = threadIdx.x; p < kBK * D / 8; p += kBT) {
-    const int r = p / (D / 8), s = p % (D / 8);
-    float e[8];
-    if (j0 + r < T_len) {
-      Elem<T>::load8(src + static_cast<size_t>(j0 + r) * D + s * 8, e);
-    } else {
-#pragma unroll
-      for (int x = 0; x < 8; ++x) e[x] = 0.f;
+struct RowTile;
+
+template <int D>
+struct RowTile<uint16_t, D> {
+  uint16_t x[kBK][D + 4];
+  __device__ __forceinline__ void stage(const uint16_t *src, int j0, int T_len) {
+    for (int p = threadIdx.x; p < kBK * D / 8; p += kBT) {
+      const int r = p / (D / 8), s = p % (D / 8);
+      uint4 u = make_uint4(0u, 0u, 0u, 0u);
+      if (j0 + r < T_len) u = *reinterpret_cast<const uint4 *>(src + static_cast<size_t>(j0 + r) * D + s * 8);
+      *reinterpret_cast<uint2 *>(&x[r][s * 8]) = make_uint2(u.x, u.y);
+      *reinterpret_cast<uint2 *>(&x[r][s * 8 + 4]) = make_uint2(u.z, u.w);
     }
-#pragma unroll
-    for (int x = 0; x < 8; x += 2) *reinterpret_cast<float2 *>(&tl[r][s * 8 + x]) = make_float2(e[x], e[x + 1]);
   }
-}
+  // elements e .. e + 3 of row j (e a multiple of 4)
+  __device__ __forceinline__ void load4(int j, int e, float *o) const {
+    const uint2 w = *reinterpret_cast<const uint2 *>(&x[j][e]);
+    o[0] = __uint_as_float(w.x << 16);
+    o[1] = __uint_as_float(w.x & 0xFFFF0000u);
+    o[2] = __uint_as_float(w.y << 16);
+    o[3] = __uint_as_float(w.y & 0xFFFF0000u);
+  }
+  // elements e .. e + N - 1 of row j (N = 1 or 2, e a multiple of N)
+  template <int N>
+  __device__ __forceinline__ void loadn(int j, int e, float *o) const {
+    if (N == 2) {
+      const uint32_t w = *reinterpret_cast<const uint32_t *>(&x[j][e]);
+      o[0] = __uint_as_float(w << 16);
+      o[N - 1] = __uint_as_float(w & 0xFFFF0000u);
+    } else {
+      o[0] = bf16_to_f32(x[j][e]);
+    }
+  }
+};
+
+template <int D>
+struct RowTile<float, D> {
+  float x[kBK][D + 2];
+  __device__ __forceinline__ void stage(const float *src, int j0, int T_len) {
+    for (int p = threadIdx.x; p < kBK * D / 4; p += kBT) {
+      const int r = p / (D / 4), s = p % (D / 4);
+      float4 u = make_float4(0.f, 0.f, 0.f, 0.f);
+      if (j0 + r < T_len) u = *reinterpret_cast<const float4 *>(src + static_cast<size_t>(j0 + r) * D + s * 4);
+      *reinterpret_cast<float2 *>(&x[r][s * 4]) = make_float2(u.x, u.y);
+      *reinterpret_cast<float2 *>(&x[r][s * 4 + 2]) = make_float2(u.z, u.w);
+    }
+  }
+  __device__ __forceinline__ void load4(int j, int e, float *o) const {
+    const float2 a = *reinterpret_cast<const float2 *>(&x[j][e]);
+    const float2 b = *reinterpret_cast<const float2 *>(&x[j][e + 2]);
+    o[0] = a.x; o[1] = a.y; o[2] = b.x; o[3] = b.y;
+  }
+  template <int N>
+  __device__ __forceinline__ void loadn(int j, int e, float *o) const {
+    if (N == 2) {
+      const float2 a = *reinterpret_cast<const float2 *>(&x[j][e]);
+      o[0] = a.x;
+      o[N - 1] = a.y;
+    } else {
+      o[0] = x[j][e];
+    }
+  }
+};
 
 }  // namespace
 
@@ -84,23 +134,32 @@ __device__ __forceinline__ void stage_tile(float (*tl)[D + 2], const T *src, int
 // order.  64 x 64 output tiles per 256-thread workgroup (4 x 4 per thread),
 // k in slabs of 16 staged in LDS.  MODE 0 stores C[m lcm + n lcn]; MODE 1 is
 // the Q-Cal q_hat: m = token b T + i, n = h D + e, and the tile adds
-// q[b, h, i, e] and stores q_hat in the same [B, Hq, T, D] layout.
+// q[b, h, i, e] and stores q_hat in the same [B, Hq, T, D] layout.  With
+// gridDim.z > 1 workgroup z takes the k range [z kc, z kc + kc) and stores
+// its partial sums at Cm + z M N, row-major (MODE 0); gemm_reduce_kernel
+// then adds the partials in z order.
 template <typename TA, typename TB, int MODE>
 __global__ void __launch_bounds__(256)
 bwd_gemm_kernel(const TA *__restrict__ A, long lam, long lak, const TB *__restrict__ Bm, long lbk, long lbn,
-                float *__restrict__ Cm, long lcm, long lcn, int M, int N, int Kd, const TB *__restrict__ qadd, int Hq,
-                int T_len, int D) {
+                float *__restrict__ Cm, long lcm, long lcn, int M, int N, int Kd, int kc, const TB *__restrict__ qadd,
+                int Hq, int T_len, int D) {
   __shared__ float As[16][64 + 4];
   __shared__ float Bs[16][64 + 4];
   const int t = threadIdx.x, tm = t >> 4, tn = t & 15;
   const int m0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
+  const int kbeg = blockIdx.z * kc, kend = min(Kd, kbeg + kc);
+  if (gridDim.z > 1) {
+    Cm += static_cast<size_t>(blockIdx.z) * M * N;
+    lcm = N;
+    lcn = 1;
+  }
   const bool a_kfast = lak == 1, b_nfast = lbn == 1;
   float acc[4][4];
 #pragma unroll
   for (int x = 0; x < 4; ++x)
 #pragma unroll
     for (int y = 0; y < 4; ++y) acc[x][y] = 0.f;
-  for (int k0 = 0; k0 < Kd; k0 += 16) {
+  for (int k0 = kbeg; k0 < kend; k0 += 16) {
     float av[4], bv[4];
     int am[4], ak[4], bk[4], bn[4];
 #pragma unroll
@@ -111,9 +170,9 @@ bwd_gemm_kernel(const TA *__restrict__ A, long lam, long lak, const TB *__restri
       bk[j] = b_nfast ? x / 64 : x % 16;
       bn[j] = b_nfast ? x % 64 : x / 16;
       const int gm = m0 + am[j], gk = k0 + ak[j];
-      av[j] = (gm < M && gk < Kd) ? Elem<TA>::load(A, gm * lam + gk * lak) : 0.f;
+      av[j] = (gm < M && gk < kend) ? Elem<TA>::load(A, gm * lam + gk * lak) : 0.f;
       const int gk2 = k0 + bk[j], gn = n0 + bn[j];
-      bv[j] = (gk2 < Kd && gn < N) ? Elem<TB>::load(Bm, gk2 * lbk + gn * lbn) : 0.f;
+      bv[j] = (gk2 < kend && gn < N) ? Elem<TB>::load(Bm, gk2 * lbk + gn * lbn) : 0.f;
     }
     __syncthreads();  // the previous slab is no longer read
 #pragma unroll
@@ -152,13 +211,31 @@ bwd_gemm_kernel(const TA *__restrict__ A, long lam, long lak, const TB *__restri
   }
 }
 
+__global__ void __launch_bounds__(256)
+gemm_reduce_kernel(const float *__restrict__ part, int nsplit, float *__restrict__ Cm, long lcm, long lcn, int M, int N) {
+  const size_t x = blockIdx.x * static_cast<size_t>(256) + threadIdx.x, MN = static_cast<size_t>(M) * N;
+  if (x >= MN) return;
+  float acc = 0.f;
+  for (int z = 0; z < nsplit; ++z) acc += part[z * MN + x];
+  const int m = static_cast<int>(x / N), n = static_cast<int>(x % N);
+  Cm[m * lcm + n * lcn] = acc;
+}
+
+// nsplit > 1 splits k over nsplit workgroups per tile, through part
+// (nsplit M N floats), then sums the partials in a fixed order.
 template <typename TA, typename TB, int MODE = 0>
 static hipError_t gemm(const TA *A, long lam, long lak, const TB *Bm, long lbk, long lbn, float *Cm, long lcm, long lcn,
-                       int M, int N, int Kd, hipStream_t st, const TB *qadd = nullptr, int Hq = 0, int T_len = 1,
-                       int D = 1) {
-  const dim3 grid((N + 63) / 64, (M + 63) / 64);
-  bwd_gemm_kernel<TA, TB, MODE><<<grid, 256, 0, st>>>(A, lam, lak, Bm, lbk, lbn, Cm, lcm, lcn, M, N, Kd, qadd, Hq,
-                                                      T_len, D);
+                       int M, int N, int Kd, hipStream_t st, int nsplit = 1, float *part = nullptr,
+                       const TB *qadd = nullptr, int Hq = 0, int T_len = 1, int D = 1) {
+  const int kc = ((Kd + nsplit - 1) / nsplit + 15) / 16 * 16;
+  nsplit = kc > 0 ? (Kd + kc - 1) / kc : 1;
+  const dim3 grid((N + 63) / 64, (M + 63) / 64, nsplit);
+  bwd_gemm_kernel<TA, TB, MODE><<<grid, 256, 0, st>>>(A, lam, lak, Bm, lbk, lbn, nsplit > 1 ? part : Cm, lcm, lcn,
+                                                      M, N, Kd, kc, qadd, Hq, T_len, D);
+  if (nsplit > 1) {
+    const size_t MN = static_cast<size_t>(M) * N;
+    gemm_reduce_kernel<<<static_cast<unsigned>((MN + 255) / 256), 256, 0, st>>>(part, nsplit, Cm, lcm, lcn, M, N);
+  }
   return hipGetLastError();
 }
 
@@ -250,9 +327,9 @@ __global__ void __launch_bounds__(kBT) bwd_inv_fill_kernel(BwdArgs a) {
 }
 
 // ------------------------------------------------------------------ rows
-template <int D>
+template <typename T, int D>
 struct RowSmem {
-  float kt[kBK][D + 2], vt[kBK][D + 2];
+  RowTile<T, D> kt, vt;
   float qs[4][D], qhs[4][D], dos[4][D];
   float ew[4][kBK], dvw[4][kBK];      // per head: the block's weights and dO.v_j
   float sl_m[4][32], sl_l[4][32];     // per selected chunk: max and sum of e^{l - max}
@@ -273,7 +350,7 @@ struct RowSmem {
 template <typename T, int D, bool QCAL>
 __global__ void __launch_bounds__(kBT)
 bwd_rows_kernel(BwdArgs a) {
-  __shared__ RowSmem<D> sm;
+  __shared__ RowSmem<T, D> sm;
   const int i = blockIdx.x, g = blockIdx.y, b = blockIdx.z, t = threadIdx.x;
   const int lane = t & 63, w = t >> 6;
   const int T_len = a.T, K = a.K, Hq = a.Hq, Hkv = a.Hkv, C = T_len / kBK;
@@ -325,22 +402,21 @@ bwd_rows_kernel(BwdArgs a) {
       if (chunk && sm.sel[x] < 0) continue;  // uniform across the workgroup
       const int j0 = chunk ? sm.sel[x] * kBK : w_lo + (x - K) * kBK;
       __syncthreads();  // the previous block's tiles are no longer read
-      stage_tile<T, D>(sm.kt, kb, j0, T_len);
-      stage_tile<T, D>(sm.vt, vb, j0, T_len);
+      sm.kt.stage(kb, j0, T_len);
+      sm.vt.stage(vb, j0, T_len);
       __syncthreads();
       if (!act) continue;
       // lane = key j of the block: l_j and dO.v_j
       float l = 0.f, dov = 0.f;
-#pragma unroll 8
+#pragma unroll 4
       for (int e = 0; e < D; e += 4) {
         const float4 q4 = *reinterpret_cast<const float4 *>(&sm.qs[w][e]);
         const float4 o4 = *reinterpret_cast<const float4 *>(&sm.dos[w][e]);
-        const float2 k0 = *reinterpret_cast<const float2 *>(&sm.kt[lane][e]);
-        const float2 k1 = *reinterpret_cast<const float2 *>(&sm.kt[lane][e + 2]);
-        const float2 v0 = *reinterpret_cast<const float2 *>(&sm.vt[lane][e]);
-        const float2 v1 = *reinterpret_cast<const float2 *>(&sm.vt[lane][e + 2]);
-        l += q4.x * k0.x + q4.y * k0.y + q4.z * k1.x + q4.w * k1.y;
-        dov += o4.x * v0.x + o4.y * v0.y + o4.z * v1.x + o4.w * v1.y;
+        float k4[4], v4[4];
+        sm.kt.load4(lane, e, k4);
+        sm.vt.load4(lane, e, v4);
+        l += q4.x * k4[0] + q4.y * k4[1] + q4.z * k4[2] + q4.w * k4[3];
+        dov += o4.x * v4[0] + o4.y * v4[1] + o4.z * v4[2] + o4.w * v4[3];
       }
       l *= tau;
       float wj, cj;  // the key's weight and the value it is compared against
@@ -393,19 +469,22 @@ bwd_rows_kernel(BwdArgs a) {
         for (int u = 0; u < EPL; ++u) acc[u] = 0.f;
         for (int j = 0; j < kBK; ++j) {
           const float c = sm.ew[w][j];
+          float kv[EPL];
+          sm.kt.template loadn<EPL>(j, lane * EPL, kv);
 #pragma unroll
-          for (int u = 0; u < EPL; ++u) acc[u] += c * sm.kt[j][lane * EPL + u];
+          for (int u = 0; u < EPL; ++u) acc[u] += c * kv[u];
         }
 #pragma unroll
         for (int u = 0; u < EPL; ++u) Bq[u] += sw * acc[u];
       } else {
         for (int j = 0; j < kBK; ++j) {
           const float e = sm.ew[w][j], ed = e * sm.dvw[w][j];
+          float kv[EPL];
+          sm.kt.template loadn<EPL>(j, lane * EPL, kv);
 #pragma unroll
           for (int u = 0; u < EPL; ++u) {
-            const float kv = sm.kt[j][lane * EPL + u];
-            A1[u] += ed * kv;
-            A2[u] += e * kv;
+            A1[u] += ed * kv[u];
+            A2[u] += e * kv[u];
           }
         }
       }
@@ -448,27 +527,52 @@ bwd_rows_kernel(BwdArgs a) {
 
 // ------------------------------------------------------------------ z
 // Per (b, g, chunk c) and head: z = sum over the chunk's list entries of
-// ds u_i (Q-Cal) and zb = sum ds, in list order.
+// ds u_i (Q-Cal) and zb = sum ds.  Thread (part, q) sums the entries
+// e = e_lo + part + P m (P = 256 / r parts, all G heads in registers); the
+// parts are then added in part order.
 __global__ void __launch_bounds__(kBT) bwd_z_kernel(BwdArgs a) {
+  __shared__ float red[kBT][kMaxBwdG + 1];
   const int c = blockIdx.x, g = blockIdx.y, b = blockIdx.z, t = threadIdx.x;
-  const int G = a.Hq / a.Hkv, C = a.T / kBK, r = a.r, K = a.K;
+  const int G = a.Hq / a.Hkv, C = a.T / kBK, K = a.K;
+  const int r = a.r > 0 ? a.r : 1;  // with r = 0 the single column sums ds only
   const size_t pg = static_cast<size_t>(b) * a.Hkv + g;
   const int e_lo = a.inv_choff[pg * (C + 1) + c], e_hi = a.inv_choff[pg * (C + 1) + c + 1];
   const int32_t *list = a.inv_list + pg * static_cast<size_t>(a.T) * K;
   const float *ds = a.ent_ds + pg * static_cast<size_t>(a.T) * K * G;
-  if (t < G) {
-    float acc = 0.f;
-    for (int e = e_lo; e < e_hi; ++e) acc += ds[static_cast<size_t>(e) * G + t];
-    a.zb[(static_cast<size_t>(b) * a.Hq + g * G + t) * C + c] = acc;
-  }
-  for (int x = t; x < G * r; x += kBT) {
-    const int hh = x / r, q = x % r;
-    float acc = 0.f;
-    for (int e = e_lo; e < e_hi; ++e) {
-      const int i = list[e] >> 5;
-      acc += ds[static_cast<size_t>(e) * G + hh] * a.u[(static_cast<size_t>(b) * a.T + i) * r + q];
+  const int P = kBT / r, part = t / r, q = t % r;
+  float acc[kMaxBwdG], accb[kMaxBwdG];
+#pragma unroll
+  for (int hh = 0; hh < kMaxBwdG; ++hh) acc[hh] = accb[hh] = 0.f;
+  if (part < P) {
+    for (int e = e_lo + part; e < e_hi; e += P) {
+      const float uq = a.r > 0 ? a.u[(static_cast<size_t>(b) * a.T + (list[e] >> 5)) * a.r + q] : 0.f;
+#pragma unroll
+      for (int hh = 0; hh < kMaxBwdG; ++hh) {
+        if (hh < G) {
+          const float d = ds[static_cast<size_t>(e) * G + hh];
+          acc[hh] += d * uq;
+          accb[hh] += d;
+        }
+      }
     }
-    a.zsum[((static_cast<size_t>(b) * a.Hq + g * G + hh) * C + c) * r + q] = acc;
+  }
+#pragma unroll
+  for (int hh = 0; hh < kMaxBwdG; ++hh) red[t][hh] = acc[hh];
+  __syncthreads();
+  if (a.r > 0 && t < a.r * G) {
+    const int hh = t / a.r, qq = t % a.r;
+    float s = 0.f;
+    for (int p2 = 0; p2 < P; ++p2) s += red[p2 * r + qq][hh];
+    a.zsum[((static_cast<size_t>(b) * a.Hq + g * G + hh) * C + c) * a.r + qq] = s;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int hh = 0; hh < kMaxBwdG; ++hh) red[t][hh] = accb[hh];
+  __syncthreads();
+  if (t < G) {  // column q = 0 of each part holds its ds sums
+    float s = 0.f;
+    for (int p2 = 0; p2 < P; ++p2) s += red[p2 * r][t];
+    a.zb[(static_cast<size_t>(b) * a.Hq + g * G + t) * C + c] = s;
   }
 }
 
@@ -614,10 +718,12 @@ static hipError_t bwd_t(const BwdArgs &a, hipStream_t st) {
           *wu = static_cast<const T *>(a.w_up);
   if (qcal) {
     // u [ntok, r] = h [ntok, Dh] . W_down^T
-    if ((e = gemm<T, T>(h, a.Dh, 1, wd, 1, a.Dh, a.u, a.r, 1, ntok, a.r, a.Dh, st)) != hipSuccess) return e;
+    if ((e = gemm<T, T>(h, a.Dh, 1, wd, 1, a.Dh, a.u, a.r, 1, ntok, a.r, a.Dh, st, kBwdSplitDu, a.gpart)) !=
+        hipSuccess)
+      return e;
     // q_hat = q + u . W_up^T   (stored [B, Hq, T, D])
-    if ((e = gemm<float, T, 1>(a.u, a.r, 1, wu, 1, a.r, a.qhat, 0, 0, ntok, HD, a.r, st, static_cast<const T *>(a.q),
-                               a.Hq, a.T, D)) != hipSuccess)
+    if ((e = gemm<float, T, 1>(a.u, a.r, 1, wu, 1, a.r, a.qhat, 0, 0, ntok, HD, a.r, st, 1, nullptr,
+                               static_cast<const T *>(a.q), a.Hq, a.T, D)) != hipSuccess)
       return e;
   }
   const int C = a.T / kBK, nqb = (a.T + kQBlk - 1) / kQBlk;
@@ -645,12 +751,16 @@ static hipError_t bwd_t(const BwdArgs &a, hipStream_t st) {
   }
   if (qcal) {
     // du [ntok, r] = dq_hat [ntok, Hq D] . W_up
-    if ((e = gemm<float, T>(a.dqhat, HD, 1, wu, a.r, 1, a.du, a.r, 1, ntok, a.r, HD, st)) != hipSuccess) return e;
-    // dW_up [Hq D, r] = dq_hat^T . u
-    if ((e = gemm<float, float>(a.dqhat, 1, HD, a.u, a.r, 1, a.dw_up, a.r, 1, HD, a.r, ntok, st)) != hipSuccess)
+    if ((e = gemm<float, T>(a.dqhat, HD, 1, wu, a.r, 1, a.du, a.r, 1, ntok, a.r, HD, st, kBwdSplitDu, a.gpart)) !=
+        hipSuccess)
+      return e;
+    // dW_up [Hq D, r] = dq_hat^T . u      (long k = tokens: split)
+    if ((e = gemm<float, float>(a.dqhat, 1, HD, a.u, a.r, 1, a.dw_up, a.r, 1, HD, a.r, ntok, st, kBwdSplitW,
+                                a.gpart)) != hipSuccess)
       return e;
     // dW_down [r, Dh] = du^T . h
-    if ((e = gemm<float, T>(a.du, 1, a.r, h, a.Dh, 1, a.dw_down, a.Dh, 1, a.r, a.Dh, ntok, st)) != hipSuccess)
+    if ((e = gemm<float, T>(a.du, 1, a.r, h, a.Dh, 1, a.dw_down, a.Dh, 1, a.r, a.Dh, ntok, st, kBwdSplitW, a.gpart)) !=
+        hipSuccess)
       return e;
     // dh [ntok, Dh] = du . W_down
     if ((e = gemm<float, T>(a.du, a.r, 1, wd, a.Dh, 1, a.dh, a.Dh, 1, ntok, a.Dh, a.r, st)) != hipSuccess) return e;

@@ -85,6 +85,8 @@ struct DenseArgs {
 // Backward pass for a fixed selection (all gradients float32).
 constexpr int kMaxBwdChunks = 512;  // C = T / S bound of the inverse selection lists
 constexpr int kMaxBwdG = 16;
+constexpr int kBwdSplitW = 16;  // k splits of the Q-Cal weight-gradient GEMMs (k = tokens)
+constexpr int kBwdSplitDu = 4;  // k splits of u = h W_down^T and du = dq_hat W_up (k = D_h, H_q d)
 struct BwdArgs {
   const void *q, *k, *v, *q_lm, *h, *w_down, *w_up, *k_sum, *d_o;
   const float *b_sum;
@@ -96,6 +98,8 @@ struct BwdArgs {
   // major); logz / delta [B,Hq,T]; per selection-list entry and head
   // ent_lw / ent_doo / ent_ds [B,Hkv,T*K,G]; zsum [B,Hq,C,r], zb [B,Hq,C]
   float *u, *du, *qhat, *dqhat, *logz, *delta, *ent_lw, *ent_doo, *ent_ds, *zsum, *zb;
+  float *gpart;  // split-k partial sums of the Q-Cal GEMMs
+
   // inverse selection lists: inv_cnt / inv_qboff [B,Hkv,nqb,C],
   // inv_choff [B,Hkv,C+1], inv_list [B,Hkv,T*K] (query << 5 | slot),
   // inv_pos [B,Hkv,T,K] (each slot's place in its list, -1: none)
