@@ -62,7 +62,9 @@ def parse():
     p.add_argument("--decode-shapes", default="decode_128k:8,decode_4m:1",
                    help="the further decode legs, workload:batch, comma separated")
     p.add_argument("--no-backward", action="store_true", help="skip the 8K backward leg")
-    p.add_argument("--only", choices=["prefill", "decode", "long", "backward"], default=None,
+    p.add_argument("--no-sweep", action="store_true", help="skip the decode latency-vs-context leg")
+    p.add_argument("--sweep-lens", default="4096,8192,16384,32768,65536,131072,262144,524288,1048576")
+    p.add_argument("--only", choices=["prefill", "decode", "long", "backward", "sweep"], default=None,
                    help="profile one path (for rocprofv3 runs)")
     p.add_argument("--decode-batches", default="1,4")
     p.add_argument("--cpu-seconds", type=float, default=12.0, help="target oracle sample time")
@@ -118,8 +120,9 @@ def source_digest(files):
     return h.hexdigest()
 
 
-ATTN_SOURCES = ["prefill_mfma.hip", "hils_common.h"]
-DECODE_SOURCES = ["decode.hip", "attn_unit.h", "hils_common.h", "api.cpp"]
+# the device code each traffic record was measured on
+ATTN_SOURCES = ["prefill_mfma.hip", "prefill_chunks.hip", "hils_common.h"]
+DECODE_SOURCES = ["decode.hip", "attn_unit.h", "hils_common.h"]
 
 
 def traffic_record(name, sources):
@@ -352,6 +355,70 @@ def bench_prefill_long(args, torch, hils, hs, flush):
     del d, k_sum, b_sum, ws, idx, tsc, o
     torch.cuda.empty_cache()
     return out
+
+
+def bench_decode_sweep(args, torch, hils, flush):
+    """Decode latency against context length: one query (B=1, 32/8 heads,
+    d=128, S=64, K=16, W=512) over caches of 4K .. 1M tokens, the sparse
+    step (summaries built beforehand, untimed) and the dense causal decode
+    on the same cache, each from cold caches.  The caches are seeded
+    N(0, 1) draws made on the device (torch's generator), since no output is
+    checked here: the leg measures where the sparse step overtakes the dense
+    one and how its latency grows with the context."""
+    lens = [int(x) for x in args.sweep_lens.split(",") if x]
+    B, Hq, Hkv, D = 1, 32, 8, 128
+    stream = torch.cuda.current_stream()
+    gen = torch.Generator(device="cuda")
+    rows = []
+    for L in lens:
+        gen.manual_seed(args.seed + L)
+        k = torch.randn((B, Hkv, L, D), generator=gen, device="cuda").to(torch.bfloat16)
+        v = torch.randn((B, Hkv, L, D), generator=gen, device="cuda").to(torch.bfloat16)
+        q = torch.randn((B, Hq, D), generator=gen, device="cuda").to(torch.bfloat16)
+        C = L // 64
+        q_lm = torch.randn((B, Hq, max(C, 1), D), generator=gen, device="cuda").to(torch.bfloat16)
+        c = hils.Config.make(B, L, Hq, Hkv, D, 64, 16, 512, 0, 0, "bf16")
+        k_sum = torch.empty((B, Hq, max(C, 1), D), dtype=torch.bfloat16, device="cuda")
+        b_sum = torch.empty((B, Hq, max(C, 1)), dtype=torch.float32, device="cuda")
+        if C:
+            hils.hils_landmark_summary(c, k, q_lm, 0, C, k_sum, b_sum, stream)
+        seq = torch.full((B,), L, dtype=torch.int32, device="cuda")
+        ws = torch.zeros((hils.hils_decode_workspace_bytes(c),), dtype=torch.uint8, device="cuda")
+        dws = torch.zeros((hils.hils_dense_decode_workspace_bytes(c),), dtype=torch.uint8, device="cuda")
+        o = torch.empty((B, Hq, D), dtype=torch.bfloat16, device="cuda")
+        idx = torch.empty((B, Hkv, 16), dtype=torch.int32, device="cuda")
+        tsc = torch.empty((B, Hq, 16), dtype=torch.float32, device="cuda")
+
+        def sparse():
+            hils.hils_sparse_attn_decode(c, q, None, None, None, k, v, k_sum, b_sum, seq, o, idx, tsc, ws, stream)
+
+        def dense():
+            hils.hils_dense_attn_decode(c, q, k, v, seq, o, dws, stream)
+
+        def timed(fn):
+            for _ in range(2):
+                fn()
+            torch.cuda.synchronize()
+            ts = []
+            for _ in range(max(3, min(args.steps, 10))):
+                flush()
+                a_ = torch.cuda.Event(enable_timing=True)
+                b_ = torch.cuda.Event(enable_timing=True)
+                a_.record(stream)
+                fn()
+                b_.record(stream)
+                torch.cuda.synchronize()
+                ts.append(a_.elapsed_time(b_) * 1e3)
+            return float(np.median(ts))
+
+        su, du = timed(sparse), timed(dense)
+        rows.append(dict(context=L, sparse_us=su, dense_us=du, speedup=du / su))
+        log(f"[decode sweep] {L:>8} tokens: sparse {su:7.1f} us, dense {du:8.1f} us ({du / su:.2f}x)")
+        del k, v, q, q_lm, k_sum, b_sum, ws, dws
+        torch.cuda.empty_cache()
+    cross = next((r["context"] for r in rows if r["speedup"] > 1.0), None)
+    return dict(what="B=1 decode step latency (median of cold-cache steps) against context, sparse vs dense",
+                rows=rows, first_context_sparse_faster=cross)
 
 
 def bench_decode(args, torch, hils, hs, flush, batch, name=None, paged=True):
@@ -631,6 +698,12 @@ def main():
             first = dec[next(iter(dec))]
             line.update(value=first["value"], ms_per_step=first["ms_per_step"], roofline=first["roofline"],
                         config=dict(workload="decode_512k", batch=first["batch"], seq_len=first["seq_len"]))
+    if args.only in (None, "sweep") and not args.no_sweep:
+        line["decode_sweep"] = bench_decode_sweep(args, torch, hils, flush)
+        if args.only == "sweep":
+            r0 = line["decode_sweep"]["rows"][-1]
+            line.update(value=1e6 / r0["sparse_us"], ms_per_step=r0["sparse_us"] / 1e3,
+                        config=dict(workload="decode_sweep", batch=1, seq_len=r0["context"]))
     if args.only in (None, "backward") and not args.no_backward:
         bw = bench_backward(args, torch, hils, hs, flush)
         line["backward_8k"] = bw

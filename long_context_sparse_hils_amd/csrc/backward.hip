@@ -733,12 +733,16 @@ static hipError_t bwd_t(const BwdArgs &a, hipStream_t st) {
     bwd_inv_fill_kernel<<<dim3(nqb, a.Hkv, a.B), kBT, 0, st>>>(a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  const dim3 rows(a.T, a.Hkv, a.B);
-  if (qcal)
-    bwd_rows_kernel<T, D, true><<<rows, kBT, 0, st>>>(a);
-  else
-    bwd_rows_kernel<T, D, false><<<rows, kBT, 0, st>>>(a);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (bwd_rows_mfma_supported(a)) {
+    if ((e = launch_bwd_rows_mfma(a, st)) != hipSuccess) return e;
+  } else {
+    const dim3 rows(a.T, a.Hkv, a.B);
+    if (qcal)
+      bwd_rows_kernel<T, D, true><<<rows, kBT, 0, st>>>(a);
+    else
+      bwd_rows_kernel<T, D, false><<<rows, kBT, 0, st>>>(a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
   if (C > 0 && a.K > 0) {
     bwd_z_kernel<<<dim3(C, a.Hkv, a.B), kBT, 0, st>>>(a);
     if ((e = hipGetLastError()) != hipSuccess) return e;

@@ -346,6 +346,408 @@ bwd_keys_mfma_kernel(BwdArgs a) {
   for (int u = 0; u < QD; u += 4) *reinterpret_cast<float4 *>(dko + u) = make_float4(dkr[u], dkr[u + 1], dkr[u + 2], dkr[u + 3]);
 }
 
+// ------------------------------------------------------------------ rows (MFMA)
+// The query-major pass on the matrix cores: one workgroup per (query i,
+// group g, batch b), its G heads the columns of one 16-row tile (rows past G
+// zero).  The row's blocks -- its selected chunks, then the 64-key blocks of
+// its window -- are staged in LDS one at a time (K row-major, V row-major,
+// K^T), the next block's loads in flight while the current one computes.
+// Wave w takes keys 16 w .. 16 w + 15 of each block:
+//   S^T = K Q^T, dP^T = V dO^T        16x16x32 bf16, keys in M, heads in N
+// and accumulates, per head, running sums over its own keys against one
+// running reference R (the largest chunk score, raised by window logits
+// past it):
+//   V1 = sum_c e^{s_c - R} / Z_c sum_j e^{l_j - m_c} (dO.v_j - dO.o_c) k_j
+//        + sum_window e^{l_j - R} dO.v_j k_j,
+//   A2 = sum_window e^{l_j - R} k_j
+// as K^T times a weight column: 16x16x16 bf16 products whose B operand is
+// the lane's own accumulator entries (keys 4 lg .. 4 lg + 3 of column ln).
+// The window weights enter as bf16 hi + lo pairs (V1 - Delta A2 cancels when
+// the row's attention is sharp), the chunk weights, already differences, as
+// one bf16 value.  A chunk's maximum, sum and dO.o_c are combined over the
+// four waves through LDS; at the end the waves' window states and vectors
+// are combined in wave order, so the result is the same on every run:
+//   dq = tau sum_w e^{R_w - logZ} (V1_w - Delta A2_w) + dq_hat.
+namespace {
+
+typedef short bf16x4r __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4k mfma_16(const uint2 &a, const uint2 &b, const f32x4k &c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(bf16x4r, a), __builtin_bit_cast(bf16x4r, b), c,
+                                                   0, 0, 0);
+}
+
+// bf16 hi part (round to nearest even) and the bf16 rounding of the rest
+__device__ __forceinline__ void split_bf16(const float (&x)[4], uint2 &hi, uint2 &lo) {
+  hi = make_uint2(pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]));
+  const float r0 = x[0] - __uint_as_float(hi.x << 16), r1 = x[1] - __uint_as_float(hi.x & 0xFFFF0000u);
+  const float r2 = x[2] - __uint_as_float(hi.y << 16), r3 = x[3] - __uint_as_float(hi.y & 0xFFFF0000u);
+  lo = make_uint2(pack_bf16x2(r0, r1), pack_bf16x2(r2, r3));
+}
+
+constexpr int kRP = 8;   // row-major tiles: rows D + 8 elements apart
+constexpr int kTQ = 72;  // K^T tile: 64 keys + 8 per d row
+
+template <int D>
+struct alignas(16) RmTiles {
+  uint16_t kr[kBK][D + kRP];
+  uint16_t vr[kBK][D + kRP];
+  uint16_t kt[D][kTQ];
+};
+template <int D>
+struct alignas(16) RmSmem {
+  union {
+    RmTiles<D> t;
+    float vec[4][16][D + 4];  // the waves' row vectors for the final sum
+  } u;
+  float red[4][16][3];        // per wave and head: a chunk's max, sum, sum e dO.v over the wave's keys
+  float fin[4][16][3];        // per wave and head: the window's max, sum, sum e dO.v
+  float sl_s[32][16], sl_m[32][16], sl_z[32][16], sl_doo[32][16];  // per slot and head
+  float row_lz[16], row_dl[16], row_mc[16];
+  int sel[32], blk[64];       // the row's chunks; the staged blocks (c, or -1 - window block)
+  int nblk;
+};
+
+}  // namespace
+
+template <int D, int G, bool QCAL>
+__global__ void __launch_bounds__(256, 2)
+bwd_rows_mfma_kernel(BwdArgs a) {
+  __shared__ RmSmem<D> sm;
+  constexpr int KS = D / 32, DT = D / 16;
+  constexpr int NKI = D / 64;  // (row pair, 8-element piece) items of K per thread; V: 2 NKI rows
+  const int i = blockIdx.x, g = blockIdx.y, b = blockIdx.z, t = threadIdx.x;
+  const int lane = t & 63, w = __builtin_amdgcn_readfirstlane(t >> 6), ln = lane & 15, lg = lane >> 4;
+  const int T_len = a.T, K = a.K, Hq = a.Hq, Hkv = a.Hkv, C = T_len / kBK;
+  const float tau = a.tau;
+  const int n = eligible_chunks(i, a.W, kBK), w_lo = n * kBK;
+  const int nwb = (i - w_lo) / kBK + 1;
+  const size_t pg = static_cast<size_t>(b) * Hkv + g;
+  const uint16_t *kg = static_cast<const uint16_t *>(a.k) + pg * T_len * D;
+  const uint16_t *vg = static_cast<const uint16_t *>(a.v) + pg * T_len * D;
+  const uint16_t *ksum = static_cast<const uint16_t *>(a.k_sum);
+  // ---- the row's blocks and the chunk scores s_hat = tau q_hat . k'_c + b'_c
+  if (t < 32) {
+    int c = -1;
+    if (t < K) c = a.topk_idx[(pg * T_len + i) * K + t];
+    sm.sel[t] = (c >= 0 && c < n) ? c : -1;
+  }
+  __syncthreads();
+  if (t == 0) {
+    int nb = 0;
+    for (int x = 0; x < K; ++x)
+      if (sm.sel[x] >= 0) sm.blk[nb++] = x;  // slot x
+    for (int x = 0; x < nwb; ++x) sm.blk[nb++] = -1 - x;
+    sm.nblk = nb;
+  }
+  for (int x = t; x < K * G; x += kBT) {  // one (slot, head) per thread
+    const int slot = x / G, hh = x % G, c = sm.sel[slot];
+    float s = -INFINITY;
+    if (c >= 0) {
+      const size_t ro = (static_cast<size_t>(b) * Hq + g * G + hh) * T_len + i;
+      const size_t so = (static_cast<size_t>(b) * Hq + g * G + hh) * C + c;
+      float acc = 0.f;
+      for (int e = 0; e < D; e += 8) {
+        float kv[8];
+        Elem<uint16_t>::load8(ksum + so * D + e, kv);
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          acc += (QCAL ? a.qhat[ro * D + e + u] : bf16_to_f32(static_cast<const uint16_t *>(a.q)[ro * D + e + u])) * kv[u];
+      }
+      s = tau * acc + a.b_sum[so];
+    }
+    sm.sl_s[slot][hh] = s;
+  }
+  __syncthreads();
+  const int nb = sm.nblk;
+  // this lane's head (column ln) and its largest chunk score
+  float Mc = -INFINITY;
+  if (ln < G)
+    for (int x = 0; x < K; ++x) Mc = fmaxf(Mc, sm.sl_s[x][ln]);
+  // Q and dO of the lane's head as B operands: d = 32 s + 8 lg .. + 8
+  uint4 qop[KS], dop[KS];
+  {
+    const size_t ro = (static_cast<size_t>(b) * Hq + g * G + (ln < G ? ln : 0)) * T_len + i;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      qop[s] = ln < G ? *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.q) + ro * D + 32 * s + 8 * lg)
+                      : make_uint4(0u, 0u, 0u, 0u);
+      dop[s] = ln < G ? *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.d_o) + ro * D + 32 * s + 8 * lg)
+                      : make_uint4(0u, 0u, 0u, 0u);
+    }
+  }
+  // ---- staging: item it of K -> rows 2 pp, 2 pp + 1, piece s; V rows plain
+  uint4 kst[NKI][2], vst[2 * NKI];
+  auto block_j0 = [&](int x) { const int bb = sm.blk[x]; return bb >= 0 ? sm.sel[bb] * kBK : w_lo - (1 + bb) * kBK; };
+  auto load_block = [&](int j0) {
+#pragma unroll
+    for (int it = 0; it < NKI; ++it) {
+      const int x = t + kBT * it, pp = x & 31, s = x >> 5;
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const int r = j0 + 2 * pp + h2;
+        kst[it][h2] = r < T_len ? *reinterpret_cast<const uint4 *>(kg + static_cast<size_t>(r) * D + 8 * s)
+                                : make_uint4(0u, 0u, 0u, 0u);
+      }
+    }
+#pragma unroll
+    for (int it = 0; it < 2 * NKI; ++it) {
+      const int x = t + kBT * it, r = x / (D / 8), s = x % (D / 8);
+      vst[it] = j0 + r < T_len ? *reinterpret_cast<const uint4 *>(vg + static_cast<size_t>(j0 + r) * D + 8 * s)
+                               : make_uint4(0u, 0u, 0u, 0u);
+    }
+  };
+  auto store_block = [&]() {
+#pragma unroll
+    for (int it = 0; it < NKI; ++it) {
+      const int x = t + kBT * it, pp = x & 31, s = x >> 5;
+      *reinterpret_cast<uint4 *>(&sm.u.t.kr[2 * pp][8 * s]) = kst[it][0];
+      *reinterpret_cast<uint4 *>(&sm.u.t.kr[2 * pp + 1][8 * s]) = kst[it][1];
+      const uint32_t r0[4] = {kst[it][0].x, kst[it][0].y, kst[it][0].z, kst[it][0].w};
+      const uint32_t r1[4] = {kst[it][1].x, kst[it][1].y, kst[it][1].z, kst[it][1].w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t lo = (r0[e >> 1] >> (16 * (e & 1))) & 0xFFFFu, hi = (r1[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+        *reinterpret_cast<uint32_t *>(&sm.u.t.kt[8 * s + e][2 * pp]) = lo | (hi << 16);
+      }
+    }
+#pragma unroll
+    for (int it = 0; it < 2 * NKI; ++it) {
+      const int x = t + kBT * it, r = x / (D / 8), s = x % (D / 8);
+      *reinterpret_cast<uint4 *>(&sm.u.t.vr[r][8 * s]) = vst[it];
+    }
+  };
+
+  f32x4k V1[DT], A2[DT];
+#pragma unroll
+  for (int x = 0; x < DT; ++x) V1[x] = A2[x] = f32x4k{0.f, 0.f, 0.f, 0.f};
+  // this wave's reference and window sums for head ln (relative to R)
+  float R = Mc, zw = 0.f, dw = 0.f;
+  if (nb > 0) {
+    load_block(block_j0(0));
+    store_block();
+  }
+  __syncthreads();
+  for (int x = 0; x < nb; ++x) {
+    const int bb = sm.blk[x];
+    const bool chunk = bb >= 0;
+    const int j0 = block_j0(x);
+    if (x + 1 < nb) load_block(block_j0(x + 1));
+    // ---- S^T and dP^T of keys 16 w .. 16 w + 15
+    f32x4k sacc = f32x4k{0.f, 0.f, 0.f, 0.f}, pacc = f32x4k{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const uint4 ak = *reinterpret_cast<const uint4 *>(&sm.u.t.kr[16 * w + ln][32 * s + 8 * lg]);
+      const uint4 av = *reinterpret_cast<const uint4 *>(&sm.u.t.vr[16 * w + ln][32 * s + 8 * lg]);
+      sacc = mfma_k(ak, qop[s], sacc);
+      pacc = mfma_k(av, dop[s], pacc);
+    }
+    // element jx: key 16 w + 4 lg + jx of the block, head ln
+    float l[4], dv[4];
+#pragma unroll
+    for (int jx = 0; jx < 4; ++jx) {
+      l[jx] = tau * sacc[jx];
+      dv[jx] = pacc[jx];
+    }
+    if (chunk) {
+      float m = fmaxf(fmaxf(l[0], l[1]), fmaxf(l[2], l[3]));
+      m = max_rows4(m);
+      float z = 0.f, dz = 0.f;
+#pragma unroll
+      for (int jx = 0; jx < 4; ++jx) {
+        const float e = __expf(l[jx] - m);
+        z += e;
+        dz += e * dv[jx];
+      }
+      z = sum_rows4(z);
+      dz = sum_rows4(dz);
+      if (lg == 0) {
+        sm.red[w][ln][0] = m;
+        sm.red[w][ln][1] = z;
+        sm.red[w][ln][2] = dz;
+      }
+      __syncthreads();
+      // the chunk's statistics for head ln, combined over the waves in order
+      float mc = sm.red[0][ln][0];
+#pragma unroll
+      for (int v = 1; v < 4; ++v) mc = fmaxf(mc, sm.red[v][ln][0]);
+      float zc = 0.f, dzc = 0.f;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const float f = __expf(sm.red[v][ln][0] - mc);
+        zc += f * sm.red[v][ln][1];
+        dzc += f * sm.red[v][ln][2];
+      }
+      const float doo = dzc / zc;
+      if (w == 0 && lg == 0) {
+        sm.sl_m[bb][ln] = mc;
+        sm.sl_z[bb][ln] = zc;
+        sm.sl_doo[bb][ln] = doo;
+      }
+      // (R >= s_hat of every selected chunk of head ln; padding heads: 0)
+      const float wgt = ln < G ? __expf(sm.sl_s[bb][ln] - R) / zc : 0.f;
+      float ed[4];
+#pragma unroll
+      for (int jx = 0; jx < 4; ++jx) ed[jx] = __expf(l[jx] - mc) * wgt * (dv[jx] - doo);
+      const uint2 eb = make_uint2(pack_bf16x2(ed[0], ed[1]), pack_bf16x2(ed[2], ed[3]));
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const uint2 akt = *reinterpret_cast<const uint2 *>(&sm.u.t.kt[16 * dt + ln][16 * w + 4 * lg]);
+        V1[dt] = mfma_16(akt, eb, V1[dt]);
+      }
+    } else {
+      float lm[4];
+      float mb = -INFINITY;
+#pragma unroll
+      for (int jx = 0; jx < 4; ++jx) {
+        lm[jx] = j0 + 16 * w + 4 * lg + jx <= i ? l[jx] : -INFINITY;
+        mb = fmaxf(mb, lm[jx]);
+      }
+      mb = max_rows4(mb);
+      const float rn = fmaxf(R, mb);
+      if (mb != -INFINITY) {  // uniform over the 4 lanes of the head
+        const float sc = R == -INFINITY ? 0.f : __expf(R - rn);
+        float e[4], ed[4], ze = 0.f, zd = 0.f;
+#pragma unroll
+        for (int jx = 0; jx < 4; ++jx) {
+          e[jx] = lm[jx] == -INFINITY ? 0.f : __expf(lm[jx] - rn);
+          ed[jx] = e[jx] * dv[jx];
+          ze += e[jx];
+          zd += ed[jx];
+        }
+        zw = zw * sc + sum_rows4(ze);
+        dw = dw * sc + sum_rows4(zd);
+        R = rn;
+        if (sc != 1.f) {
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt) {
+            V1[dt] *= sc;
+            A2[dt] *= sc;
+          }
+        }
+        uint2 eh, el, dh, dl;
+        split_bf16(e, eh, el);
+        split_bf16(ed, dh, dl);
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const uint2 akt = *reinterpret_cast<const uint2 *>(&sm.u.t.kt[16 * dt + ln][16 * w + 4 * lg]);
+          V1[dt] = mfma_16(akt, dh, V1[dt]);
+          V1[dt] = mfma_16(akt, dl, V1[dt]);
+          A2[dt] = mfma_16(akt, eh, A2[dt]);
+          A2[dt] = mfma_16(akt, el, A2[dt]);
+        }
+      }
+    }
+    __syncthreads();  // every wave is done with this block's tiles
+    if (x + 1 < nb) store_block();
+    __syncthreads();
+  }
+  // ---- the joint normaliser and Delta per head
+  if (lg == 0) {
+    sm.fin[w][ln][0] = R;
+    sm.fin[w][ln][1] = zw;
+    sm.fin[w][ln][2] = dw;
+  }
+  __syncthreads();
+  if (t < 16) {  // head t
+    const int hh = t;
+    float mc = -INFINITY;
+    for (int x = 0; x < K; ++x) mc = fmaxf(mc, sm.sl_s[x][hh]);
+    float M = mc;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) M = fmaxf(M, sm.fin[v][hh][0]);
+    float z = 0.f;
+    for (int x = 0; x < K; ++x)
+      if (sm.sel[x] >= 0) z += __expf(sm.sl_s[x][hh] - M);
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+      if (sm.fin[v][hh][0] != -INFINITY) z += sm.fin[v][hh][1] * __expf(sm.fin[v][hh][0] - M);
+    const float lz = M + __logf(z);
+    float dl = 0.f;
+    for (int x = 0; x < K; ++x)
+      if (sm.sel[x] >= 0) dl += __expf(sm.sl_s[x][hh] - lz) * sm.sl_doo[x][hh];
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+      if (sm.fin[v][hh][0] != -INFINITY) dl += sm.fin[v][hh][2] * __expf(sm.fin[v][hh][0] - lz);
+    sm.row_lz[hh] = lz;
+    sm.row_dl[hh] = dl;
+    sm.row_mc[hh] = mc;
+    if (hh < G) {
+      const size_t ro = (static_cast<size_t>(b) * Hq + g * G + hh) * T_len + i;
+      a.logz[ro] = lz;
+      a.delta[ro] = dl;
+    }
+  }
+  __syncthreads();
+  // ---- each wave's row vectors into LDS (element j of d tile dt: d = 16 dt + 4 lg + j, head ln)
+  {
+    const float lz = sm.row_lz[ln], dl = sm.row_dl[ln];
+    const float f = R == -INFINITY ? 0.f : __expf(R - lz);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int jx = 0; jx < 4; ++jx) sm.u.vec[w][ln][16 * dt + 4 * lg + jx] = f * (V1[dt][jx] - dl * A2[dt][jx]);
+  }
+  __syncthreads();
+  // ---- dq and dq_hat per (head, d); the list entries' values
+  for (int x = t; x < G * D; x += kBT) {
+    const int hh = x / D, e = x % D, h = g * G + hh;
+    const float lz = sm.row_lz[hh], dl = sm.row_dl[hh], mc = sm.row_mc[hh];
+    float b1 = 0.f, b2 = 0.f;
+    for (int y = 0; y < K; ++y) {
+      const int c = sm.sel[y];
+      if (c < 0) continue;
+      const float sw = __expf(sm.sl_s[y][hh] - mc);
+      const float kp = bf16_to_f32(ksum[((static_cast<size_t>(b) * Hq + h) * C + c) * D + e]);
+      b1 += sw * sm.sl_doo[y][hh] * kp;
+      b2 += sw * kp;
+    }
+    const float fc = mc == -INFINITY ? 0.f : __expf(mc - lz);
+    const float dqh = tau * fc * (b1 - dl * b2);
+    const float v = sm.u.vec[0][hh][e] + sm.u.vec[1][hh][e] + sm.u.vec[2][hh][e] + sm.u.vec[3][hh][e];
+    const size_t ro = (static_cast<size_t>(b) * Hq + h) * T_len + i;
+    a.dq[ro * D + e] = tau * v + dqh;
+    if (QCAL) a.dqhat[((static_cast<size_t>(b) * T_len + i) * Hq + h) * D + e] = dqh;
+  }
+  for (int x = t; x < K * G; x += kBT) {
+    const int y = x / G, hh = x % G;
+    if (sm.sel[y] < 0) continue;
+    const int pos = a.inv_pos[(pg * T_len + i) * K + y];
+    const size_t eo = (pg * T_len * K + pos) * G + hh;
+    const float lz = sm.row_lz[hh];
+    a.ent_lw[eo] = sm.sl_s[y][hh] - lz - sm.sl_m[y][hh] - __logf(sm.sl_z[y][hh]);
+    a.ent_doo[eo] = sm.sl_doo[y][hh];
+    a.ent_ds[eo] = __expf(sm.sl_s[y][hh] - lz) * (sm.sl_doo[y][hh] - sm.row_dl[hh]);
+  }
+}
+
+bool bwd_rows_mfma_supported(const BwdArgs &a) { return bwd_keys_mfma_supported(a); }
+
+template <int D, int G>
+static hipError_t rows_dg(const BwdArgs &a, hipStream_t st) {
+  const dim3 grid(a.T, a.Hkv, a.B);
+  if (a.r > 0)
+    bwd_rows_mfma_kernel<D, G, true><<<grid, kBT, 0, st>>>(a);
+  else
+    bwd_rows_mfma_kernel<D, G, false><<<grid, kBT, 0, st>>>(a);
+  return hipGetLastError();
+}
+
+template <int D>
+static hipError_t rows_d(const BwdArgs &a, hipStream_t st) {
+  switch (a.Hq / a.Hkv) {
+    case 1: return rows_dg<D, 1>(a, st);
+    case 2: return rows_dg<D, 2>(a, st);
+    case 4: return rows_dg<D, 4>(a, st);
+    case 8: return rows_dg<D, 8>(a, st);
+    default: return rows_dg<D, 16>(a, st);
+  }
+}
+
+hipError_t launch_bwd_rows_mfma(const BwdArgs &a, hipStream_t st) {
+  return a.d == 128 ? rows_d<128>(a, st) : rows_d<64>(a, st);
+}
+
 bool bwd_keys_mfma_supported(const BwdArgs &a) {
   const int G = a.Hq / a.Hkv;
   return a.bf16 && (a.d == 64 || a.d == 128) && (G == 1 || G == 2 || G == 4 || G == 8 || G == 16);

@@ -113,6 +113,8 @@ hipError_t launch_summary(const SummaryArgs &a, hipStream_t st);
 hipError_t launch_score_valu(const ScoreArgs &a, hipStream_t st);
 hipError_t launch_backward(const BwdArgs &a, hipStream_t st);
 bool bwd_keys_mfma_supported(const BwdArgs &a);
+bool bwd_rows_mfma_supported(const BwdArgs &a);
+hipError_t launch_bwd_rows_mfma(const BwdArgs &a, hipStream_t st);
 hipError_t launch_bwd_keys_mfma(const BwdArgs &a, hipStream_t st);
 bool score_mfma_supported(const ScoreArgs &a);
 size_t score_mfma_ws_bytes(int B, int T, int Hq, int C, int r);
