@@ -188,12 +188,20 @@ def qcal(cfg: OracleConfig, q_rows, h_rows=None, w_down=None, w_up=None) -> np.n
     return out
 
 
+def _positions(qpos, B: int, nq: int) -> np.ndarray:
+    """Query positions as the C routines index them: [B, nq] int32."""
+    qpos = _c(np.asarray(qpos, dtype=np.int32))
+    if qpos.shape != (B, nq):
+        raise ValueError(f"query positions of shape {qpos.shape}, expected {(B, nq)}")
+    return qpos
+
+
 def scores(cfg: OracleConfig, qhat, qpos, k_sum, b_sum) -> np.ndarray:
     """s [B,Hq,nq,C]; -inf where the chunk is not eligible."""
     qhat = _c(np.asarray(qhat, dtype=np.float64))
-    qpos = _c(np.asarray(qpos, dtype=np.int32))
     k_sum, b_sum = _c(k_sum), _c(b_sum)
     B, Hq, nq, d = qhat.shape
+    qpos = _positions(qpos, B, nq)
     out = np.empty((B, Hq, nq, cfg.n_chunks))
     _load().orc_scores(ctypes.byref(cfg.c()), _ptr(qhat), _ptr(qpos), nq, _ptr(k_sum),
                        _dt(k_sum), _ptr(b_sum), _dt(b_sum), _ptr(out), threads())
@@ -203,8 +211,8 @@ def scores(cfg: OracleConfig, qhat, qpos, k_sum, b_sum) -> np.ndarray:
 def select(cfg: OracleConfig, s, qpos, top_k: int | None = None):
     """(idx [B,Hkv,nq,K] int32, tsc [B,Hq,nq,K] f64, sigma [B,Hkv,nq,C] f64)."""
     s = _c(np.asarray(s, dtype=np.float64))
-    qpos = _c(np.asarray(qpos, dtype=np.int32))
     B, Hq, nq, C = s.shape
+    qpos = _positions(qpos, B, nq)
     K = cfg.top_k if top_k is None else top_k
     idx = np.empty((B, cfg.n_kv_heads, nq, K), dtype=np.int32)
     tsc = np.empty((B, Hq, nq, K))
@@ -218,10 +226,10 @@ def fuse(cfg: OracleConfig, q_rows, k, v, qpos, idx, tsc, exact_mass: bool = Fal
     """Eq. 10 with the window term: (o [B,Hq,nq,d], sum of weights [B,Hq,nq])."""
     q_rows, k, v = _c(q_rows), _c(k), _c(v)
     assert k.dtype == v.dtype
-    qpos = _c(np.asarray(qpos, dtype=np.int32))
     idx = _c(np.asarray(idx, dtype=np.int32))
     tsc = _c(np.asarray(tsc, dtype=np.float64))
     B, Hq, nq, d = q_rows.shape
+    qpos = _positions(qpos, B, nq)
     K = idx.shape[-1]
     T = k.shape[2]
     o = np.empty((B, Hq, nq, d))
@@ -234,8 +242,8 @@ def fuse(cfg: OracleConfig, q_rows, k, v, qpos, idx, tsc, exact_mass: bool = Fal
 
 def causal_attention(cfg: OracleConfig, q_rows, k, v, qpos) -> np.ndarray:
     q_rows, k, v = _c(q_rows), _c(k), _c(v)
-    qpos = _c(np.asarray(qpos, dtype=np.int32))
     B, Hq, nq, d = q_rows.shape
+    qpos = _positions(qpos, B, nq)
     o = np.empty((B, Hq, nq, d))
     _load().orc_causal_attention(ctypes.byref(cfg.c(T=k.shape[2])), _ptr(q_rows), _dt(q_rows),
                                  _ptr(k), _ptr(v), _dt(k), _ptr(qpos), nq, _ptr(o), threads())
