@@ -16,7 +16,7 @@ OUT = os.path.join(HERE, "libhils.so")
 OBJ = os.path.join(HERE, "_build")
 ARCH = os.environ.get("HILS_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["summary.hip", "prefill_valu.hip", "prefill_mfma.hip", "prefill_chunks.hip", "score_mfma.hip", "decode.hip", "backward.hip", "backward_mfma.hip",
+SOURCES = ["summary.hip", "prefill_valu.hip", "prefill_mfma.hip", "prefill_chunks.hip", "prefill_long.hip", "score_mfma.hip", "decode.hip", "backward.hip", "backward_mfma.hip",
            "api.cpp"]
 
 FLAGS = [

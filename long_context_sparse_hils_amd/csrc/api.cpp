@@ -238,7 +238,7 @@ size_t hils_prefill_workspace_bytes(const hils_config *cfg) {
                        kAlign;
   const size_t attn = cfg->dtype == HILS_BF16
                           ? align_up(hils::attn_mfma_ws_bytes(cfg->batch, cfg->n_q_heads, cfg->n_kv_heads, cfg->seq_len,
-                                              cfg->head_dim))
+                                              cfg->head_dim, cfg->top_k))
                           : 0;
   return score > attn ? score : attn;
 }

@@ -121,9 +121,19 @@ size_t score_mfma_ws_bytes(int B, int T, int Hq, int C, int r);
 hipError_t launch_score_mfma(const ScoreArgs &a, hipStream_t st);
 hipError_t launch_attn_valu(const AttnArgs &a, hipStream_t st);
 bool attn_mfma_supported(const AttnArgs &a);
-size_t attn_mfma_ws_bytes(int B, int Hq, int Hkv, int T, int d);
+size_t attn_mfma_ws_bytes(int B, int Hq, int Hkv, int T, int d, int K);
 hipError_t launch_attn_chunks(const AttnArgs &a, uint16_t *ops, float *lse, const float *vmax, int nblk,
                               hipStream_t st);
+// every complete chunk's K and V^T in the chunk passes' MFMA operand order
+hipError_t launch_kv_operand_order(const AttnArgs &a, uint16_t *ops, hipStream_t st);
+// The chunk terms of sequences longer than kLongMinChunks chunks run
+// chunk-major over the whole sequence, in segments of queries whose
+// per-(query, slot) partial results take at most kLongPartBytes.
+constexpr int kLongMinChunks = 256;
+constexpr size_t kLongPartBytes = size_t(8) << 30;
+bool attn_long_used(int T, int K);
+size_t attn_long_ws_bytes(int B, int Hq, int Hkv, int T, int d, int K);
+hipError_t launch_attn_long(const AttnArgs &a, uint16_t *ops, float *lse, uint8_t *ws, hipStream_t st);
 inline int eligible_chunks_host(int i, int W, int S) {
   const int w0 = i - W + 1;
   return w0 > 0 ? w0 / S : 0;

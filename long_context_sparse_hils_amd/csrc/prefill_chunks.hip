@@ -532,6 +532,19 @@ static hipError_t chunks_g(const AttnArgs &a, uint16_t *ops, float *lse, const f
   return chunks_t<D, G, QB32, 32>(a, ops, lse, vmax, nblk, st);
 }
 
+hipError_t launch_kv_operand_order(const AttnArgs &a, uint16_t *ops, hipStream_t st) {
+  const dim3 grid(a.T / kCK, a.B * a.Hkv);
+  const uint16_t *k = static_cast<const uint16_t *>(a.k), *v = static_cast<const uint16_t *>(a.v);
+  if (grid.x == 0) return hipSuccess;
+  if (a.d == 128)
+    kv_operand_order_kernel<128><<<grid, 256, 0, st>>>(k, v, ops, a.T, a.T / kCK);
+  else if (a.d == 64)
+    kv_operand_order_kernel<64><<<grid, 256, 0, st>>>(k, v, ops, a.T, a.T / kCK);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
 hipError_t launch_attn_chunks(const AttnArgs &a, uint16_t *ops, float *lse, const float *vmax, int nblk,
                               hipStream_t st) {
   const int G = a.Hq / a.Hkv;

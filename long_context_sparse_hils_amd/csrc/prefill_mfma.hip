@@ -481,13 +481,18 @@ static hipError_t attn_mfma_t(const AttnArgs &a_in, hipStream_t st) {
   uint16_t *ops = reinterpret_cast<uint16_t *>(ws_after_vt + attn_chunk_meta_bytes(a_in.B, a_in.Hq, a_in.Hkv, a_in.T));
   vt_transpose_kernel<D><<<dim3(nblk, npairs), 256, 0, st>>>(static_cast<const uint16_t *>(a_in.v),
                                                              static_cast<uint16_t *>(a_in.vt_ws),
-                                                             chunks ? vmax : nullptr, a_in.T, nblk);
+                                                             chunks && !attn_long_used(a_in.T, a_in.K) ? vmax : nullptr, a_in.T, nblk);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   AttnArgs a = a_in;
   a.lse_c = nullptr;
   if (chunks) {
-    e = launch_attn_chunks(a_in, ops, lse, vmax, nblk, st);
+    if (attn_long_used(a_in.T, a_in.K)) {
+      const size_t ops_bytes = static_cast<size_t>(npairs) * (a_in.T / kItemKeys) * kItemKeys * D * 2 * 2;
+      e = launch_attn_long(a_in, ops, lse, reinterpret_cast<uint8_t *>(ops) + ops_bytes, st);
+    } else {
+      e = launch_attn_chunks(a_in, ops, lse, vmax, nblk, st);
+    }
     if (e != hipSuccess) return e;
     a.lse_c = lse;
   }
@@ -508,10 +513,12 @@ bool attn_mfma_supported(const AttnArgs &a) {
 
 // value tiles, then the chunk log-mass of every (b, query head, query) and
 // the largest |v| of every 64-key block, then every complete chunk's K and
-// V^T in operand order
-size_t attn_mfma_ws_bytes(int B, int Hq, int Hkv, int T, int d) {
+// V^T in operand order; for long sequences the chunk-major pass's lists and
+// partial results
+size_t attn_mfma_ws_bytes(int B, int Hq, int Hkv, int T, int d, int K) {
   const size_t chunks = static_cast<size_t>(B) * Hkv * (T / kItemKeys);
-  return attn_vt_bytes(B, Hkv, T, d) + attn_chunk_meta_bytes(B, Hq, Hkv, T) + chunks * kItemKeys * d * 2 * 2;
+  return attn_vt_bytes(B, Hkv, T, d) + attn_chunk_meta_bytes(B, Hq, Hkv, T) + chunks * kItemKeys * d * 2 * 2 +
+         attn_long_ws_bytes(B, Hq, Hkv, T, d, K);
 }
 
 hipError_t launch_attn_mfma(const AttnArgs &a, hipStream_t st) {

@@ -64,10 +64,14 @@ def test_long_score_topk_parity(name):
     print(f"{name}: {rows.size} sampled rows, near-tie rows {ties}")
 
 
-def test_long_prefill_attention_sampled_rows():
-    """The attention kernel over a 20K sequence's own selection: sampled rows
-    against the oracle's fusion of the same selection and scores."""
-    wl = LONG_CASES["t20k_qcal"]
+@pytest.mark.parametrize("name", list(LONG_CASES) + ["t17k_g16"])
+def test_long_prefill_attention_sampled_rows(name):
+    """The attention call over a long sequence's own selection (more than 256
+    chunks: the chunk-major pass over the whole sequence): sampled rows
+    against the oracle's fusion of the same selection and scores, and a
+    second call gives the same bits."""
+    wl = LONG_CASES.get(name) or _wl(1, 17000, 16, 1, 64, 8, 300)
+    assert wl.n_chunks > 256
     inp = hs.prefill_inputs(wl, 4141)
     c = hils.Config.from_dict(wl.config_dict())
     d = {k: dev(v) for k, v in inp.items() if isinstance(v, np.ndarray)}
@@ -75,12 +79,15 @@ def test_long_prefill_attention_sampled_rows():
     k_sum = torch.empty((wl.batch, wl.n_q_heads, C, wl.head_dim), dtype=torch.bfloat16, device="cuda")
     b_sum = torch.empty((wl.batch, wl.n_q_heads, C), dtype=torch.float32, device="cuda")
     hils.hils_landmark_summary(c, d["k"], d["q_lm"], 0, C, k_sum, b_sum)
-    gidx, gtsc = gpu_score(c, d["q"], k_sum, b_sum, d["h"], d["w_down"], d["w_up"])
+    gidx, gtsc = gpu_score(c, d["q"], k_sum, b_sum, d.get("h"), d.get("w_down"), d.get("w_up"))
     o = gpu_attn(c, d["q"], d["k"], d["v"], gidx, gtsc, torch.bfloat16)
+    o2 = gpu_attn(c, d["q"], d["k"], d["v"], gidx, gtsc, torch.bfloat16)
+    assert torch.equal(o.view(torch.int16), o2.view(torch.int16)), "two calls differ"
     rows = _rows(wl.seq_len)
     oc = oracle.OracleConfig.from_dict(wl.config_dict())
     qr = inp["q"][:, :, rows]
-    o_ref, _ = oracle.fuse(oc, qr, inp["k"], inp["v"], rows[None, :], host(gidx)[:, :, rows],
+    o_ref, _ = oracle.fuse(oc, qr, inp["k"], inp["v"], np.broadcast_to(rows, (wl.batch, rows.size)),
+                           host(gidx)[:, :, rows],
                            host(gtsc)[:, :, rows].astype(np.float64))
     err = check_out(host(o)[:, :, rows], o_ref, "bf16")
-    print(f"sampled rows {rows.size}: max |d| {err:.3g}")
+    print(f"{name}: sampled rows {rows.size}: max |d| {err:.3g}")
