@@ -240,6 +240,40 @@ __device__ __forceinline__ void reset_counter(unsigned *counter) {
 }
 
 
+// ---------------------------------------------------------------- LDS DMA
+// A wave-wide load from global memory straight into LDS: lane l's bytes
+// (16 or 4) land at LDS byte address lds_base + size * l, lds_base being
+// wave-uniform (M0).  Issued as inline assembly so that the compiler's wait
+// insertion does not tie later LDS reads of other buffers to it (with the
+// builtin it waits for every DMA in flight before the next LDS read, which
+// serialises a multi-buffered pipeline).  The caller therefore waits
+// itself: s_waitcnt vmcnt before the barrier that publishes the buffer.
+// The kernels that use it issue no other loads into registers while DMAs
+// are in flight unless they wait for everything first, so the compiler's
+// own waits stay exact or conservative.
+__device__ __forceinline__ uint32_t lds_address(const void *p) {
+  return __builtin_amdgcn_readfirstlane(
+      static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void *)p)));
+}
+// M0 (the LDS base of the DMA) is saved and restored inside the statement:
+// the compiler reserves it and does not expect it to change.
+__device__ __forceinline__ void lds_dma16(const void *src, uint32_t lds_base) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(src), "s"(lds_base)
+      : "memory");
+}
+__device__ __forceinline__ void lds_dma4(const void *src, uint32_t lds_base) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %1, off\n\ts_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(src), "s"(lds_base)
+      : "memory");
+}
+
 // R1 partition: complete chunks before query i's window
 __device__ __forceinline__ int eligible_chunks(int i, int W, int S) {
   int w0 = i - W + 1;

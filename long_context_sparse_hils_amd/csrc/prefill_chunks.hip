@@ -198,6 +198,14 @@ attn_chunks_kernel(AttnArgs a, const uint16_t *__restrict__ ops, float *__restri
     const int q = x / (G * K_MAX), hh = (x / K_MAX) % G, k = x % K_MAX;
     sv[r] = tsc_b[(static_cast<size_t>(g * G + hh) * T + min(q0 + q, T - 1)) * K + min(k, kmax)];
   }
+  // B_v of the block needs the largest |v| of every 64-key block it selects
+  // (chunk ids below C <= 256 here: one pass covers longer sequences)
+  float vpre[4] = {0.f, 0.f, 0.f, 0.f};
+  const float *vm = vmax + static_cast<size_t>(pair) * nblk;
+  if (tid < 64) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) vpre[j] = lane + 64 * j < C_chunks ? vm[lane + 64 * j] : 0.f;
+  }
   for (int x = tid; x < 256; x += C::kThreads) sm.umask[x] = 0u;
   for (int x = tid; x < C::kEnt; x += C::kThreads) sm.ucnt[x] = 0;
   if (tid == 0) sm.next = 0;
@@ -284,11 +292,15 @@ attn_chunks_kernel(AttnArgs a, const uint16_t *__restrict__ ops, float *__restri
   if (tid < 64) {  // exclusive prefix of the counts; B_v of the block's chunks
     int base = 0;
     float bv = 0.f;
-    const float *vm = vmax + static_cast<size_t>(pair) * nblk;
+    auto selected = [&](int c) { return (sm.umask[c >> 5] >> (c & 31)) & 1u; };
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (lane + 64 * j < C_chunks && selected(lane + 64 * j)) bv = fmaxf(bv, vpre[j]);
+    for (int c = lane + 256; c < C_chunks; c += 64)
+      if (selected(c)) bv = fmaxf(bv, vm[c]);
     for (int u0 = 0; u0 < nunion; u0 += 64) {
       const int u = u0 + lane;
       const int cnt = u < nunion ? sm.ucnt[u] : 0;
-      if (u < nunion) bv = fmaxf(bv, vm[sm.ulist[u]]);
       int incl = cnt;
 #pragma unroll
       for (int o = 1; o < 64; o <<= 1) {

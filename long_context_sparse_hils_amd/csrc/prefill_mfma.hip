@@ -329,6 +329,11 @@ attn_window_mfma_kernel(AttnArgs a, int ntiles, int xcd_map, int nblk) {
     R.m_row[t] = -INFINITY;
     R.l_row[t] = 0.f;
   }
+  // the rows' chunk log-mass, read now so that it has landed by the epilogue
+  float lse_pre[TPW];
+#pragma unroll
+  for (int t = 0; t < TPW; ++t)
+    lse_pre[t] = (a.lse_c && row_ok[t]) ? a.lse_c[(static_cast<size_t>(b) * Hq + row_h) * T + row_i[t]] : -INFINITY;
 
   // window band of the tile: 64-key blocks from n_{first} * S to the last query
   const int i_first = q0, i_last = min(q0 + C::kQT - 1, T - 1);
@@ -348,8 +353,7 @@ attn_window_mfma_kernel(AttnArgs a, int ntiles, int xcd_map, int nblk) {
       const int r = sl / C::kRowPieces, pp = sl % C::kRowPieces;
       const int pc = pp ^ k_swz<D>(r);
       const int key = min(j0 + r, T - 1);  // rows past T are never used unmasked
-      __builtin_amdgcn_global_load_lds(kb + static_cast<uint32_t>(key * D + pc * 8),
-                                       (__attribute__((address_space(3))) void *)(sm.ks[buf] + slice * 512), 16, 0, 0);
+      lds_dma16(kb + static_cast<uint32_t>(key * D + pc * 8), lds_address(sm.ks[buf] + slice * 512));
     }
 #pragma unroll
     for (int i = 0; i < C::kLoadsV; ++i) {
@@ -357,8 +361,7 @@ attn_window_mfma_kernel(AttnArgs a, int ntiles, int xcd_map, int nblk) {
       const int sl = slice * 64 + lane;
       const int d = sl / 8, pp = sl % 8;
       const int pc = pp ^ v_swz(d);
-      __builtin_amdgcn_global_load_lds(vsrc + static_cast<uint32_t>(d * kItemKeys + pc * 8),
-                                       (__attribute__((address_space(3))) void *)(sm.vt[buf] + slice * 512), 16, 0, 0);
+      lds_dma16(vsrc + static_cast<uint32_t>(d * kItemKeys + pc * 8), lds_address(sm.vt[buf] + slice * 512));
     }
   };
   issue_loads(jw0, 0);
@@ -419,7 +422,17 @@ attn_window_mfma_kernel(AttnArgs a, int ntiles, int xcd_map, int nblk) {
   //   o = (acc e^{m} + o_C e^{lse_C}) / (l e^{m} + e^{lse_C}),
   // both scaled by e^{-max(m, lse_C)} (m, l: the row's window reference and
   // sum; the window always holds key i itself, so m is finite).
+  // The chunk parts of both tiles load at once (one round trip); a row
+  // without a chunk (lse_C = -inf) ignores what its slot holds.
   uint16_t *ob = static_cast<uint16_t *>(a.o);
+  uint2 part[TPW][C::kDT];
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) {
+    const size_t oo = ((static_cast<size_t>(b) * Hq + row_h) * T + min(row_i[t], T - 1)) * D;
+#pragma unroll
+    for (int dt = 0; dt < C::kDT; ++dt)
+      part[t][dt] = a.lse_c ? *reinterpret_cast<const uint2 *>(ob + oo + 16 * dt + 4 * lg) : make_uint2(0u, 0u);
+  }
 #pragma unroll
   for (int t = 0; t < TPW; ++t) {
     if (!row_ok[t]) continue;
@@ -427,7 +440,7 @@ attn_window_mfma_kernel(AttnArgs a, int ntiles, int xcd_map, int nblk) {
     const size_t oo = ro * D;
     float fw = 1.f, fc = 0.f, inv = 1.f / R.l_row[t];
     if (a.lse_c) {
-      const float lc = a.lse_c[ro];
+      const float lc = lse_pre[t];
       const float mx = fmaxf(R.m_row[t], lc);
       fw = __expf(R.m_row[t] - mx);
       fc = lc == -INFINITY ? 0.f : __expf(lc - mx);
@@ -437,7 +450,7 @@ attn_window_mfma_kernel(AttnArgs a, int ntiles, int xcd_map, int nblk) {
     for (int dt = 0; dt < C::kDT; ++dt) {
       float c4[4] = {0.f, 0.f, 0.f, 0.f};
       if (fc != 0.f) {
-        const uint2 pc = *reinterpret_cast<const uint2 *>(ob + oo + 16 * dt + 4 * lg);
+        const uint2 pc = part[t][dt];
         c4[0] = __uint_as_float(pc.x << 16);
         c4[1] = __uint_as_float(pc.x & 0xFFFF0000u);
         c4[2] = __uint_as_float(pc.y << 16);

@@ -260,7 +260,7 @@ __device__ __forceinline__ int score_swz(int r, int P) { return (r >> (P == 16 ?
 // a second pass recomputes the winners' per-head scores.  QR = RP / 32 when
 // known at compile time (0: no Q-Cal), else -1.
 template <int D, int NJ, int WAVES, int IC, int HR, int QR>
-__global__ void __launch_bounds__(WAVES * 64)
+__global__ void __launch_bounds__(WAVES * 64, 8 / WAVES)
 score_topk_mfma_kernel(ScoreArgs a, const uint16_t *__restrict__ u_hi, const uint16_t *__restrict__ u_lo,
                        const uint16_t *__restrict__ m_hi, const uint16_t *__restrict__ m_lo, int RP_arg) {
   const int RP = QR >= 0 ? 32 * QR : RP_arg;
@@ -319,7 +319,6 @@ score_topk_mfma_kernel(ScoreArgs a, const uint16_t *__restrict__ u_hi, const uin
   constexpr int kSlK = IC * D * 2 / 1024;  // k' slices
   const int Pm = RP / 8;                  // pieces per m row
   const int slm = qcal ? IC * RP * 2 / 1024 : 0;  // m slices (hi or lo)
-  float bs_reg = 0.f;
   auto issue_item = [&](int x, int buf) {
     const int hh = x / nblk, cb = x % nblk;
     const int h = g * G + hh, c0 = cb * IC;
@@ -341,17 +340,11 @@ score_topk_mfma_kernel(ScoreArgs a, const uint16_t *__restrict__ u_hi, const uin
         src = (lohi ? m_lo : m_hi) + ((static_cast<size_t>(b) * Hq + h) * C + c) * RP + ((pp ^ score_swz(r, Pm)) << 3);
         dst = (lohi ? item_ml(buf) : item_mh(buf)) + part * 512;
       }
-      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)dst, 16, 0, 0);
+      lds_dma16(src, lds_address(dst));
     }
-    const int wb = wave - (WAVES - 2);  // 0 or 1 for the last two waves
-    if (wb >= 0) {
-      const int c = c0 + 64 * wb + lane;
-      bs_reg = (64 * wb + lane < IC && c < C) ? a.b_sum[(static_cast<size_t>(b) * Hq + h) * C + c] : 0.f;
-    }
-  };
-  auto finish_item = [&](int buf) {
-    const int wb = wave - (WAVES - 2);
-    if (wb >= 0 && 64 * wb + lane < IC) item_bs(buf)[64 * wb + lane] = bs_reg;
+    static_assert(IC == 64, "one entropy piece per lane");
+    if (wave == WAVES - 1)  // rows past C are never used
+      lds_dma4(a.b_sum + (static_cast<size_t>(b) * Hq + h) * C + min(c0 + lane, C - 1), lds_address(item_bs(buf)));
   };
 
   // Q operands of head hh: lane holds query ln, d = 32 s + 8 lg .. +8
@@ -406,12 +399,12 @@ score_topk_mfma_kernel(ScoreArgs a, const uint16_t *__restrict__ u_hi, const uin
   // each head's score into sc).  PASS 2 (HR = 0): each head's own score of
   // the winners into topk_score (the same arithmetic as pass 1, so the
   // values are bit-identical).
+  // Item x + 1 streams into the other buffer while item x computes; the DMA
+  // is invisible to the compiler's waits (its LDS reads of item x do not
+  // wait for it) and each wave waits for its own loads before the barrier.
   auto run_pass = [&](bool pass2) {
-    if (nitems > 0) {
-      issue_item(0, 0);
-      __builtin_amdgcn_s_waitcnt(0);
-      finish_item(0);
-    }
+    if (nitems > 0) issue_item(0, 0);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     for (int x = 0; x < nitems; ++x) {
       const int buf = x & 1;
@@ -448,7 +441,6 @@ score_topk_mfma_kernel(ScoreArgs a, const uint16_t *__restrict__ u_hi, const uin
         }
       }
       __builtin_amdgcn_s_waitcnt(0);
-      if (x + 1 < nitems) finish_item(buf ^ 1);
       __syncthreads();
     }
   };
@@ -720,7 +712,6 @@ score_topk_stream_kernel(ScoreArgs a, const uint16_t *__restrict__ u_hi, const u
   constexpr int kSlK = IC * D * 2 / 1024;
   const int Pm = RP / 8;
   const int slm = qcal ? IC * RP * 2 / 1024 : 0;
-  float bs_reg = 0.f;
   auto issue_item = [&](int x, int buf) {
     const int hh = x % G, cb = x / G;
     const int h = g * G + hh, c0 = cb * IC;
@@ -741,15 +732,10 @@ score_topk_stream_kernel(ScoreArgs a, const uint16_t *__restrict__ u_hi, const u
         src = (lohi ? m_lo : m_hi) + ((static_cast<size_t>(b) * Hq + h) * C + c) * RP + ((pp ^ score_swz(r, Pm)) << 3);
         dst = (lohi ? item_ml(buf) : item_mh(buf)) + part * 512;
       }
-      __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)dst, 16, 0, 0);
+      lds_dma16(src, lds_address(dst));
     }
-    if (wave == WAVES - 1) {
-      const int c = c0 + lane;
-      bs_reg = c < C ? a.b_sum[(static_cast<size_t>(b) * Hq + h) * C + c] : 0.f;
-    }
-  };
-  auto finish_item = [&](int buf) {
-    if (wave == WAVES - 1) item_bs(buf)[lane] = bs_reg;
+    if (wave == WAVES - 1)  // the entropies, one 4-byte piece per lane (rows past C are never used)
+      lds_dma4(a.b_sum + (static_cast<size_t>(b) * Hq + h) * C + min(c0 + lane, C - 1), lds_address(item_bs(buf)));
   };
   // s of chunk tile ctl of the staged item for head hh
   auto score_tile = [&](int buf, int ctl, const uint4 (&qh)[KS]) -> f32x4s {
@@ -793,11 +779,11 @@ score_topk_stream_kernel(ScoreArgs a, const uint16_t *__restrict__ u_hi, const u
   unsigned long long theta = kNoKey;  // the query's smallest kept key
   float scb[GM][16];                  // this block's scores: candidate v = chunk 16 (v >> 2) + 4 lg + (v & 3)
 
-  if (nitems > 0) {
-    issue_item(0, 0);
-    __builtin_amdgcn_s_waitcnt(0);
-    finish_item(0);
-  }
+  // Item x + 1 streams into the other buffer while item x computes (the
+  // DMA is invisible to the compiler's waits, so LDS reads of item x do not
+  // wait for it); each wave waits for its own loads before the barrier.
+  if (nitems > 0) issue_item(0, 0);
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   for (int x = 0; x < nitems; ++x) {
     const int buf = x & 1;
@@ -817,7 +803,6 @@ score_topk_stream_kernel(ScoreArgs a, const uint16_t *__restrict__ u_hi, const u
       }
     }
     __builtin_amdgcn_s_waitcnt(0);
-    if (x + 1 < nitems) finish_item(buf ^ 1);
     __syncthreads();
     if (hh != G - 1 || IC * cb >= n_wave) continue;
     // ---- block cb complete: merge its candidates into the running lists
@@ -986,10 +971,10 @@ hipError_t launch_score_mfma(const ScoreArgs &a, hipStream_t st) {
     kern<<<dim3((a.T + WW * 16 - 1) / (WW * 16) * a.Hkv * a.B), WW * 64, smem, st>>>(a, u_hi, u_lo, m_hi, m_lo, RPa); \
     return hipGetLastError();                                                                             \
   }
-  HILS_SCORE(128, 1, 8, 4, 0) HILS_SCORE(128, 1, 8, 4, 1) HILS_SCORE(128, 1, 8, 4, 2)
-  HILS_SCORE(128, 2, 8, 4, 0) HILS_SCORE(128, 2, 8, 4, 1) HILS_SCORE(128, 2, 8, 4, 2)
-  HILS_SCORE(64, 1, 8, 4, 0) HILS_SCORE(64, 1, 8, 4, 1) HILS_SCORE(64, 1, 8, 4, 2)
-  HILS_SCORE(64, 2, 8, 4, 0) HILS_SCORE(64, 2, 8, 4, 1) HILS_SCORE(64, 2, 8, 4, 2)
+  HILS_SCORE(128, 1, 4, 4, 0) HILS_SCORE(128, 1, 4, 4, 1) HILS_SCORE(128, 1, 4, 4, 2)
+  HILS_SCORE(128, 2, 4, 4, 0) HILS_SCORE(128, 2, 4, 4, 1) HILS_SCORE(128, 2, 4, 4, 2)
+  HILS_SCORE(64, 1, 4, 4, 0) HILS_SCORE(64, 1, 4, 4, 1) HILS_SCORE(64, 1, 4, 4, 2)
+  HILS_SCORE(64, 2, 4, 4, 0) HILS_SCORE(64, 2, 4, 4, 1) HILS_SCORE(64, 2, 4, 4, 2)
   HILS_SCORE(128, 1, 8, 0, -1) HILS_SCORE(128, 2, 8, 0, -1) HILS_SCORE(128, 4, 4, 0, -1)
   HILS_SCORE(64, 1, 8, 0, -1) HILS_SCORE(64, 2, 8, 0, -1) HILS_SCORE(64, 4, 4, 0, -1)
 #undef HILS_SCORE
