@@ -242,9 +242,15 @@ struct ScoreItemLayout {
     bytes = bs + IC * 4;
   }
 };
+// The two staged items share their space with the score write-out that
+// follows the selection (256 K bytes per wave): whichever is larger.
+__host__ __device__ inline int score_stage_area(int item_bytes, int waves, int K) {
+  return 2 * item_bytes > waves * 256 * K ? 2 * item_bytes : waves * 256 * K;
+}
 template <int D, int NJ, int WAVES>
-size_t score_smem_bytes(int IC, int RP) {
-  return 2 * static_cast<size_t>(ScoreItemLayout(D, IC, RP).bytes) + sizeof(ScoreSelect<D, NJ, WAVES>);
+size_t score_smem_bytes(int IC, int RP, int K) {
+  return static_cast<size_t>(score_stage_area(ScoreItemLayout(D, IC, RP).bytes, WAVES, K)) +
+         sizeof(ScoreSelect<D, NJ, WAVES>);
 }
 
 // swizzled piece of logical piece pc in row r of a row of P pieces (P = 4, 8, 16)
@@ -271,7 +277,8 @@ score_topk_mfma_kernel(ScoreArgs a, const uint16_t *__restrict__ u_hi, const uin
   constexpr int TPI = IC / 16;        // chunk tiles per item
   extern __shared__ __align__(16) unsigned char smem_raw[];
   const ScoreItemLayout lay(D, IC, RP);
-  ScoreSelect<D, NJ, WAVES> &sm = *reinterpret_cast<ScoreSelect<D, NJ, WAVES> *>(smem_raw + 2 * lay.bytes);
+  ScoreSelect<D, NJ, WAVES> &sm =
+      *reinterpret_cast<ScoreSelect<D, NJ, WAVES> *>(smem_raw + score_stage_area(lay.bytes, WAVES, a.K));
   auto item_ks = [&](int buf) { return reinterpret_cast<uint16_t *>(smem_raw + buf * lay.bytes + lay.ks); };
   auto item_mh = [&](int buf) { return reinterpret_cast<uint16_t *>(smem_raw + buf * lay.bytes + lay.mh); };
   auto item_ml = [&](int buf) { return reinterpret_cast<uint16_t *>(smem_raw + buf * lay.bytes + lay.ml); };
@@ -533,7 +540,10 @@ score_topk_mfma_kernel(ScoreArgs a, const uint16_t *__restrict__ u_hi, const uin
       need_eq = m == 0xFFFFu ? 0 : need_eq - 1;
     }
   }
-  // compact each query's winners (in lane-row order) into LDS
+  // compact each query's winners (in lane-row order) into LDS; with HR,
+  // each winner's per-head scores go beside it, into this wave's part of
+  // the staging space (free after the last item): [query][position] x 4
+  float4 *wsc = reinterpret_cast<float4 *>(smem_raw + wave * 256 * K);
   {
     uint32_t pos = uprefix_rows4(static_cast<uint32_t>(NV > 32 ? __popcll(winm) : __popc(static_cast<uint32_t>(winm))));
 #pragma unroll
@@ -543,6 +553,7 @@ score_topk_mfma_kernel(ScoreArgs a, const uint16_t *__restrict__ u_hi, const uin
         // the higher score, then the lower chunk)
         sm.win[wave][ln][pos] = (static_cast<unsigned long long>(ord[v]) << 32) |
                                 (0xFFFFu - static_cast<uint32_t>(16 * (v >> 2) + 4 * lg + (v & 3)));
+        if constexpr (HR > 0) wsc[ln * K + pos] = make_float4(sc[0][v], sc[1][v], sc[2][v], sc[3][v]);
         ++pos;
       }
     }
@@ -555,10 +566,12 @@ score_topk_mfma_kernel(ScoreArgs a, const uint16_t *__restrict__ u_hi, const uin
     constexpr int PPL = 8;  // winners per lane (K <= 32); j < ceil(K / 4) used
     unsigned long long pk[PPL];
     int pr[PPL];
+    float4 ps[HR > 0 ? PPL : 1];  // the winners' per-head scores (HR)
 #pragma unroll
     for (int j = 0; j < PPL; ++j) {
       const int p = lg + 4 * j;
       pk[j] = (4 * j < K && p < keep) ? sm.win[wave][ln][p] : 0ull;
+      if constexpr (HR > 0) ps[j] = (4 * j < K && p < keep) ? wsc[ln * K + p] : make_float4(0.f, 0.f, 0.f, 0.f);
       pr[j] = 0;
     }
     const ulonglong2 *row = reinterpret_cast<const ulonglong2 *>(&sm.win[wave][ln][0]);
@@ -586,26 +599,47 @@ score_topk_mfma_kernel(ScoreArgs a, const uint16_t *__restrict__ u_hi, const uin
     // padding of the lists past keep
     if (q_ok) {
       for (int k = keep + lg; k < K; k += 4) a.topk_idx[ibase + k] = -1;
+      if constexpr (HR == 0) {
+        for (int x = lg; x < G * (K - keep); x += 4) {
+          const int hh = x / (K - keep), k = keep + x % (K - keep);
+          a.topk_score[((static_cast<size_t>(b) * Hq + g * G + hh) * T + i_me) * K + k] = -INFINITY;
+        }
+      }
+    }
+    if constexpr (HR > 0) {
+      // ---- each head's own score of the winners in list order: the
+      // wave's lists [head][query][K] in LDS (over the parked scores, which
+      // are in registers now), then one contiguous run per head: the 16
+      // queries' lists of a head follow each other in topk_score
+      __builtin_amdgcn_wave_barrier();
+      float *wout = reinterpret_cast<float *>(wsc);
+#pragma unroll
+      for (int j = 0; j < PPL; ++j) {
+        const int p = lg + 4 * j;
+        if (4 * j >= K) break;
+        if (p < keep) {
+          const float s4[4] = {ps[j].x, ps[j].y, ps[j].z, ps[j].w};
+#pragma unroll
+          for (int h2 = 0; h2 < HR; ++h2)
+            if (h2 < G) wout[(h2 * 16 + ln) * K + pr[j]] = s4[h2];
+        }
+      }
       for (int x = lg; x < G * (K - keep); x += 4) {
         const int hh = x / (K - keep), k = keep + x % (K - keep);
-        a.topk_score[((static_cast<size_t>(b) * Hq + g * G + hh) * T + i_me) * K + k] = -INFINITY;
+        wout[(hh * 16 + ln) * K + k] = -INFINITY;
+      }
+      __builtin_amdgcn_wave_barrier();
+      const int nvalid = (qw0 < T ? min(16, T - qw0) : 0) * K;  // rows past T are not written
+      for (int h2 = 0; h2 < G; ++h2) {
+        float *dst = a.topk_score + ((static_cast<size_t>(b) * Hq + g * G + h2) * T + qw0) * K;
+        for (int e = lane; e < nvalid; e += 64) dst[e] = wout[h2 * 16 * K + e];
       }
     }
   }
   __builtin_amdgcn_wave_barrier();
 
   if constexpr (HR > 0) {
-    // ---- each head's own score of the winners, from registers
-#pragma unroll
-    for (int v = 0; v < NV; ++v) {
-      if ((winm >> v) & 1u) {
-        const int c = 16 * (v >> 2) + 4 * lg + (v & 3);
-        const int rk = sm.rtab[wave][ln][c];
-#pragma unroll
-        for (int h2 = 0; h2 < HR; ++h2)
-          if (h2 < G) a.topk_score[((static_cast<size_t>(b) * Hq + g * G + h2) * T + i_me) * K + rk] = sc[h2][v];
-      }
-    }
+    // (the per-head scores were written with the lists above)
   } else {
 #pragma unroll
     for (int v = 0; v < NV; ++v) {
@@ -964,7 +998,7 @@ hipError_t launch_score_mfma(const ScoreArgs &a, hipStream_t st) {
 #define HILS_SCORE(DD, NN, WW, HRR, QRR)                                                                    \
   if (a.d == DD && nj == NN && hr == HRR && (QRR < 0 || qr == QRR)) {                                     \
     auto kern = score_topk_mfma_kernel<DD, NN, WW, 64, HRR, QRR>;                                         \
-    const size_t smem = score_smem_bytes<DD, NN, WW>(64, RPa);                                           \
+    const size_t smem = score_smem_bytes<DD, NN, WW>(64, RPa, a.K);                                      \
     hipError_t e2 = hipFuncSetAttribute(reinterpret_cast<const void *>(kern),                              \
                                         hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(smem)); \
     if (e2 != hipSuccess) return e2;                                                                      \
