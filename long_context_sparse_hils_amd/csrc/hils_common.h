@@ -240,6 +240,10 @@ __device__ __forceinline__ void reset_counter(unsigned *counter) {
 }
 
 
+// Word 3 of a raw buffer resource for gfx9 (32-bit data format, so that
+// untyped loads return data; no swizzle, no index stride).
+constexpr int kBufWord3 = 0x00020000;
+
 // ---------------------------------------------------------------- LDS DMA
 // A wave-wide load from global memory straight into LDS: lane l's bytes
 // (16 or 4) land at LDS byte address lds_base + size * l, lds_base being

@@ -336,7 +336,17 @@ attn_chunks_kernel(AttnArgs a, const uint16_t *__restrict__ ops, float *__restri
   // chunk's K as soon as that tile's S^T has read K, its V^T as soon as the
   // tile's last product has read V^T.
   constexpr int kKB = 4 * C::kKS, kVB = 2 * C::kDT;  // 1 KB operand blocks of a chunk
-  const uint16_t *opg = ops + static_cast<size_t>(pair) * C_chunks * (kKB + kVB) * 512 + lane * 8;
+  // the pair's operand-order blocks through a buffer resource: the block's
+  // byte offset is a scalar (soffset), the lane's 16 bytes the vector offset
+  // (no per-block address arithmetic on the vector unit)
+  const __amdgpu_buffer_rsrc_t oprs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t *>(ops + static_cast<size_t>(pair) * C_chunks * (kKB + kVB) * 512), static_cast<short>(0),
+      C_chunks * (kKB + kVB) * 1024, kBufWord3);
+  const uint32_t op_lane = lane * 16;
+  auto op_block = [&](int byte_off) -> uint4 {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(oprs, op_lane, byte_off, 0);
+    return make_uint4(v[0], v[1], v[2], v[3]);
+  };
   const uint16_t *qb = static_cast<const uint16_t *>(a.q);
   const int s_slot = ln / G, hh = ln % G;  // this lane's column: query slot, head
   const float tl2e = a.tau * kL2e;
@@ -350,32 +360,38 @@ attn_chunks_kernel(AttnArgs a, const uint16_t *__restrict__ ops, float *__restri
     int row;
     bool valid;
   };
+  // the block's query rows and fusion scores from workgroup-uniform bases
+  // with 32-bit per-lane offsets (head hh of the group: hh T rows further;
+  // G T D < 2^32 for the sequences this pass takes)
+  const char *qwg = reinterpret_cast<const char *>(qb + ((static_cast<size_t>(b) * Hq + g * G) * T + q0) * D);
+  const char *swg = reinterpret_cast<const char *>(a.topk_score + ((static_cast<size_t>(b) * Hq + g * G) * T + q0) * K);
+  const uint32_t qlane = (static_cast<uint32_t>(hh) * static_cast<uint32_t>(T) * D + 8 * lg) * 2;  // bytes
+  const uint32_t slane = static_cast<uint32_t>(hh) * static_cast<uint32_t>(T) * static_cast<uint32_t>(K) * 4;
   auto load_col = [&](Col &cl, int seg0, int cnt, int t) {
     const int e = t * C::kQPT + s_slot;
     cl.valid = e < cnt;
     const int ent = sm.slist[seg0 + min(e, cnt - 1)];
-    const int q = ent & 0xFF, k = ent >> 8;
+    const uint32_t q = ent & 0xFF, k = ent >> 8;
     cl.row = q * G + hh;
-    const size_t ro = (static_cast<size_t>(b) * Hq + g * G + hh) * T + (q0 + q);
-    const uint16_t *qr = qb + ro * D;
+    const uint32_t qo = qlane + q * (D * 2);
 #pragma unroll
-    for (int s = 0; s < C::kKS; ++s) cl.qop[s] = *reinterpret_cast<const uint4 *>(qr + 32 * s + 8 * lg);
-    cl.sh = a.topk_score[ro * K + k];
+    for (int s = 0; s < C::kKS; ++s) cl.qop[s] = *reinterpret_cast<const uint4 *>(qwg + (qo + 64 * s));
+    cl.sh = *reinterpret_cast<const float *>(swg + (slane + (q * static_cast<uint32_t>(K) + k) * 4));
   };
   uint4 kop[4][C::kKS], vop[C::kDT][2];
   auto load_k = [&](int c) {  // blocks kt * kKS + s of the chunk's operand order
-    const uint16_t *kc = opg + static_cast<size_t>(c) * (kKB + kVB) * 512;
+    const int kc = c * (kKB + kVB) * 1024;
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt)
 #pragma unroll
-      for (int s = 0; s < C::kKS; ++s) kop[kt][s] = *reinterpret_cast<const uint4 *>(kc + (kt * C::kKS + s) * 512);
+      for (int s = 0; s < C::kKS; ++s) kop[kt][s] = op_block(kc + (kt * C::kKS + s) * 1024);
   };
   auto load_v = [&](int c) {  // blocks kKB + 2 dt + sl
-    const uint16_t *vc = opg + (static_cast<size_t>(c) * (kKB + kVB) + kKB) * 512;
+    const int vc = (c * (kKB + kVB) + kKB) * 1024;
 #pragma unroll
     for (int dt = 0; dt < C::kDT; ++dt)
 #pragma unroll
-      for (int sl = 0; sl < 2; ++sl) vop[dt][sl] = *reinterpret_cast<const uint4 *>(vc + (2 * dt + sl) * 512);
+      for (int sl = 0; sl < 2; ++sl) vop[dt][sl] = op_block(vc + (2 * dt + sl) * 1024);
   };
   auto ticket = [&]() -> int {
     int x = 0;
@@ -390,7 +406,7 @@ attn_chunks_kernel(AttnArgs a, const uint16_t *__restrict__ ops, float *__restri
     const int x = ticket();
     live = x < nunion;
     if (live) {
-      const int c = sm.ulist[x];
+      const int c = __builtin_amdgcn_readfirstlane(sm.ulist[x]);  // uniform: one LDS slot
       seg0 = sm.useg[x];
       cnt = sm.ucnt[x];
       ntile = (cnt + C::kQPT - 1) / C::kQPT;
@@ -417,7 +433,7 @@ attn_chunks_kernel(AttnArgs a, const uint16_t *__restrict__ ops, float *__restri
       const int xn = ticket();
       more = xn < nunion;
       if (more) {
-        cn = sm.ulist[xn];
+        cn = __builtin_amdgcn_readfirstlane(sm.ulist[xn]);  // uniform: one LDS slot
         segn = sm.useg[xn];
         cntn = sm.ucnt[xn];
         load_k(cn);
