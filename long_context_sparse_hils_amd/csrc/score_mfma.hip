@@ -683,10 +683,11 @@ __device__ __forceinline__ unsigned long long umax64_rows4(unsigned long long v)
 }
 __device__ __forceinline__ unsigned long long umin64_rows4(unsigned long long v) { return ~umax64_rows4(~v); }
 
-template <int D, int WAVES, int KPL>
+template <int D, int WAVES, int KPL, int QR>
 __global__ void __launch_bounds__(WAVES * 64)
 score_topk_stream_kernel(ScoreArgs a, const uint16_t *__restrict__ u_hi, const uint16_t *__restrict__ u_lo,
-                         const uint16_t *__restrict__ m_hi, const uint16_t *__restrict__ m_lo, int RP) {
+                         const uint16_t *__restrict__ m_hi, const uint16_t *__restrict__ m_lo) {
+  constexpr int RP = 32 * QR;  // Q-Cal rank padded to the MFMA k-step (0: no Q-Cal)
   constexpr int KS = D / 32;
   constexpr int IC = 64;         // chunks per block
   constexpr int QW = WAVES * 16;  // queries per workgroup
@@ -708,7 +709,7 @@ score_topk_stream_kernel(ScoreArgs a, const uint16_t *__restrict__ u_hi, const u
   const int nqb = (T + QW - 1) / QW;
   const int q_wg = (nqb - 1 - xq) * QW;
   const int qw0 = q_wg + wave * 16;
-  const bool qcal = a.r > 0;
+  constexpr bool qcal = QR > 0;
   const int i_me = qw0 + ln;
   const bool q_ok = i_me < T;
   const int n_me = q_ok ? min(eligible_chunks(i_me, a.W, a.S), C) : 0;
@@ -740,12 +741,17 @@ score_topk_stream_kernel(ScoreArgs a, const uint16_t *__restrict__ u_hi, const u
     for (int s = 0; s < KS; ++s)
       qv[hh][s] = (q_ok && hh < G) ? *reinterpret_cast<const uint4 *>(qb + qo + 32 * s) : make_uint4(0, 0, 0, 0);
   }
+  // The operands above are complete before the streaming loop: otherwise
+  // the compiler, not knowing that a head's first product in an iteration
+  // follows the same loads, waits for every memory operation in flight (the
+  // staged item included) before it on every item.
+  __builtin_amdgcn_s_waitcnt(0);
 
   // ---- staging of item x = (chunk block x / G, head x % G), as above
   constexpr int kPk = D / 8;
   constexpr int kSlK = IC * D * 2 / 1024;
-  const int Pm = RP / 8;
-  const int slm = qcal ? IC * RP * 2 / 1024 : 0;
+  constexpr int Pm = RP / 8;
+  constexpr int slm = IC * RP * 2 / 1024;
   auto issue_item = [&](int x, int buf) {
     const int hh = x % G, cb = x / G;
     const int h = g * G + hh, c0 = cb * IC;
@@ -931,11 +937,12 @@ bool score_mfma_supported(const ScoreArgs &a) {
          (a.r == 0 || (a.Dh % 32 == 0 && a.r <= 64));
 }
 
-template <int D, int KPL>
-static hipError_t launch_score_stream(const ScoreArgs &a, const uint16_t *u_hi, const uint16_t *u_lo,
-                                      const uint16_t *m_hi, const uint16_t *m_lo, int RPa, hipStream_t st) {
+template <int D, int KPL, int QR>
+static hipError_t launch_score_stream_q(const ScoreArgs &a, const uint16_t *u_hi, const uint16_t *u_lo,
+                                        const uint16_t *m_hi, const uint16_t *m_lo, hipStream_t st) {
   constexpr int WAVES = 8;
-  auto kern = score_topk_stream_kernel<D, WAVES, KPL>;
+  constexpr int RPa = 32 * QR;
+  auto kern = score_topk_stream_kernel<D, WAVES, KPL, QR>;
   const size_t items = 2 * static_cast<size_t>(ScoreItemLayout(D, 64, RPa).bytes);
   const size_t lists = static_cast<size_t>(WAVES) * 16 * 4 * KPL * sizeof(unsigned long long);
   const size_t smem = items > lists ? items : lists;
@@ -943,8 +950,15 @@ static hipError_t launch_score_stream(const ScoreArgs &a, const uint16_t *u_hi, 
                                      static_cast<int>(smem));
   if (e != hipSuccess) return e;
   kern<<<dim3((a.T + WAVES * 16 - 1) / (WAVES * 16) * a.Hkv * a.B), WAVES * 64, smem, st>>>(a, u_hi, u_lo, m_hi,
-                                                                                            m_lo, RPa);
+                                                                                            m_lo);
   return hipGetLastError();
+}
+template <int D, int KPL>
+static hipError_t launch_score_stream(const ScoreArgs &a, const uint16_t *u_hi, const uint16_t *u_lo,
+                                      const uint16_t *m_hi, const uint16_t *m_lo, int RPa, hipStream_t st) {
+  if (RPa == 0) return launch_score_stream_q<D, KPL, 0>(a, u_hi, u_lo, m_hi, m_lo, st);
+  if (RPa == 32) return launch_score_stream_q<D, KPL, 1>(a, u_hi, u_lo, m_hi, m_lo, st);
+  return launch_score_stream_q<D, KPL, 2>(a, u_hi, u_lo, m_hi, m_lo, st);
 }
 
 size_t score_mfma_ws_bytes(int B, int T, int Hq, int C, int r) {
