@@ -180,23 +180,27 @@ attn_chunks_kernel(AttnArgs a, const uint16_t *__restrict__ ops, float *__restri
   const float *tsc_b = a.topk_score + static_cast<size_t>(b) * Hq * T * K;
 
   // ---- set-up.  Every global load is issued at once, with clamped indices
-  // and no lane-dependent branch: the block's selections (entry (q, k)) and
-  // the rows' fusion scores ([q][hh][k]).
+  // and no lane-dependent branch: the block's selections (entry (q, k)),
+  // and for the row statistics each row's chunk ids and fusion scores, two
+  // threads per row (thread t: row t / 2, list half t % 2).
   constexpr int kEPT = (C::kEnt + C::kThreads - 1) / C::kThreads;
-  constexpr int kSPT = (C::kRows * K_MAX + C::kThreads - 1) / C::kThreads;
+  constexpr int KH = K_MAX / 2;
+  static_assert(2 * C::kRows <= C::kThreads, "two threads per row");
   const int kmax = K - 1;
   int ec[kEPT];
-  float sv[kSPT];
 #pragma unroll
   for (int r = 0; r < kEPT; ++r) {
     const int x = tid + r * C::kThreads, q = x / K_MAX, k = x % K_MAX;
     ec[r] = idx_bg[static_cast<size_t>(min(q0 + q, T - 1)) * K + min(k, kmax)];
   }
+  const int rs_row = min(tid >> 1, C::kRows - 1), rs_k0 = (tid & 1) * KH;
+  const int rs_q = rs_row / G, rs_hh = rs_row % G, rs_i = min(q0 + rs_q, T - 1);
+  int rc[KH];
+  float rv[KH];
 #pragma unroll
-  for (int r = 0; r < kSPT; ++r) {
-    const int x = tid + r * C::kThreads;
-    const int q = x / (G * K_MAX), hh = (x / K_MAX) % G, k = x % K_MAX;
-    sv[r] = tsc_b[(static_cast<size_t>(g * G + hh) * T + min(q0 + q, T - 1)) * K + min(k, kmax)];
+  for (int k = 0; k < KH; ++k) {
+    rc[k] = idx_bg[static_cast<size_t>(rs_i) * K + min(rs_k0 + k, kmax)];
+    rv[k] = tsc_b[(static_cast<size_t>(g * G + rs_hh) * T + rs_i) * K + min(rs_k0 + k, kmax)];
   }
   // B_v of the block needs the largest |v| of every 64-key block it selects
   // (chunk ids below C <= 256 here: one pass covers longer sequences)
@@ -211,42 +215,40 @@ attn_chunks_kernel(AttnArgs a, const uint16_t *__restrict__ ops, float *__restri
   if (tid == 0) sm.next = 0;
   __syncthreads();
   // Entry (q, k) holds chunk c when q0 + q < T, k < K and 0 <= c < n_i (any
-  // other id is no chunk).  Until the grouping below, slist holds each
-  // entry's chunk (or -1) and the accumulator memory the fusion scores.
-  float *wl = reinterpret_cast<float *>(sm.acc);
-  int16_t *ent_c = reinterpret_cast<int16_t *>(sm.slist);
+  // other id is no chunk).
 #pragma unroll
   for (int r = 0; r < kEPT; ++r) {
     const int x = tid + r * C::kThreads, q = x / K_MAX, k = x % K_MAX;
     const int i = q0 + q;
     const bool ok = x < C::kEnt && k < K && i < T && ec[r] >= 0 && ec[r] < eligible_chunks(i, W, kCK);
     ec[r] = ok ? ec[r] : -1;
-    if (x < C::kEnt) ent_c[x] = static_cast<int16_t>(ec[r]);
     if (ok) atomicOr(&sm.umask[ec[r] >> 5], 1u << (ec[r] & 31));
   }
-#pragma unroll
-  for (int r = 0; r < kSPT; ++r) {
-    const int x = tid + r * C::kThreads;
-    if (x < C::kRows * K_MAX) wl[x] = sv[r];
-  }
-  __syncthreads();
   // ---- row statistics: M_row = largest selected chunk score of the row,
   // L_row = sum of e^{s_hat - M_row} over its selected chunks; lse_C of
-  // the row to the workspace (-inf: no chunk)
-  for (int row = tid; row < C::kRows; row += C::kThreads) {
-    const int q = row / G, hh = row % G, i = q0 + q;
-    const float *sr = wl + row * K_MAX;
-    const int16_t *cr = ent_c + q * K_MAX;
-    float mx = -INFINITY, l = 0.f;
+  // the row to the workspace (-inf: no chunk).  The two halves of a row
+  // meet by a lane swap.
+  {
+    const int i = q0 + rs_q, n = eligible_chunks(i, W, kCK);
+    bool okk[KH];
+    float mx = -INFINITY;
 #pragma unroll
-    for (int k = 0; k < K_MAX; ++k) mx = cr[k] >= 0 ? fmaxf(mx, sr[k]) : mx;
+    for (int k = 0; k < KH; ++k) {
+      okk[k] = rs_k0 + k < K && i < T && rc[k] >= 0 && rc[k] < n;
+      mx = okk[k] ? fmaxf(mx, rv[k]) : mx;
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 1, 64));
+    float l = 0.f;
     if (mx > -INFINITY) {
 #pragma unroll
-      for (int k = 0; k < K_MAX; ++k) l += cr[k] >= 0 ? __expf(sr[k] - mx) : 0.f;
+      for (int k = 0; k < KH; ++k) l += okk[k] ? __expf(rv[k] - mx) : 0.f;
     }
-    if (i < T) lse_out[(static_cast<size_t>(b) * Hq + g * G + hh) * T + i] = l > 0.f ? mx + __logf(l) : -INFINITY;
-    sm.row_m[row] = mx;
-    sm.row_il[row] = l > 0.f ? 1.f / l : 0.f;
+    l += __shfl_xor(l, 1, 64);
+    if ((tid & 1) == 0 && (tid >> 1) < C::kRows) {
+      if (i < T) lse_out[(static_cast<size_t>(b) * Hq + g * G + rs_hh) * T + i] = l > 0.f ? mx + __logf(l) : -INFINITY;
+      sm.row_m[rs_row] = mx;
+      sm.row_il[rs_row] = l > 0.f ? 1.f / l : 0.f;
+    }
   }
   __syncthreads();
   // ---- clear the accumulators; union positions in ascending chunk order
