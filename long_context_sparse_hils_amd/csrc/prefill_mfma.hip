@@ -364,6 +364,31 @@ attn_window_mfma_kernel(AttnArgs a, int ntiles, int xcd_map, int nblk) {
       lds_dma16(vsrc + static_cast<uint32_t>(d * kItemKeys + pc * 8), lds_address(sm.vt[buf] + slice * 512));
     }
   };
+  // The rows' chunk parts (bf16, written into o by the chunk pass) for the
+  // epilogue, into the idle buffer during the last block: the workgroup's
+  // kQT G = 128 rows of 2 D bytes fill the K and V^T halves of one buffer
+  // exactly (rows 0 .. 63, then 64 .. 127).  Row R's 16-byte piece p sits at
+  // position p ^ (R mod pieces), so that the 16 rows one epilogue read
+  // touches fall in 16 different bank groups.  Wave w loads its own rows
+  // 32 w .. 32 w + 31, one 1 KB slice per instruction.
+  constexpr int kPartPieces = 2 * D / 16;
+  static_assert(C::kQT * G == 128 && 2 * kItemKeys * D == 128 * D, "the parts fill one staging buffer");
+  auto part_row = [&](int t, int bufp, int R) -> uint16_t * {
+    return (R < 64 ? sm.ks[bufp] : sm.vt[bufp]) + (R & 63) * D;
+  };
+  auto issue_parts = [&](int bufp) {
+    const uint16_t *ob_in = static_cast<const uint16_t *>(a.o);
+    constexpr int kRowsPerSlice = 1024 / (2 * D);
+#pragma unroll
+    for (int sl = 0; sl < 32 / kRowsPerSlice; ++sl) {
+      const int R = wave * 32 + sl * kRowsPerSlice + lane / kPartPieces;  // this lane's row
+      const int pp = lane % kPartPieces, pc = pp ^ (R % kPartPieces);
+      const int t = (R >> 4) & (TPW - 1), c = R & 15;                      // its tile and column
+      const int qi = min(q0 + wave * C::kQPW + t * C::kQPT + c / G, T - 1);
+      const uint16_t *src = ob_in + ((static_cast<size_t>(b) * Hq + g * G + c % G) * T + qi) * D + pc * 8;
+      lds_dma16(src, lds_address(part_row(t, bufp, wave * 32 + sl * kRowsPerSlice)));
+    }
+  };
   issue_loads(jw0, 0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
@@ -378,16 +403,13 @@ attn_window_mfma_kernel(AttnArgs a, int ntiles, int xcd_map, int nblk) {
 
   const float tau = a.tau;
   const float tl2e = tau * kLog2e;
-  for (int x = 0; x < nitems; ++x) {
+  // one block: query i's window starts at n_i * S, a multiple of the block
+  // size (S = 64): a block lies in it from its first key on, up to key i,
+  // or not at all.  lim: the last key of the block the row takes, as a
+  // lane-relative offset (key - j0 - 8 lg); -1 takes none.
+  auto block = [&](int x) {
     const int buf = x & 1;
     const int j0 = jw0 + x * kItemKeys;
-    // buffer buf ^ 1 was last read in iteration x - 1, before the barrier
-    // that ended it
-    if (x + 1 < nitems) issue_loads(j0 + kItemKeys, buf ^ 1);
-    // Query i's window starts at n_i * S, a multiple of the block size
-    // (S = 64): a block lies in it from its first key on, up to key i, or
-    // not at all.  lim: the last key of the block the row takes, as a
-    // lane-relative offset (key - j0 - 8 lg); -1 takes none.
     int lim[TPW];
     int mask = 0;
     bool edge = false;
@@ -410,10 +432,22 @@ attn_window_mfma_kernel(AttnArgs a, int ntiles, int xcd_map, int nblk) {
       run_item<D, TPW, true>(mask, R, sm.ks[buf], sm.vt[buf], koff, voff, lim, tau, tl2e);
     else
       run_item<D, TPW, false>(mask, R, sm.ks[buf], sm.vt[buf], koff, voff, lim, tau, tl2e);
+  };
+  // Block x + 1 loads into buffer (x + 1) & 1, last read in iteration
+  // x - 1 (before the barrier that ended it).  The last block, peeled off
+  // (the window always holds key i: nitems >= 1), loads the rows' chunk
+  // parts for the epilogue into the buffer it leaves idle instead.
+  for (int x = 0; x + 1 < nitems; ++x) {
+    issue_loads(jw0 + (x + 1) * kItemKeys, (x & 1) ^ 1);
+    block(x);
     // this wave's loads of block x + 1 have landed; after the barrier, all have
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
+  if (a.lse_c) issue_parts(nitems & 1);
+  block(nitems - 1);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
 
   // ---- epilogue: o = acc / l, lane holds d = 16 dt + 4 lg + (0..3) of row ln.
   // With a chunk pass before this one (a.lse_c), o holds each row's chunk
@@ -422,16 +456,20 @@ attn_window_mfma_kernel(AttnArgs a, int ntiles, int xcd_map, int nblk) {
   //   o = (acc e^{m} + o_C e^{lse_C}) / (l e^{m} + e^{lse_C}),
   // both scaled by e^{-max(m, lse_C)} (m, l: the row's window reference and
   // sum; the window always holds key i itself, so m is finite).
-  // The chunk parts of both tiles load at once (one round trip); a row
-  // without a chunk (lse_C = -inf) ignores what its slot holds.
+  // The chunk parts of both tiles, from the buffer the last block left
+  // idle (a row without a chunk, lse_C = -inf, ignores what its slot holds).
   uint16_t *ob = static_cast<uint16_t *>(a.o);
+  const int pbuf = nitems & 1;  // the buffer the last iteration did not read
   uint2 part[TPW][C::kDT];
 #pragma unroll
   for (int t = 0; t < TPW; ++t) {
-    const size_t oo = ((static_cast<size_t>(b) * Hq + row_h) * T + min(row_i[t], T - 1)) * D;
+    const int R = wave * 32 + t * 16 + ln;
+    const uint16_t *pr = part_row(t, pbuf, R);
 #pragma unroll
-    for (int dt = 0; dt < C::kDT; ++dt)
-      part[t][dt] = a.lse_c ? *reinterpret_cast<const uint2 *>(ob + oo + 16 * dt + 4 * lg) : make_uint2(0u, 0u);
+    for (int dt = 0; dt < C::kDT; ++dt) {
+      const int pc = 2 * dt + (lg >> 1), pos = pc ^ (R % kPartPieces);
+      part[t][dt] = a.lse_c ? *reinterpret_cast<const uint2 *>(pr + pos * 8 + (lg & 1) * 4) : make_uint2(0u, 0u);
+    }
   }
 #pragma unroll
   for (int t = 0; t < TPW; ++t) {
