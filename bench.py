@@ -427,7 +427,88 @@ def bench_decode_sweep(args, torch, hils, flush):
                 rows=rows, first_context_sparse_faster=cross)
 
 
-def bench_decode(args, torch, hils, hs, flush, batch, name=None, paged=True):
+class HbmReference:
+    """What a plain streaming read reaches on this GPU at a given byte count:
+    a kernel that reads the bytes once with 16-byte loads
+    (libhils_hbm_ref.so), timed cold (the cache flush runs before each
+    timing) with HIP events on the kernels' stream, best median over a few
+    launch shapes.  A decode step reads tens to hundreds of MB, where launch
+    and ramp-up keep any read below the 8 TB/s peak; the fraction of this
+    line says how far a decode leg sits from a read of its own size.  `copy`
+    is torch's 1 GiB to 1 GiB device copy (2 GiB moved)."""
+
+    SHAPES = [(blocks, unroll) for blocks in (1024, 2048, 4096, 8192) for unroll in (4, 8)]
+
+    def __init__(self, torch, flush, max_bytes=4 << 30, reps=10):
+        import ctypes
+        path = os.path.join(ROOT, "long_context_sparse_hils_amd", "libhils_hbm_ref.so")
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is not built (__graft_entry__.build())")
+        self.lib = ctypes.CDLL(path)
+        self.lib.hbm_ref_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_int,
+                                          ctypes.c_uint32, ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hbm_ref_read.restype = ctypes.c_int
+        self.torch, self.flush, self.reps = torch, flush, reps
+        # all-ones fp32: every 16-byte piece XORs to 0, so the kernel's store
+        # (taken only when a thread's XOR is 1) never happens
+        self.buf = torch.ones(max_bytes // 4, dtype=torch.float32, device="cuda")
+        self.sink = torch.zeros(256, dtype=torch.int32, device="cuda")
+        self.read = {}
+        self.copy = None
+
+    def _time(self, fn):
+        torch = self.torch
+        stream = torch.cuda.current_stream()
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(self.reps):
+            self.flush()
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        return float(np.median(ts))
+
+    def read_gbs(self, nbytes):
+        n = max(4096, min(int(nbytes), self.buf.numel() * 4)) // 16 * 16
+        if n not in self.read:
+            st = self.torch.cuda.current_stream().cuda_stream
+            best = None
+            for blocks, unroll in self.SHAPES:
+                def run():
+                    e = self.lib.hbm_ref_read(self.buf.data_ptr(), n, blocks, unroll, 1, self.sink.data_ptr(), st)
+                    assert e == 0, e
+                ms = self._time(run)
+                if best is None or ms < best[0]:
+                    best = (ms, blocks, unroll)
+            ms, blocks, unroll = best
+            assert int(self.sink.abs().sum()) == 0
+            self.read[n] = dict(bytes=n, us=ms * 1e3, GBps=n / (ms * 1e-3) / 1e9, blocks=blocks, unroll=unroll)
+        return self.read[n]["GBps"]
+
+    def copy_gbs(self):
+        if self.copy is None:
+            n = (1 << 30) // 4
+            src, dst = self.buf[:n], self.buf[n:2 * n]
+            ms = self._time(lambda: dst.copy_(src))
+            self.copy = dict(bytes_moved=2 * n * 4, us=ms * 1e3, GBps=2 * n * 4 / (ms * 1e-3) / 1e9)
+            self.buf[n:2 * n].fill_(1.0)
+        return self.copy["GBps"]
+
+    def record(self):
+        self.read_gbs(self.buf.numel() * 4)
+        self.copy_gbs()
+        return dict(kind="streaming-read kernel (16-byte loads, best median of "
+                         f"{self.reps} over {len(self.SHAPES)} launch shapes), cold cache, HIP events; "
+                         "copy: torch copy_", peak_GBps=PEAK_HBM_GBS,
+                    read=sorted(self.read.values(), key=lambda r: r["bytes"]), copy=self.copy)
+
+
+def bench_decode(args, torch, hils, hs, flush, batch, name=None, paged=True, hbm_ref=None):
     wl = hs.WORKLOADS[name or ("decode_512k_b1" if batch == 1 else "decode_512k_b4")]
     if wl.batch != batch:
         wl = wl.with_(batch=batch)
@@ -489,6 +570,12 @@ def bench_decode(args, torch, hils, hs, flush, batch, name=None, paged=True):
                                                     DECODE_SOURCES),
                              kernel="decode step (score+select kernel, attend+combine kernel)"),
                needle_hits=f"{hits}/{len(inp['needles'])}")
+    if hbm_ref is not None:
+        ref = hbm_ref.read_gbs(nb["total"] * B)
+        out["roofline"]["achievable_read_GBps"] = ref
+        out["roofline"]["frac_of_achievable"] = out["roofline"]["achieved"] / ref
+        log(f"[{wl.name} b{batch}] a plain read of {nb['total'] * B / 1e6:.1f} MB reaches {ref:.0f} GB/s; "
+            f"decode reaches {out['roofline']['achieved']:.0f} GB/s")
     if paged and not args.no_paged:
         # the same caches as a shuffled pool of 64-key pages behind a block table
         S = wl.chunk_size
@@ -699,9 +786,10 @@ def main():
                 line["cpu_baseline"]["decode_512k_b1"] = cpu_baseline_decode(args, oracle, hs_)
         del res
     if args.only in (None, "decode") and not args.no_decode:
+        hbm_ref = HbmReference(torch, flush)
         dec = {}
         for b in [int(x) for x in args.decode_batches.split(",") if x]:
-            dec[f"b{b}"] = bench_decode(args, torch, hils, hs, flush, b)
+            dec[f"b{b}"] = bench_decode(args, torch, hils, hs, flush, b, hbm_ref=hbm_ref)
         line["decode_512k"] = dec
         if not args.no_decode_more:
             # the other decode shapes of the method's efficiency study: 128K
@@ -709,8 +797,13 @@ def main():
             more = {}
             for spec in [x for x in args.decode_shapes.split(",") if x]:
                 nm, bb = spec.split(":")
-                more[f"{nm}_b{bb}"] = bench_decode(args, torch, hils, hs, flush, int(bb), name=nm, paged=False)
+                more[f"{nm}_b{bb}"] = bench_decode(args, torch, hils, hs, flush, int(bb), name=nm, paged=False,
+                                                   hbm_ref=hbm_ref)
             line["decode_more"] = more
+        line["hbm_reference"] = hbm_ref.record()
+        log(f"[hbm] streaming read of 4 GiB {hbm_ref.read_gbs(4 << 30):.0f} GB/s, "
+            f"copy {hbm_ref.copy_gbs():.0f} GB/s")
+        del hbm_ref
         if args.only == "decode" and dec:
             first = dec[next(iter(dec))]
             line.update(value=first["value"], ms_per_step=first["ms_per_step"], roofline=first["roofline"],

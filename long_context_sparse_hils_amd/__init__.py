@@ -13,6 +13,8 @@ import os
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libhils.so")
+# the same C ABI built with HILS_DEBUG_SYNC (LDS race check): see build.py
+DEBUG_SYNC_LIB_PATH = os.path.join(HERE, "libhils_debug_sync.so")
 
 HILS_OK, HILS_ERR_INVALID_ARG, HILS_ERR_UNSUPPORTED, HILS_ERR_WORKSPACE, HILS_ERR_HIP = 0, -1, -2, -3, -4
 HILS_BF16, HILS_F32 = 0, 1
@@ -77,7 +79,17 @@ def _load() -> ctypes.CDLL:
     # device pointers and streams torch hands over are valid in libhils; a
     # second runtime loaded from /opt/rocm would not see torch's allocations.
     import torch  # noqa: F401
-    lib = ctypes.CDLL(LIB_PATH)
+    return open_library(LIB_PATH)
+
+
+def open_library(path: str) -> ctypes.CDLL:
+    """Open a build of the libhils C ABI at `path` with the argument types
+    set.  The functions of this module call the library held in the module
+    variable `lib`; a test may point it at another build of the same sources
+    (the HILS_DEBUG_SYNC build) to compare the two bit for bit."""
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is not built")
+    lib = ctypes.CDLL(path)
     P, C, I32, SZ = ctypes.c_void_p, ctypes.POINTER(Config), ctypes.c_int32, ctypes.c_size_t
     sig = {
         "hils_landmark_summary": [C, P, P, I32, I32, P, P, P],
@@ -243,7 +255,8 @@ def hils_dense_attn_decode(cfg: Config, q, k_cache, v_cache, seq_lens, o, worksp
                                       _stream(stream)), "hils_dense_attn_decode")
 
 
-__all__ = ["Config", "HilsError", "lib", "LIB_PATH", "ENTRY_POINTS", "last_error", "status_string",
+__all__ = ["Config", "HilsError", "lib", "LIB_PATH", "DEBUG_SYNC_LIB_PATH", "open_library", "ENTRY_POINTS",
+           "last_error", "status_string",
            "hils_landmark_summary", "hils_prefill_workspace_bytes", "hils_chunk_score_topk",
            "hils_sparse_attn_prefill", "hils_decode_workspace_bytes", "hils_decode_error_offset",
            "hils_sparse_attn_decode", "hils_dense_decode_workspace_bytes", "hils_dense_attn_decode",

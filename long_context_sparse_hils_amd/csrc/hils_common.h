@@ -240,6 +240,22 @@ __device__ __forceinline__ void reset_counter(unsigned *counter) {
 }
 
 
+// ---------------------------------------------------------------- race check
+// A library built with -DHILS_DEBUG_SYNC (libhils_debug_sync.so) serialises
+// every LDS hand-off that the kernels otherwise leave to ordering: each LDS
+// DMA waits for itself, and debug_sync() adds a full memory wait and a
+// workgroup barrier where a buffer is refilled or a wave reuses LDS after
+// its own earlier phase.  Results must be bit-identical with and without
+// it.  Call sites are reached by every wave of the workgroup the same number
+// of times (the control flow of a neighbouring __syncthreads, or the kernel's
+// top level), never after a return that only some waves take.
+__device__ __forceinline__ void debug_sync() {
+#ifdef HILS_DEBUG_SYNC
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+#endif
+}
+
 // Word 3 of a raw buffer resource for gfx9 (32-bit data format, so that
 // untyped loads return data; no swizzle, no index stride).
 constexpr int kBufWord3 = 0x00020000;
@@ -268,6 +284,9 @@ __device__ __forceinline__ void lds_dma16(const void *src, uint32_t lds_base) {
       : "=&s"(saved)
       : "v"(src), "s"(lds_base)
       : "memory");
+#ifdef HILS_DEBUG_SYNC
+  __builtin_amdgcn_s_waitcnt(0);
+#endif
 }
 __device__ __forceinline__ void lds_dma4(const void *src, uint32_t lds_base) {
   uint32_t saved;
@@ -276,6 +295,9 @@ __device__ __forceinline__ void lds_dma4(const void *src, uint32_t lds_base) {
       : "=&s"(saved)
       : "v"(src), "s"(lds_base)
       : "memory");
+#ifdef HILS_DEBUG_SYNC
+  __builtin_amdgcn_s_waitcnt(0);
+#endif
 }
 
 // R1 partition: complete chunks before query i's window

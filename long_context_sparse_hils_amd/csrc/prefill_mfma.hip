@@ -438,12 +438,14 @@ attn_window_mfma_kernel(AttnArgs a, int ntiles, int xcd_map, int nblk) {
   // (the window always holds key i: nitems >= 1), loads the rows' chunk
   // parts for the epilogue into the buffer it leaves idle instead.
   for (int x = 0; x + 1 < nitems; ++x) {
+    debug_sync();
     issue_loads(jw0 + (x + 1) * kItemKeys, (x & 1) ^ 1);
     block(x);
     // this wave's loads of block x + 1 have landed; after the barrier, all have
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
+  debug_sync();
   if (a.lse_c) issue_parts(nitems & 1);
   block(nitems - 1);
   __builtin_amdgcn_s_waitcnt(0);

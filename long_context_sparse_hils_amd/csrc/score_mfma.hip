@@ -418,6 +418,7 @@ score_topk_mfma_kernel(ScoreArgs a, const uint16_t *__restrict__ u_hi, const uin
       const int hh = x / nblk, cb = x % nblk;
       if (cb == 0) load_q(qv, hh);
       // buffer buf ^ 1 was last read in iteration x - 1, before its barrier
+      debug_sync();
       if (x + 1 < nitems) issue_item(x + 1, buf ^ 1);
 #pragma unroll
       for (int cbb = 0; cbb < NT / TPI + (NT % TPI ? 1 : 0); ++cbb) {
@@ -560,6 +561,7 @@ score_topk_mfma_kernel(ScoreArgs a, const uint16_t *__restrict__ u_hi, const uin
   }
   // (LDS operations of one wave complete in order: no wait needed)
   __builtin_amdgcn_wave_barrier();
+  debug_sync();
   // position of winner p among the query's winners by (score desc, chunk
   // asc); lane (ln, lg) ranks winners p = lg, lg + 4, ...
   {
@@ -612,6 +614,7 @@ score_topk_mfma_kernel(ScoreArgs a, const uint16_t *__restrict__ u_hi, const uin
       // are in registers now), then one contiguous run per head: the 16
       // queries' lists of a head follow each other in topk_score
       __builtin_amdgcn_wave_barrier();
+      debug_sync();
       float *wout = reinterpret_cast<float *>(wsc);
 #pragma unroll
       for (int j = 0; j < PPL; ++j) {
@@ -629,6 +632,7 @@ score_topk_mfma_kernel(ScoreArgs a, const uint16_t *__restrict__ u_hi, const uin
         wout[(hh * 16 + ln) * K + k] = -INFINITY;
       }
       __builtin_amdgcn_wave_barrier();
+      debug_sync();
       const int nvalid = (qw0 < T ? min(16, T - qw0) : 0) * K;  // rows past T are not written
       for (int h2 = 0; h2 < G; ++h2) {
         float *dst = a.topk_score + ((static_cast<size_t>(b) * Hq + g * G + h2) * T + qw0) * K;
@@ -637,6 +641,7 @@ score_topk_mfma_kernel(ScoreArgs a, const uint16_t *__restrict__ u_hi, const uin
     }
   }
   __builtin_amdgcn_wave_barrier();
+  debug_sync();
 
   if constexpr (HR > 0) {
     // (the per-head scores were written with the lists above)
@@ -828,6 +833,7 @@ score_topk_stream_kernel(ScoreArgs a, const uint16_t *__restrict__ u_hi, const u
   for (int x = 0; x < nitems; ++x) {
     const int buf = x & 1;
     const int hh = x % G, cb = x / G;
+    debug_sync();
     if (x + 1 < nitems) issue_item(x + 1, buf ^ 1);
     if (IC * cb < n_wave) {  // wave-uniform: some query of the wave has eligible chunks here
 #pragma unroll
@@ -904,6 +910,7 @@ score_topk_stream_kernel(ScoreArgs a, const uint16_t *__restrict__ u_hi, const u
 
   // ---- the lists in selection order: an entry's position = number of the
   // query's kept keys above it (the staging buffers are free now)
+  debug_sync();
   if (!q_ok) return;
   unsigned long long *lk = reinterpret_cast<unsigned long long *>(smem_raw) + (wave * 16 + ln) * (4 * KPL);
 #pragma unroll

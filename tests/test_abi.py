@@ -32,6 +32,14 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(lib, s), s
 
 
+def test_race_check_build_exports_every_declared_symbol():
+    # the HILS_DEBUG_SYNC build of the same sources (extra LDS barriers)
+    lib = hils.open_library(hils.DEBUG_SYNC_LIB_PATH)
+    for s in declared_symbols():
+        assert hasattr(lib, s), s
+    assert lib.hils_status_string(0).decode() == "HILS_OK"
+
+
 def _cfg(**kw):
     base = dict(batch=2, seq_len=8192, n_q_heads=32, n_kv_heads=8, head_dim=128, chunk_size=64,
                 top_k=16, window=512, qcal_rank=32, hidden_dim=4096, dtype="bf16")
