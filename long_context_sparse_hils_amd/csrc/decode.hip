@@ -265,10 +265,11 @@ __device__ __forceinline__ void combine_slots(const float *recs, int nslots, int
     lv[x] = v.y;
   }
   __syncthreads();
-  // weights e^{m - M} and the normaliser per head: wave 0, slots over lanes
-  if ((t >> 6) == 0) {
+  // weights e^{m - M} and the normaliser per head: one wave per head,
+  // slots over lanes
+  {
     const int lane = t & 63;
-    for (int hh = 0; hh < G; ++hh) {
+    for (int hh = t >> 6; hh < G; hh += kDecThreads / 64) {
       float mloc = -INFINITY;
       for (int s = lane; s < nslots; s += 64) mloc = fmaxf(mloc, w[s * G + hh]);
       const float M = wave_reduce_f32<1>(mloc);
@@ -288,12 +289,16 @@ __device__ __forceinline__ void combine_slots(const float *recs, int nslots, int
     const int hh = p / (D / 2), e2 = p % (D / 2);
     float2 acc = make_float2(0.f, 0.f);
     if (p == t) {
+      // (the weights are read without a branch, so that the reads go out
+      // together; past npre the term is skipped)
+      float wq[kPre];
+#pragma unroll
+      for (int q = 0; q < kPre; ++q) wq[q] = w[(q < npre ? q : 0) * G + hh];
 #pragma unroll
       for (int q = 0; q < kPre; ++q)
         if (q < npre) {
-          const float wq = w[q * G + hh];
-          acc.x += wq * ov[q].x;
-          acc.y += wq * ov[q].y;
+          acc.x += wq[q] * ov[q].x;
+          acc.y += wq[q] * ov[q].y;
         }
     } else {
       for (int q = 0; q < npre; ++q) {
@@ -636,6 +641,32 @@ __device__ __forceinline__ int block_topk(const float *sig, int n, int cmax, int
   return keep;
 }
 
+// After the survivors are in ss.surv[0 .. ss.nsurv) (a barrier behind):
+// one wave selects exactly among them, and the winners are ranked into
+// ss.sorted; too many survivors (many equal scores): block_topk on sig.
+// Returns keep.
+__device__ __forceinline__ int select_ranked(const float *sig, int n, int cmax, int K, SelSmem &ss) {
+  const int t = threadIdx.x, wave = t >> 6;
+  const int tot = ss.nsurv;
+  if (tot > kSurvMax) return block_topk(sig, n, cmax, K, ss);
+  if (wave == 0) {
+    if (tot <= 64)
+      select_survivors<1>(ss, tot, K);
+    else
+      select_survivors<kSurvNJ>(ss, tot, K);
+  }
+  __syncthreads();
+  const int keep = ss.nkey;
+  if (t < keep) {
+    const unsigned long long k0 = ss.key[t];
+    int r = 0;
+    for (int e = 0; e < keep; ++e) r += ss.key[e] > k0 ? 1 : 0;
+    ss.sorted[r] = k0;
+  }
+  __syncthreads();
+  return keep;
+}
+
 // The same selection, narrowed first by the slices' maxima (each the largest
 // group score of 64 consecutive chunks, stored by D1):
 //  1. a lower bound of the threshold from the maxima, as in step 1 above:
@@ -645,18 +676,19 @@ __device__ __forceinline__ int block_topk(const float *sig, int n, int cmax, int
 //     scores at or above the bound are the survivors;
 //  3. one wave selects exactly among them.
 // Too many surviving slices or scores (many equal scores): block_topk.
+// The slice maxima come preloaded: smv[j] = the maximum of slice
+// j * kDecThreads + t (any value past the stored slices).
 constexpr int kSlicePT = 8;                          // slice maxima per thread
 constexpr int kSliceMax = kDecThreads * kSelVPT;     // surviving slices kept (LDS: ss.sord)
-__device__ __forceinline__ int block_topk_sliced(const float *sig, const float *smax, int n, int cmax, int K,
-                                                 SelSmem &ss) {
+__device__ __forceinline__ int block_topk_sliced(const float *sig, const float (&smv)[kSlicePT], int n, int cmax,
+                                                 int K, SelSmem &ss) {
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int ns = (n + kCPB - 1) / kCPB;  // slices holding eligible chunks
   uint32_t mx = 0u, so[kSlicePT];
 #pragma unroll
   for (int j = 0; j < kSlicePT; ++j) {
     const int s = j * kDecThreads + t;
-    const float v = smax[s < ns ? s : 0];
-    so[j] = s < ns ? orderable(v) : 0u;
+    so[j] = s < ns ? orderable(smv[j]) : 0u;
     mx = max(mx, so[j]);
   }
   {
@@ -704,25 +736,9 @@ __device__ __forceinline__ int block_topk_sliced(const float *sig, const float *
     }
   }
   __syncthreads();
-  const int tot = ss.nsurv;
-  if (tot > kSurvMax) return block_topk(sig, n, cmax, K, ss);
-  if (wave == 0) {
-    if (tot <= 64)
-      select_survivors<1>(ss, tot, K);
-    else
-      select_survivors<kSurvNJ>(ss, tot, K);
-  }
-  __syncthreads();
-  const int keep = ss.nkey;
-  if (t < keep) {
-    const unsigned long long k0 = ss.key[t];
-    int r = 0;
-    for (int e = 0; e < keep; ++e) r += ss.key[e] > k0 ? 1 : 0;
-    ss.sorted[r] = k0;
-  }
-  __syncthreads();
-  return keep;
+  return select_ranked(sig, n, cmax, K, ss);
 }
+
 
 // D2: every slot workgroup of (b, g) selects the top-K from the group scores
 // (the same arithmetic in each, so they agree), slot 0 writes the lists,
@@ -736,29 +752,48 @@ decode_attend_kernel(DecodeArgs a) {
   __shared__ int is_last;
   const int g = blockIdx.y, b = blockIdx.z, slot = blockIdx.x, t = threadIdx.x;
   const int G = a.Hq / a.Hkv, K = a.K;
+  const size_t bg = static_cast<size_t>(b) * a.Hkv + g;
+  float *recs = a.parts + bg * a.nslots * G * (D + 2);
+  // The query rows (parked in LDS after the selection) and the slice maxima
+  // go out before the sequence length (itself a load) is known, so that they
+  // arrive with it; n masks the maxima afterwards.  (Loading every group
+  // score here as well, to skip the survivors' dependent load, was slower:
+  // the larger transfer delays the rest.)
+  constexpr int QPT = (kMaxG * D + kDecThreads - 1) / kDecThreads;
+  T qraw[QPT];  // raw: converted when parked, so that nothing waits for it before
+  float smv[kSlicePT];
+  const bool sliced = K > 0 && a.Cmax > kCPB * K;  // the slice maxima can be used
+  const float *sig = a.sig + bg * a.Cmax;
+  {
+    // (no load under a branch, whose end would wait for it: past G * D a
+    // thread reads element 0 again and does not park it; with K = 0 the
+    // rows are read and not used)
+    const T *qsrc = static_cast<const T *>(a.q) + (static_cast<size_t>(b) * a.Hq + g * G) * D;
+#pragma unroll
+    for (int r = 0; r < QPT; ++r) {
+      const int x = t + r * kDecThreads;
+      qraw[r] = qsrc[x < G * D ? x : 0];
+    }
+  }
+  if (sliced) {
+    const float *sx = a.smax + bg * a.P;
+#pragma unroll
+    for (int j = 0; j < kSlicePT; ++j) {
+      const int x = j * kDecThreads + t;
+      smv[j] = sx[x < a.P ? x : 0];
+    }
+  }
   const int seq = clamp_seq(a.seq_lens, b, a.Tmax, a.err, false);
   const int i = seq - 1;
   const int n = eligible_chunks(i, a.W, a.S);
-  const size_t bg = static_cast<size_t>(b) * a.Hkv + g;
-  float *recs = a.parts + bg * a.nslots * G * (D + 2);
   if (K > 0) {
-    // the query rows are loaded (into registers) together with the group
-    // scores, and parked in LDS after the selection
-    constexpr int QPT = (kMaxG * D + kDecThreads - 1) / kDecThreads;
-    const T *qsrc = static_cast<const T *>(a.q) + (static_cast<size_t>(b) * a.Hq + g * G) * D;
-    float qreg[QPT];
+    const int keep = !(n > kCPB * K && (n + kCPB - 1) / kCPB <= kSlicePT * kDecThreads)
+                         ? block_topk(sig, n, a.Cmax, K, ss)
+                         : block_topk_sliced(sig, smv, n, a.Cmax, K, ss);
 #pragma unroll
     for (int r = 0; r < QPT; ++r) {
       const int x = t + r * kDecThreads;
-      if (r * kDecThreads < G * D) qreg[r] = Elem<T>::load(qsrc, x < G * D ? x : 0);
-    }
-    const int keep = (n > kCPB * K && (n + kCPB - 1) / kCPB <= kSlicePT * kDecThreads)
-                         ? block_topk_sliced(a.sig + bg * a.Cmax, a.smax + bg * a.P, n, a.Cmax, K, ss)
-                         : block_topk(a.sig + bg * a.Cmax, n, a.Cmax, K, ss);
-#pragma unroll
-    for (int r = 0; r < QPT; ++r) {
-      const int x = t + r * kDecThreads;
-      if (x < G * D) us.q[x / D][x % D] = qreg[r];
+      if (x < G * D) us.q[x / D][x % D] = Elem<T>::load(qraw, r);
     }
     __syncthreads();
     if (slot == 0) {

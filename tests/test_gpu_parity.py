@@ -196,6 +196,10 @@ DECODE_CASES = {
     "g8_k32": (wl_decode(B=1, T=8192, Hq=8, Hkv=1, d=64, K=32, W=256), [8000]),
     # a cache shorter than one chunk: no summary stored, window only
     "no_chunk": (wl_decode(B=2, T=48, Hq=4, Hkv=1, d=64, K=4, W=32, needles="none"), [48, 17]),
+    # more than 64 K eligible chunks: the selection is narrowed by the
+    # 64-chunk slices' maxima; the last sequence has too few eligible chunks
+    # for it and takes the tiled search in the same launch
+    "sliced_k4": (wl_decode(B=3, T=40960, Hq=8, Hkv=2, d=128, K=4, W=512), [40960, 20000, 5000]),
 }
 
 
@@ -246,6 +250,27 @@ def test_decode_all_scores_tied():
     assert (gidx == r["idx"]).all()
     assert (gidx[..., :wl.top_k] == np.arange(wl.top_k)).all()
     check_scores(host(res["tsc"]), r["tsc"], gidx, r["idx"], wl.group)
+    check_out(host(res["o"]), r["o"], wl.dtype)
+
+
+def test_decode_all_scores_tied_sliced():
+    """The same with more than 64 K eligible chunks: every score reaches the
+    bound taken from the slice maxima, the survivors overflow and the
+    selection falls back to the tiled search."""
+    wl = wl_decode(B=2, T=40960, Hq=4, Hkv=1, d=64, K=4, W=128, needles="none")
+    sl = np.array([40960, 30000], dtype=np.int32)
+    inp = hs.decode_inputs(wl, 919, seq_lens=sl)
+    kc = inp["k_cache"]
+    inp["k_cache"] = np.ascontiguousarray(np.broadcast_to(kc[:, :, :1], kc.shape))
+    oc = ocfg(wl)
+    ks64, bs64 = oracle.summary(oc, inp["k_cache"], inp["q_lm"])
+    ks, bs = oracle.store(oc, ks64), bs64.astype(np.float32)
+    d = upload(inp)
+    res = gpu_decode(wl.config_dict(), d, dev(ks), dev(bs), d["seq_lens"])
+    r = oracle.decode(oc, inp, ks, bs)
+    gidx = host(res["idx"])
+    assert (gidx == r["idx"]).all()
+    assert (gidx[..., :wl.top_k] == np.arange(wl.top_k)).all()
     check_out(host(res["o"]), r["o"], wl.dtype)
 
 
