@@ -325,7 +325,7 @@ constexpr int kSurvNJ = (kSurvMax + 32 + 63) / 64;
 struct SelSmem {
   unsigned long long key[32];     // winners so far: (ordered score, ~chunk)
   unsigned long long sorted[32];  // final winners in rank order
-  unsigned long long surv[kSurvMax + 32];
+  alignas(16) unsigned long long surv[kSurvMax + 32];
   uint32_t tw[kSelWaves];         // per-wave lower bound of the threshold
   uint32_t red[2][kSelWaves];     // per-wave partial sums / minima, double buffered
   uint32_t red2[2][kSelWaves];
@@ -649,6 +649,27 @@ __device__ __forceinline__ int select_ranked(const float *sig, int n, int cmax, 
   const int t = threadIdx.x, wave = t >> 6;
   const int tot = ss.nsurv;
   if (tot > kSurvMax) return block_topk(sig, n, cmax, K, ss);
+  if (tot <= 64) {
+    // At most 64 survivors (the usual case): lane x of wave 0 takes
+    // survivor x; its position in (score desc, chunk asc) order is the
+    // number of larger keys (the keys are distinct: they hold the chunk),
+    // and the first min(K, tot) positions are the winners.
+    if (wave == 0) {
+      const int lane = t & 63;
+      const unsigned long long kx = lane < tot ? ss.surv[lane] : 0ull;
+      const ulonglong2 *s2 = reinterpret_cast<const ulonglong2 *>(ss.surv);
+      int r = 0;
+#pragma unroll
+      for (int e = 0; e < 32; ++e) {
+        const ulonglong2 w2 = s2[e];  // keys 2 e and 2 e + 1 (past tot: not counted)
+        r += (2 * e < tot && w2.x > kx) ? 1 : 0;
+        r += (2 * e + 1 < tot && w2.y > kx) ? 1 : 0;
+      }
+      if (lane < tot && r < K) ss.sorted[r] = kx;
+    }
+    __syncthreads();
+    return min(K, tot);
+  }
   if (wave == 0) {
     if (tot <= 64)
       select_survivors<1>(ss, tot, K);
