@@ -151,21 +151,57 @@ __global__ void __launch_bounds__(256) long_scan_kernel(int C, int *cnt, int *cu
   }
 }
 
-// list[b, g][off[c] + cursor] = (i - q0) << 5 | slot
+// list[b, g][off[c] + cursor] = (i - q0) << 5 | slot.  The block places its
+// own entries first (an LDS counter per chunk gives each entry its place in
+// the block's run of that chunk), then reserves one run per chunk it holds
+// with a single global atomic, all of them issued before any is used.  The
+// order inside a chunk's list is not fixed; no result depends on it (each
+// entry is one column of the chunk kernel's tiles, computed on its own).
+constexpr int kLMaxK = 32;  // list slots per query handled here (top-K <= 32)
 __global__ void __launch_bounds__(256) long_fill_kernel(AttnArgs a, int q0, int nq, const int *off, int *cur,
                                                         int *list) {
+  __shared__ int run[kLMaxC];  // entries of the block per chunk, then where its run starts
   const int g = blockIdx.y, b = blockIdx.z, t = threadIdx.x, C = a.T / kLK;
-  const int i = q0 + blockIdx.x * kLQB + t;
-  if (i >= q0 + nq) return;
   const size_t pg = static_cast<size_t>(b) * a.Hkv + g;
+  for (int c = t; c < C; c += 256) run[c] = 0;
+  __syncthreads();
+  const int i = q0 + blockIdx.x * kLQB + t;
+  const bool q_ok = i < q0 + nq;
   const int n = eligible_chunks(i, a.W, kLK);
-  const int32_t *ir = a.topk_idx + (pg * a.T + i) * a.K;
-  int *lg = list + pg * static_cast<size_t>(nq) * a.K;
-  for (int k = 0; k < a.K; ++k) {
-    const int c = ir[k];
-    if (c < 0 || c >= n) continue;
-    lg[off[pg * (C + 1) + c] + atomicAdd(&cur[pg * C + c], 1)] = ((i - q0) << 5) | k;
+  const int32_t *ir = a.topk_idx + (pg * a.T + (q_ok ? i : q0)) * a.K;
+  // the query's list read first, without a branch (slots past K read slot
+  // K - 1 again and are dropped): a load under a branch waits at its end
+  int cc[kLMaxK], pos[kLMaxK];
+#pragma unroll
+  for (int k = 0; k < kLMaxK; ++k) cc[k] = ir[k < a.K ? k : a.K - 1];
+#pragma unroll
+  for (int k = 0; k < kLMaxK; ++k) {
+    const int c = cc[k];
+    const bool ok = q_ok && k < a.K && c >= 0 && c < n;
+    cc[k] = ok ? c : -1;
+    pos[k] = ok ? atomicAdd(&run[c], 1) : 0;
   }
+  __syncthreads();
+  // one reservation per chunk the block holds: the counts up to 32 per thread
+  // (C <= 8192), the atomics issued together, their results used after
+  constexpr int kPer = kLMaxC / 256;
+  int base[kPer];
+#pragma unroll
+  for (int r = 0; r < kPer; ++r) {
+    const int c = t + 256 * r;
+    const int h = c < C ? run[c] : 0;
+    base[r] = h ? atomicAdd(&cur[pg * C + c], h) : 0;
+  }
+#pragma unroll
+  for (int r = 0; r < kPer; ++r) {
+    const int c = t + 256 * r;
+    if (c < C) run[c] = off[pg * (C + 1) + c] + base[r];
+  }
+  __syncthreads();
+  int *lg = list + pg * static_cast<size_t>(nq) * a.K;
+#pragma unroll
+  for (int k = 0; k < kLMaxK; ++k)
+    if (cc[k] >= 0) lg[run[cc[k]] + pos[k]] = ((i - q0) << 5) | k;
 }
 
 // ------------------------------------------------------------------ chunks
