@@ -47,22 +47,43 @@ landmark_summary_kernel(const T *__restrict__ k, const T *__restrict__ q_lm, T *
   } else {
     kc = k + ((static_cast<size_t>(b) * Hkv + g) * T_len + static_cast<size_t>(c) * kSumS) * D;
   }
-  // stage the chunk's keys: 64 x D elements, 8 per thread per step
-  for (int e8 = tid; e8 < kSumS * D / 8; e8 += kSumThreads) {
+  // The chunk's keys (64 x D, pieces of 8 elements) and the first four
+  // heads' landmark rows (lane e and e + 64 of the wave's head): every load
+  // issued before any is used, raw, so that they share one round trip.
+  constexpr int KP = kSumS * D / 8 / kSumThreads;  // pieces per thread
+  constexpr int RPP = static_cast<int>(sizeof(T)) / 2;  // 16-byte loads per piece
+  static_assert(kSumS * D / 8 % kSumThreads == 0, "whole pieces per thread");
+  uint4 raw[KP][RPP];
+#pragma unroll
+  for (int r = 0; r < KP; ++r)
+#pragma unroll
+    for (int u = 0; u < RPP; ++u) raw[r][u] = reinterpret_cast<const uint4 *>(kc + (tid + r * kSumThreads) * 8)[u];
+  T qraw[D / 64];
+  {
+    const int hq = g * G + (wave < G ? wave : 0);  // (a wave past G reads head 0 of the group, unused)
+    const size_t so = (static_cast<size_t>(b) * Hq + hq) * C + c;
+#pragma unroll
+    for (int i = 0; i < D / 64; ++i) qraw[i] = q_lm[so * D + lane + 64 * i];
+  }
+#pragma unroll
+  for (int r = 0; r < KP; ++r) {
     float v[8];
-    Elem<T>::load8(kc + e8 * 8, v);
-    int row = (e8 * 8) / D, col = (e8 * 8) % D;
+    Elem<T>::load8(reinterpret_cast<const T *>(&raw[r][0]), v);
+    const int e8 = tid + r * kSumThreads, row = (e8 * 8) / D, col = (e8 * 8) % D;
 #pragma unroll
     for (int t = 0; t < 8; ++t) keys[row * LD + col + t] = v[t];
   }
-  __syncthreads();
+  // (parked by every wave, used or not: a use under a branch would let the
+  // compiler move the loads there, a round trip later)
+#pragma unroll
+  for (int i = 0; i < D / 64; ++i) qrow[wave][lane + 64 * i] = Elem<T>::load(qraw, i);
 
   __shared__ float ent_s[4];
   for (int h0 = 0; h0 < G; h0 += 4) {
     const int h = g * G + h0 + wave;
     const bool active = (h0 + wave) < G;
     const size_t so = (static_cast<size_t>(b) * Hq + h) * C + c;
-    if (active)
+    if (active && h0 > 0)  // the first four heads' rows are in place already
       for (int e = lane; e < D; e += 64) qrow[wave][e] = Elem<T>::load(q_lm, so * D + e);
     __syncthreads();
     if (active) {
