@@ -347,11 +347,15 @@ bwd_keys_mfma_kernel(BwdArgs a) {
 }
 
 // ------------------------------------------------------------------ rows (MFMA)
-// The query-major pass on the matrix cores: one workgroup per (query i,
-// group g, batch b), its G heads the columns of one 16-row tile (rows past G
-// zero).  The row's blocks -- its selected chunks, then the 64-key blocks of
-// its window -- are staged in LDS one at a time (K row-major, V row-major,
-// K^T), the next block's loads in flight while the current one computes.
+// The query-major pass on the matrix cores: one workgroup per 16 / G
+// consecutive queries of group g and batch b, their G heads the 16 columns of
+// one tile (column = query i0 + col / G, head col % G).  The workgroup's
+// blocks -- the union of its queries' selected chunks, each staged once, then
+// the 64-key blocks covering their windows -- are staged in LDS one at a
+// time (K row-major, V row-major, K^T), the next block's loads in flight
+// while the current one computes; a column takes a chunk block only if its
+// query selected that chunk, and from a window block only the keys of its
+// own window.
 // Wave w takes keys 16 w .. 16 w + 15 of each block:
 //   S^T = K Q^T, dP^T = V dO^T        16x16x32 bf16, keys in M, heads in N
 // and accumulates, per head, running sums over its own keys against one
@@ -394,18 +398,23 @@ struct alignas(16) RmTiles {
   uint16_t vr[kBK][D + kRP];
   uint16_t kt[D][kTQ];
 };
-template <int D>
+template <int D, int QPW>
 struct alignas(16) RmSmem {
   union {
     RmTiles<D> t;
     float vec[4][16][D + 4];  // the waves' row vectors for the final sum
   } u;
-  float red[4][16][3];        // per wave and head: a chunk's max, sum, sum e dO.v over the wave's keys
-  float fin[4][16][3];        // per wave and head: the window's max, sum, sum e dO.v
-  float sl_s[32][16], sl_m[32][16], sl_z[32][16], sl_doo[32][16];  // per slot and head
+  float red[4][16][3];        // per wave and column: a chunk's max, sum, sum e dO.v over the wave's keys
+  float fin[4][16][3];        // per wave and column: the window's max, sum, sum e dO.v
+  float sl_s[32][16], sl_m[32][16], sl_z[32][16], sl_doo[32][16];  // per slot of the column's query, and column
   float row_lz[16], row_dl[16], row_mc[16];
-  int sel[32], blk[64];       // the row's chunks; the staged blocks (c, or -1 - window block)
-  int nblk;
+  int sel[QPW][32];                            // each query's chunk per slot (-1: none)
+  uint32_t umask[kMaxBwdChunks / 32];          // the chunks any query of the workgroup selected
+  int wbase[kMaxBwdChunks / 32];
+  int16_t ulist[kMaxBwdChunks];                // those chunks, ascending
+  int8_t uslot[kMaxBwdChunks][16];             // per union chunk and column: the slot in the column's query's list, or -1
+  int16_t blk[2 * kMaxBwdChunks + 4];          // staged blocks: union chunk u, or -1 - window block
+  int nblk, nunion;
 };
 
 }  // namespace
@@ -413,38 +422,81 @@ struct alignas(16) RmSmem {
 template <int D, int G, bool QCAL>
 __global__ void __launch_bounds__(256, 2)
 bwd_rows_mfma_kernel(BwdArgs a) {
-  __shared__ RmSmem<D> sm;
+  constexpr int QPW = 16 / G;  // queries per workgroup: their G heads fill the tile's 16 columns
+  __shared__ RmSmem<D, QPW> sm;
   constexpr int KS = D / 32, DT = D / 16;
   constexpr int NKI = D / 64;  // (row pair, 8-element piece) items of K per thread; V: 2 NKI rows
-  const int i = blockIdx.x, g = blockIdx.y, b = blockIdx.z, t = threadIdx.x;
+  const int i0 = blockIdx.x * QPW, g = blockIdx.y, b = blockIdx.z, t = threadIdx.x;
   const int lane = t & 63, w = __builtin_amdgcn_readfirstlane(t >> 6), ln = lane & 15, lg = lane >> 4;
   const int T_len = a.T, K = a.K, Hq = a.Hq, Hkv = a.Hkv, C = T_len / kBK;
   const float tau = a.tau;
-  const int n = eligible_chunks(i, a.W, kBK), w_lo = n * kBK;
-  const int nwb = (i - w_lo) / kBK + 1;
+  // column ln of the tile: query i0 + ln / G, head ln % G (a query past T
+  // is no query: it reads the last row and stores nothing); its window is
+  // the keys [wlo_c, ic]
+  const int cq = ln / G, ch = ln % G, ic = i0 + cq;
+  const bool col_ok = ic < T_len;
+  const int icc = col_ok ? ic : T_len - 1;
+  const int wlo_c = eligible_chunks(icc, a.W, kBK) * kBK;
+  // the workgroup's window blocks: from the first query's window start (the
+  // smallest) to its last query
+  const int i_last = min(i0 + QPW - 1, T_len - 1);
+  const int w_lo = eligible_chunks(i0, a.W, kBK) * kBK;
+  const int nwb = (i_last - w_lo) / kBK + 1;
   const size_t pg = static_cast<size_t>(b) * Hkv + g;
   const uint16_t *kg = static_cast<const uint16_t *>(a.k) + pg * T_len * D;
   const uint16_t *vg = static_cast<const uint16_t *>(a.v) + pg * T_len * D;
   const uint16_t *ksum = static_cast<const uint16_t *>(a.k_sum);
-  // ---- the row's blocks and the chunk scores s_hat = tau q_hat . k'_c + b'_c
-  if (t < 32) {
+  // ---- each query's chunks, their union (each staged once), and per union
+  // chunk and column the slot that chunk has in the column's query's list
+  for (int x = t; x < QPW * 32; x += kBT) {
+    const int q = x / 32, y = x % 32, iq = i0 + q;
     int c = -1;
-    if (t < K) c = a.topk_idx[(pg * T_len + i) * K + t];
-    sm.sel[t] = (c >= 0 && c < n) ? c : -1;
+    if (y < K && iq < T_len) {
+      c = a.topk_idx[(pg * T_len + iq) * K + y];
+      if (c < 0 || c >= eligible_chunks(iq, a.W, kBK)) c = -1;
+    }
+    sm.sel[q][y] = c;
+  }
+  for (int x = t; x < kMaxBwdChunks / 32; x += kBT) sm.umask[x] = 0u;
+  for (int x = t; x < kMaxBwdChunks * 16 / 4; x += kBT) reinterpret_cast<int *>(&sm.uslot[0][0])[x] = -1;
+  __syncthreads();
+  for (int x = t; x < QPW * 32; x += kBT) {
+    const int c = sm.sel[x / 32][x % 32];
+    if (c >= 0) atomicOr(&sm.umask[c >> 5], 1u << (c & 31));
   }
   __syncthreads();
-  if (t == 0) {
-    int nb = 0;
-    for (int x = 0; x < K; ++x)
-      if (sm.sel[x] >= 0) sm.blk[nb++] = x;  // slot x
-    for (int x = 0; x < nwb; ++x) sm.blk[nb++] = -1 - x;
-    sm.nblk = nb;
+  if (t < 64) {  // union positions in ascending chunk order: prefix over the mask words (C <= 512)
+    const int nw = (C + 31) >> 5;
+    const uint32_t bits = t < nw ? sm.umask[t] : 0u;
+    const int cnt = __popc(bits);
+    int incl = cnt;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(incl, o, 64);
+      if (t >= o) incl += y;
+    }
+    if (t < nw) sm.wbase[t] = incl - cnt;
+    if (t == 63) sm.nunion = incl;
   }
-  for (int x = t; x < K * G; x += kBT) {  // one (slot, head) per thread
-    const int slot = x / G, hh = x % G, c = sm.sel[slot];
+  __syncthreads();
+  for (int x = t; x < QPW * 32; x += kBT) {
+    const int q = x / 32, y = x % 32, c = sm.sel[q][y];
+    if (c >= 0) {
+      const int u = sm.wbase[c >> 5] + __popc(sm.umask[c >> 5] & ((1u << (c & 31)) - 1u));
+      sm.ulist[u] = static_cast<int16_t>(c);  // (the same value from every query that holds c)
+#pragma unroll
+      for (int h = 0; h < G; ++h) sm.uslot[u][q * G + h] = static_cast<int8_t>(y);
+    }
+  }
+  const int nu = sm.nunion;
+  for (int x = t; x < nu + nwb; x += kBT) sm.blk[x] = static_cast<int16_t>(x < nu ? x : -1 - (x - nu));
+  // ---- the chunk scores s_hat = tau q_hat . k'_c + b'_c per (slot, column)
+  for (int x = t; x < K * 16; x += kBT) {
+    const int slot = x / 16, col = x % 16, q = col / G, hh = col % G, iq = i0 + q;
+    const int c = iq < T_len ? sm.sel[q][slot] : -1;
     float s = -INFINITY;
     if (c >= 0) {
-      const size_t ro = (static_cast<size_t>(b) * Hq + g * G + hh) * T_len + i;
+      const size_t ro = (static_cast<size_t>(b) * Hq + g * G + hh) * T_len + iq;
       const size_t so = (static_cast<size_t>(b) * Hq + g * G + hh) * C + c;
       float acc = 0.f;
       for (int e = 0; e < D; e += 8) {
@@ -456,29 +508,28 @@ bwd_rows_mfma_kernel(BwdArgs a) {
       }
       s = tau * acc + a.b_sum[so];
     }
-    sm.sl_s[slot][hh] = s;
+    sm.sl_s[slot][col] = s;
   }
   __syncthreads();
-  const int nb = sm.nblk;
-  // this lane's head (column ln) and its largest chunk score
+  const int nb = nu + nwb;
+  // this lane's column and its largest chunk score
   float Mc = -INFINITY;
-  if (ln < G)
-    for (int x = 0; x < K; ++x) Mc = fmaxf(Mc, sm.sl_s[x][ln]);
-  // Q and dO of the lane's head as B operands: d = 32 s + 8 lg .. + 8
+  for (int x = 0; x < K; ++x) Mc = fmaxf(Mc, sm.sl_s[x][ln]);
+  // Q and dO of the lane's column as B operands: d = 32 s + 8 lg .. + 8
   uint4 qop[KS], dop[KS];
   {
-    const size_t ro = (static_cast<size_t>(b) * Hq + g * G + (ln < G ? ln : 0)) * T_len + i;
+    const size_t ro = (static_cast<size_t>(b) * Hq + g * G + ch) * T_len + icc;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
-      qop[s] = ln < G ? *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.q) + ro * D + 32 * s + 8 * lg)
+      qop[s] = col_ok ? *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.q) + ro * D + 32 * s + 8 * lg)
                       : make_uint4(0u, 0u, 0u, 0u);
-      dop[s] = ln < G ? *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.d_o) + ro * D + 32 * s + 8 * lg)
+      dop[s] = col_ok ? *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(a.d_o) + ro * D + 32 * s + 8 * lg)
                       : make_uint4(0u, 0u, 0u, 0u);
     }
   }
   // ---- staging: item it of K -> rows 2 pp, 2 pp + 1, piece s; V rows plain
   uint4 kst[NKI][2], vst[2 * NKI];
-  auto block_j0 = [&](int x) { const int bb = sm.blk[x]; return bb >= 0 ? sm.sel[bb] * kBK : w_lo - (1 + bb) * kBK; };
+  auto block_j0 = [&](int x) { const int bb = sm.blk[x]; return bb >= 0 ? sm.ulist[bb] * kBK : w_lo - (1 + bb) * kBK; };
   auto load_block = [&](int j0) {
 #pragma unroll
     for (int it = 0; it < NKI; ++it) {
@@ -567,7 +618,7 @@ bwd_rows_mfma_kernel(BwdArgs a) {
         sm.red[w][ln][2] = dz;
       }
       __syncthreads();
-      // the chunk's statistics for head ln, combined over the waves in order
+      // the chunk's statistics for column ln, combined over the waves in order
       float mc = sm.red[0][ln][0];
 #pragma unroll
       for (int v = 1; v < 4; ++v) mc = fmaxf(mc, sm.red[v][ln][0]);
@@ -579,13 +630,15 @@ bwd_rows_mfma_kernel(BwdArgs a) {
         dzc += f * sm.red[v][ln][2];
       }
       const float doo = dzc / zc;
-      if (w == 0 && lg == 0) {
-        sm.sl_m[bb][ln] = mc;
-        sm.sl_z[bb][ln] = zc;
-        sm.sl_doo[bb][ln] = doo;
+      const int slot = sm.uslot[bb][ln];  // the chunk's slot in column ln's list; -1: not selected there
+      if (w == 0 && lg == 0 && slot >= 0) {
+        sm.sl_m[slot][ln] = mc;
+        sm.sl_z[slot][ln] = zc;
+        sm.sl_doo[slot][ln] = doo;
       }
-      // (R >= s_hat of every selected chunk of head ln; padding heads: 0)
-      const float wgt = ln < G ? __expf(sm.sl_s[bb][ln] - R) / zc : 0.f;
+      // (R >= s_hat of every selected chunk of column ln; a column that did
+      // not select the chunk: weight 0)
+      const float wgt = slot >= 0 ? __expf(sm.sl_s[slot][ln] - R) / zc : 0.f;
       float ed[4];
 #pragma unroll
       for (int jx = 0; jx < 4; ++jx) ed[jx] = __expf(l[jx] - mc) * wgt * (dv[jx] - doo);
@@ -596,17 +649,22 @@ bwd_rows_mfma_kernel(BwdArgs a) {
         V1[dt] = mfma_16(akt, eb, V1[dt]);
       }
     } else {
+      // keys of column ln's window, [wlo_c, ic]
       float lm[4];
       float mb = -INFINITY;
 #pragma unroll
       for (int jx = 0; jx < 4; ++jx) {
-        lm[jx] = j0 + 16 * w + 4 * lg + jx <= i ? l[jx] : -INFINITY;
+        const int j = j0 + 16 * w + 4 * lg + jx;
+        lm[jx] = (col_ok && j >= wlo_c && j <= ic) ? l[jx] : -INFINITY;
         mb = fmaxf(mb, lm[jx]);
       }
       mb = max_rows4(mb);
       const float rn = fmaxf(R, mb);
-      if (mb != -INFINITY) {  // uniform over the 4 lanes of the head
-        const float sc = R == -INFINITY ? 0.f : __expf(R - rn);
+      // No branch around the update: the matrix products run for every
+      // column whatever EXEC holds, so a column without keys in this block
+      // (mb = -inf) takes weights 0 and rescale 1 and keeps its state.
+      {
+        const float sc = mb == -INFINITY ? 1.f : (R == -INFINITY ? 0.f : __expf(R - rn));
         float e[4], ed[4], ze = 0.f, zd = 0.f;
 #pragma unroll
         for (int jx = 0; jx < 4; ++jx) {
@@ -649,31 +707,31 @@ bwd_rows_mfma_kernel(BwdArgs a) {
     sm.fin[w][ln][2] = dw;
   }
   __syncthreads();
-  if (t < 16) {  // head t
-    const int hh = t;
+  if (t < 16) {  // column t: query i0 + t / G, head t % G
+    const int col = t, q = t / G, hh = t % G, iq = i0 + q;
     float mc = -INFINITY;
-    for (int x = 0; x < K; ++x) mc = fmaxf(mc, sm.sl_s[x][hh]);
+    for (int x = 0; x < K; ++x) mc = fmaxf(mc, sm.sl_s[x][col]);
     float M = mc;
 #pragma unroll
-    for (int v = 0; v < 4; ++v) M = fmaxf(M, sm.fin[v][hh][0]);
+    for (int v = 0; v < 4; ++v) M = fmaxf(M, sm.fin[v][col][0]);
     float z = 0.f;
     for (int x = 0; x < K; ++x)
-      if (sm.sel[x] >= 0) z += __expf(sm.sl_s[x][hh] - M);
+      if (sm.sel[q][x] >= 0) z += __expf(sm.sl_s[x][col] - M);
 #pragma unroll
     for (int v = 0; v < 4; ++v)
-      if (sm.fin[v][hh][0] != -INFINITY) z += sm.fin[v][hh][1] * __expf(sm.fin[v][hh][0] - M);
+      if (sm.fin[v][col][0] != -INFINITY) z += sm.fin[v][col][1] * __expf(sm.fin[v][col][0] - M);
     const float lz = M + __logf(z);
     float dl = 0.f;
     for (int x = 0; x < K; ++x)
-      if (sm.sel[x] >= 0) dl += __expf(sm.sl_s[x][hh] - lz) * sm.sl_doo[x][hh];
+      if (sm.sel[q][x] >= 0) dl += __expf(sm.sl_s[x][col] - lz) * sm.sl_doo[x][col];
 #pragma unroll
     for (int v = 0; v < 4; ++v)
-      if (sm.fin[v][hh][0] != -INFINITY) dl += sm.fin[v][hh][2] * __expf(sm.fin[v][hh][0] - lz);
-    sm.row_lz[hh] = lz;
-    sm.row_dl[hh] = dl;
-    sm.row_mc[hh] = mc;
-    if (hh < G) {
-      const size_t ro = (static_cast<size_t>(b) * Hq + g * G + hh) * T_len + i;
+      if (sm.fin[v][col][0] != -INFINITY) dl += sm.fin[v][col][2] * __expf(sm.fin[v][col][0] - lz);
+    sm.row_lz[col] = lz;
+    sm.row_dl[col] = dl;
+    sm.row_mc[col] = mc;
+    if (iq < T_len) {
+      const size_t ro = (static_cast<size_t>(b) * Hq + g * G + hh) * T_len + iq;
       a.logz[ro] = lz;
       a.delta[ro] = dl;
     }
@@ -690,34 +748,35 @@ bwd_rows_mfma_kernel(BwdArgs a) {
   }
   __syncthreads();
   // ---- dq and dq_hat per (head, d); the list entries' values
-  for (int x = t; x < G * D; x += kBT) {
-    const int hh = x / D, e = x % D, h = g * G + hh;
-    const float lz = sm.row_lz[hh], dl = sm.row_dl[hh], mc = sm.row_mc[hh];
+  for (int x = t; x < 16 * D; x += kBT) {
+    const int col = x / D, e = x % D, q = col / G, hh = col % G, iq = i0 + q, h = g * G + hh;
+    if (iq >= T_len) continue;
+    const float lz = sm.row_lz[col], dl = sm.row_dl[col], mc = sm.row_mc[col];
     float b1 = 0.f, b2 = 0.f;
     for (int y = 0; y < K; ++y) {
-      const int c = sm.sel[y];
+      const int c = sm.sel[q][y];
       if (c < 0) continue;
-      const float sw = __expf(sm.sl_s[y][hh] - mc);
+      const float sw = __expf(sm.sl_s[y][col] - mc);
       const float kp = bf16_to_f32(ksum[((static_cast<size_t>(b) * Hq + h) * C + c) * D + e]);
-      b1 += sw * sm.sl_doo[y][hh] * kp;
+      b1 += sw * sm.sl_doo[y][col] * kp;
       b2 += sw * kp;
     }
     const float fc = mc == -INFINITY ? 0.f : __expf(mc - lz);
     const float dqh = tau * fc * (b1 - dl * b2);
-    const float v = sm.u.vec[0][hh][e] + sm.u.vec[1][hh][e] + sm.u.vec[2][hh][e] + sm.u.vec[3][hh][e];
-    const size_t ro = (static_cast<size_t>(b) * Hq + h) * T_len + i;
+    const float v = sm.u.vec[0][col][e] + sm.u.vec[1][col][e] + sm.u.vec[2][col][e] + sm.u.vec[3][col][e];
+    const size_t ro = (static_cast<size_t>(b) * Hq + h) * T_len + iq;
     a.dq[ro * D + e] = tau * v + dqh;
-    if (QCAL) a.dqhat[((static_cast<size_t>(b) * T_len + i) * Hq + h) * D + e] = dqh;
+    if (QCAL) a.dqhat[((static_cast<size_t>(b) * T_len + iq) * Hq + h) * D + e] = dqh;
   }
-  for (int x = t; x < K * G; x += kBT) {
-    const int y = x / G, hh = x % G;
-    if (sm.sel[y] < 0) continue;
-    const int pos = a.inv_pos[(pg * T_len + i) * K + y];
+  for (int x = t; x < QPW * K * G; x += kBT) {
+    const int q = x / (K * G), y = (x / G) % K, hh = x % G, col = q * G + hh, iq = i0 + q;
+    if (iq >= T_len || sm.sel[q][y] < 0) continue;
+    const int pos = a.inv_pos[(pg * T_len + iq) * K + y];
     const size_t eo = (pg * T_len * K + pos) * G + hh;
-    const float lz = sm.row_lz[hh];
-    a.ent_lw[eo] = sm.sl_s[y][hh] - lz - sm.sl_m[y][hh] - __logf(sm.sl_z[y][hh]);
-    a.ent_doo[eo] = sm.sl_doo[y][hh];
-    a.ent_ds[eo] = __expf(sm.sl_s[y][hh] - lz) * (sm.sl_doo[y][hh] - sm.row_dl[hh]);
+    const float lz = sm.row_lz[col];
+    a.ent_lw[eo] = sm.sl_s[y][col] - lz - sm.sl_m[y][col] - __logf(sm.sl_z[y][col]);
+    a.ent_doo[eo] = sm.sl_doo[y][col];
+    a.ent_ds[eo] = __expf(sm.sl_s[y][col] - lz) * (sm.sl_doo[y][col] - sm.row_dl[col]);
   }
 }
 
@@ -725,7 +784,7 @@ bool bwd_rows_mfma_supported(const BwdArgs &a) { return bwd_keys_mfma_supported(
 
 template <int D, int G>
 static hipError_t rows_dg(const BwdArgs &a, hipStream_t st) {
-  const dim3 grid(a.T, a.Hkv, a.B);
+  const dim3 grid((a.T + 16 / G - 1) / (16 / G), a.Hkv, a.B);  // 16 / G queries per workgroup
   if (a.r > 0)
     bwd_rows_mfma_kernel<D, G, true><<<grid, kBT, 0, st>>>(a);
   else
