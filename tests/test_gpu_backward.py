@@ -56,6 +56,9 @@ CASES = {
     "bf16_k0": wl(T=640, Hq=4, Hkv=2, d=64, K=0, W=192),
     # every query inside the window: no chunk is eligible
     "bf16_short_T_le_W": wl(T=300, Hq=4, Hkv=2, d=128, K=4, W=512),
+    # a window of ~58 blocks: with the chunks of four queries, far more staged
+    # blocks per row workgroup than one query's K + window (once the limit)
+    "bf16_wide_window": wl(T=4096, Hq=4, Hkv=1, d=64, K=8, W=3600),
 }
 
 
