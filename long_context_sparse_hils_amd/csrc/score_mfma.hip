@@ -862,15 +862,22 @@ score_topk_stream_kernel(ScoreArgs a, const uint16_t *__restrict__ u_hi, const u
         if (h2 < G) sg = fmaxf(sg, scb[h2][v]);
       kv[v] = c < n_me ? make_key(sg, c) : kNoKey;
     }
+    // A lane's candidates are taken in descending key order (each round the
+    // query takes the best of its lanes' best remaining ones), so the ones
+    // still left are those below the last key the lane gave up (keys are
+    // distinct: they hold the chunk).
+    unsigned long long ceil_k = kFull;
     for (int round = 0; round < 64; ++round) {
-      // this lane's best candidate above theta, and its heads' scores
+      // this lane's best remaining candidate and its heads' scores (no test
+      // against theta here: the query takes its best only if that is above
+      // theta, and that best is then this lane's best)
       unsigned long long mb = kNoKey;
       float bs[GM];
 #pragma unroll
       for (int h2 = 0; h2 < GM; ++h2) bs[h2] = -INFINITY;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const bool take = kv[v] > theta && kv[v] > mb;
+        const bool take = kv[v] > mb && kv[v] < ceil_k;
         mb = take ? kv[v] : mb;
 #pragma unroll
         for (int h2 = 0; h2 < GM; ++h2) bs[h2] = take ? scb[h2][v] : bs[h2];
@@ -879,8 +886,7 @@ score_topk_stream_kernel(ScoreArgs a, const uint16_t *__restrict__ u_hi, const u
       const bool ins = qbest > theta;  // the query takes qbest this round
       if (!__ballot(ins)) break;
       const bool owner = ins && mb == qbest;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) kv[v] = (owner && kv[v] == qbest) ? kNoKey : kv[v];
+      ceil_k = owner ? mb : ceil_k;
 #pragma unroll
       for (int h2 = 0; h2 < GM; ++h2) bs[h2] = max_rows4(owner ? bs[h2] : -INFINITY);
       // the slot to replace: the smallest key (= theta) of the lowest row holding it
