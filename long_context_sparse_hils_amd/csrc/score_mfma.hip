@@ -827,14 +827,16 @@ score_topk_stream_kernel(ScoreArgs a, const uint16_t *__restrict__ u_hi, const u
   // Item x + 1 streams into the other buffer while item x computes (the
   // DMA is invisible to the compiler's waits, so LDS reads of item x do not
   // wait for it); each wave waits for its own loads before the barrier.
+  // Item x + 2 is issued right after that barrier, into the buffer item x
+  // leaves, so that it is in flight during the merge that may follow.
   if (nitems > 0) issue_item(0, 0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+  if (nitems > 1) issue_item(1, 1);
   for (int x = 0; x < nitems; ++x) {
     const int buf = x & 1;
     const int hh = x % G, cb = x / G;
     debug_sync();
-    if (x + 1 < nitems) issue_item(x + 1, buf ^ 1);
     if (IC * cb < n_wave) {  // wave-uniform: some query of the wave has eligible chunks here
 #pragma unroll
       for (int h2 = 0; h2 < GM; ++h2) {
@@ -848,8 +850,12 @@ score_topk_stream_kernel(ScoreArgs a, const uint16_t *__restrict__ u_hi, const u
         }
       }
     }
+    // this wave's loads of item x + 1 (the only ones in flight) have landed;
+    // after the barrier all have, and no wave reads item x's buffer any more
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+    debug_sync();
+    if (x + 2 < nitems) issue_item(x + 2, buf);
     if (hh != G - 1 || IC * cb >= n_wave) continue;
     // ---- block cb complete: merge its candidates into the running lists
     unsigned long long kv[16];
