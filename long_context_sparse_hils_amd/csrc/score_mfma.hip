@@ -704,7 +704,7 @@ score_topk_stream_kernel(ScoreArgs a, const uint16_t *__restrict__ u_hi, const u
   auto item_mh = [&](int buf) { return reinterpret_cast<uint16_t *>(smem_raw + buf * lay.bytes + lay.mh); };
   auto item_ml = [&](int buf) { return reinterpret_cast<uint16_t *>(smem_raw + buf * lay.bytes + lay.ml); };
   auto item_bs = [&](int buf) { return reinterpret_cast<float *>(smem_raw + buf * lay.bytes + lay.bs); };
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int ln = lane & 15, lg = lane >> 4;
   const int T = a.T, C = a.C, K = a.K, Hq = a.Hq, Hkv = a.Hkv, G = Hq / Hkv;
   // heaviest (latest) query blocks first, as above
@@ -757,14 +757,19 @@ score_topk_stream_kernel(ScoreArgs a, const uint16_t *__restrict__ u_hi, const u
   constexpr int kSlK = IC * D * 2 / 1024;
   constexpr int Pm = RP / 8;
   constexpr int slm = IC * RP * 2 / 1024;
+  // Slices sl = wave + WAVES k: a whole number per wave, k' slices first, so
+  // each k is a k' or an m slice for every wave alike (no branch)
+  constexpr int nsl = kSlK + 2 * slm;
+  static_assert(nsl % WAVES == 0 && kSlK % WAVES == 0, "whole slices per wave");
   auto issue_item = [&](int x, int buf) {
     const int hh = x % G, cb = x / G;
     const int h = g * G + hh, c0 = cb * IC;
-    const int nsl = kSlK + 2 * slm;
-    for (int sl = wave; sl < nsl; sl += WAVES) {
+#pragma unroll
+    for (int k = 0; k < nsl / WAVES; ++k) {
+      const int sl = wave + WAVES * k;
       const uint16_t *src;
       uint16_t *dst;
-      if (sl < kSlK) {
+      if (k < kSlK / WAVES) {
         const int slot = sl * 64 + lane, r = slot / kPk, pp = slot % kPk;
         const int c = min(c0 + r, C - 1);  // rows past C are never used
         src = ksb + ((static_cast<size_t>(b) * Hq + h) * C + c) * D + ((pp ^ score_swz(r, kPk)) << 3);
