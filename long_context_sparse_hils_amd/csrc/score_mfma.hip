@@ -283,7 +283,7 @@ score_topk_mfma_kernel(ScoreArgs a, const uint16_t *__restrict__ u_hi, const uin
   auto item_mh = [&](int buf) { return reinterpret_cast<uint16_t *>(smem_raw + buf * lay.bytes + lay.mh); };
   auto item_ml = [&](int buf) { return reinterpret_cast<uint16_t *>(smem_raw + buf * lay.bytes + lay.ml); };
   auto item_bs = [&](int buf) { return reinterpret_cast<float *>(smem_raw + buf * lay.bytes + lay.bs); };
-  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int ln = lane & 15, lg = lane >> 4;
   const int T = a.T, C = a.C, K = a.K, Hq = a.Hq, Hkv = a.Hkv, G = Hq / Hkv;
   // one-dimensional grid, query block slowest: the latest (heaviest: most
@@ -326,27 +326,28 @@ score_topk_mfma_kernel(ScoreArgs a, const uint16_t *__restrict__ u_hi, const uin
   constexpr int kSlK = IC * D * 2 / 1024;  // k' slices
   const int Pm = RP / 8;                  // pieces per m row
   const int slm = qcal ? IC * RP * 2 / 1024 : 0;  // m slices (hi or lo)
-  static_assert(kSlK % WAVES == 0, "whole k' slices per wave");
   auto issue_item = [&](int x, int buf) {
     const int hh = x / nblk, cb = x % nblk;
     const int h = g * G + hh, c0 = cb * IC;
-    // k' slices sl = wave + WAVES k (a fixed count per wave: no branch)
-#pragma unroll
-    for (int k = 0; k < kSlK / WAVES; ++k) {
-      const int sl = wave + WAVES * k;
-      const int slot = sl * 64 + lane, r = slot / kPk, pp = slot % kPk;
-      const int c = min(c0 + r, C - 1);  // rows past C are never used
-      lds_dma16(ksb + ((static_cast<size_t>(b) * Hq + h) * C + c) * D + ((pp ^ score_swz(r, kPk)) << 3),
-                lds_address(item_ks(buf) + sl * 512));
-    }
-    // m slices y = wave, wave + WAVES, ... (Q-Cal only: slm, Pm > 0)
-    for (int y = wave; y < 2 * slm; y += WAVES) {
-      const int slm1 = slm > 0 ? slm : 1, Pm1 = Pm > 0 ? Pm : 1;
-      const int lohi = y / slm1, part = y % slm1;
-      const int slot = part * 64 + lane, r = slot / Pm1, pp = slot % Pm1;
-      const int c = min(c0 + r, C - 1);
-      lds_dma16((lohi ? m_lo : m_hi) + ((static_cast<size_t>(b) * Hq + h) * C + c) * RP + ((pp ^ score_swz(r, Pm)) << 3),
-                lds_address((lohi ? item_ml(buf) : item_mh(buf)) + part * 512));
+    const int nsl = kSlK + 2 * slm;
+    for (int sl = wave; sl < nsl; sl += WAVES) {
+      const uint16_t *src;
+      uint16_t *dst;
+      if (sl < kSlK) {
+        const int slot = sl * 64 + lane, r = slot / kPk, pp = slot % kPk;
+        const int c = min(c0 + r, C - 1);  // rows past C are never used
+        src = ksb + ((static_cast<size_t>(b) * Hq + h) * C + c) * D + ((pp ^ score_swz(r, kPk)) << 3);
+        dst = item_ks(buf) + sl * 512;
+      } else {
+        // (reached only with Q-Cal: slm, Pm > 0)
+        const int slm1 = slm > 0 ? slm : 1, Pm1 = Pm > 0 ? Pm : 1;
+        const int y = sl - kSlK, lohi = y / slm1, part = y % slm1;
+        const int slot = part * 64 + lane, r = slot / Pm1, pp = slot % Pm1;
+        const int c = min(c0 + r, C - 1);
+        src = (lohi ? m_lo : m_hi) + ((static_cast<size_t>(b) * Hq + h) * C + c) * RP + ((pp ^ score_swz(r, Pm)) << 3);
+        dst = (lohi ? item_ml(buf) : item_mh(buf)) + part * 512;
+      }
+      lds_dma16(src, lds_address(dst));
     }
     static_assert(IC == 64, "one entropy piece per lane");
     if (wave == WAVES - 1)  // rows past C are never used
