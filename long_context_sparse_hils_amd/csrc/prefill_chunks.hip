@@ -420,7 +420,25 @@ attn_chunks_kernel(AttnArgs a, const uint16_t *__restrict__ ops, float *__restri
   // one tile with the column `use`; loads the next tile's column into `pre`
   auto step = [&](const Col &use, Col &pre) {
     const bool last = t + 1 == ntile;
-    if (!last) load_col(pre, seg0, cnt, t + 1);
+    // The next tile's column loads go out first, on every path: the next
+    // chunk's first column on a chunk's last tile (its ticket taken first),
+    // the current chunk's first again when no chunk is left.  The same loads
+    // in the same order on every path let the compiler count them exactly,
+    // so the uses below wait only for loads of earlier steps (a load under a
+    // branch makes it wait for every load in flight at the next use).
+    int cn = 0, segn = seg0, cntn = cnt, tn = t + 1;
+    bool more = false;
+    if (last) {
+      const int xn = ticket();
+      more = xn < nunion;
+      tn = 0;
+      if (more) {
+        cn = __builtin_amdgcn_readfirstlane(sm.ulist[xn]);  // uniform: one LDS slot
+        segn = sm.useg[xn];
+        cntn = sm.ucnt[xn];
+      }
+    }
+    load_col(pre, segn, cntn, tn);
     // S^T = K Q^T: lane holds keys chunk_perm_key(kt, 4 lg + j) of column ln
     f32x4c st[4];
 #pragma unroll
@@ -429,19 +447,7 @@ attn_chunks_kernel(AttnArgs a, const uint16_t *__restrict__ ops, float *__restri
     for (int s = 0; s < C::kKS; ++s)
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) st[kt] = mfma16c(as_bf16x8c(kop[kt][s]), as_bf16x8c(use.qop[s]), st[kt]);
-    int cn = 0, segn = 0, cntn = 1;
-    bool more = false;
-    if (last) {  // the next chunk: its K now, its first column
-      const int xn = ticket();
-      more = xn < nunion;
-      if (more) {
-        cn = __builtin_amdgcn_readfirstlane(sm.ulist[xn]);  // uniform: one LDS slot
-        segn = sm.useg[xn];
-        cntn = sm.ucnt[xn];
-        load_k(cn);
-        load_col(pre, segn, cntn, 0);
-      }
-    }
+    if (more) load_k(cn);  // the next chunk's K, once this tile's S^T has read K
     // exact softmax over the chunk's 64 keys, scaled by the fusion weight
     float mc = -INFINITY;
 #pragma unroll
