@@ -3,10 +3,12 @@
 // group, p = softmax(tau q'_c . k_j), k' = sum_j p_j k_j, b' = -sum_j p_j log p_j.
 //
 // One workgroup per (chunk, KV head, batch).  The chunk's keys are read from
-// HBM once (coalesced 16-byte loads), widened to fp32 in LDS with a padded
-// row stride so that one key per lane reads conflict-free, and shared by the
-// G query heads of the group (one wave per head).  HBM-bound: 16 KB of keys
-// per (b, g, c) against G*(d*2+4) bytes written.
+// HBM once (coalesced 16-byte loads) and kept in LDS in their storage type
+// (bf16: 16 KB, so that eight workgroups share a CU), rows padded by one
+// 32-bit word so that one key per lane reads conflict-free; they are shared
+// by the G query heads of the group (one wave per head) and widened to fp32
+// as they are read, two bf16 per 32-bit read.  HBM-bound: 16 KB of keys per
+// (b, g, c) against G*(d*2+4) bytes written.
 #include "hils_common.h"
 #include "launch.h"
 
@@ -16,14 +18,25 @@ constexpr int kSumS = 64;      // chunk size handled here
 constexpr int kSumThreads = 256;
 
 template <typename T, int D>
-__global__ void __launch_bounds__(kSumThreads)
+__global__ void __launch_bounds__(kSumThreads, sizeof(T) == 2 ? 8 : 4)  // bf16: eight workgroups per CU (LDS)
 landmark_summary_kernel(const T *__restrict__ k, const T *__restrict__ q_lm, T *__restrict__ k_sum,
                         float *__restrict__ b_sum, int T_len, int Hq, int Hkv, int C, int c0,
                         float tau, const int32_t *__restrict__ block_table, int max_pages, int num_pages) {
-  constexpr int LD = D + 1;  // padded fp32 row stride (conflict-free column reads)
-  __shared__ float keys[kSumS * LD];
-  __shared__ float qrow[4][D];
-  __shared__ float prob[4][kSumS];
+  constexpr int EPW = 4 / static_cast<int>(sizeof(T));  // elements per 32-bit word
+  constexpr int LW = D / EPW + 1;                       // padded row stride in words
+  __shared__ uint32_t keys[kSumS * LW];
+  __shared__ __align__(16) float qrow[4][D];
+  __shared__ __align__(16) float prob[4][kSumS];
+  // word x of key row j as EPW floats
+  auto key_word = [&](int j, int x, float (&o)[EPW]) {
+    const uint32_t w = keys[j * LW + x];
+    if constexpr (EPW == 2) {
+      o[0] = __uint_as_float(w << 16);
+      o[1] = __uint_as_float(w & 0xFFFF0000u);
+    } else {
+      o[0] = __uint_as_float(w);
+    }
+  };
   const int c = c0 + blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int G = Hq / Hkv;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -67,11 +80,10 @@ landmark_summary_kernel(const T *__restrict__ k, const T *__restrict__ q_lm, T *
   }
 #pragma unroll
   for (int r = 0; r < KP; ++r) {
-    float v[8];
-    Elem<T>::load8(reinterpret_cast<const T *>(&raw[r][0]), v);
     const int e8 = tid + r * kSumThreads, row = (e8 * 8) / D, col = (e8 * 8) % D;
+    const uint32_t *w = reinterpret_cast<const uint32_t *>(&raw[r][0]);
 #pragma unroll
-    for (int t = 0; t < 8; ++t) keys[row * LD + col + t] = v[t];
+    for (int t = 0; t < 8 / EPW; ++t) keys[row * LW + col / EPW + t] = w[t];
   }
   // (parked by every wave, used or not: a use under a branch would let the
   // compiler move the loads there, a round trip later)
@@ -87,10 +99,20 @@ landmark_summary_kernel(const T *__restrict__ k, const T *__restrict__ q_lm, T *
       for (int e = lane; e < D; e += 64) qrow[wave][e] = Elem<T>::load(q_lm, so * D + e);
     __syncthreads();
     if (active) {
-      // logit of key j = lane
+      // logit of key j = lane (products in order of e)
       float acc = 0.f;
 #pragma unroll 8
-      for (int e = 0; e < D; ++e) acc += qrow[wave][e] * keys[lane * LD + e];
+      for (int e4 = 0; e4 < D; e4 += 4) {
+        const float4 q4 = *reinterpret_cast<const float4 *>(&qrow[wave][e4]);
+        const float qv[4] = {q4.x, q4.y, q4.z, q4.w};
+#pragma unroll
+        for (int x = 0; x < 4 / EPW; ++x) {
+          float kv[EPW];
+          key_word(lane, e4 / EPW + x, kv);
+#pragma unroll
+          for (int u = 0; u < EPW; ++u) acc = fmaf(qv[x * EPW + u], kv[u], acc);
+        }
+      }
       const float l = tau * acc;
       const float m = wave_max(l);
       const float ex = expf(l - m);
@@ -103,11 +125,30 @@ landmark_summary_kernel(const T *__restrict__ k, const T *__restrict__ q_lm, T *
     }
     __syncthreads();
     if (active) {
-      for (int e = lane; e < D; e += 64) {
-        float s = 0.f;
-#pragma unroll 8
-        for (int j = 0; j < kSumS; ++j) s += prob[wave][j] * keys[j * LD + e];
-        Elem<T>::store(k_sum, so * D + e, s);
+      // k' over the keys in order of j; lane x owns the EPW elements of
+      // word x of a row
+      for (int x = lane; x < D / EPW; x += 64) {
+        float sacc[EPW];
+#pragma unroll
+        for (int u = 0; u < EPW; ++u) sacc[u] = 0.f;
+#pragma unroll 4
+        for (int j4 = 0; j4 < kSumS; j4 += 4) {
+          const float4 p4 = *reinterpret_cast<const float4 *>(&prob[wave][j4]);
+          const float pv[4] = {p4.x, p4.y, p4.z, p4.w};
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            float kv[EPW];
+            key_word(j4 + jj, x, kv);
+#pragma unroll
+            for (int u = 0; u < EPW; ++u) sacc[u] = fmaf(pv[jj], kv[u], sacc[u]);
+          }
+        }
+        if constexpr (EPW == 2) {
+          reinterpret_cast<uint32_t *>(k_sum)[(so * D) / 2 + x] =
+              static_cast<uint32_t>(f32_to_bf16(sacc[0])) | (static_cast<uint32_t>(f32_to_bf16(sacc[1])) << 16);
+        } else {
+          Elem<T>::store(k_sum, so * D + x, sacc[0]);
+        }
       }
       if (lane == 0) b_sum[so] = fmaxf(ent_s[wave], 0.f);
     }
