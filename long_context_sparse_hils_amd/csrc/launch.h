@@ -38,7 +38,7 @@ struct AttnArgs {
   const int32_t *topk_idx;
   const float *topk_score;
   void *o;
-  void *vt_ws;  // prefill workspace: transposed value tiles of the MFMA path, then the rows' chunk log-mass
+  void *vt_ws;  // prefill workspace of the MFMA path: chunk log-mass, block |v| bounds, K/V in operand order
   int B, T, Hq, Hkv, d, S, K, W;
   float tau;
   bool bf16;
@@ -124,8 +124,10 @@ bool attn_mfma_supported(const AttnArgs &a);
 size_t attn_mfma_ws_bytes(int B, int Hq, int Hkv, int T, int d, int K);
 hipError_t launch_attn_chunks(const AttnArgs &a, uint16_t *ops, float *lse, const float *vmax, int nblk,
                               hipStream_t st);
-// every complete chunk's K and V^T in the chunk passes' MFMA operand order
-hipError_t launch_kv_operand_order(const AttnArgs &a, uint16_t *ops, hipStream_t st);
+// every 64-key block's K and V^T in the MFMA passes' operand order: complete
+// chunks into ops, a partial last block into ops_tail; each block's largest
+// |v| into vmax (when given)
+hipError_t launch_kv_operand_order(const AttnArgs &a, uint16_t *ops, uint16_t *ops_tail, float *vmax, hipStream_t st);
 // The chunk terms of sequences longer than kLongMinChunks chunks run
 // chunk-major over the whole sequence, in segments of queries whose
 // per-(query, slot) partial results take at most kLongPartBytes.

@@ -104,37 +104,54 @@ struct ChunkSmem {
 }  // namespace
 
 // ------------------------------------------------------------------ operand order
-// Each complete chunk's K and V^T, written in the order the chunk kernel's
-// MFMA operand loads consume them: 2 D / 16 blocks of 1 KB, block i read
-// by one wave-wide 16-byte load in which lane l = 16 lg + ln takes bytes
+// Each 64-key block's K and V^T, written in the order the MFMA passes'
+// operand loads consume them: 2 D / 16 pieces of 1 KB, piece i read by one
+// wave-wide 16-byte load in which lane l = 16 lg + ln takes bytes
 // 16 l .. 16 l + 15:
-//   K block  kt * (D/32) + s :  K[key chunk_perm_key(kt, ln)][d = 32 s + 8 lg .. + 8]
-//   V block  4 D/32 + 2 dt + sl: V[keys 32 sl + 8 lg .. + 8][d = 16 dt + ln]
-// so every operand load reads 1 KB of consecutive bytes.
+//   K piece  kt * (D/32) + s :  K[key chunk_perm_key(kt, ln)][d = 32 s + 8 lg .. + 8]
+//   V piece  4 D/32 + 2 dt + sl: V[keys 32 sl + 8 lg .. + 8][d = 16 dt + ln]
+// so every operand load reads 1 KB of consecutive bytes.  Complete chunks go
+// to ops ([pair][chunk]); the partial block that ends a sequence whose
+// length is not a multiple of 64 goes to ops_tail ([pair]), its keys past T
+// zero.  vmax (when given) [pair][block]: each block's largest |v|.
 template <int D>
 __global__ void __launch_bounds__(256)
 kv_operand_order_kernel(const uint16_t *__restrict__ k, const uint16_t *__restrict__ v, uint16_t *__restrict__ ops,
-                        int T, int C) {
+                        uint16_t *__restrict__ ops_tail, float *__restrict__ vmax, int T, int C, int nblk) {
   constexpr int LD = D + 2;  // padded V rows in LDS (spreads the column reads over banks)
   constexpr int KB = 4 * (D / 32), VB = 2 * (D / 16);
   __shared__ uint16_t vs[kCK * LD];
+  __shared__ uint32_t wmax[4];
   const int c = blockIdx.x, pair = blockIdx.y, tid = threadIdx.x;
+  const int nk = min(kCK, T - c * kCK);  // keys of the block inside the sequence
   const uint16_t *kc = k + (static_cast<size_t>(pair) * T + static_cast<size_t>(c) * kCK) * D;
   const uint16_t *vc = v + (static_cast<size_t>(pair) * T + static_cast<size_t>(c) * kCK) * D;
-  uint16_t *out = ops + (static_cast<size_t>(pair) * C + c) * (KB + VB) * 512;
+  uint16_t *out = c < C ? ops + (static_cast<size_t>(pair) * C + c) * (KB + VB) * 512
+                        : ops_tail + static_cast<size_t>(pair) * (KB + VB) * 512;
+  uint32_t amax = 0u;  // |v| as bf16 bits: the order of non-negative floats
   for (int p = tid; p < kCK * D / 8; p += 256) {  // V rows into LDS
     const int key = p / (D / 8), seg = p % (D / 8);
-    const uint4 u = *reinterpret_cast<const uint4 *>(vc + key * D + seg * 8);
+    const uint4 u = key < nk ? *reinterpret_cast<const uint4 *>(vc + key * D + seg * 8) : make_uint4(0u, 0u, 0u, 0u);
     uint32_t *row = reinterpret_cast<uint32_t *>(vs + key * LD + seg * 8);
     row[0] = u.x; row[1] = u.y; row[2] = u.z; row[3] = u.w;
+    const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) amax = max(amax, max(w4[e] & 0x7FFFu, (w4[e] >> 16) & 0x7FFFu));
   }
   for (int p = tid; p < KB * 64; p += 256) {  // K pieces: straight copies
     const int blk = p / 64, l = p % 64, ln = l & 15, lg = l >> 4;
-    const int kt = blk / (D / 32), s = blk % (D / 32);
+    const int kt = blk / (D / 32), s = blk % (D / 32), key = chunk_perm_key(kt, ln);
     *reinterpret_cast<uint4 *>(out + p * 8) =
-        *reinterpret_cast<const uint4 *>(kc + chunk_perm_key(kt, ln) * D + 32 * s + 8 * lg);
+        key < nk ? *reinterpret_cast<const uint4 *>(kc + key * D + 32 * s + 8 * lg) : make_uint4(0u, 0u, 0u, 0u);
+  }
+  if (vmax) {
+    amax = wave_reduce_u32<1>(amax);
+    if ((tid & 63) == 0) wmax[tid >> 6] = amax;
   }
   __syncthreads();
+  if (vmax && tid == 0)
+    vmax[static_cast<size_t>(pair) * nblk + c] =
+        bf16_to_f32(static_cast<uint16_t>(max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]))));
   for (int p = tid; p < VB * 64; p += 256) {  // V^T pieces from LDS
     const int blk = p / 64, l = p % 64, ln = l & 15, lg = l >> 4;
     const int dt = blk / 2, sl = blk % 2, d = 16 * dt + ln, key0 = 32 * sl + 8 * lg;
@@ -540,10 +557,6 @@ static hipError_t chunks_t(const AttnArgs &a, uint16_t *ops, float *lse, const f
   using C = ChunkCfg<D, G, QB, K_MAX, WAVES>;
   const int nblocks = (a.T + QB - 1) / QB;
   const int npairs = a.B * a.Hkv;
-  kv_operand_order_kernel<D><<<dim3(a.T / kCK, npairs), 256, 0, st>>>(
-      static_cast<const uint16_t *>(a.k), static_cast<const uint16_t *>(a.v), ops, a.T, a.T / kCK);
-  hipError_t e0 = hipGetLastError();
-  if (e0 != hipSuccess) return e0;
   const bool pair_fits_l2 = static_cast<size_t>(a.T) * D * 2 * 2 <= (size_t{4} << 20);
   const int xcd_map = (npairs % 8 == 0 && pair_fits_l2) ? 1 : 0;
   const size_t smem = sizeof(ChunkSmem<D, G, QB, K_MAX, WAVES>);
@@ -568,14 +581,15 @@ static hipError_t chunks_g(const AttnArgs &a, uint16_t *ops, float *lse, const f
   return chunks_t<D, G, QB32, 32>(a, ops, lse, vmax, nblk, st);
 }
 
-hipError_t launch_kv_operand_order(const AttnArgs &a, uint16_t *ops, hipStream_t st) {
-  const dim3 grid(a.T / kCK, a.B * a.Hkv);
+hipError_t launch_kv_operand_order(const AttnArgs &a, uint16_t *ops, uint16_t *ops_tail, float *vmax, hipStream_t st) {
+  const int C = a.T / kCK, nblk = (a.T + kCK - 1) / kCK;
+  const dim3 grid(nblk, a.B * a.Hkv);
   const uint16_t *k = static_cast<const uint16_t *>(a.k), *v = static_cast<const uint16_t *>(a.v);
-  if (grid.x == 0) return hipSuccess;
+  if (grid.x == 0 || grid.y == 0) return hipSuccess;
   if (a.d == 128)
-    kv_operand_order_kernel<128><<<grid, 256, 0, st>>>(k, v, ops, a.T, a.T / kCK);
+    kv_operand_order_kernel<128><<<grid, 256, 0, st>>>(k, v, ops, ops_tail, vmax, a.T, C, nblk);
   else if (a.d == 64)
-    kv_operand_order_kernel<64><<<grid, 256, 0, st>>>(k, v, ops, a.T, a.T / kCK);
+    kv_operand_order_kernel<64><<<grid, 256, 0, st>>>(k, v, ops, ops_tail, vmax, a.T, C, nblk);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

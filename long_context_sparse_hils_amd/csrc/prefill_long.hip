@@ -388,8 +388,7 @@ template <int D, int G>
 static hipError_t long_t(const AttnArgs &a, uint16_t *ops, float *lse, uint8_t *ws, hipStream_t st) {
   const int C = a.T / kLK, npairs = a.B * a.Hkv;
   const LongWs L = long_layout(ws, a.B, a.Hq, a.Hkv, a.T, D, a.K);
-  hipError_t e = launch_kv_operand_order(a, ops, st);
-  if (e != hipSuccess) return e;
+  hipError_t e;
   const size_t ncnt = static_cast<size_t>(npairs) * C;
   const unsigned zb = static_cast<unsigned>(std::min<size_t>((ncnt + 255) / 256, 4096));
   long_zero_kernel<<<zb, 256, 0, st>>>(L.cnt, ncnt);

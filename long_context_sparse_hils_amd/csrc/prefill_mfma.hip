@@ -13,17 +13,19 @@
 // each other's barrier waits and softmax phases with MFMA work.  Each wave
 // owns 32 (query, head) rows = two 16-row MFMA tiles of 16/G adjacent
 // queries x G heads, with fp32 output accumulators in registers.  The
-// workgroup walks the 64-key blocks of its window band: each block's K
-// (row-major, XOR-swizzled 16-byte pieces) and V^T ([d][key]; read from
-// value tiles transposed once per call by a small kernel) are staged in LDS
-// straight from global memory, double buffered, and shared by all waves;
-// each wave runs the tiles whose rows overlap the block:
+// workgroup walks the 64-key blocks of its window band: each block's K and
+// V^T, in the MFMA operand order that one pass per call writes (every
+// operand read is one wave-wide 1 KB piece), are staged in LDS straight from
+// global memory, double buffered, and shared by all waves; each wave runs
+// the tiles whose rows overlap the block:
 //   S^T = K Q^T           16x16x32 bf16 MFMA, keys in M, rows in N
 //   softmax against the row's reference maximum, masked to [n_i * S, i]
 //                         only on blocks that cross a row's window edge
 //   O^T += V^T P^T        16x16x32 bf16 MFMA, d in M, rows in N
 // The key order inside S^T is permuted so that its accumulator layout is
-// exactly the B-operand layout of the P^T product (no cross-lane moves).
+// exactly the B-operand layout of the P^T product (no cross-lane moves):
+// row m of S^T tile kt holds key 32 (kt >> 1) + 8 (m >> 2) + 4 (kt & 1) +
+// (m & 3), the order in which the operand-order pass lays out K.
 // A block moves the reference only when its own maximum exceeds it by more
 // than kLazyRescale; numerator and denominator always share the reference,
 // so the result does not depend on when it moves.
@@ -54,79 +56,19 @@ struct AttnCfg {
   static constexpr int kKS = D / 32;          // k-steps of S^T
   static constexpr int kDT = D / 16;          // d tiles of O^T
   static constexpr int kRowPieces = D / 8;    // 16-byte pieces per K row
-  // one staged block = 64 K rows + D V^T rows of 128 bytes, loaded straight
-  // into LDS in 1 KB wave-wide pieces
-  static constexpr int kLoadsK = kItemKeys * D * 2 / 1024 / WAVES;
-  static constexpr int kLoadsV = D * kItemKeys * 2 / 1024 / WAVES;
-  static_assert(kLoadsK * WAVES * 1024 == kItemKeys * D * 2, "K block must split evenly over the waves");
+  // one staged block = the K and V^T pieces of the operand order (1 KB each,
+  // K pieces first), loaded straight into LDS
+  static constexpr int kPiecesK = 4 * kKS, kPiecesV = 2 * kDT;
+  static constexpr int kLoadsK = kPiecesK / WAVES;
+  static constexpr int kLoadsV = kPiecesV / WAVES;
+  static_assert(kLoadsK * WAVES == kPiecesK && kLoadsV * WAVES == kPiecesV, "pieces must split evenly over the waves");
 };
 
 template <int D, int G, int WAVES, int TPW>
 struct AttnSmem {
-  uint16_t ks[2][kItemKeys * D];   // K rows, 16-byte pieces XOR-swizzled per row
-  uint16_t vt[2][D * kItemKeys];   // V^T rows, 16-byte pieces XOR-swizzled per row
+  uint16_t ks[2][kItemKeys * D];   // K pieces in operand order (piece kt * D/32 + s at 512 kt + ...)
+  uint16_t vt[2][D * kItemKeys];   // V^T pieces in operand order (piece 2 dt + sl)
 };
-
-// key held by S^T tile kt, row m (the permutation described above)
-__device__ __forceinline__ int perm_key(int kt, int m) {
-  return 32 * (kt >> 1) + 8 * (m >> 2) + 4 * (kt & 1) + (m & 3);
-}
-
-// XOR swizzle of the 16-byte pieces of K row r.  The 16 rows that one MFMA
-// operand read touches (perm_key(kt, 0..15)) then fall in 16 different bank
-// groups; for those rows the swizzle equals ln (D = 128) or ln >> 1 (D = 64).
-template <int D>
-__device__ __forceinline__ int k_swz(int r) {
-  return D == 128 ? ((r & 3) | ((r >> 1) & 12)) : (((r >> 1) & 1) | ((r >> 2) & 6));
-}
-// XOR swizzle of the 8 pieces of V^T row d: rows d and d ^ 1 share a 256-byte
-// bank line, so the swizzle runs over d >> 1.
-__device__ __forceinline__ int v_swz(int d) { return (d >> 1) & 7; }
-
-// ------------------------------------------------------------------ V^T tiles
-// v [B, Hkv, T, D] -> vt [B, Hkv, nblk, D, 64]: block blk holds keys
-// 64 blk .. 64 blk + 63 transposed (keys at or past T are zero); vmax
-// [B, Hkv, nblk] (when given): the largest |v| element of each block.
-template <int D>
-__global__ void __launch_bounds__(256)
-vt_transpose_kernel(const uint16_t *__restrict__ v, uint16_t *__restrict__ vt, float *__restrict__ vmax, int T,
-                    int nblk) {
-  constexpr int LD = D + 2;  // padded row (4-byte aligned, spreads column reads over banks)
-  __shared__ uint16_t tile[kItemKeys * LD];
-  __shared__ uint32_t wmax[4];
-  const int blk = blockIdx.x, pair = blockIdx.y;
-  const uint16_t *src = v + static_cast<size_t>(pair) * T * D;
-  const int j0 = blk * kItemKeys;
-  uint32_t amax = 0u;  // |v| as bf16 bits: the order of non-negative floats
-  for (int p = threadIdx.x; p < kItemKeys * D / 8; p += 256) {
-    const int key = p / (D / 8), seg = p % (D / 8);
-    const uint4 u = (j0 + key < T) ? *reinterpret_cast<const uint4 *>(src + static_cast<size_t>(j0 + key) * D + seg * 8)
-                                   : make_uint4(0u, 0u, 0u, 0u);
-    uint32_t *row = reinterpret_cast<uint32_t *>(tile + key * LD + seg * 8);
-    row[0] = u.x; row[1] = u.y; row[2] = u.z; row[3] = u.w;
-    const uint32_t w4[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-    for (int e = 0; e < 4; ++e) amax = max(amax, max(w4[e] & 0x7FFFu, (w4[e] >> 16) & 0x7FFFu));
-  }
-  if (vmax) {
-    amax = wave_reduce_u32<1>(amax);
-    if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = amax;
-  }
-  __syncthreads();
-  if (vmax && threadIdx.x == 0)
-    vmax[static_cast<size_t>(pair) * nblk + blk] =
-        bf16_to_f32(static_cast<uint16_t>(max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]))));
-  uint16_t *dst = vt + (static_cast<size_t>(pair) * nblk + blk) * D * kItemKeys;
-  for (int p = threadIdx.x; p < D * kItemKeys / 8; p += 256) {
-    const int d = p / 8, kp = p % 8;
-    uint32_t w[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      w[e] = static_cast<uint32_t>(tile[(8 * kp + 2 * e) * LD + d]) |
-             (static_cast<uint32_t>(tile[(8 * kp + 2 * e + 1) * LD + d]) << 16);
-    *reinterpret_cast<uint4 *>(dst + d * kItemKeys + kp * 8) = make_uint4(w[0], w[1], w[2], w[3]);
-  }
-}
 
 // ------------------------------------------------------------------ one item
 // Per-lane state of a wave's row tiles.
@@ -141,14 +83,13 @@ struct RowState {
 // while the MFMAs of step s run, and the scheduling barrier keeps later reads
 // from being hoisted further (registers).
 template <int D>
-__device__ __forceinline__ void tile_scores(const bf16x8 (&qop)[D / 32], const uint16_t *ksb, int koff,
+__device__ __forceinline__ void tile_scores(const bf16x8 (&qop)[D / 32], const uint16_t *ksb, int lane8,
                                             f32x4 (&st)[4]) {
   constexpr int KS = D / 32;
   uint4 u[2][4];
-  auto load_k = [&](uint4 (&dst)[4], int s) {
+  auto load_k = [&](uint4 (&dst)[4], int s) {  // K piece kt * KS + s
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt)
-      dst[kt] = *reinterpret_cast<const uint4 *>(ksb + (koff ^ (32 * s)) + (32 * (kt >> 1) + 4 * (kt & 1)) * D);
+    for (int kt = 0; kt < 4; ++kt) dst[kt] = *reinterpret_cast<const uint4 *>(ksb + (kt * KS + s) * 512 + lane8);
   };
 #pragma unroll
   for (int kt = 0; kt < 4; ++kt) st[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -163,9 +104,9 @@ __device__ __forceinline__ void tile_scores(const bf16x8 (&qop)[D / 32], const u
 }
 
 // Softmax of one tile's S^T into the bf16 P^T operand (this lane holds keys
-// perm_key(kt, 4 lg + i) of row ln) against the row's reference maximum
-// m_row; when MASKED, only the lane's keys with perm_key(kt, 4 lg + i) -
-// 8 lg <= lim count (see the window limit below).  The reference moves to
+// 32 (kt >> 1) + 8 lg + 4 (kt & 1) + i of row ln) against the row's
+// reference maximum m_row; when MASKED, only the lane's keys whose offset
+// from 8 lg is at most lim count (see the window limit below).  The reference moves to
 // the block's maximum only when that exceeds it by more than kLazyRescale,
 // and the returned factor (1 otherwise) rescales the row's accumulator.
 template <bool MASKED>
@@ -178,7 +119,7 @@ __device__ __forceinline__ float tile_softmax(const f32x4 (&st)[4], bf16x8 (&pb)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       float x = st[kt][i];
-      // perm_key(kt, 4 lg + i) - 8 lg, a constant
+      // the key's offset from 8 lg, a constant
       if (MASKED) x = (32 * (kt >> 1) + 4 * (kt & 1) + i <= lim) ? x : -INFINITY;
       p[kt][i] = x;
       mb = fmaxf(mb, x);
@@ -227,15 +168,15 @@ __device__ __forceinline__ void rescale_acc(f32x4 (&acc)[D / 16], float sc) {
 // O^T += V^T P^T; the next d-tile pair's operands are read while this pair's
 // MFMAs run
 template <int D>
-__device__ __forceinline__ void tile_pv(f32x4 (&acc)[D / 16], const bf16x8 (&pb)[2], const uint16_t *vtb, int voff) {
+__device__ __forceinline__ void tile_pv(f32x4 (&acc)[D / 16], const bf16x8 (&pb)[2], const uint16_t *vtb, int lane8) {
   constexpr int DT = D / 16;
   uint4 v[2][2][2];
-  auto load_v = [&](uint4 (&dst)[2][2], int dt) {
+  auto load_v = [&](uint4 (&dst)[2][2], int dt) {  // V^T piece 2 (dt + d2) + sl
 #pragma unroll
     for (int d2 = 0; d2 < 2; ++d2)
 #pragma unroll
       for (int sl = 0; sl < 2; ++sl)
-        dst[d2][sl] = *reinterpret_cast<const uint4 *>(vtb + (voff ^ (32 * sl)) + 16 * (dt + d2) * kItemKeys);
+        dst[d2][sl] = *reinterpret_cast<const uint4 *>(vtb + (2 * (dt + d2) + sl) * 512 + lane8);
   };
   load_v(v[0], 0);
 #pragma unroll
@@ -253,24 +194,24 @@ __device__ __forceinline__ void tile_pv(f32x4 (&acc)[D / 16], const bf16x8 (&pb)
 // Attend one staged block with one 16-row tile.
 template <int D, bool MASKED>
 __device__ __forceinline__ void attend_tile(const bf16x8 (&qop)[D / 32], f32x4 (&acc)[D / 16], float &m_row,
-                                            float &l_row, const uint16_t *ksb, const uint16_t *vtb, int koff,
-                                            int voff, int lim, float tau, float tl2e) {
+                                            float &l_row, const uint16_t *ksb, const uint16_t *vtb, int lane8,
+                                            int lim, float tau, float tl2e) {
   f32x4 st[4];
-  tile_scores<D>(qop, ksb, koff, st);
+  tile_scores<D>(qop, ksb, lane8, st);
   bf16x8 pb[2];
   const float sc = tile_softmax<MASKED>(st, pb, m_row, l_row, lim, tau, tl2e);
   rescale_acc<D>(acc, sc);
-  tile_pv<D>(acc, pb, vtb, voff);
+  tile_pv<D>(acc, pb, vtb, lane8);
 }
 
 // Run the block for the wave's tiles that take part (bit t of `mask`).
 template <int D, int TPW, bool MASKED>
 __device__ __forceinline__ void run_item(int mask, RowState<D, TPW> &R, const uint16_t *ksb, const uint16_t *vtb,
-                                         int koff, int voff, const int (&lim)[TPW], float tau, float tl2e) {
+                                         int lane8, const int (&lim)[TPW], float tau, float tl2e) {
 #pragma unroll
   for (int t = 0; t < TPW; ++t)
     if ((mask >> t) & 1)
-      attend_tile<D, MASKED>(R.qop[t], R.acc[t], R.m_row[t], R.l_row[t], ksb, vtb, koff, voff, lim[t], tau, tl2e);
+      attend_tile<D, MASKED>(R.qop[t], R.acc[t], R.m_row[t], R.l_row[t], ksb, vtb, lane8, lim[t], tau, tl2e);
 }
 
 // ------------------------------------------------------------------ kernel
@@ -278,7 +219,8 @@ __device__ __forceinline__ void run_item(int mask, RowState<D, TPW> &R, const ui
 // registers; two tiles per wave: two waves per SIMD, at most 256.
 template <int D, int G, int WAVES, int TPW>
 __global__ void __launch_bounds__(WAVES * 64, TPW == 1 ? 4 : 2)
-attn_window_mfma_kernel(AttnArgs a, int ntiles, int xcd_map, int nblk) {
+attn_window_mfma_kernel(AttnArgs a, const uint16_t *__restrict__ ops, const uint16_t *__restrict__ ops_tail,
+                        int ntiles, int xcd_map) {
   using C = AttnCfg<D, G, WAVES, TPW>;
   __shared__ AttnSmem<D, G, WAVES, TPW> sm;
 
@@ -306,8 +248,12 @@ attn_window_mfma_kernel(AttnArgs a, int ntiles, int xcd_map, int nblk) {
   const int ln = lane & 15, lg = lane >> 4;
 
   const uint16_t *qb = static_cast<const uint16_t *>(a.q);
-  const uint16_t *kb = static_cast<const uint16_t *>(a.k) + (static_cast<size_t>(b) * Hkv + g) * T * D;
-  const uint16_t *vtg = static_cast<const uint16_t *>(a.vt_ws) + (static_cast<size_t>(b) * Hkv + g) * nblk * D * kItemKeys;
+  // the pair's blocks in operand order: complete chunks, then the partial
+  // block that ends a sequence whose length is not a multiple of 64
+  const int nchunks = T / kItemKeys;
+  constexpr int kBlockElems = (C::kPiecesK + C::kPiecesV) * 512;
+  const uint16_t *opg = ops + (static_cast<size_t>(b) * Hkv + g) * nchunks * kBlockElems;
+  const uint16_t *optail = ops_tail + (static_cast<size_t>(b) * Hkv + g) * kBlockElems;
 
   // ---- rows: tile t of this wave holds queries q0 + wave * kQPW + t * kQPT
   // + (0 .. kQPT - 1), lane column ln = (query ln / G, head g G + ln % G)
@@ -340,28 +286,21 @@ attn_window_mfma_kernel(AttnArgs a, int ntiles, int xcd_map, int nblk) {
   const int jw0 = eligible_chunks(i_first, W, kItemKeys) * kItemKeys;
   const int nitems = (i_last - jw0) / kItemKeys + 1;
 
-  // ---- staging: block x -> LDS buffer, straight from global memory.  Wave w
-  // fills 1 KB slices w, w + WAVES, ... of each tensor; lane l's 16 bytes land
-  // at byte 16 l of the slice, i.e. at one (row, physical piece) pair, and the
-  // lane fetches the logical piece the swizzle puts there.
+  // ---- staging: block x -> LDS buffer, straight from global memory.  Wave
+  // w copies pieces w, w + WAVES, ... of the block (1 KB each, lane l's 16
+  // bytes at byte 16 l), K pieces into ks, V^T pieces into vt.
   auto issue_loads = [&](int j0, int buf) {
-    const uint16_t *vsrc = vtg + static_cast<size_t>(j0 / kItemKeys) * D * kItemKeys;
+    const int blk = j0 / kItemKeys;
+    const uint16_t *src = (blk < nchunks ? opg + static_cast<size_t>(blk) * kBlockElems : optail) + lane * 8;
 #pragma unroll
     for (int i = 0; i < C::kLoadsK; ++i) {
-      const int slice = i * WAVES + wave;
-      const int sl = slice * 64 + lane;  // 16-byte slot
-      const int r = sl / C::kRowPieces, pp = sl % C::kRowPieces;
-      const int pc = pp ^ k_swz<D>(r);
-      const int key = min(j0 + r, T - 1);  // rows past T are never used unmasked
-      lds_dma16(kb + static_cast<uint32_t>(key * D + pc * 8), lds_address(sm.ks[buf] + slice * 512));
+      const int piece = i * WAVES + wave;
+      lds_dma16(src + piece * 512, lds_address(sm.ks[buf] + piece * 512));
     }
 #pragma unroll
     for (int i = 0; i < C::kLoadsV; ++i) {
-      const int slice = i * WAVES + wave;
-      const int sl = slice * 64 + lane;
-      const int d = sl / 8, pp = sl % 8;
-      const int pc = pp ^ v_swz(d);
-      lds_dma16(vsrc + static_cast<uint32_t>(d * kItemKeys + pc * 8), lds_address(sm.vt[buf] + slice * 512));
+      const int piece = i * WAVES + wave;
+      lds_dma16(src + (C::kPiecesK + piece) * 512, lds_address(sm.vt[buf] + piece * 512));
     }
   };
   // The rows' chunk parts (bf16, written into o by the chunk pass) for the
@@ -393,13 +332,8 @@ attn_window_mfma_kernel(AttnArgs a, int ntiles, int xcd_map, int nblk) {
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  // per-lane LDS offsets of the S^T A operand (K rows perm_key(kt, ln); their
-  // swizzle does not depend on kt) and of the O^T A operand (V^T rows 16 dt + ln)
-  // k-step s reads piece (4 s + lg) ^ swizzle = piece(0) ^ 4 s: offset koff ^ 32 s;
-  // key slot sl reads piece (lg + 4 sl) ^ swizzle: offset voff ^ 32 sl
-  const int r0 = 8 * (ln >> 2) + (ln & 3);
-  const int koff = r0 * D + ((lg ^ k_swz<D>(r0)) << 3);
-  const int voff = ln * kItemKeys + ((lg ^ v_swz(ln)) << 3);
+  // every operand read: lane l's 16 bytes of a 1 KB piece
+  const int lane8 = lane * 8;
 
   const float tau = a.tau;
   const float tl2e = tau * kLog2e;
@@ -429,9 +363,9 @@ attn_window_mfma_kernel(AttnArgs a, int ntiles, int xcd_map, int nblk) {
       if (__ballot(mine)) mask |= 1 << t;
     }
     if (__ballot(edge))
-      run_item<D, TPW, true>(mask, R, sm.ks[buf], sm.vt[buf], koff, voff, lim, tau, tl2e);
+      run_item<D, TPW, true>(mask, R, sm.ks[buf], sm.vt[buf], lane8, lim, tau, tl2e);
     else
-      run_item<D, TPW, false>(mask, R, sm.ks[buf], sm.vt[buf], koff, voff, lim, tau, tl2e);
+      run_item<D, TPW, false>(mask, R, sm.ks[buf], sm.vt[buf], lane8, lim, tau, tl2e);
   };
   // Block x + 1 loads into buffer (x + 1) & 1, last read in iteration
   // x - 1 (before the barrier that ended it).  The last block, peeled off
@@ -510,10 +444,14 @@ static size_t attn_chunk_meta_bytes(int B, int Hq, int Hkv, int T) {
   return ((static_cast<size_t>(B) * Hq * T + static_cast<size_t>(B) * Hkv * nblk) * sizeof(float) + 255) / 256 * 256;
 }
 
-// value tiles (bf16), rounded up to 256 bytes
-static size_t attn_vt_bytes(int B, int Hkv, int T, int d) {
-  const size_t nblk = (static_cast<size_t>(T) + kItemKeys - 1) / kItemKeys;
-  return (static_cast<size_t>(B) * Hkv * nblk * kItemKeys * d * 2 + 255) / 256 * 256;
+// the 64-key blocks' K and V^T in operand order: every complete chunk, then
+// one partial block per (b, g) pair (present whatever T, so that the layout
+// does not depend on T mod 64)
+static size_t attn_ops_bytes(int B, int Hkv, int T, int d) {
+  return static_cast<size_t>(B) * Hkv * (T / kItemKeys) * kItemKeys * d * 2 * 2;
+}
+static size_t attn_ops_tail_bytes(int B, int Hkv, int d) {
+  return static_cast<size_t>(B) * Hkv * kItemKeys * d * 2 * 2;
 }
 
 template <int D, int G>
@@ -523,29 +461,28 @@ static hipError_t attn_mfma_t(const AttnArgs &a_in, hipStream_t st) {
   const int ntiles = (a_in.T + C::kQT - 1) / C::kQT;
   const int npairs = a_in.Hkv * a_in.B;
   const int nblk = (a_in.T + kItemKeys - 1) / kItemKeys;
-  // The chunk terms first (chunk-major, rows compacted per chunk): each
-  // row's chunk part into o, its chunk log-mass into the workspace after the
-  // value tiles.  Then the window band through the kernel below, which
-  // combines the two.  No query has an eligible chunk when T - W < S.
+  // Every block's K and V^T in operand order (and its largest |v|) first.
+  // Then the chunk terms (chunk-major, rows compacted per chunk): each row's
+  // chunk part into o, its chunk log-mass into the workspace.  Then the
+  // window band through the kernel above, which combines the two.  No query
+  // has an eligible chunk when T - W < S.
   const bool chunks = a_in.K > 0 && eligible_chunks_host(a_in.T - 1, a_in.W, kItemKeys) > 0;
-  uint8_t *ws_after_vt = static_cast<uint8_t *>(a_in.vt_ws) + attn_vt_bytes(a_in.B, a_in.Hkv, a_in.T, D);
-  float *lse = reinterpret_cast<float *>(ws_after_vt);
+  uint8_t *ws = static_cast<uint8_t *>(a_in.vt_ws);
+  float *lse = reinterpret_cast<float *>(ws);
   float *vmax = lse + static_cast<size_t>(a_in.B) * a_in.Hq * a_in.T;
-  uint16_t *ops = reinterpret_cast<uint16_t *>(ws_after_vt + attn_chunk_meta_bytes(a_in.B, a_in.Hq, a_in.Hkv, a_in.T));
-  vt_transpose_kernel<D><<<dim3(nblk, npairs), 256, 0, st>>>(static_cast<const uint16_t *>(a_in.v),
-                                                             static_cast<uint16_t *>(a_in.vt_ws),
-                                                             chunks && !attn_long_used(a_in.T, a_in.K) ? vmax : nullptr, a_in.T, nblk);
-  hipError_t e = hipGetLastError();
+  uint16_t *ops = reinterpret_cast<uint16_t *>(ws + attn_chunk_meta_bytes(a_in.B, a_in.Hq, a_in.Hkv, a_in.T));
+  uint16_t *ops_tail = reinterpret_cast<uint16_t *>(reinterpret_cast<uint8_t *>(ops) +
+                                                    attn_ops_bytes(a_in.B, a_in.Hkv, a_in.T, D));
+  uint8_t *ws_after_ops = reinterpret_cast<uint8_t *>(ops_tail) + attn_ops_tail_bytes(a_in.B, a_in.Hkv, D);
+  hipError_t e = launch_kv_operand_order(a_in, ops, ops_tail, chunks && !attn_long_used(a_in.T, a_in.K) ? vmax : nullptr, st);
   if (e != hipSuccess) return e;
   AttnArgs a = a_in;
   a.lse_c = nullptr;
   if (chunks) {
-    if (attn_long_used(a_in.T, a_in.K)) {
-      const size_t ops_bytes = static_cast<size_t>(npairs) * (a_in.T / kItemKeys) * kItemKeys * D * 2 * 2;
-      e = launch_attn_long(a_in, ops, lse, reinterpret_cast<uint8_t *>(ops) + ops_bytes, st);
-    } else {
+    if (attn_long_used(a_in.T, a_in.K))
+      e = launch_attn_long(a_in, ops, lse, ws_after_ops, st);
+    else
       e = launch_attn_chunks(a_in, ops, lse, vmax, nblk, st);
-    }
     if (e != hipSuccess) return e;
     a.lse_c = lse;
   }
@@ -554,7 +491,8 @@ static hipError_t attn_mfma_t(const AttnArgs &a_in, hipStream_t st) {
   // that the blocks its queries read stay in the shared memory-side cache
   const bool pair_fits_l2 = static_cast<size_t>(a.T) * D * 2 * 2 <= (size_t{4} << 20);
   const int xcd_map = (npairs % 8 == 0 && pair_fits_l2) ? 1 : 0;
-  attn_window_mfma_kernel<D, G, WAVES, TPW><<<dim3(ntiles * npairs), C::kThreads, 0, st>>>(a, ntiles, xcd_map, nblk);
+  attn_window_mfma_kernel<D, G, WAVES, TPW><<<dim3(ntiles * npairs), C::kThreads, 0, st>>>(a, ops, ops_tail, ntiles,
+                                                                                           xcd_map);
   return hipGetLastError();
 }
 
@@ -564,13 +502,11 @@ bool attn_mfma_supported(const AttnArgs &a) {
          a.S == kItemKeys && a.K <= 32 && a.T / a.S <= 8192;
 }
 
-// value tiles, then the chunk log-mass of every (b, query head, query) and
-// the largest |v| of every 64-key block, then every complete chunk's K and
-// V^T in operand order; for long sequences the chunk-major pass's lists and
-// partial results
+// the chunk log-mass of every (b, query head, query) and the largest |v| of
+// every 64-key block, then every block's K and V^T in operand order; for
+// long sequences the chunk-major pass's lists and partial results
 size_t attn_mfma_ws_bytes(int B, int Hq, int Hkv, int T, int d, int K) {
-  const size_t chunks = static_cast<size_t>(B) * Hkv * (T / kItemKeys);
-  return attn_vt_bytes(B, Hkv, T, d) + attn_chunk_meta_bytes(B, Hq, Hkv, T) + chunks * kItemKeys * d * 2 * 2 +
+  return attn_chunk_meta_bytes(B, Hq, Hkv, T) + attn_ops_bytes(B, Hkv, T, d) + attn_ops_tail_bytes(B, Hkv, d) +
          attn_long_ws_bytes(B, Hq, Hkv, T, d, K);
 }
 
