@@ -204,10 +204,89 @@ __device__ __forceinline__ void attend_tile(const bf16x8 (&qop)[D / 32], f32x4 (
   tile_pv<D>(acc, pb, vtb, lane8);
 }
 
+// The same for a wave's two tiles at once: every K and V^T operand is read
+// from LDS once and feeds both tiles' products (each accumulator sees the
+// same products in the same order as in attend_tile), halving the LDS reads
+// of the block, which the workgroups of a CU otherwise share at twice the
+// rate the matrix units consume them.
+template <int D>
+__device__ __forceinline__ void tile_scores2(const bf16x8 (&q0)[D / 32], const bf16x8 (&q1)[D / 32],
+                                             const uint16_t *ksb, int lane8, f32x4 (&s0)[4], f32x4 (&s1)[4]) {
+  constexpr int KS = D / 32;
+  uint4 u[2][4];
+  auto load_k = [&](uint4 (&dst)[4], int s) {  // K piece kt * KS + s
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) dst[kt] = *reinterpret_cast<const uint4 *>(ksb + (kt * KS + s) * 512 + lane8);
+  };
+#pragma unroll
+  for (int kt = 0; kt < 4; ++kt) {
+    s0[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    s1[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  load_k(u[0], 0);
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    if (s + 1 < KS) load_k(u[(s + 1) & 1], s + 1);
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) s0[kt] = mfma16(as_bf16x8(u[s & 1][kt]), q0[s], s0[kt]);
+#pragma unroll
+    for (int kt = 0; kt < 4; ++kt) s1[kt] = mfma16(as_bf16x8(u[s & 1][kt]), q1[s], s1[kt]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void tile_pv2(f32x4 (&acc0)[D / 16], f32x4 (&acc1)[D / 16], const bf16x8 (&p0)[2],
+                                         const bf16x8 (&p1)[2], const uint16_t *vtb, int lane8) {
+  constexpr int DT = D / 16;
+  uint4 v[2][2][2];
+  auto load_v = [&](uint4 (&dst)[2][2], int dt) {  // V^T piece 2 (dt + d2) + sl
+#pragma unroll
+    for (int d2 = 0; d2 < 2; ++d2)
+#pragma unroll
+      for (int sl = 0; sl < 2; ++sl)
+        dst[d2][sl] = *reinterpret_cast<const uint4 *>(vtb + (2 * (dt + d2) + sl) * 512 + lane8);
+  };
+  load_v(v[0], 0);
+#pragma unroll
+  for (int st2 = 0; st2 < DT / 2; ++st2) {
+    const int dt = 2 * st2;
+    if (st2 + 1 < DT / 2) load_v(v[(st2 + 1) & 1], dt + 2);
+#pragma unroll
+    for (int d2 = 0; d2 < 2; ++d2)
+#pragma unroll
+      for (int sl = 0; sl < 2; ++sl) acc0[dt + d2] = mfma16(as_bf16x8(v[st2 & 1][d2][sl]), p0[sl], acc0[dt + d2]);
+#pragma unroll
+    for (int d2 = 0; d2 < 2; ++d2)
+#pragma unroll
+      for (int sl = 0; sl < 2; ++sl) acc1[dt + d2] = mfma16(as_bf16x8(v[st2 & 1][d2][sl]), p1[sl], acc1[dt + d2]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+template <int D, bool MASKED>
+__device__ __forceinline__ void attend_two(RowState<D, 2> &R, const uint16_t *ksb, const uint16_t *vtb, int lane8,
+                                           const int (&lim)[2], float tau, float tl2e) {
+  f32x4 s0[4], s1[4];
+  tile_scores2<D>(R.qop[0], R.qop[1], ksb, lane8, s0, s1);
+  bf16x8 p0[2], p1[2];
+  const float sc0 = tile_softmax<MASKED>(s0, p0, R.m_row[0], R.l_row[0], lim[0], tau, tl2e);
+  const float sc1 = tile_softmax<MASKED>(s1, p1, R.m_row[1], R.l_row[1], lim[1], tau, tl2e);
+  rescale_acc<D>(R.acc[0], sc0);
+  rescale_acc<D>(R.acc[1], sc1);
+  tile_pv2<D>(R.acc[0], R.acc[1], p0, p1, vtb, lane8);
+}
+
 // Run the block for the wave's tiles that take part (bit t of `mask`).
 template <int D, int TPW, bool MASKED>
 __device__ __forceinline__ void run_item(int mask, RowState<D, TPW> &R, const uint16_t *ksb, const uint16_t *vtb,
                                          int lane8, const int (&lim)[TPW], float tau, float tl2e) {
+  if constexpr (TPW == 2) {
+    if (mask == 3) {
+      attend_two<D, MASKED>(R, ksb, vtb, lane8, lim, tau, tl2e);
+      return;
+    }
+  }
 #pragma unroll
   for (int t = 0; t < TPW; ++t)
     if ((mask >> t) & 1)
