@@ -232,7 +232,7 @@ size_t hils_prefill_workspace_bytes(const hils_config *cfg) {
   if (check_config(cfg) != HILS_OK) return 0;
   const int C = cfg->seq_len / cfg->chunk_size;
   // scoring uses the workspace first; the attention call then reuses it for
-  // the transposed value tiles of its MFMA path (bf16)
+  // the K/V operand-order copy and row statistics of its MFMA path (bf16)
   const size_t score = prefill_u_bytes(cfg) +
                        align_up(hils::score_mfma_ws_bytes(cfg->batch, cfg->seq_len, cfg->n_q_heads, C, cfg->qcal_rank)) +
                        kAlign;
