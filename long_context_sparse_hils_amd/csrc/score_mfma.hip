@@ -54,14 +54,13 @@ __device__ __forceinline__ void split_bf16(float x, uint16_t &hi, uint16_t &lo) 
 // so one W_down operand serves TT MFMAs: the vector-memory requests, not
 // HBM, bound this kernel, and W_down's share of them falls as 1 / TT.
 template <int NT, int TT>  // output tiles of 16 (RP / 16); token tiles per wave
-__global__ void __launch_bounds__(256, 4)
-qcal_u_mfma_kernel(const uint16_t *__restrict__ h, const uint16_t *__restrict__ w_down, uint16_t *__restrict__ u_hi,
-                   uint16_t *__restrict__ u_lo, int Ntok, int r, int Dh) {
+__device__ __forceinline__ void qcal_u_block(const uint16_t *__restrict__ h, const uint16_t *__restrict__ w_down,
+                                             uint16_t *__restrict__ u_hi, uint16_t *__restrict__ u_lo, int Ntok, int r,
+                                             int Dh, int bx, float (&part)[4][16 * TT][16 * NT + 1]) {
   constexpr int RP = 16 * NT;
-  __shared__ float part[4][16 * TT][RP + 1];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int ln = lane & 15, lg = lane >> 4;
-  const int tok0 = blockIdx.x * 16 * TT;
+  const int tok0 = bx * 16 * TT;
   const uint16_t *hrow[TT];
   bool tok_ok[TT];
 #pragma unroll
@@ -139,12 +138,17 @@ qcal_u_mfma_kernel(const uint16_t *__restrict__ h, const uint16_t *__restrict__ 
 // the 32 summaries in LDS.  Thread (chunk t / 8, a4 = t % 8) forms the
 // outputs a = 32 j + 4 a4 .. + 4 of its chunk.
 template <int D>
-__global__ void __launch_bounds__(256)
-qcal_m_kernel(const uint16_t *__restrict__ k_sum, const uint16_t *__restrict__ w_up, uint16_t *__restrict__ m_hi,
-              uint16_t *__restrict__ m_lo, int Hq, int C, int r, int RP) {
-  __shared__ float4 wu[D][16];  // [e][a / 4], zero for a >= r
-  __shared__ float kc[32][D + 1];
-  const int c0 = blockIdx.x * 32, h = blockIdx.y, b = blockIdx.z, t = threadIdx.x;
+struct QcalMSmem {
+  float4 wu[D][16];  // [e][a / 4], zero for a >= r
+  float kc[32][D + 1];
+};
+template <int D>
+__device__ __forceinline__ void qcal_m_block(const uint16_t *__restrict__ k_sum, const uint16_t *__restrict__ w_up,
+                                             uint16_t *__restrict__ m_hi, uint16_t *__restrict__ m_lo, int Hq, int C,
+                                             int r, int RP, int bx, int h, int b, QcalMSmem<D> &ms) {
+  float4 (&wu)[D][16] = ms.wu;
+  float (&kc)[32][D + 1] = ms.kc;
+  const int c0 = bx * 32, t = threadIdx.x;
   // The head's W_up slice (D x r, contiguous) and the 32 summaries
   // (32 x D, contiguous) are read with 16-byte loads, all issued before any
   // is used.
@@ -216,6 +220,28 @@ qcal_m_kernel(const uint16_t *__restrict__ k_sum, const uint16_t *__restrict__ w
         m_lo[o + 32 * j + 4 * a4 + q] = lo;
       }
     }
+  }
+}
+
+// Both Q-Cal products in one launch: workgroups [0, nub) form u, the rest m
+// (gmx chunk blocks x Hq x B).  The two are independent, so m's workgroups
+// run beside u's stream instead of after it.
+template <int NT, int TT, int D>
+__global__ void __launch_bounds__(256, 3)
+qcal_kernel(const uint16_t *__restrict__ h, const uint16_t *__restrict__ w_down, uint16_t *__restrict__ u_hi,
+            uint16_t *__restrict__ u_lo, int Ntok, int Dh, const uint16_t *__restrict__ k_sum,
+            const uint16_t *__restrict__ w_up, uint16_t *__restrict__ m_hi, uint16_t *__restrict__ m_lo, int Hq, int C,
+            int r, int nub, int gmx) {
+  __shared__ union {
+    float part[4][16 * TT][16 * NT + 1];
+    QcalMSmem<D> m;
+  } sm;
+  const int bx = blockIdx.x;
+  if (bx < nub) {
+    qcal_u_block<NT, TT>(h, w_down, u_hi, u_lo, Ntok, r, Dh, bx, sm.part);
+  } else {
+    const int y = bx - nub;
+    qcal_m_block<D>(k_sum, w_up, m_hi, m_lo, Hq, C, r, 16 * NT, y % gmx, (y / gmx) % Hq, y / (gmx * Hq), sm.m);
   }
 }
 
@@ -1000,22 +1026,22 @@ hipError_t launch_score_mfma(const ScoreArgs &a, hipStream_t st) {
   if (a.r > 0) {
     const int ntok = a.B * a.T;
     const uint16_t *hp = static_cast<const uint16_t *>(a.h), *wd = static_cast<const uint16_t *>(a.w_down);
-    if (RP == 32)
-      qcal_u_mfma_kernel<2, 2><<<(ntok + 31) / 32, 256, 0, st>>>(hp, wd, u_hi, u_lo, ntok, a.r, a.Dh);
-    else
-      qcal_u_mfma_kernel<4, 1><<<(ntok + 15) / 16, 256, 0, st>>>(hp, wd, u_hi, u_lo, ntok, a.r, a.Dh);
+    const uint16_t *ks = static_cast<const uint16_t *>(a.k_sum), *wu = static_cast<const uint16_t *>(a.w_up);
+    const int gmx = (a.C + 31) / 32;  // (no complete chunk: nothing to project)
+    const int nm = gmx * a.Hq * a.B;
+#define HILS_QCAL(NT, TT, DD)                                                                                      \
+  {                                                                                                               \
+    const int nub = (ntok + 16 * (TT) - 1) / (16 * (TT));                                                         \
+    qcal_kernel<NT, TT, DD><<<nub + nm, 256, 0, st>>>(hp, wd, u_hi, u_lo, ntok, a.Dh, ks, wu, m_hi, m_lo, a.Hq, \
+                                                      a.C, a.r, nub, gmx);                                        \
+  }
+    if (RP == 32) {
+      if (a.d == 128) HILS_QCAL(2, 2, 128) else HILS_QCAL(2, 2, 64)
+    } else {
+      if (a.d == 128) HILS_QCAL(4, 1, 128) else HILS_QCAL(4, 1, 64)
+    }
+#undef HILS_QCAL
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    dim3 gm((a.C + 31) / 32, a.Hq, a.B);
-    if (a.C == 0) {
-      // no complete chunk: nothing to project
-    } else if (a.d == 128)
-      qcal_m_kernel<128><<<gm, 256, 0, st>>>(static_cast<const uint16_t *>(a.k_sum), static_cast<const uint16_t *>(a.w_up),
-                                              m_hi, m_lo, a.Hq, a.C, a.r, RP);
-    else
-      qcal_m_kernel<64><<<gm, 256, 0, st>>>(static_cast<const uint16_t *>(a.k_sum), static_cast<const uint16_t *>(a.w_up),
-                                             m_hi, m_lo, a.Hq, a.C, a.r, RP);
-    e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (a.C > kScoreMaxC) {  // long sequences: the streaming selection
